@@ -1,0 +1,145 @@
+"""The five synthetic decode workloads and their seeded input generators.
+
+This module draws random numbers and nothing else: it holds no quantization or
+attention arithmetic, so both the HIP path and the CPU oracle can take their inputs
+from it without sharing any of the method.
+
+Shapes follow the workloads on the pages: Llama-2-7B-shaped heads (32 heads of 128
+channels, 32 layers) as in page "DeepSeek-R1推理延迟骤降41.8%？…" §2.1; batch 8 at
+context 8192 as in page "第一章：DeepSeek R1推理模型性能跃迁全景概览" chapter 1's deployment
+table; batch 16 at 32K context as in that page's §2.3 table.
+
+Recipe (every draw from numpy PCG64 seeded by SeedSequence([SEED, workload index,
+layer, stream id, sequence])):
+  * normal_outliers: x ~ N(0, 1) drawn in binary32; a Binomial(n, 0.001) number of
+    positions, uniform with replacement over the n elements, is multiplied by 20
+    (so about 0.1% of entries are outliers); then rounded to fp16 (nearest-even).
+  * normal(mu): x ~ N(mu, 1) in binary32, rounded to fp16.
+  * student_t3_half: x = 0.5 * Z / sqrt(2G/3), Z ~ N(0,1), G ~ Gamma(1.5, 1)
+    (2G ~ chi-square with 3 degrees of freedom), binary32, rounded to fp16.
+  * the query is N(0, 1) for every workload, one token per sequence and head.
+  * ragged lengths: integers uniform on [1024, 8192] inclusive, one per sequence,
+    shared by all layers.
+Streams: 0 = prefill K, 1 = prefill V, 2 = query, 3 = lengths, 4 = appended K,
+5 = appended V.
+"""
+import dataclasses
+
+import numpy as np
+
+SEED = 20261202
+BLOCK = 64
+INT4_SYM = 0
+UINT8_ASYM = 1
+
+STREAM_K, STREAM_V, STREAM_Q, STREAM_LENS, STREAM_K_APPEND, STREAM_V_APPEND = range(6)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    batch: int
+    heads: int
+    head_dim: int
+    context: int            # prefill length (upper bound for ragged lengths)
+    scheme: int
+    k_dist: str
+    v_dist: str
+    layers: int = 1
+    decode_steps: int = 0   # tokens appended per sequence, one per decode step
+    ragged: tuple = None    # (lo, hi) inclusive range of per-sequence lengths
+
+    @property
+    def max_len(self):
+        return self.context + self.decode_steps
+
+    @property
+    def max_blocks(self):
+        return (self.max_len + BLOCK - 1) // BLOCK
+
+
+WORKLOADS = [
+    Workload(0, "tiny_b1_h2_d64_ctx256_int4", 1, 2, 64, 256, INT4_SYM,
+             "normal_outliers", "normal_outliers"),
+    Workload(1, "llama7b_b8_h32_d128_ctx8k_int4", 8, 32, 128, 8192, INT4_SYM,
+             "normal_outliers", "normal_outliers"),
+    Workload(2, "llama7b_b8_h32_d128_ctx8k_uint8", 8, 32, 128, 8192, UINT8_ASYM,
+             "normal0", "normal0.5"),
+    Workload(3, "long_b16_h32_d128_ctx32k_append64_int4", 16, 32, 128, 32768, INT4_SYM,
+             "normal_outliers", "normal_outliers", decode_steps=64),
+    Workload(4, "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4", 8, 32, 128, 8192,
+             INT4_SYM, "student_t3_half", "student_t3_half", layers=32,
+             ragged=(1024, 8192)),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def rng(workload, layer, stream, seq):
+    ss = np.random.SeedSequence([SEED, workload.index, layer, stream, seq])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def draw(g, dist, shape):
+    """float16 samples of `dist` with the given shape from generator g."""
+    n = int(np.prod(shape))
+    if dist == "normal_outliers":
+        x = g.standard_normal(n, dtype=np.float32)
+        k = int(g.binomial(n, 0.001)) if n else 0
+        if k:
+            idx = g.integers(0, n, size=k)
+            x[idx] *= np.float32(20.0)
+    elif dist.startswith("normal"):
+        mu = np.float32(float(dist[len("normal"):] or 0.0))
+        x = g.standard_normal(n, dtype=np.float32)
+        if mu != 0:
+            x += mu
+    elif dist == "student_t3_half":
+        z = g.standard_normal(n, dtype=np.float32)
+        gam = g.standard_gamma(1.5, n, dtype=np.float32)
+        x = np.float32(0.5) * z / np.sqrt(np.float32(2.0 / 3.0) * gam)
+    else:
+        raise ValueError(dist)
+    return x.astype(np.float16).reshape(shape)
+
+
+def prefill_kv(w, layer, seq, which, n_tokens=None):
+    """float16 [n_tokens][H][D] prefill K (which=0) or V (which=1) of one sequence."""
+    n = w.context if n_tokens is None else n_tokens
+    dist = w.k_dist if which == 0 else w.v_dist
+    stream = STREAM_K if which == 0 else STREAM_V
+    return draw(rng(w, layer, stream, seq), dist, (n, w.heads, w.head_dim))
+
+
+def appended_kv(w, layer, seq, which, n_steps=None):
+    """float16 [n_steps][H][D]: the tokens appended one per decode step."""
+    n = w.decode_steps if n_steps is None else n_steps
+    dist = w.k_dist if which == 0 else w.v_dist
+    stream = STREAM_K_APPEND if which == 0 else STREAM_V_APPEND
+    return draw(rng(w, layer, stream, seq), dist, (n, w.heads, w.head_dim))
+
+
+def query(w, layer, step=0):
+    """float16 [B][H][D] query for one decode step of one layer."""
+    g = rng(w, layer, STREAM_Q, step)
+    return draw(g, "normal0", (w.batch, w.heads, w.head_dim))
+
+
+def lengths(w):
+    """int32 [B] context lengths (ragged workloads draw them; others use `context`)."""
+    if w.ragged is None:
+        return np.full(w.batch, w.context, dtype=np.int32)
+    lo, hi = w.ragged
+    g = rng(w, 0, STREAM_LENS, 0)
+    return g.integers(lo, hi + 1, size=w.batch).astype(np.int32)
+
+
+def prefill_batch(w, layer, which, n_tokens=None, seqs=None):
+    """float16 [B][S][H][D] prefill tensor for all (or the listed) sequences."""
+    seqs = range(w.batch) if seqs is None else seqs
+    return np.stack([prefill_kv(w, layer, s, which, n_tokens) for s in seqs])
+
+
+def softmax_scale(w):
+    """binary32 1/sqrt(head_dim), the query scaling the workloads use."""
+    return float(np.float32(1.0) / np.sqrt(np.float32(w.head_dim)))

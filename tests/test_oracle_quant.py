@@ -1,0 +1,196 @@
+"""Pins of the oracle's quantizer against values the pages and arithmetic fix.
+
+The quantizer is an encoding, so the oracle must reproduce it bit for bit: these tests
+hold it to hand-worked examples (tests/golden/quant_examples.txt), to the fp16 format
+definition, to closed-form invariants and to the round-trip error bound.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_block_amd import workloads as wl
+from golden_io import read_sections
+
+INT4, UINT8 = oracle.INT4_SYM, oracle.UINT8_ASYM
+
+
+def f32bits(x):
+    return int(np.array(x, dtype=np.float32).view(np.uint32))
+
+
+def unpack_int4(row_bytes):
+    """Signed int4 codes from packed bytes: channel 2k = low nibble of byte k."""
+    b = np.asarray(row_bytes, dtype=np.uint8)
+    lo = (b & 0x0F).astype(np.int64)
+    hi = (b >> 4).astype(np.int64)
+    out = np.empty(2 * b.size, np.int64)
+    out[0::2] = np.where(lo >= 8, lo - 16, lo)
+    out[1::2] = np.where(hi >= 8, hi - 16, hi)
+    return out
+
+
+def single_block(values, D=64, fill=None, ntok=1):
+    """float16 [1][64][1][D]: token 0 carries the example, other tokens zero."""
+    x = np.zeros((1, 64, 1, D), np.float16)
+    if fill is not None:
+        x[0, :ntok, 0, :] = np.float16(fill)
+    else:
+        x[0, 0, 0, :len(values)] = np.asarray(values, np.float16)
+    return x
+
+
+def test_fp16_decoder_matches_format_on_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.half_to_float(bits)
+    want = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("name", list(read_sections("quant_examples.txt")))
+def test_golden_example(name):
+    ex = read_sections("quant_examples.txt")[name]
+    scheme = INT4 if ex["scheme"] == "int4" else UINT8
+    fill = float(ex["fill"]) if "fill" in ex else None
+    xs = [float(t) for t in ex["x"].split()] if "x" in ex else []
+    x = single_block(xs, fill=fill)
+    c = oracle.quantize_cache(scheme, x, x.copy(), np.array([1], np.int32), 1)
+    for which in ("k", "v"):
+        assert f32bits(c[which + "_scale"][0, 0, 0]) == int(ex["scale"], 16), which
+        assert f32bits(c[which + "_zero"][0, 0, 0]) == int(ex["zero"], 16), which
+        row = c[which + "_codes"][0, 0, 0, 0]
+        codes = unpack_int4(row) if scheme == INT4 else row.astype(np.int64)
+        want = [int(t) for t in ex["codes"].split()]
+        if fill is not None:
+            assert (codes == want[0]).all()
+        else:
+            assert list(codes[:len(want)]) == want
+            # channels holding 0.0 take the code of zero: 0 (int4) or zp (uint8)
+            zero_code = 0 if scheme == INT4 else int(c[which + "_zero"][0, 0, 0])
+            assert (codes[len(want):] == zero_code).all()
+        if "packed" in ex:
+            packed = [int(t, 16) for t in ex["packed"].split()]
+            assert list(row[:len(packed)]) == packed
+        # tokens 1..63 are padding: code byte 0
+        assert not c[which + "_codes"][0, 0, 0, 1:].any()
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+def test_padding_and_untouched_blocks(scheme):
+    rs = np.random.default_rng(1)
+    B, S, H, D, MB = 2, 200, 3, 64, 5
+    x = rs.standard_normal((B, S, H, D)).astype(np.float16)
+    lens = np.array([130, 64], np.int32)
+    c = oracle.empty_cache(scheme, B, H, D, MB)
+    for k in ("k_codes", "v_codes"):
+        c[k][:] = 0xAA
+    for k in ("k_scale", "v_scale", "k_zero", "v_zero"):
+        c[k][:] = -7.0
+    oracle.quantize_cache(scheme, x, x, lens, MB, cache=c)
+    # row b=0: blocks 0,1 full, block 2 holds 2 tokens; blocks 3,4 untouched
+    assert not c["k_codes"][0, :, 2, 2:].any()
+    assert (c["k_codes"][0, :, 3:] == 0xAA).all() and (c["k_scale"][0, :, 3:] == -7).all()
+    assert (c["k_codes"][1, :, 1:] == 0xAA).all()
+    assert (c["k_scale"][0, :, :3] > 0).all()
+
+
+def _blocks(x, lens):
+    """Yields (b, h, j, block values float32 [ntok][D])."""
+    B, S, H, D = x.shape
+    for b in range(B):
+        for h in range(H):
+            for j in range((lens[b] + 63) // 64):
+                t1 = min(lens[b], 64 * j + 64)
+                yield b, h, j, x[b, 64 * j:t1, h, :].astype(np.float32)
+
+
+DISTS = ["normal_outliers", "normal0.5", "student_t3_half"]
+
+
+@pytest.mark.parametrize("dist", DISTS)
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+def test_roundtrip_bound_and_invariants(scheme, dist):
+    """|x - dequant(code(x))| <= s/2 for every element (the clamp never bites for these
+    scales), the scale is the stated binary32 quotient, and the extreme elements map to
+    the extreme codes."""
+    w = wl.WORKLOADS[1]
+    g = wl.rng(w, 99, 0, 0)
+    B, S, H, D = 2, 300, 4, 128
+    x = wl.draw(g, dist, (B, S, H, D))
+    lens = np.array([300, 171], np.int32)
+    c = oracle.quantize_cache(scheme, x, x, lens, 5)
+    for b, h, j, blk in _blocks(x, lens):
+        s = c["k_scale"][b, h, j]
+        kh, _ = oracle.dequantize(c, b, h, lens[b])
+        err = np.abs(blk.astype(np.float64) - kh[64 * j:64 * j + blk.shape[0]])
+        assert err.max() <= 0.5 * float(s) * (1 + 1e-5)
+        if scheme == INT4:
+            a = np.abs(blk).max()
+            assert f32bits(s) == f32bits(np.float32(a) / np.float32(7.5))
+            codes = unpack_int4(c["k_codes"][b, h, j, :blk.shape[0]].ravel())
+            codes = codes.reshape(blk.shape)
+            assert (codes[blk == a] == 7).all()
+            assert set(codes[blk == -a].tolist()) <= {-7, -8}
+            assert codes.min() >= -8 and codes.max() <= 7
+        else:
+            codes = c["k_codes"][b, h, j, :blk.shape[0]].astype(np.int64)
+            mn, mx = blk.min(), blk.max()
+            assert f32bits(s) == f32bits(np.float32(mx - mn) / np.float32(255))
+            assert (codes[blk == mn] == 0).all()
+            assert set(codes[blk == mx].tolist()) <= {254, 255}
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+def test_token_permutation_within_block(scheme):
+    rs = np.random.default_rng(5)
+    x = rs.standard_normal((1, 64, 1, 64)).astype(np.float16)
+    perm = rs.permutation(64)
+    xp = x[:, perm].copy()
+    one = np.array([64], np.int32)
+    c1 = oracle.quantize_cache(scheme, x, x, one, 1)
+    c2 = oracle.quantize_cache(scheme, xp, xp, one, 1)
+    assert c1["k_scale"][0, 0, 0] == c2["k_scale"][0, 0, 0]
+    assert c1["k_zero"][0, 0, 0] == c2["k_zero"][0, 0, 0]
+    assert np.array_equal(c1["k_codes"][0, 0, 0][perm], c2["k_codes"][0, 0, 0])
+
+
+def test_int4_matches_listing_expression_in_torch():
+    """The listing's own expression (scale = |blk|.max()/7.5, round, clamp(-8,7)),
+    evaluated by torch on CPU in binary32 with one block per (sequence, head) row."""
+    torch = pytest.importorskip("torch")
+    w = wl.WORKLOADS[0]
+    x = wl.prefill_batch(w, 0, 0)  # [1][256][2][64]
+    lens = wl.lengths(w)
+    c = oracle.quantize_cache(INT4, x, x, lens, w.max_blocks)
+    xt = torch.from_numpy(x.astype(np.float32))
+    for h in range(w.heads):
+        for j in range(4):
+            blk = xt[0, 64 * j:64 * j + 64, h, :]
+            scale = blk.abs().max() / 7.5
+            q = torch.round(blk / scale).clamp(-8, 7).to(torch.int64).numpy()
+            got = unpack_int4(c["k_codes"][0, h, j].ravel()).reshape(64, 64)
+            assert np.array_equal(got, q)
+            assert f32bits(c["k_scale"][0, h, j]) == f32bits(scale.numpy())
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+def test_append_is_requantized_tail(scheme):
+    """Appending token by token (oracle_append) ends in the same cache as quantizing the
+    whole history at once, at every length crossed (0->1, 63->64, 64->65, ...)."""
+    w = wl.WORKLOADS[0]
+    B, H, D = 2, 2, 64
+    S = 140
+    g = wl.rng(w, 7, 0, 0)
+    k = wl.draw(g, "normal_outliers", (B, S, H, D))
+    v = wl.draw(g, "normal0.5", (B, S, H, D))
+    MB = 3
+    start = np.array([0, 61], np.int32)
+    c = oracle.quantize_cache(scheme, k, v, start, MB)
+    lens = start.copy()
+    while lens.max() < S:
+        lens = np.minimum(lens + 1, S)
+        oracle.append(c, k, v, lens)
+        ref = oracle.quantize_cache(scheme, k, v, lens, MB)
+        for key in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
+            assert np.array_equal(c[key], ref[key]), (key, lens)
