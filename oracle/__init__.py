@@ -142,7 +142,7 @@ def attention(cache, q, lens, sm_scale, rows=None):
 
 def dequantize(cache, b, h, length):
     """Dequantized K^ and V^ (float64 [length][D]) of row (b, h), straight from the
-    cache layout: int4 c*s with 4-bit two's-complement nibbles (low nibble = even
+    cache layout: int4 (nibble - 8)*s with offset-binary nibbles (low nibble = even
     channel), uint8 (c - zp)*s."""
     c = cache
     D = c["D"]
@@ -152,11 +152,9 @@ def dequantize(cache, b, h, length):
         codes = c[which + "_codes"][b, h, :nb].reshape(nb * BLOCK, -1)[:length]
         s = np.repeat(c[which + "_scale"][b, h, :nb].astype(np.float64), BLOCK)[:length]
         if c["scheme"] == INT4_SYM:
-            lo = (codes & 0x0F).astype(np.int64)
-            hi = (codes >> 4).astype(np.int64)
             vals = np.empty((length, D), np.int64)
-            vals[:, 0::2] = np.where(lo >= 8, lo - 16, lo)
-            vals[:, 1::2] = np.where(hi >= 8, hi - 16, hi)
+            vals[:, 0::2] = (codes & 0x0F).astype(np.int64) - 8
+            vals[:, 1::2] = (codes >> 4).astype(np.int64) - 8
             out.append(vals.astype(np.float64) * s[:, None])
         else:
             z = np.repeat(c[which + "_zero"][b, h, :nb].astype(np.float64), BLOCK)[:length]

@@ -28,9 +28,9 @@
 //     zero-point added after rounding; -0.0 zero-points are stored as +0.0;
 //   * degenerate blocks: int4 absmax 0 -> s = 0, codes 0; uint8 with max == min == c:
 //     c == 0 -> s = 0, zp = 0, codes 0; otherwise the range is widened to include 0;
-//   * tokens at or past the sequence length inside the open tail block get code 0;
-//   * int4 packing: byte k of a token's row holds channel 2k in bits 0-3 and
-//     channel 2k+1 in bits 4-7, each as a 4-bit two's-complement value;
+//   * int4 packing: each code c is stored as the offset-binary nibble c + 8 (0..15);
+//     byte k of a token's row holds channel 2k in bits 0-3 and channel 2k+1 in bits 4-7;
+//   * bytes of tokens at or past the length inside the last block are 0;
 //   * cache layout: codes [B][H][max_blocks][64][D/2 or D] bytes, scales and zero
 //     points [B][H][max_blocks] binary32;
 //   * a row of length 0 attends to nothing; its output is defined as all zeros.
@@ -89,20 +89,21 @@ void quantize_block_int4(RowIn x, int first, int ntok, int D, uint8_t* codes,
     }
   // step 2: scale = absmax / 7.5 (one binary32 division)
   const float s = (a == 0.0f) ? 0.0f : a / 7.5f;
-  // step 3: code = clamp(round(x / s), -8, 7), packed two per byte
+  // step 3: code = clamp(round(x / s), -8, 7) (0 when s = 0), stored as c + 8, two per byte
   std::memset(codes, 0, static_cast<size_t>(kBlock) * (D / 2));
-  if (s != 0.0f) {
-    for (int t = 0; t < ntok; ++t)
-      for (int d = 0; d < D; ++d) {
+  for (int t = 0; t < ntok; ++t)
+    for (int d = 0; d < D; ++d) {
+      int c = 0;
+      if (s != 0.0f) {
         const float q = half_to_f32(x.p[(first + t) * x.st + d]) / s;
-        int c = static_cast<int>(round_half_even(q));
+        c = static_cast<int>(round_half_even(q));
         if (c < -8) c = -8;
         if (c > 7) c = 7;
-        const uint8_t nib = static_cast<uint8_t>(c) & 0x0F;
-        uint8_t& byte = codes[t * (D / 2) + d / 2];
-        byte |= (d % 2 == 0) ? nib : static_cast<uint8_t>(nib << 4);
       }
-  }
+      const uint8_t nib = static_cast<uint8_t>(c + 8);
+      uint8_t& byte = codes[t * (D / 2) + d / 2];
+      byte |= (d % 2 == 0) ? nib : static_cast<uint8_t>(nib << 4);
+    }
   *scale = s;
   *zero = 0.0f;
 }
@@ -162,9 +163,8 @@ double dequant(int scheme, int D, int max_blocks, const uint8_t* codes, const fl
   const uint8_t* row = codes + (blk * kBlock + tt) * static_cast<int64_t>(row_bytes(scheme, D));
   const double s = static_cast<double>(scale[blk]);
   if (scheme == 0) {
-    int nib = (d % 2 == 0) ? (row[d / 2] & 0x0F) : (row[d / 2] >> 4);
-    if (nib >= 8) nib -= 16;  // 4-bit two's complement
-    return static_cast<double>(nib) * s;
+    const int nib = (d % 2 == 0) ? (row[d / 2] & 0x0F) : (row[d / 2] >> 4);
+    return static_cast<double>(nib - 8) * s;  // offset-binary nibble
   }
   return (static_cast<double>(row[d]) - static_cast<double>(zero[blk])) * s;
 }

@@ -19,13 +19,12 @@ def f32bits(x):
 
 
 def unpack_int4(row_bytes):
-    """Signed int4 codes from packed bytes: channel 2k = low nibble of byte k."""
+    """Signed int4 codes from packed bytes: channel 2k = low nibble of byte k, each
+    nibble the offset-binary value code + 8."""
     b = np.asarray(row_bytes, dtype=np.uint8)
-    lo = (b & 0x0F).astype(np.int64)
-    hi = (b >> 4).astype(np.int64)
     out = np.empty(2 * b.size, np.int64)
-    out[0::2] = np.where(lo >= 8, lo - 16, lo)
-    out[1::2] = np.where(hi >= 8, hi - 16, hi)
+    out[0::2] = (b & 0x0F).astype(np.int64) - 8
+    out[1::2] = (b >> 4).astype(np.int64) - 8
     return out
 
 
