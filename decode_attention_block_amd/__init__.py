@@ -1,0 +1,213 @@
+"""decode_attention_block_amd — block-quantized KV cache and single-token decode
+attention for AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of libkvq.so (include/kvq.h): the functions here carry
+the same names as the library's entry points and only marshal arguments (tensor data
+pointers, strides, the current HIP stream). Every step of the computation runs in the
+library's HIP kernels; there is no CPU fallback, and a missing or unloadable library
+raises. PyTorch provides device memory and streams.
+"""
+import ctypes
+import os
+
+from . import build as _build
+
+INT4_SYM = 0
+UINT8_ASYM = 1
+BLOCK_TOKENS = 64
+
+STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_ENOTSUP", -3: "KVQ_ECAPACITY",
+          -4: "KVQ_EALIGN", -5: "KVQ_EWORKSPACE", -6: "KVQ_EHIP"}
+
+EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan",
+           "decode_attn_workspace_bytes", "decode_attn_qkv", "decode_attn_split",
+           "decode_attn_combine", "kvq_strerror", "kvq_version"]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({kvq_strerror(status)})")
+
+
+class kvq_cache(ctypes.Structure):
+    """Mirror of struct kvq_cache in include/kvq.h."""
+    _fields_ = [("scheme", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32),
+                ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("k_zero", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+                ("k_tail", ctypes.c_void_p), ("v_tail", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib_path():
+    return _build.LIB
+
+
+def load_library():
+    """Loads libkvq.so, building it first only if no built library exists."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    C = ctypes.POINTER(kvq_cache)
+    sig = {
+        "kv_quantize_blocks": ([C, P, P, i64, i64, i64, i32, P], ctypes.c_int),
+        "kv_append": ([C, P, P, i32, P], ctypes.c_int),
+        "decode_attn_plan": ([C, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
+                             ctypes.c_int),
+        "decode_attn_workspace_bytes": ([C, i32, i32], sz),
+        "decode_attn_qkv": ([C, P, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
+        "decode_attn_split": ([C, P, ctypes.c_float, P, sz, i32, i32, P], ctypes.c_int),
+        "decode_attn_combine": ([C, P, P, sz, i32, i32, P], ctypes.c_int),
+        "kvq_strerror": ([ctypes.c_int], ctypes.c_char_p),
+        "kvq_version": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise KvqError(rc, where)
+
+
+def _desc(cache):
+    return ctypes.byref(cache.desc if isinstance(cache, KVCache) else cache)
+
+
+def kvq_strerror(status):
+    return load_library().kvq_strerror(status).decode()
+
+
+def kvq_version():
+    return load_library().kvq_version()
+
+
+def kv_quantize_blocks(cache, k, v, max_len, stream=None):
+    """k, v: fp16 CUDA tensors [B][S][H][D] (any strides, channels contiguous)."""
+    if k.dim() != 4 or tuple(k.stride()) != tuple(v.stride()) or k.shape != v.shape:
+        raise ValueError("k and v must be 4-D [B][S][H][D] tensors with equal strides")
+    if k.stride(3) != 1:
+        raise ValueError("channels must be contiguous")
+    sb, st, sh = k.stride(0), k.stride(1), k.stride(2)
+    rc = load_library().kv_quantize_blocks(_desc(cache), _ptr(k), _ptr(v), sb, st, sh,
+                                           int(max_len), _stream(stream))
+    _check(rc, "kv_quantize_blocks")
+
+
+def kv_append(cache, k_new, v_new, max_len_after, stream=None):
+    """k_new, v_new: fp16 CUDA tensors [B][H][D] contiguous."""
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("k_new and v_new must be contiguous [B][H][D]")
+    rc = load_library().kv_append(_desc(cache), _ptr(k_new), _ptr(v_new), int(max_len_after),
+                                  _stream(stream))
+    _check(rc, "kv_append")
+
+
+def decode_attn_plan(cache, max_len, blocks_per_split=0):
+    bps, ns = ctypes.c_int32(), ctypes.c_int32()
+    rc = load_library().decode_attn_plan(_desc(cache), int(max_len), int(blocks_per_split),
+                                         ctypes.byref(bps), ctypes.byref(ns))
+    _check(rc, "decode_attn_plan")
+    return bps.value, ns.value
+
+
+def decode_attn_workspace_bytes(cache, max_len, blocks_per_split=0):
+    return load_library().decode_attn_workspace_bytes(_desc(cache), int(max_len),
+                                                      int(blocks_per_split))
+
+
+def decode_attn_qkv(cache, q, softmax_scale, out, workspace, max_len, blocks_per_split=0,
+                    stream=None):
+    """q, out: fp16 CUDA tensors [B][H][D] contiguous; workspace: CUDA tensor of at least
+    decode_attn_workspace_bytes(...) bytes."""
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B][H][D]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().decode_attn_qkv(_desc(cache), _ptr(q), float(softmax_scale), _ptr(out),
+                                        _ptr(workspace), ws_bytes, int(max_len),
+                                        int(blocks_per_split), _stream(stream))
+    _check(rc, "decode_attn_qkv")
+
+
+def decode_attn_split(cache, q, softmax_scale, workspace, max_len, blocks_per_split=0,
+                      stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().decode_attn_split(_desc(cache), _ptr(q), float(softmax_scale),
+                                          _ptr(workspace), ws_bytes, int(max_len),
+                                          int(blocks_per_split), _stream(stream))
+    _check(rc, "decode_attn_split")
+
+
+def decode_attn_combine(cache, out, workspace, max_len, blocks_per_split=0, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().decode_attn_combine(_desc(cache), _ptr(out), _ptr(workspace), ws_bytes,
+                                            int(max_len), int(blocks_per_split),
+                                            _stream(stream))
+    _check(rc, "decode_attn_combine")
+
+
+class KVCache:
+    """Device buffers of one quantized cache, allocated with torch, plus the C
+    descriptor pointing at them. Code buffers start zeroed."""
+
+    def __init__(self, scheme, batch, heads, head_dim, max_blocks, device="cuda",
+                 with_tail=True, with_zero=None):
+        import torch
+        self.scheme, self.batch, self.heads = scheme, batch, heads
+        self.head_dim, self.max_blocks = head_dim, max_blocks
+        rb = head_dim // 2 if scheme == INT4_SYM else head_dim
+        shape = (batch, heads, max_blocks, BLOCK_TOKENS, rb)
+        self.k_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
+        self.k_scale = torch.zeros((batch, heads, max_blocks), dtype=torch.float32, device=device)
+        self.v_scale = torch.zeros_like(self.k_scale)
+        if with_zero is None:
+            with_zero = True
+        self.k_zero = torch.zeros_like(self.k_scale) if with_zero else None
+        self.v_zero = torch.zeros_like(self.k_scale) if with_zero else None
+        tshape = (batch, heads, BLOCK_TOKENS, head_dim)
+        self.k_tail = torch.zeros(tshape, dtype=torch.float16, device=device) if with_tail else None
+        self.v_tail = torch.zeros(tshape, dtype=torch.float16, device=device) if with_tail else None
+        self.seq_lens = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.desc = kvq_cache(scheme, batch, heads, head_dim, max_blocks,
+                              _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale),
+                              _ptr(self.v_scale), _ptr(self.k_zero), _ptr(self.v_zero),
+                              _ptr(self.k_tail), _ptr(self.v_tail), _ptr(self.seq_lens))
+
+    @property
+    def capacity(self):
+        return self.max_blocks * BLOCK_TOKENS
+
+    def host_arrays(self):
+        """The cache buffers copied to numpy, keyed like the oracle's cache dicts."""
+        out = {"scheme": self.scheme, "B": self.batch, "H": self.heads, "D": self.head_dim,
+               "max_blocks": self.max_blocks}
+        for key in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
+            t = getattr(self, key)
+            out[key] = None if t is None else t.cpu().numpy()
+        return out

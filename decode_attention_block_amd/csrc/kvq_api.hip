@@ -1,0 +1,254 @@
+// kvq_api.hip — the C ABI of libkvq (declared in include/kvq.h): argument validation,
+// the split plan and kernel launches. No allocation, no state between calls.
+#include <stdint.h>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+constexpr int kBlockTokens = KVQ_BLOCK_TOKENS;
+constexpr int kSplitWavesHost = 4;      // waves per split workgroup (kvq_attn.hip)
+constexpr int64_t kTargetSplitGroups = 1024;  // workgroups the automatic plan aims for
+constexpr int kMaxAutoBlocksPerSplit = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_cache(const kvq_cache* c) {
+  if (!c) return KVQ_EINVAL;
+  if (c->scheme != KVQ_INT4_SYM && c->scheme != KVQ_UINT8_ASYM) return KVQ_EINVAL;
+  if (c->batch <= 0 || c->heads <= 0 || c->max_blocks <= 0) return KVQ_EINVAL;
+  if (c->batch > 32767 || c->heads > 65535) return KVQ_EINVAL;  // launch-grid limits
+  if (static_cast<int64_t>(c->max_blocks) * kBlockTokens > INT32_MAX) return KVQ_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ENOTSUP;
+  if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale || !c->seq_lens)
+    return KVQ_EINVAL;
+  if (c->scheme == KVQ_UINT8_ASYM && (!c->k_zero || !c->v_zero)) return KVQ_EINVAL;
+  if (!aligned16(c->k_codes) || !aligned16(c->v_codes)) return KVQ_EALIGN;
+  if ((c->k_tail && !aligned16(c->k_tail)) || (c->v_tail && !aligned16(c->v_tail)))
+    return KVQ_EALIGN;
+  return KVQ_OK;
+}
+
+int check_len(const kvq_cache* c, int32_t max_len) {
+  if (max_len < 0) return KVQ_EINVAL;
+  if (static_cast<int64_t>(max_len) > static_cast<int64_t>(c->max_blocks) * kBlockTokens)
+    return KVQ_ECAPACITY;
+  return KVQ_OK;
+}
+
+int n_blocks_for(int32_t len) { return (len + kBlockTokens - 1) / kBlockTokens; }
+
+// Blocks per split when the caller leaves it to the library: enough splits per row
+// that the launch has about kTargetSplitGroups workgroups, each split a whole number
+// of blocks per wave, at most kMaxAutoBlocksPerSplit blocks.
+int auto_blocks_per_split(const kvq_cache* c, int nb) {
+  const int64_t rows = static_cast<int64_t>(c->batch) * c->heads;
+  int64_t splits = (kTargetSplitGroups + rows - 1) / rows;
+  if (splits < 1) splits = 1;
+  int64_t bps = (nb + splits - 1) / splits;
+  bps = (bps + kSplitWavesHost - 1) / kSplitWavesHost * kSplitWavesHost;
+  if (bps < kSplitWavesHost) bps = kSplitWavesHost;
+  if (bps > kMaxAutoBlocksPerSplit) bps = kMaxAutoBlocksPerSplit;
+  return static_cast<int>(bps);
+}
+
+int plan(const kvq_cache* c, int32_t max_len, int32_t bps_req, int* bps, int* n_split) {
+  int rc = check_cache(c);
+  if (rc != KVQ_OK) return rc;
+  rc = check_len(c, max_len);
+  if (rc != KVQ_OK) return rc;
+  if (bps_req < 0) return KVQ_EINVAL;
+  const int nb = n_blocks_for(max_len);
+  *bps = bps_req > 0 ? bps_req : auto_blocks_per_split(c, nb);
+  *n_split = nb == 0 ? 0 : (nb + *bps - 1) / *bps;
+  return KVQ_OK;
+}
+
+size_t workspace_bytes(const kvq_cache* c, int n_split) {
+  const size_t parts = static_cast<size_t>(c->batch) * c->heads * n_split;
+  return parts * (static_cast<size_t>(c->head_dim) + 2) * sizeof(float);
+}
+
+// Fills the attention launch descriptor after validating the workspace.
+int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
+              void* workspace, size_t workspace_bytes_given, int32_t max_len, int32_t bps_req,
+              kvq::AttnArgs* a) {
+  int bps, n_split;
+  int rc = plan(c, max_len, bps_req, &bps, &n_split);
+  if (rc != KVQ_OK) return rc;
+  if (n_split > 0) {
+    if (!workspace || workspace_bytes_given < workspace_bytes(c, n_split))
+      return KVQ_EWORKSPACE;
+    if (!aligned16(workspace)) return KVQ_EALIGN;
+  }
+  const size_t parts = static_cast<size_t>(c->batch) * c->heads * n_split;
+  a->k_codes = static_cast<const uint8_t*>(c->k_codes);
+  a->v_codes = static_cast<const uint8_t*>(c->v_codes);
+  a->k_scale = c->k_scale;
+  a->v_scale = c->v_scale;
+  a->k_zero = c->k_zero;
+  a->v_zero = c->v_zero;
+  a->seq_lens = c->seq_lens;
+  a->q = static_cast<const uint16_t*>(q);
+  a->out = static_cast<uint16_t*>(out);
+  a->ws_o = static_cast<float*>(workspace);
+  a->ws_ml = n_split > 0 ? static_cast<float*>(workspace) + parts * c->head_dim : nullptr;
+  a->heads = c->heads;
+  a->max_blocks = c->max_blocks;
+  a->max_len = max_len;
+  a->bps = bps;
+  a->n_split = n_split;
+  a->qk_scale = softmax_scale * 1.44269504088896340736f;  // log2(e)
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_quantize_blocks(const kvq_cache* cache, const void* k, const void* v,
+                       int64_t stride_b, int64_t stride_t, int64_t stride_h, int32_t max_len,
+                       void* stream) {
+  int rc = check_cache(cache);
+  if (rc != KVQ_OK) return rc;
+  rc = check_len(cache, max_len);
+  if (rc != KVQ_OK) return rc;
+  if (!k || !v) return KVQ_EINVAL;
+  if (stride_b < 0 || stride_t < 0 || stride_h < 0) return KVQ_EINVAL;
+  if (!aligned16(k) || !aligned16(v) || stride_b % 8 || stride_t % 8 || stride_h % 8)
+    return KVQ_EALIGN;
+  const int nb = n_blocks_for(max_len);
+  if (nb == 0) return KVQ_OK;
+  kvq::QuantArgs a;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.stride_b = stride_b;
+  a.stride_t = stride_t;
+  a.stride_h = stride_h;
+  a.k_codes = static_cast<uint8_t*>(cache->k_codes);
+  a.v_codes = static_cast<uint8_t*>(cache->v_codes);
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.k_zero = cache->k_zero;
+  a.v_zero = cache->v_zero;
+  a.k_tail = static_cast<uint16_t*>(cache->k_tail);
+  a.v_tail = static_cast<uint16_t*>(cache->v_tail);
+  a.seq_lens = cache->seq_lens;
+  a.heads = cache->heads;
+  a.max_blocks = cache->max_blocks;
+  a.max_len = max_len;
+  const hipError_t e = kvq::launch_quantize(cache->scheme, cache->head_dim, cache->batch, nb, a,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+int kv_append(const kvq_cache* cache, const void* k_new, const void* v_new,
+              int32_t max_len_after, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != KVQ_OK) return rc;
+  if (max_len_after < 1) return KVQ_EINVAL;
+  rc = check_len(cache, max_len_after);
+  if (rc != KVQ_OK) return rc;
+  if (!cache->k_tail || !cache->v_tail || !k_new || !v_new) return KVQ_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_EALIGN;
+  kvq::AppendArgs a;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_codes = static_cast<uint8_t*>(cache->k_codes);
+  a.v_codes = static_cast<uint8_t*>(cache->v_codes);
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.k_zero = cache->k_zero;
+  a.v_zero = cache->v_zero;
+  a.k_tail = static_cast<uint16_t*>(cache->k_tail);
+  a.v_tail = static_cast<uint16_t*>(cache->v_tail);
+  a.seq_lens = cache->seq_lens;
+  a.batch = cache->batch;
+  a.heads = cache->heads;
+  a.max_blocks = cache->max_blocks;
+  const hipError_t e = kvq::launch_append(cache->scheme, cache->head_dim, a,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+int decode_attn_plan(const kvq_cache* cache, int32_t max_len, int32_t blocks_per_split,
+                     int32_t* blocks_per_split_out, int32_t* splits_per_row_out) {
+  int bps, n_split;
+  const int rc = plan(cache, max_len, blocks_per_split, &bps, &n_split);
+  if (rc != KVQ_OK) return rc;
+  if (blocks_per_split_out) *blocks_per_split_out = bps;
+  if (splits_per_row_out) *splits_per_row_out = n_split;
+  return KVQ_OK;
+}
+
+size_t decode_attn_workspace_bytes(const kvq_cache* cache, int32_t max_len,
+                                   int32_t blocks_per_split) {
+  int bps, n_split;
+  if (plan(cache, max_len, blocks_per_split, &bps, &n_split) != KVQ_OK) return 0;
+  return workspace_bytes(cache, n_split);
+}
+
+int decode_attn_split(const kvq_cache* cache, const void* q, float softmax_scale,
+                      void* workspace, size_t workspace_bytes_given, int32_t max_len,
+                      int32_t blocks_per_split, void* stream) {
+  if (!q) return KVQ_EINVAL;
+  if (!aligned16(q)) return KVQ_EALIGN;
+  kvq::AttnArgs a;
+  const int rc = attn_args(cache, q, softmax_scale, nullptr, workspace, workspace_bytes_given,
+                           max_len, blocks_per_split, &a);
+  if (rc != KVQ_OK) return rc;
+  if (a.n_split == 0) return KVQ_OK;
+  const hipError_t e = kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+int decode_attn_combine(const kvq_cache* cache, void* out, void* workspace,
+                        size_t workspace_bytes_given, int32_t max_len, int32_t blocks_per_split,
+                        void* stream) {
+  if (!out) return KVQ_EINVAL;
+  if (!aligned16(out)) return KVQ_EALIGN;
+  kvq::AttnArgs a;
+  const int rc = attn_args(cache, nullptr, 1.0f, out, workspace, workspace_bytes_given, max_len,
+                           blocks_per_split, &a);
+  if (rc != KVQ_OK) return rc;
+  const hipError_t e = kvq::launch_attn_combine(cache->head_dim, cache->batch, a,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, void* out,
+                    void* workspace, size_t workspace_bytes_given, int32_t max_len,
+                    int32_t blocks_per_split, void* stream) {
+  if (!q || !out) return KVQ_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_EALIGN;
+  kvq::AttnArgs a;
+  const int rc = attn_args(cache, q, softmax_scale, out, workspace, workspace_bytes_given,
+                           max_len, blocks_per_split, &a);
+  if (rc != KVQ_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.n_split > 0) {
+    if (kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a, s) != hipSuccess)
+      return KVQ_EHIP;
+  }
+  return kvq::launch_attn_combine(cache->head_dim, cache->batch, a, s) == hipSuccess ? KVQ_OK
+                                                                                      : KVQ_EHIP;
+}
+
+const char* kvq_strerror(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument (null pointer, bad scheme, shape, count or length)";
+    case KVQ_ENOTSUP: return "unsupported head_dim (64 and 128 are supported)";
+    case KVQ_ECAPACITY: return "length bound exceeds the cache capacity (max_blocks * 64)";
+    case KVQ_EALIGN: return "pointer or stride breaks the 16-byte alignment rule";
+    case KVQ_EWORKSPACE: return "workspace missing or too small";
+    case KVQ_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int kvq_version(void) { return KVQ_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,380 @@
+// kvq_attn.hip — single-token decode attention over the block-quantized cache.
+//
+// Attention is textbook scaled dot-product attention of one query row over the
+// dequantized cache. The context is cut into splits of whole 64-token blocks handled by
+// independent workgroups (the schedulable sub-blocks of the chunked attention in page
+// "第一章：DeepSeek R1推理模型性能跃迁全景概览" chapter 1), and a second kernel merges
+// the splits by their log-sum-exp. Decode attention at long context is bound by reads
+// of the cache (that page's §2.3 and page "DeepSeek-R1推理延迟骤降41.8%？…" §2.1), so
+// the kernel is written around streaming the packed codes once at full HBM rate:
+//
+//  * every wave-wide load is a 16-byte-per-lane read of 1 KiB of consecutive codes;
+//    lane l holds channel chunk l % LPT of token group l / LPT (LPT = 16-byte chunks
+//    per token row), so a 64-token block is LPT loads per tensor per wave;
+//  * codes are never converted one by one: a mask turns two stored 4-bit (or 8-bit)
+//    codes into a pair of fp16 subnormals u * 2^-24 (or u * 2^-20 for a high nibble),
+//    u the unsigned stored code, which v_fma_mix_f32 reads directly (fp16 operand,
+//    binary32 product and accumulate, one rounding) against the binary32 query (QK^T)
+//    and the binary32 weights (P.V). For QK^T the code offset (8 for int4, the zero
+//    point for uint8) is removed once per score; for P.V it is removed from each fp16
+//    pair by a packed fp16 add (exact), since a dominant weight on codes equal to the
+//    offset would otherwise cancel catastrophically. The power-of-two units are
+//    removed once per score / per split. (The
+//    fp16 dot-product instruction was measured to round its result far more coarsely
+//    than binary32, so it is not used.)
+//  * the block scale is folded into the score (K) and into the weight (V), once per
+//    token per lane;
+//  * online softmax in base 2 with a wave-uniform running max: the rescale of the
+//    accumulators happens only when a block raises the max;
+//  * at the end of a split the waves' states are merged through LDS into one partial
+//    (max, sum, o[D]) per split.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kSplitWaves = 4;
+
+template <int SCHEME, int D>
+struct AGeo {
+  static constexpr int kRowBytes = SCHEME == KVQ_INT4_SYM ? D / 2 : D;  // bytes per token
+  static constexpr int kLPT = kRowBytes / 16;       // lanes per token row
+  static constexpr int kGroups = kWave / kLPT;      // tokens per wave-wide load
+  static constexpr int kTPL = kLPT;                 // tokens per lane per block
+  static constexpr int kDPL = SCHEME == KVQ_INT4_SYM ? 32 : 16;  // channels per lane
+  static constexpr int kWords = 4;                  // 32-bit words per 16-byte load
+};
+
+__device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+
+
+template <int SCHEME, int D>
+struct Query {
+  using G = AGeo<SCHEME, D>;
+  // The lane's query channels in binary32. For int4 the odd channels are read from a
+  // high nibble (unit 2^-20 instead of 2^-24) and are stored pre-divided by 16 (exact),
+  // so every product lands in the unit 2^-24.
+  float qf[G::kDPL];
+  float sum;  // sum of the lane's query channels (unscaled)
+
+  __device__ __forceinline__ void load(const uint16_t* q) {
+    constexpr int kLoads = G::kDPL / 8;
+    sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const uint4 r = *reinterpret_cast<const uint4*>(q + 8 * i);
+      float x[8];
+      unpack8(r, x);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        sum += x[k];
+        qf[8 * i + k] = (SCHEME == KVQ_INT4_SYM && (k & 1)) ? x[k] * 0.0625f : x[k];
+      }
+    }
+  }
+};
+
+// Partial dot product of one 16-byte code chunk (channels c0 .. c0+31 for int4,
+// c0 .. c0+15 for uint8) with the lane's query, in units of the stored unsigned code u
+// (int4: u = c + 8; uint8: u = c) times 2^-24.
+template <int SCHEME>
+__device__ __forceinline__ float chunk_dot(const uint4& raw, const float* qf) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float a0 = 0.0f, a1 = 0.0f;
+  if constexpr (SCHEME == KVQ_INT4_SYM) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t u = w[j];
+      const uint32_t u8 = u >> 8;
+      const half2_t p0 = as_h2(u & 0x000F000Fu);   // channels 0, 4   (2^-24)
+      const half2_t p1 = as_h2(u & 0x00F000F0u);   // channels 1, 5   (2^-20)
+      const half2_t p2 = as_h2(u8 & 0x000F000Fu);  // channels 2, 6   (2^-24)
+      const half2_t p3 = as_h2(u8 & 0x00F000F0u);  // channels 3, 7   (2^-20)
+      const float* qj = qf + 8 * j;
+      a0 = __builtin_fmaf(static_cast<float>(p0.x), qj[0], a0);
+      a1 = __builtin_fmaf(static_cast<float>(p0.y), qj[4], a1);
+      a0 = __builtin_fmaf(static_cast<float>(p1.x), qj[1], a0);
+      a1 = __builtin_fmaf(static_cast<float>(p1.y), qj[5], a1);
+      a0 = __builtin_fmaf(static_cast<float>(p2.x), qj[2], a0);
+      a1 = __builtin_fmaf(static_cast<float>(p2.y), qj[6], a1);
+      a0 = __builtin_fmaf(static_cast<float>(p3.x), qj[3], a0);
+      a1 = __builtin_fmaf(static_cast<float>(p3.y), qj[7], a1);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half2_t e = as_h2(w[j] & 0x00FF00FFu);         // channels 0, 2
+      const half2_t f = as_h2((w[j] >> 8) & 0x00FF00FFu);  // channels 1, 3
+      const float* qj = qf + 4 * j;
+      a0 = __builtin_fmaf(static_cast<float>(e.x), qj[0], a0);
+      a1 = __builtin_fmaf(static_cast<float>(e.y), qj[2], a1);
+      a0 = __builtin_fmaf(static_cast<float>(f.x), qj[1], a0);
+      a1 = __builtin_fmaf(static_cast<float>(f.y), qj[3], a1);
+    }
+  }
+  return (a0 + a1) * 16777216.0f;
+}
+
+// o[k] += p * c_k for the 16-byte code chunk, c = u - offset. The offset is taken out
+// of each fp16 pair with one packed fp16 add before the binary32 FMA, so a heavily
+// weighted token whose codes sit at the offset adds (almost) nothing instead of two
+// large terms that cancel later. off_lo / off_hi: the pair (-offset * unit) for the
+// 2^-24 and 2^-20 unit positions (int4: exact; uint8: exact while |u - zp| < 2048,
+// else rounded to fp16, a 2^-11 relative error on a term that then dominates).
+template <int SCHEME>
+__device__ __forceinline__ void chunk_axpy(const uint4& raw, float p, half2_t off_lo,
+                                           half2_t off_hi, float* o) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  if constexpr (SCHEME == KVQ_INT4_SYM) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t u = w[j];
+      const uint32_t u8 = u >> 8;
+      const half2_t p0 = as_h2(u & 0x000F000Fu) + off_lo;   // channels 0, 4   (2^-24)
+      const half2_t p1 = as_h2(u & 0x00F000F0u) + off_hi;   // channels 1, 5   (2^-20)
+      const half2_t p2 = as_h2(u8 & 0x000F000Fu) + off_lo;  // channels 2, 6   (2^-24)
+      const half2_t p3 = as_h2(u8 & 0x00F000F0u) + off_hi;  // channels 3, 7   (2^-20)
+      float* oj = o + 8 * j;
+      oj[0] = __builtin_fmaf(static_cast<float>(p0.x), p, oj[0]);
+      oj[4] = __builtin_fmaf(static_cast<float>(p0.y), p, oj[4]);
+      oj[1] = __builtin_fmaf(static_cast<float>(p1.x), p, oj[1]);
+      oj[5] = __builtin_fmaf(static_cast<float>(p1.y), p, oj[5]);
+      oj[2] = __builtin_fmaf(static_cast<float>(p2.x), p, oj[2]);
+      oj[6] = __builtin_fmaf(static_cast<float>(p2.y), p, oj[6]);
+      oj[3] = __builtin_fmaf(static_cast<float>(p3.x), p, oj[3]);
+      oj[7] = __builtin_fmaf(static_cast<float>(p3.y), p, oj[7]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half2_t e = as_h2(w[j] & 0x00FF00FFu) + off_lo;         // channels 0, 2
+      const half2_t f = as_h2((w[j] >> 8) & 0x00FF00FFu) + off_lo;  // channels 1, 3
+      float* oj = o + 4 * j;
+      oj[0] = __builtin_fmaf(static_cast<float>(e.x), p, oj[0]);
+      oj[2] = __builtin_fmaf(static_cast<float>(e.y), p, oj[2]);
+      oj[1] = __builtin_fmaf(static_cast<float>(f.x), p, oj[1]);
+      oj[3] = __builtin_fmaf(static_cast<float>(f.y), p, oj[3]);
+    }
+  }
+}
+
+// ---- split kernel: grid (n_split, heads, batch), kSplitWaves waves ------------------
+template <int SCHEME, int D>
+__global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArgs a) {
+  using G = AGeo<SCHEME, D>;
+  constexpr int TPL = G::kTPL, DPL = G::kDPL, LPT = G::kLPT, GROUPS = G::kGroups;
+  __shared__ float red_o[kSplitWaves][kWave][DPL + 1];
+  __shared__ float red_l[kSplitWaves][kWave];
+  __shared__ float red_m[kSplitWaves];
+
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int cap = a.max_blocks * kBlock;
+  int len = a.seq_lens[b];
+  len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+  const int nb = (len + kBlock - 1) / kBlock;
+  const int blk_begin = split * a.bps;
+  if (blk_begin >= nb) return;  // uniform over the workgroup
+  const int blk_end = min(blk_begin + a.bps, nb);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int chunk = lane % LPT;
+  const int group = lane / LPT;
+  const int64_t row = static_cast<int64_t>(b) * a.heads + h;
+
+  Query<SCHEME, D> q;
+  q.load(a.q + row * D + chunk * DPL);
+  const float qsum_row = group_sum<LPT>(q.sum);
+
+  const uint8_t* kbase = a.k_codes + row * a.max_blocks * kBlock * G::kRowBytes + lane * 16;
+  const uint8_t* vbase = a.v_codes + row * a.max_blocks * kBlock * G::kRowBytes + lane * 16;
+  const float* ks = a.k_scale + row * a.max_blocks;
+  const float* vs = a.v_scale + row * a.max_blocks;
+  const float* kz = a.k_zero + row * a.max_blocks;
+  const float* vz = a.v_zero + row * a.max_blocks;
+
+  float o[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) o[k] = 0.0f;
+  float m = -__builtin_inff();  // running max of the base-2 scores (wave-uniform)
+  float l = 0.0f;               // sum of weights over this lane's tokens
+
+  auto load_block = [&](int blk, uint4 (&kk)[TPL], uint4 (&vv)[TPL]) {
+    const int64_t off = static_cast<int64_t>(blk) * kBlock * G::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      kk[i] = *reinterpret_cast<const uint4*>(kbase + off + i * kWave * 16);
+      vv[i] = *reinterpret_cast<const uint4*>(vbase + off + i * kWave * 16);
+    }
+  };
+
+  auto process_block = [&](int blk, const uint4 (&kr)[TPL], const uint4 (&vr)[TPL]) {
+    const float sk = ks[blk] * a.qk_scale;
+    const float sv = vs[blk];
+    float bias_k;
+    half2_t off_lo, off_hi;
+    if constexpr (SCHEME == KVQ_INT4_SYM) {
+      bias_k = 8.0f * qsum_row;
+      off_lo = as_h2(0x80088008u);  // -8 * 2^-24 in both halves
+      off_hi = as_h2(0x80808080u);  // -8 * 2^-20 = -128 * 2^-24
+    } else {
+      bias_k = kz[blk] * qsum_row;
+      const _Float16 zh = static_cast<_Float16>(vz[blk] * -5.9604644775390625e-08f);
+      off_lo = half2_t{zh, zh};
+      off_hi = off_lo;
+    }
+    float s[TPL];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const float part = chunk_dot<SCHEME>(kr[i], q.qf);
+      s[i] = (group_sum<LPT>(part) - bias_k) * sk;
+    }
+    if (blk == nb - 1) {  // tokens past the length in the last block weigh nothing
+      const int valid = len - blk * kBlock;
+#pragma unroll
+      for (int i = 0; i < TPL; ++i)
+        if (i * GROUPS + group >= valid) s[i] = -__builtin_inff();
+    }
+    float mb = s[0];
+#pragma unroll
+    for (int i = 1; i < TPL; ++i) mb = fmaxf(mb, s[i]);
+    mb = wave_max(mb);
+    if (mb > m) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mb);
+      l *= alpha;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[k] *= alpha;
+      m = mb;
+    }
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const float p = __builtin_amdgcn_exp2f(s[i] - m);
+      psum += p;
+      chunk_axpy<SCHEME>(vr[i], p * sv, off_lo, off_hi, o);
+    }
+    l += psum;
+  };
+
+  // Each wave takes blocks wave, wave + W, wave + 2W, ... of the split; the next
+  // block's codes are in flight while the current one is processed (ping-pong).
+  uint4 ka[TPL], va[TPL], kb[TPL], vb[TPL];
+  int blk = blk_begin + wave;
+  if (blk < blk_end) load_block(blk, ka, va);
+  while (blk < blk_end) {
+    int next = blk + kSplitWaves;
+    if (next < blk_end) load_block(next, kb, vb);
+    process_block(blk, ka, va);
+    blk = next;
+    if (blk >= blk_end) break;
+    next = blk + kSplitWaves;
+    if (next < blk_end) load_block(next, ka, va);
+    process_block(blk, kb, vb);
+    blk = next;
+  }
+
+  // Per-lane result in true units: o_true[k] = o[k] * unit(k).
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    float unit = 16777216.0f;
+    if constexpr (SCHEME == KVQ_INT4_SYM) unit = (k & 1) ? 1048576.0f : 16777216.0f;
+    red_o[wave][lane][k] = o[k] * unit;
+  }
+  red_l[wave][lane] = l;
+  if (lane == 0) red_m[wave] = m;
+  __syncthreads();
+
+  float M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kSplitWaves; ++w) M = fmaxf(M, red_m[w]);
+  float alpha[kSplitWaves];
+#pragma unroll
+  for (int w = 0; w < kSplitWaves; ++w) alpha[w] = __builtin_amdgcn_exp2f(red_m[w] - M);
+
+  float* ws_o = a.ws_o + (row * a.n_split + split) * D;
+  for (int d = threadIdx.x; d < D; d += kSplitWaves * kWave) {
+    const int c = d / DPL, k = d % DPL;
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+      float sw = 0.0f;
+#pragma unroll
+      for (int g = 0; g < GROUPS; ++g) sw += red_o[w][g * LPT + c][k];
+      acc = __builtin_fmaf(alpha[w], sw, acc);
+    }
+    ws_o[d] = acc;
+  }
+  if (threadIdx.x == 0) {
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+      float sw = 0.0f;
+      for (int g = 0; g < GROUPS; ++g) sw += red_l[w][g * LPT];
+      L = __builtin_fmaf(alpha[w], sw, L);
+    }
+    float* ml = a.ws_ml + (row * a.n_split + split) * 2;
+    ml[0] = M;
+    ml[1] = L;
+  }
+}
+
+// ---- combine kernel: grid (heads, batch), D threads ---------------------------------
+template <int D>
+__global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int d = threadIdx.x;
+  const int cap = a.max_blocks * kBlock;
+  int len = a.seq_lens[b];
+  len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+  const int nb = (len + kBlock - 1) / kBlock;
+  const int n = (nb + a.bps - 1) / a.bps;
+  const int64_t row = static_cast<int64_t>(b) * a.heads + h;
+  _Float16 r = 0;
+  if (n > 0) {
+    const float* ml = a.ws_ml + row * a.n_split * 2;
+    const float* po = a.ws_o + row * a.n_split * D + d;
+    float M = ml[0];
+    for (int j = 1; j < n; ++j) M = fmaxf(M, ml[2 * j]);
+    float L = 0.0f, acc = 0.0f;
+    for (int j = 0; j < n; ++j) {
+      const float w = __builtin_amdgcn_exp2f(ml[2 * j] - M);
+      L = __builtin_fmaf(w, ml[2 * j + 1], L);
+      acc = __builtin_fmaf(w, po[j * D], acc);
+    }
+    r = static_cast<_Float16>(acc / L);
+  }
+  a.out[row * D + d] = __builtin_bit_cast(uint16_t, r);
+}
+
+template <int SCHEME, int D>
+hipError_t split_t(int batch, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.n_split, a.heads, batch);
+  hipLaunchKernelGGL((attn_split_kernel<SCHEME, D>), grid, dim3(kSplitWaves * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_split(int scheme, int head_dim, int batch, const AttnArgs& a,
+                             hipStream_t s) {
+  if (scheme == KVQ_INT4_SYM)
+    return head_dim == 128 ? split_t<KVQ_INT4_SYM, 128>(batch, a, s)
+                           : split_t<KVQ_INT4_SYM, 64>(batch, a, s);
+  return head_dim == 128 ? split_t<KVQ_UINT8_ASYM, 128>(batch, a, s)
+                         : split_t<KVQ_UINT8_ASYM, 64>(batch, a, s);
+}
+
+hipError_t launch_attn_combine(int head_dim, int batch, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.heads, batch);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((attn_combine_kernel<128>), grid, dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<64>), grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

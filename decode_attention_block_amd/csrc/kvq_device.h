@@ -1,0 +1,128 @@
+// kvq_device.h — device-side helpers shared by the libkvq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kBlock = 64;  // tokens per quantization block
+constexpr int kWave = 64;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// ---- DPP lane exchanges (all 64 lanes active) --------------------------------------
+// quad_perm [1,0,3,2] / [2,3,0,1]; row_half_mirror (lane i of each 8 <- 7-i);
+// row_mirror (lane i of each 16 <- 15-i).
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each group of N consecutive lanes (N in {1, 2, 4, 8}); every lane of the
+// group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<kDppQuadXor1>(v);
+  if constexpr (N >= 4) v += dpp<kDppQuadXor2>(v);
+  if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v);
+  static_assert(N <= 8, "group too wide");
+  return v;
+}
+
+// Maximum over the whole wave, returned uniformly.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  const int iv = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ float wave_min(float v) { return -wave_max(-v); }
+
+// ---- fp16 helpers -------------------------------------------------------------------
+__device__ __forceinline__ float h2f_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(half2_t, w).x);
+}
+__device__ __forceinline__ float h2f_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(half2_t, w).y);
+}
+
+// 8 fp16 values held in a 16-byte load -> binary32 (exact, subnormals included).
+__device__ __forceinline__ void unpack8(const uint4& r, float (&x)[8]) {
+  x[0] = h2f_lo(r.x); x[1] = h2f_hi(r.x);
+  x[2] = h2f_lo(r.y); x[3] = h2f_hi(r.y);
+  x[4] = h2f_lo(r.z); x[5] = h2f_hi(r.z);
+  x[6] = h2f_lo(r.w); x[7] = h2f_hi(r.w);
+}
+
+// ---- block statistics and scales (IEEE binary32, round-to-nearest) ------------------
+// int4: s = absmax / 7.5 (0 for an all-zero block).
+__device__ __forceinline__ float int4_scale(float absmax) {
+  return absmax == 0.0f ? 0.0f : absmax / 7.5f;
+}
+
+// uint8: s = (max - min) / 255, zp = rint(-min / s) + 0.0 with the degenerate-chunk
+// rule (all elements equal to c: c == 0 -> s = zp = 0; else widen the range to 0).
+__device__ __forceinline__ void uint8_scale_zero(float mn, float mx, float& s, float& zp) {
+  if (mx == mn) {
+    if (mx == 0.0f) {
+      s = 0.0f;
+      zp = 0.0f;
+      return;
+    }
+    mn = fminf(mn, 0.0f);
+    mx = fmaxf(mx, 0.0f);
+  }
+  const float range = mx - mn;
+  s = range / 255.0f;
+  zp = __builtin_rintf(-mn / s) + 0.0f;
+}
+
+// int4 code c = clamp(rint(x / s), -8, 7) (0 when s = 0), returned as the stored
+// offset-binary nibble c + 8.
+__device__ __forceinline__ uint32_t int4_code(float x, float s) {
+  if (s == 0.0f) return 8u;
+  int c = static_cast<int>(__builtin_rintf(x / s));
+  c = c < -8 ? -8 : (c > 7 ? 7 : c);
+  return static_cast<uint32_t>(c + 8);
+}
+
+__device__ __forceinline__ uint32_t uint8_code(float x, float s, int zpi) {
+  if (s == 0.0f) return 0u;
+  int c = static_cast<int>(__builtin_rintf(x / s)) + zpi;
+  c = c < 0 ? 0 : (c > 255 ? 255 : c);
+  return static_cast<uint32_t>(c);
+}
+
+// 8 consecutive channels -> 4 bytes of int4 nibbles (channel 2k low, 2k+1 high).
+__device__ __forceinline__ uint32_t pack_int4x8(const float (&x)[8], float s) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= int4_code(x[i], s) << (4 * i);
+  return w;
+}
+
+// 8 consecutive channels -> 8 bytes of uint8 codes.
+__device__ __forceinline__ uint2 pack_uint8x8(const float (&x)[8], float s, int zpi) {
+  uint2 r;
+  r.x = uint8_code(x[0], s, zpi) | (uint8_code(x[1], s, zpi) << 8) |
+        (uint8_code(x[2], s, zpi) << 16) | (uint8_code(x[3], s, zpi) << 24);
+  r.y = uint8_code(x[4], s, zpi) | (uint8_code(x[5], s, zpi) << 8) |
+        (uint8_code(x[6], s, zpi) << 16) | (uint8_code(x[7], s, zpi) << 24);
+  return r;
+}
+
+}  // namespace kvq

@@ -1,0 +1,66 @@
+// kvq_internal.h — host-side launch descriptors shared by the libkvq sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+struct QuantArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t stride_b, stride_t, stride_h;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_scale;
+  float* v_scale;
+  float* k_zero;
+  float* v_zero;
+  uint16_t* k_tail;
+  uint16_t* v_tail;
+  const int32_t* seq_lens;
+  int heads, max_blocks, max_len;
+};
+
+struct AppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_scale;
+  float* v_scale;
+  float* k_zero;
+  float* v_zero;
+  uint16_t* k_tail;
+  uint16_t* v_tail;
+  int32_t* seq_lens;
+  int batch, heads, max_blocks;
+};
+
+struct AttnArgs {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float* k_scale;
+  const float* v_scale;
+  const float* k_zero;
+  const float* v_zero;
+  const int32_t* seq_lens;
+  const uint16_t* q;
+  uint16_t* out;
+  float* ws_o;   // [rows][n_split][D] unnormalised partial outputs
+  float* ws_ml;  // [rows][n_split][2]  (running max in log2 units, sum of weights)
+  int heads, max_blocks, max_len, bps, n_split;
+  float qk_scale;  // softmax_scale * log2(e)
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_quantize(int scheme, int head_dim, int batch, int n_blocks,
+                           const QuantArgs& a, hipStream_t s);
+hipError_t launch_append(int scheme, int head_dim, const AppendArgs& a, hipStream_t s);
+hipError_t launch_attn_split(int scheme, int head_dim, int batch, const AttnArgs& a,
+                             hipStream_t s);
+hipError_t launch_attn_combine(int head_dim, int batch, const AttnArgs& a, hipStream_t s);
+
+}  // namespace kvq

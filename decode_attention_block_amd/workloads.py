@@ -24,6 +24,8 @@ Streams: 0 = prefill K, 1 = prefill V, 2 = query, 3 = lengths, 4 = appended K,
 5 = appended V.
 """
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -135,9 +137,19 @@ def lengths(w):
 
 
 def prefill_batch(w, layer, which, n_tokens=None, seqs=None):
-    """float16 [B][S][H][D] prefill tensor for all (or the listed) sequences."""
-    seqs = range(w.batch) if seqs is None else seqs
-    return np.stack([prefill_kv(w, layer, s, which, n_tokens) for s in seqs])
+    """float16 [B][S][H][D] prefill tensor for all (or the listed) sequences. Each
+    sequence has its own stream, so drawing them on parallel threads changes nothing."""
+    seqs = list(range(w.batch) if seqs is None else seqs)
+    n = w.context if n_tokens is None else n_tokens
+    out = np.empty((len(seqs), n, w.heads, w.head_dim), np.float16)
+
+    def fill(i):
+        out[i] = prefill_kv(w, layer, seqs[i], which, n)
+
+    workers = max(1, min(len(seqs), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, range(len(seqs))))
+    return out
 
 
 def softmax_scale(w):

@@ -1,0 +1,184 @@
+/*
+ * kvq.h — C ABI of libkvq: a block-quantized KV cache and single-token decode
+ * attention that reads it, for AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (web pages on DeepSeek-R1 inference optimisation):
+ *   [Pg1] "第一章：DeepSeek R1推理模型性能跃迁全景概览" (aicoding.csdn.net)
+ *         §2.2 — INT8 KV codes whose scales come from each chunk's extreme values;
+ *         §2.3 and chapter 1 — decode attention at long context is bound by reads of
+ *         the cache; attention is split into schedulable sub-blocks.
+ *   [Pg2] "DeepSeek-R1推理延迟骤降41.8%？独家披露3类硬件感知调度策略" (jsqmd.com)
+ *         §2.1 "基于A100显存带宽瓶颈的KV Cache分块压缩策略", sub-section
+ *         "分块量化压缩设计" — 4-bit codes with one scale per 64-token block,
+ *         scale = block absmax / 7.5, codes rounded and clamped to [-8, 7].
+ *
+ * Conventions shared by every call:
+ *   * Ownership: the caller allocates every buffer (device memory unless stated) and
+ *     keeps it alive until the work queued on `stream` has finished. The library
+ *     allocates nothing and keeps no state between calls; calls on different streams
+ *     that touch different buffers may run concurrently.
+ *   * Execution: every call validates its arguments on the host, then queues its
+ *     kernels on `stream` (a hipStream_t; NULL means the null stream) and returns
+ *     without waiting. Faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   * Errors: a negative KVQ_E* code means nothing was queued, except KVQ_EHIP, which
+ *     means a launch failed (earlier launches of the same call may have been queued).
+ *   * Block: 64 tokens of one (sequence, head) row, all head_dim channels — one scale
+ *     (and, for uint8, one zero point) per block.
+ *   * Rounding: codes use round-half-to-even of the IEEE binary32 quotient x / s, the
+ *     division correctly rounded (never a reciprocal multiply).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_BLOCK_TOKENS 64
+#define KVQ_VERSION 1
+
+/* Cache formats. */
+enum kvq_scheme {
+  /* [Pg2] §2.1: s = RN(absmax / 7.5f) (s = 0 for an all-zero block);
+   * code = clamp(rint(RN(x / s)), -8, 7), stored as a 4-bit two's-complement nibble.
+   * Byte k of a token's D/2-byte row holds channel 2k in bits 0-3 and 2k+1 in bits 4-7.
+   * Zero points (if the buffers are given) are written +0.0f. */
+  KVQ_INT4_SYM = 0,
+  /* [Pg1] §2.2, asymmetric per-chunk reading: s = RN(RN(max - min) / 255f),
+   * zp = rint(RN(-min / s)) + 0.0f, code = clamp(rint(RN(x / s)) + (int)zp, 0, 255).
+   * A chunk whose elements all equal c: c == 0 gives s = 0, zp = 0, codes 0;
+   * otherwise the range is widened to [min(c,0), max(c,0)]. */
+  KVQ_UINT8_ASYM = 1
+};
+
+/* Status codes. */
+enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_EINVAL = -1,     /* null pointer, bad scheme/shape/count, negative length */
+  KVQ_ENOTSUP = -2,    /* head_dim other than 64 or 128 */
+  KVQ_ECAPACITY = -3,  /* a length bound exceeds max_blocks * 64 */
+  KVQ_EALIGN = -4,     /* a pointer or stride breaks the 16-byte alignment rule */
+  KVQ_EWORKSPACE = -5, /* workspace missing or smaller than decode_attn_workspace_bytes */
+  KVQ_EHIP = -6        /* a kernel launch failed */
+};
+
+/* Cache descriptor. Plain data; every pointer is device memory owned by the caller.
+ * B = batch, H = heads, D = head_dim, MB = max_blocks (capacity MB * 64 tokens/row).
+ *   k_codes, v_codes : uint8 [B][H][MB][64][D/2 (int4) | D (uint8)], 16-byte aligned.
+ *                      Bytes of tokens at or past a row's length inside its last block
+ *                      are written 0 by the quantizing calls.
+ *   k_scale, v_scale : float [B][H][MB].
+ *   k_zero,  v_zero  : float [B][H][MB]; required for KVQ_UINT8_ASYM, may be NULL for
+ *                      KVQ_INT4_SYM.
+ *   k_tail,  v_tail  : fp16 [B][H][64][D], 16-byte aligned: the original fp16 values
+ *                      of each row's open (partially filled) block, which kv_append
+ *                      needs to re-quantize that block. May be NULL if kv_append is
+ *                      never called.
+ *   seq_lens         : int32 [B], the number of valid tokens of each sequence (device
+ *                      memory). Entries are clamped to [0, MB*64] by every kernel. */
+typedef struct kvq_cache {
+  int32_t scheme;
+  int32_t batch;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t max_blocks;
+  void* k_codes;
+  void* v_codes;
+  float* k_scale;
+  float* v_scale;
+  float* k_zero;
+  float* v_zero;
+  void* k_tail;
+  void* v_tail;
+  int32_t* seq_lens;
+} kvq_cache;
+
+/* Quantizes the prefill: for every row (b, h), blocks [0, ceil(n_b / 64)) of K and V,
+ * where n_b = min(seq_lens[b], max_len), and stages the fp16 values of a partially
+ * filled last block into k_tail/v_tail (when those are non-NULL). Blocks past
+ * ceil(n_b / 64) are not touched. [Pg2] §2.1 (int4), [Pg1] §2.2 (uint8).
+ *   k, v      : fp16 device tensors; element (b, t, h, d) at base[b*stride_b +
+ *               t*stride_t + h*stride_h + d] (strides in elements, channels
+ *               contiguous). Pointers 16-byte aligned, strides multiples of 8.
+ *               [B][S][H][D] contiguous means stride_b = S*H*D, stride_t = H*D,
+ *               stride_h = D. Only tokens t < n_b are read.
+ *   max_len   : host-side bound on seq_lens, sizes the launch; 0 <= max_len <= MB*64.
+ * Returns KVQ_OK or a negative kvq_status. */
+int kv_quantize_blocks(const kvq_cache* cache, const void* k, const void* v,
+                       int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                       int32_t max_len, void* stream);
+
+/* Appends one decoded token per sequence: for every row, the token is written at
+ * position n_b = seq_lens[b] (its fp16 value staged in the tail buffer), the row's
+ * tail block is brought to exactly what kv_quantize_blocks would produce for the first
+ * n_b + 1 tokens, and then seq_lens[b] is incremented. When the new token leaves the
+ * block's statistic (absmax, or min and max) unchanged only its own codes are written;
+ * otherwise the whole tail block is re-quantized from the staged fp16 values.
+ * Sequences with seq_lens[b] >= MB*64 are left unchanged. The tail staging (written
+ * by kv_quantize_blocks or earlier appends) must be present.
+ *   k_new, v_new  : fp16 [B][H][D] contiguous, 16-byte aligned.
+ *   max_len_after : host-side bound on the lengths after the append; must be
+ *                   <= MB*64 (KVQ_ECAPACITY otherwise).
+ * Returns KVQ_OK or a negative kvq_status. */
+int kv_append(const kvq_cache* cache, const void* k_new, const void* v_new,
+              int32_t max_len_after, void* stream);
+
+/* Work split of decode_attn_qkv: the context of each row is cut into splits of
+ * `blocks_per_split` 64-token blocks (0 = chosen by the library from the shape), each
+ * handled by one workgroup, then merged. Writes the effective blocks per split and the
+ * number of splits per row for this max_len. Host only. */
+int decode_attn_plan(const kvq_cache* cache, int32_t max_len, int32_t blocks_per_split,
+                     int32_t* blocks_per_split_out, int32_t* splits_per_row_out);
+
+/* Bytes of device workspace decode_attn_qkv needs for these arguments (0 on invalid
+ * arguments). The workspace holds per-split partial softmax states; its contents
+ * need not be initialised and are overwritten by every call. */
+size_t decode_attn_workspace_bytes(const kvq_cache* cache, int32_t max_len,
+                                   int32_t blocks_per_split);
+
+/* Decode attention of one query token per row against the quantized cache:
+ *   out[b][h][:] = sum_t softmax_t(softmax_scale * q . K^_t) * V^_t,  t < n_b,
+ * with K^, V^ the dequantized cache (c*s, or (c - zp)*s), n_b = min(seq_lens[b],
+ * max_len). Codes are dequantized in registers; QK^T, an online softmax (base 2,
+ * softmax_scale*log2(e) folded into the scores) and the weighted sum of V accumulate
+ * in binary32 per split of the context; a second kernel merges the splits by their
+ * log-sum-exp and rounds to fp16. Rows with n_b = 0 get zeros. (Attention is the
+ * textbook scaled dot product; splitting it into schedulable pieces follows [Pg1]
+ * chapter 1's chunked attention.)
+ *   q               : fp16 [B][H][D] contiguous, 16-byte aligned.
+ *   out             : fp16 [B][H][D] contiguous, 16-byte aligned.
+ *   workspace       : device buffer of >= decode_attn_workspace_bytes(...) bytes,
+ *                     16-byte aligned; must not be shared by concurrent calls.
+ *   max_len         : host-side bound on seq_lens, sizes the launch; <= MB*64.
+ *   blocks_per_split: 0 = automatic, else the split size in blocks.
+ * Returns KVQ_OK or a negative kvq_status. */
+int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, void* out,
+                    void* workspace, size_t workspace_bytes, int32_t max_len,
+                    int32_t blocks_per_split, void* stream);
+
+/* The two kernels of decode_attn_qkv, queued separately (same arguments and same
+ * plan). decode_attn_split writes the partial states to the workspace;
+ * decode_attn_combine reads them and writes `out`. Running split then combine on one
+ * stream is exactly decode_attn_qkv. */
+int decode_attn_split(const kvq_cache* cache, const void* q, float softmax_scale,
+                      void* workspace, size_t workspace_bytes, int32_t max_len,
+                      int32_t blocks_per_split, void* stream);
+int decode_attn_combine(const kvq_cache* cache, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t max_len, int32_t blocks_per_split,
+                        void* stream);
+
+/* Human-readable text of a kvq_status (static storage). */
+const char* kvq_strerror(int status);
+
+/* KVQ_VERSION of the built library. */
+int kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

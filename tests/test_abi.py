@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every entry point include/kvq.h declares, and
+rejects bad arguments on the host before launching anything (no GPU needed: every
+case below fails validation, so no HIP call is made; device pointers are fake)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_block_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # 16-byte aligned stand-in for device memory, never dereferenced
+
+# The cases below pass fake device pointers and rely on host validation rejecting
+# them; they never run where a GPU is present, so a validation bug cannot launch.
+no_gpu_only = pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                                 reason="fake-pointer validation cases run only without a GPU")
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h"), encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(kvq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvq.load_library()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert kvq.kvq_version() == 1
+
+
+def cache(scheme=0, B=2, H=4, D=128, MB=3, **kw):
+    fields = dict(k_codes=FAKE, v_codes=FAKE, k_scale=FAKE, v_scale=FAKE, k_zero=FAKE,
+                  v_zero=FAKE, k_tail=FAKE, v_tail=FAKE, seq_lens=FAKE)
+    fields.update(kw)
+    return kvq.kvq_cache(scheme, B, H, D, MB, *[fields[f] for f in (
+        "k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero", "k_tail", "v_tail",
+        "seq_lens")])
+
+
+def rc_quant(c, k=FAKE, v=FAKE, strides=(3 * 64 * 4 * 128, 4 * 128, 128), max_len=100):
+    L = kvq.load_library()
+    return L.kv_quantize_blocks(ctypes.byref(c), k, v, *strides, max_len, None)
+
+
+def rc_attn(c, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30, max_len=100, bps=0):
+    L = kvq.load_library()
+    return L.decode_attn_qkv(ctypes.byref(c), q, 0.1, out, ws, ws_bytes, max_len, bps, None)
+
+
+def rc_append(c, k=FAKE, v=FAKE, max_len_after=100):
+    return kvq.load_library().kv_append(ctypes.byref(c), k, v, max_len_after, None)
+
+
+EINVAL, ENOTSUP, ECAP, EALIGN, EWS = -1, -2, -3, -4, -5
+
+
+@no_gpu_only
+def test_null_and_bad_descriptor():
+    L = kvq.load_library()
+    assert L.kv_quantize_blocks(None, FAKE, FAKE, 0, 0, 0, 10, None) == EINVAL
+    assert rc_quant(cache(scheme=2)) == EINVAL
+    assert rc_quant(cache(B=0)) == EINVAL
+    assert rc_quant(cache(H=-1)) == EINVAL
+    assert rc_quant(cache(MB=0)) == EINVAL
+    assert rc_quant(cache(D=96)) == ENOTSUP
+    assert rc_quant(cache(k_codes=0)) == EINVAL
+    assert rc_quant(cache(seq_lens=0)) == EINVAL
+    assert rc_quant(cache(scheme=1, v_zero=0)) == EINVAL
+    assert rc_quant(cache(), k=0) == EINVAL
+
+
+@no_gpu_only
+def test_alignment_rules():
+    assert rc_quant(cache(k_codes=FAKE + 8)) == EALIGN
+    assert rc_quant(cache(), k=FAKE + 2) == EALIGN
+    assert rc_quant(cache(), strides=(3 * 64 * 4 * 128, 4 * 128, 4)) == EALIGN
+    assert rc_attn(cache(), q=FAKE + 4) == EALIGN
+    assert rc_attn(cache(), out=FAKE + 4) == EALIGN
+    assert rc_append(cache(), k=FAKE + 2) == EALIGN
+
+
+@no_gpu_only
+def test_capacity_and_lengths():
+    assert rc_quant(cache(MB=3), max_len=3 * 64 + 1) == ECAP
+    assert rc_quant(cache(), max_len=-1) == EINVAL
+    assert rc_attn(cache(MB=3), max_len=193) == ECAP
+    assert rc_append(cache(MB=3), max_len_after=193) == ECAP
+    assert rc_append(cache(), max_len_after=0) == EINVAL
+    assert rc_append(cache(k_tail=0)) == EINVAL
+
+
+@no_gpu_only
+def test_workspace_rules():
+    c = cache(B=2, H=4, D=128, MB=3)
+    need = kvq.decode_attn_workspace_bytes(c, 192, 1)
+    assert need == 2 * 4 * 3 * (128 + 2) * 4
+    assert rc_attn(c, ws_bytes=need - 1, max_len=192, bps=1) == EWS
+    assert rc_attn(c, ws=0, max_len=192, bps=1) == EWS
+    assert rc_attn(c, ws=FAKE + 4, ws_bytes=need, max_len=192, bps=1) == EALIGN
+    assert rc_attn(c, max_len=192, bps=-1) == EINVAL
+    assert kvq.decode_attn_workspace_bytes(cache(D=96), 10) == 0
+
+
+def test_plan_is_whole_blocks_and_covers_context():
+    c = cache(B=8, H=32, D=128, MB=129)
+    for max_len in (1, 64, 65, 8192, 8256):
+        bps, ns = kvq.decode_attn_plan(c, max_len)
+        nb = (max_len + 63) // 64
+        assert bps >= 1 and ns == (nb + bps - 1) // bps
+    assert kvq.decode_attn_plan(c, 0) == (kvq.decode_attn_plan(c, 0)[0], 0)
+    assert kvq.decode_attn_plan(c, 8192, 5) == (5, (128 + 4) // 5)
+
+
+def test_strerror_names_every_status():
+    for code in range(-6, 1):
+        assert kvq.kvq_strerror(code) != "unknown status"
+    assert kvq.kvq_strerror(-99) == "unknown status"

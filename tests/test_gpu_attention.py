@@ -1,0 +1,134 @@
+"""GPU parity of decode_attn_qkv against the oracle's fp64 attention over the same
+dequantized cache (max over rows of ||o_gpu - o_ref||_inf / ||o_ref||_inf <= 2e-3),
+plus the properties that hold at any size: split-count invariance, padding-poison
+invariance, determinism and empty rows."""
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_block_amd import workloads as wl
+from helpers import (ATTN_TOL, attn_errors, gpu_attention, gpu_quantize, oracle_cache, say,
+                     to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+INT4, UINT8 = oracle.INT4_SYM, oracle.UINT8_ASYM
+
+
+def _workload_case(index, layer=0, seqs=None):
+    w = wl.WORKLOADS[index]
+    lens = wl.lengths(w)
+    n = int(lens.max())
+    k = wl.prefill_batch(w, layer, 0, n_tokens=n)
+    v = wl.prefill_batch(w, layer, 1, n_tokens=n)
+    q = wl.query(w, layer)
+    return w, k, v, q, lens
+
+
+@pytest.mark.parametrize("index", [0, 1, 2])
+def test_workload_attention_all_rows(index):
+    w, k, v, q, lens = _workload_case(index)
+    say("attention", w.name)
+    c = gpu_quantize(w.scheme, k, v, lens, w.max_blocks)
+    sm = wl.softmax_scale(w)
+    o = gpu_attention(c, q, sm, int(lens.max()))
+    ref = oracle.attention(c.host_arrays(), q, lens, sm)
+    norm_err, elem_err = attn_errors(o, ref)
+    print(f"{w.name}: normwise {norm_err:.3e} elementwise(floored) {elem_err:.3e}")
+    assert norm_err <= ATTN_TOL
+
+
+def test_ragged_32_layer_attention_sampled_layers():
+    w = wl.WORKLOADS[4]
+    for layer in (0, 13, 31):
+        _, k, v, q, lens = _workload_case(4, layer)
+        say("attention", w.name, "layer", layer)
+        c = gpu_quantize(w.scheme, k, v, lens, w.max_blocks)
+        sm = wl.softmax_scale(w)
+        o = gpu_attention(c, q, sm, int(lens.max()))
+        ref = oracle.attention(c.host_arrays(), q, lens, sm)
+        norm_err, _ = attn_errors(o, ref)
+        print(f"{w.name} layer {layer}: normwise {norm_err:.3e}")
+        assert norm_err <= ATTN_TOL
+
+
+def _small_case(scheme, D, seed=7, B=4, H=3, S=700, lens=(700, 1, 333, 64)):
+    g = wl.rng(wl.WORKLOADS[0], 60 + seed, scheme, D)
+    dist_v = "normal0.5" if scheme == UINT8 else "normal_outliers"
+    k = wl.draw(g, "normal_outliers", (B, S, H, D))
+    v = wl.draw(g, dist_v, (B, S, H, D))
+    q = wl.draw(g, "normal0", (B, H, D))
+    return k, v, q, np.array(lens, np.int32)
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_counts_all_agree_with_oracle(scheme, D):
+    """Every split size (1 block .. one split for the whole row, and the automatic
+    plan) is within tolerance of the oracle and within 1e-5 of each other."""
+    k, v, q, lens = _small_case(scheme, D)
+    MB = 11
+    c = gpu_quantize(scheme, k, v, lens, MB)
+    sm = float(np.float32(1) / np.sqrt(np.float32(D)))
+    ref = oracle.attention(c.host_arrays(), q, lens, sm)
+    outs = []
+    for bps in (0, 1, 2, 3, 4, 8, 11, 64):
+        say("split", scheme, D, "bps", bps)
+        o = gpu_attention(c, q, sm, int(lens.max()), bps)
+        norm_err, _ = attn_errors(o, ref)
+        assert norm_err <= ATTN_TOL, (bps, norm_err)
+        outs.append(o.astype(np.float64))
+    spread = max(np.abs(a - outs[0]).max() for a in outs)
+    assert spread <= 1e-5 * max(1.0, np.abs(outs[0]).max()) + 2 ** -10 * np.abs(outs[0]).max()
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+def test_padding_poison_and_determinism(scheme):
+    """Garbage in the padding bytes of each last block changes nothing (bitwise), and
+    repeated calls are bitwise identical."""
+    import torch
+    k, v, q, lens = _small_case(scheme, 128, seed=3, lens=(699, 5, 130, 64))
+    MB = 11
+    c = gpu_quantize(scheme, k, v, lens, MB)
+    sm = 0.08838834764831845
+    say("poison", scheme)
+    base = gpu_attention(c, q, sm, int(lens.max()))
+    for _ in range(3):
+        assert np.array_equal(gpu_attention(c, q, sm, int(lens.max())), base)
+    rs = np.random.default_rng(1)
+    for b, n in enumerate(lens):
+        j, t = divmod(int(n), 64)
+        if t:
+            for codes in (c.k_codes, c.v_codes):
+                junk = rs.integers(0, 256, codes[b, :, j, t:].shape, dtype=np.uint8)
+                codes[b, :, j, t:] = torch.from_numpy(junk).cuda()
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu_attention(c, q, sm, int(lens.max())), base)
+
+
+def test_empty_and_single_token_rows():
+    k, v, q, lens = _small_case(INT4, 128, seed=5, B=3, S=70, lens=(0, 1, 70))
+    c = gpu_quantize(INT4, k, v, lens, 2)
+    say("empty rows")
+    o = gpu_attention(c, q, 0.0883883476, 70)
+    ref = oracle.attention(c.host_arrays(), q, lens, 0.0883883476)
+    assert not o[0].any()
+    norm_err, _ = attn_errors(o, ref, rows=[(1, h) for h in range(3)] + [(2, h) for h in range(3)])
+    assert norm_err <= ATTN_TOL
+
+
+def test_split_and_combine_phases_equal_fused_call():
+    import decode_attention_block_amd as kvq
+    import torch
+    k, v, q, lens = _small_case(UINT8, 64, seed=8)
+    c = gpu_quantize(UINT8, k, v, lens, 11)
+    say("phases")
+    fused = gpu_attention(c, q, 0.125, int(lens.max()), 2)
+    qt = to_gpu(q)
+    out = torch.empty_like(qt)
+    ws = torch.empty(kvq.decode_attn_workspace_bytes(c, int(lens.max()), 2), dtype=torch.uint8,
+                     device="cuda")
+    kvq.decode_attn_split(c, qt, 0.125, ws, int(lens.max()), 2)
+    kvq.decode_attn_combine(c, out, ws, int(lens.max()), 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), fused)

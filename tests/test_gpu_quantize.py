@@ -1,0 +1,132 @@
+"""GPU parity of kv_quantize_blocks and kv_append against the oracle: bit-exact codes,
+scales and zero points (the quantizer is an encoding; the pages fix one result)."""
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_block_amd import workloads as wl
+from helpers import assert_cache_equal, gpu_quantize, oracle_cache, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+INT4, UINT8 = oracle.INT4_SYM, oracle.UINT8_ASYM
+
+
+@pytest.mark.parametrize("index", [0, 1, 2])
+def test_workload_prefill_bitexact(index):
+    """Whole-workload prefill of the tiny and both 8K workloads; the oracle checks
+    sequences 0 and B-1 of the 8K ones (all heads, all blocks)."""
+    w = wl.WORKLOADS[index]
+    say("prefill", w.name)
+    k = wl.prefill_batch(w, 0, 0)
+    v = wl.prefill_batch(w, 0, 1)
+    lens = wl.lengths(w)
+    c = gpu_quantize(w.scheme, k, v, lens, w.max_blocks)
+    gpu = c.host_arrays()
+    seqs = list(range(w.batch)) if w.batch <= 2 else [0, w.batch - 1]
+    ref = oracle_cache(w.scheme, k[seqs], v[seqs], lens[seqs], w.max_blocks)
+    sub = {kk: (vv[seqs] if isinstance(vv, np.ndarray) else vv) for kk, vv in gpu.items()}
+    sub["B"] = len(seqs)
+    assert_cache_equal(sub, ref, lens[seqs])
+
+
+def test_ragged_long_student_t_prefill_bitexact():
+    """The 32-layer ragged workload's layer 0 and layer 31 (Student-t values, lengths
+    not multiples of 64); sequences 0 and 7 checked by the oracle."""
+    w = wl.WORKLOADS[4]
+    lens = wl.lengths(w)
+    for layer in (0, 31):
+        say("prefill", w.name, "layer", layer)
+        k = wl.prefill_batch(w, layer, 0, n_tokens=int(lens.max()))
+        v = wl.prefill_batch(w, layer, 1, n_tokens=int(lens.max()))
+        c = gpu_quantize(w.scheme, k, v, lens, w.max_blocks)
+        gpu = c.host_arrays()
+        seqs = [0, 7]
+        ref = oracle_cache(w.scheme, k[seqs], v[seqs], lens[seqs], w.max_blocks)
+        sub = {kk: (vv[seqs] if isinstance(vv, np.ndarray) else vv) for kk, vv in gpu.items()}
+        sub["B"] = 2
+        assert_cache_equal(sub, ref, lens[seqs])
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("D", [64, 128])
+def test_edge_cases_bitexact(scheme, D):
+    """Ragged lengths 0, 1, 63, 64, 65, 200; a transposed [B][H][S][D] input layout;
+    constant, all-zero, subnormal and tie-valued blocks."""
+    say("edge", scheme, D)
+    rs = np.random.default_rng(100 + D + scheme)
+    B, H, S = 6, 3, 200
+    base = rs.standard_normal((B, H, S, D)).astype(np.float16)
+    base[1, 0, :64] = 0                       # all-zero block
+    base[1, 1, :64] = np.float16(3.0)         # positive constant block
+    base[1, 2, :64] = np.float16(-2.0)        # negative constant block
+    base[2, 0, :64] = (rs.standard_normal((64, D)) * 1e-6).astype(np.float16)  # subnormals
+    base[2, 1, :64] = (rs.integers(-15, 16, (64, D)) * 0.5).astype(np.float16)  # ties
+    base[2, 1, 0, 0] = np.float16(7.5)
+    k = base.transpose(0, 2, 1, 3)            # [B][S][H][D] view with S stride D
+    v = np.ascontiguousarray(base[::-1]).transpose(0, 2, 1, 3)
+    lens = np.array([0, 64, 200, 1, 63, 65], np.int32)
+    MB = 4
+    import decode_attention_block_amd as kvq
+    import torch
+    c = kvq.KVCache(scheme, B, H, D, MB)
+    c.seq_lens.copy_(torch.from_numpy(lens))
+    kt = to_gpu(base).permute(0, 2, 1, 3)
+    vt = to_gpu(np.ascontiguousarray(base[::-1])).permute(0, 2, 1, 3)
+    kvq.kv_quantize_blocks(c, kt, vt, int(lens.max()))
+    torch.cuda.synchronize()
+    ref = oracle_cache(scheme, np.ascontiguousarray(k), np.ascontiguousarray(v), lens, MB)
+    assert_cache_equal(c.host_arrays(), ref, lens)
+    # padding bytes of each row's last block are 0; blocks past the length untouched
+    g = c.host_arrays()
+    assert not g["k_codes"][3, :, 0, 1:].any()
+    assert not g["k_codes"][3, :, 1:].any() and not g["k_scale"][3, :, 1:].any()
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("D", [64, 128])
+def test_append_matches_bulk_every_step(scheme, D):
+    """Token-by-token kv_append from prefill lengths 0, 1, 61, 64 and 127 through 0->1,
+    63->64, 64->65 and 127->128; after every step the whole cache equals the oracle's
+    quantization of the history and seq_lens has advanced by one."""
+    import decode_attention_block_amd as kvq
+    import torch
+    say("append", scheme, D)
+    B, H, S = 5, 2, 200
+    w = wl.WORKLOADS[0]
+    g = wl.rng(w, 50, scheme, D)
+    dist_v = "normal0.5" if scheme == UINT8 else "normal_outliers"
+    k = wl.draw(g, "normal_outliers", (B, S, H, D))
+    v = wl.draw(g, dist_v, (B, S, H, D))
+    start = np.array([0, 1, 61, 64, 127], np.int32)
+    MB = 4
+    c = gpu_quantize(scheme, k, v, start, MB)
+    lens = start.copy()
+    for step in range(72):
+        kn = to_gpu(k[np.arange(B), lens])   # [B][H][D]
+        vn = to_gpu(v[np.arange(B), lens])
+        kvq.kv_append(c, kn, vn, int(lens.max()) + 1)
+        lens = lens + 1
+        torch.cuda.synchronize()
+        assert np.array_equal(c.seq_lens.cpu().numpy(), lens)
+        ref = oracle_cache(scheme, k, v, lens, MB)
+        assert_cache_equal(c.host_arrays(), ref, lens)
+
+
+def test_append_at_capacity_leaves_row_unchanged():
+    import decode_attention_block_amd as kvq
+    import torch
+    say("append capacity")
+    B, H, D, MB = 2, 2, 64, 1
+    rs = np.random.default_rng(9)
+    k = rs.standard_normal((B, 64, H, D)).astype(np.float16)
+    lens = np.array([64, 10], np.int32)
+    c = gpu_quantize(INT4, k, k, lens, MB)
+    before = c.host_arrays()
+    kn = to_gpu(rs.standard_normal((B, H, D)).astype(np.float16))
+    kvq.kv_append(c, kn, kn, 11)
+    torch.cuda.synchronize()
+    assert list(c.seq_lens.cpu().numpy()) == [64, 11]
+    after = c.host_arrays()
+    assert np.array_equal(after["k_codes"][0], before["k_codes"][0])
+    assert np.array_equal(after["k_scale"][0], before["k_scale"][0])
