@@ -52,11 +52,10 @@ __device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast
 template <int SCHEME, int D>
 struct Query {
   using G = AGeo<SCHEME, D>;
-  // The lane's query channels in binary32. For int4 the odd channels are read from a
-  // high nibble (unit 2^-20 instead of 2^-24) and are stored pre-divided by 16 (exact),
-  // so every product lands in the unit 2^-24.
-  float qf[G::kDPL];
-  float sum;  // sum of the lane's query channels (unscaled)
+  // The lane's query channels as loaded: fp16, two per register (channel 2k in the low
+  // half). v_fma_mix_f32 reads either half as an fp16 operand.
+  uint32_t qh[G::kDPL / 2];
+  float sum;  // sum of the lane's query channels
 
   __device__ __forceinline__ void load(const uint16_t* q) {
     constexpr int kLoads = G::kDPL / 8;
@@ -64,56 +63,69 @@ struct Query {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const uint4 r = *reinterpret_cast<const uint4*>(q + 8 * i);
+      qh[4 * i + 0] = r.x;
+      qh[4 * i + 1] = r.y;
+      qh[4 * i + 2] = r.z;
+      qh[4 * i + 3] = r.w;
       float x[8];
       unpack8(r, x);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        sum += x[k];
-        qf[8 * i + k] = (SCHEME == KVQ_INT4_SYM && (k & 1)) ? x[k] * 0.0625f : x[k];
-      }
+      for (int k = 0; k < 8; ++k) sum += x[k];
     }
+  }
+  // query channel c (0 <= c < DPL) as an fp16 value
+  __device__ __forceinline__ _Float16 at(int c) const {
+    const half2_t h = as_h2(qh[c >> 1]);
+    return (c & 1) ? h.y : h.x;
   }
 };
 
+__device__ __forceinline__ float fma_h(_Float16 a, _Float16 b, float c) {
+  return __builtin_fmaf(static_cast<float>(a), static_cast<float>(b), c);
+}
+
 // Partial dot product of one 16-byte code chunk (channels c0 .. c0+31 for int4,
 // c0 .. c0+15 for uint8) with the lane's query, in units of the stored unsigned code u
-// (int4: u = c + 8; uint8: u = c) times 2^-24.
-template <int SCHEME>
-__device__ __forceinline__ float chunk_dot(const uint4& raw, const float* qf) {
+// (int4: u = c + 8; uint8: u = c). Code and query are both fp16 operands of
+// v_fma_mix_f32; the products are exact in binary32.
+template <int SCHEME, int D>
+__device__ __forceinline__ float chunk_dot(const uint4& raw, const Query<SCHEME, D>& q) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  float a0 = 0.0f, a1 = 0.0f;
   if constexpr (SCHEME == KVQ_INT4_SYM) {
+    float lo = 0.0f, hi = 0.0f;  // units 2^-24 (low nibbles) and 2^-20 (high nibbles)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t u = w[j];
       const uint32_t u8 = u >> 8;
-      const half2_t p0 = as_h2(u & 0x000F000Fu);   // channels 0, 4   (2^-24)
-      const half2_t p1 = as_h2(u & 0x00F000F0u);   // channels 1, 5   (2^-20)
-      const half2_t p2 = as_h2(u8 & 0x000F000Fu);  // channels 2, 6   (2^-24)
-      const half2_t p3 = as_h2(u8 & 0x00F000F0u);  // channels 3, 7   (2^-20)
-      const float* qj = qf + 8 * j;
-      a0 = __builtin_fmaf(static_cast<float>(p0.x), qj[0], a0);
-      a1 = __builtin_fmaf(static_cast<float>(p0.y), qj[4], a1);
-      a0 = __builtin_fmaf(static_cast<float>(p1.x), qj[1], a0);
-      a1 = __builtin_fmaf(static_cast<float>(p1.y), qj[5], a1);
-      a0 = __builtin_fmaf(static_cast<float>(p2.x), qj[2], a0);
-      a1 = __builtin_fmaf(static_cast<float>(p2.y), qj[6], a1);
-      a0 = __builtin_fmaf(static_cast<float>(p3.x), qj[3], a0);
-      a1 = __builtin_fmaf(static_cast<float>(p3.y), qj[7], a1);
+      const half2_t p0 = as_h2(u & 0x000F000Fu);   // channels 0, 4
+      const half2_t p1 = as_h2(u & 0x00F000F0u);   // channels 1, 5
+      const half2_t p2 = as_h2(u8 & 0x000F000Fu);  // channels 2, 6
+      const half2_t p3 = as_h2(u8 & 0x00F000F0u);  // channels 3, 7
+      const int c = 8 * j;
+      lo = fma_h(p0.x, q.at(c + 0), lo);
+      hi = fma_h(p1.x, q.at(c + 1), hi);
+      lo = fma_h(p2.x, q.at(c + 2), lo);
+      hi = fma_h(p3.x, q.at(c + 3), hi);
+      lo = fma_h(p0.y, q.at(c + 4), lo);
+      hi = fma_h(p1.y, q.at(c + 5), hi);
+      lo = fma_h(p2.y, q.at(c + 6), lo);
+      hi = fma_h(p3.y, q.at(c + 7), hi);
     }
+    return __builtin_fmaf(hi, 1048576.0f, lo * 16777216.0f);
   } else {
+    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const half2_t e = as_h2(w[j] & 0x00FF00FFu);         // channels 0, 2
       const half2_t f = as_h2((w[j] >> 8) & 0x00FF00FFu);  // channels 1, 3
-      const float* qj = qf + 4 * j;
-      a0 = __builtin_fmaf(static_cast<float>(e.x), qj[0], a0);
-      a1 = __builtin_fmaf(static_cast<float>(e.y), qj[2], a1);
-      a0 = __builtin_fmaf(static_cast<float>(f.x), qj[1], a0);
-      a1 = __builtin_fmaf(static_cast<float>(f.y), qj[3], a1);
+      const int c = 4 * j;
+      a0 = fma_h(e.x, q.at(c + 0), a0);
+      a1 = fma_h(f.x, q.at(c + 1), a1);
+      a0 = fma_h(e.y, q.at(c + 2), a0);
+      a1 = fma_h(f.y, q.at(c + 3), a1);
     }
+    return (a0 + a1) * 16777216.0f;
   }
-  return (a0 + a1) * 16777216.0f;
 }
 
 // o[k] += p * c_k for the 16-byte code chunk, c = u - offset. The offset is taken out
@@ -189,8 +201,10 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   q.load(a.q + row * D + chunk * DPL);
   const float qsum_row = group_sum<LPT>(q.sum);
 
-  const uint8_t* kbase = a.k_codes + row * a.max_blocks * kBlock * G::kRowBytes + lane * 16;
-  const uint8_t* vbase = a.v_codes + row * a.max_blocks * kBlock * G::kRowBytes + lane * 16;
+  // Row bases are wave-uniform (scalar registers); each lane adds only its 32-bit offset.
+  const uint8_t* kbase = a.k_codes + row * a.max_blocks * kBlock * G::kRowBytes;
+  const uint8_t* vbase = a.v_codes + row * a.max_blocks * kBlock * G::kRowBytes;
+  const uint32_t lane_off = static_cast<uint32_t>(lane) * 16u;
   const float* ks = a.k_scale + row * a.max_blocks;
   const float* vs = a.v_scale + row * a.max_blocks;
   const float* kz = a.k_zero + row * a.max_blocks;
@@ -202,34 +216,22 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   float m = -__builtin_inff();  // running max of the base-2 scores (wave-uniform)
   float l = 0.0f;               // sum of weights over this lane's tokens
 
-  auto load_block = [&](int blk, uint4 (&kk)[TPL], uint4 (&vv)[TPL]) {
-    const int64_t off = static_cast<int64_t>(blk) * kBlock * G::kRowBytes;
+  auto load_codes = [&](const uint8_t* base, int blk, uint4 (&r)[TPL]) {
+    const uint8_t* blk_base = base + static_cast<int64_t>(blk) * kBlock * G::kRowBytes;
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      kk[i] = *reinterpret_cast<const uint4*>(kbase + off + i * kWave * 16);
-      vv[i] = *reinterpret_cast<const uint4*>(vbase + off + i * kWave * 16);
-    }
+    for (int i = 0; i < TPL; ++i)
+      r[i] = *reinterpret_cast<const uint4*>(blk_base + (lane_off + i * kWave * 16));
   };
 
-  auto process_block = [&](int blk, const uint4 (&kr)[TPL], const uint4 (&vr)[TPL]) {
+  // Scores of the lane's TPL tokens of block blk (base-2 logits), then the online
+  // softmax update; returns the weights p (relative to the running max m).
+  auto block_weights = [&](int blk, const uint4 (&kr)[TPL], float (&p)[TPL]) {
     const float sk = ks[blk] * a.qk_scale;
-    const float sv = vs[blk];
-    float bias_k;
-    half2_t off_lo, off_hi;
-    if constexpr (SCHEME == KVQ_INT4_SYM) {
-      bias_k = 8.0f * qsum_row;
-      off_lo = as_h2(0x80088008u);  // -8 * 2^-24 in both halves
-      off_hi = as_h2(0x80808080u);  // -8 * 2^-20 = -128 * 2^-24
-    } else {
-      bias_k = kz[blk] * qsum_row;
-      const _Float16 zh = static_cast<_Float16>(vz[blk] * -5.9604644775390625e-08f);
-      off_lo = half2_t{zh, zh};
-      off_hi = off_lo;
-    }
+    const float bias_k = (SCHEME == KVQ_INT4_SYM ? 8.0f : kz[blk]) * qsum_row;
     float s[TPL];
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
-      const float part = chunk_dot<SCHEME>(kr[i], q.qf);
+      const float part = chunk_dot<SCHEME, D>(kr[i], q);
       s[i] = (group_sum<LPT>(part) - bias_k) * sk;
     }
     if (blk == nb - 1) {  // tokens past the length in the last block weigh nothing
@@ -242,38 +244,64 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
 #pragma unroll
     for (int i = 1; i < TPL; ++i) mb = fmaxf(mb, s[i]);
     mb = wave_max(mb);
-    if (mb > m) {
+    if (mb > m) {  // wave-uniform
       const float alpha = __builtin_amdgcn_exp2f(m - mb);
       l *= alpha;
 #pragma unroll
       for (int k = 0; k < DPL; ++k) o[k] *= alpha;
       m = mb;
     }
-    float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
-      const float p = __builtin_amdgcn_exp2f(s[i] - m);
-      psum += p;
-      chunk_axpy<SCHEME>(vr[i], p * sv, off_lo, off_hi, o);
+      p[i] = __builtin_amdgcn_exp2f(s[i] - m);
+      l += p[i];
     }
-    l += psum;
   };
 
-  // Each wave takes blocks wave, wave + W, wave + 2W, ... of the split; the next
-  // block's codes are in flight while the current one is processed (ping-pong).
-  uint4 ka[TPL], va[TPL], kb[TPL], vb[TPL];
+  // o += sum_i p_i * sv * (V code - offset) over the lane's TPL tokens of block blk.
+  auto block_accumulate = [&](int blk, const uint4 (&vr)[TPL], const float (&p)[TPL]) {
+    const float sv = vs[blk];
+    half2_t off_lo, off_hi;
+    if constexpr (SCHEME == KVQ_INT4_SYM) {
+      off_lo = as_h2(0x80088008u);  // -8 * 2^-24 in both halves
+      off_hi = as_h2(0x80808080u);  // -8 * 2^-20 = -128 * 2^-24
+    } else {
+      const _Float16 zh = static_cast<_Float16>(vz[blk] * -5.9604644775390625e-08f);
+      off_lo = half2_t{zh, zh};
+      off_hi = off_lo;
+    }
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) chunk_axpy<SCHEME>(vr[i], p[i] * sv, off_lo, off_hi, o);
+  };
+
+  // Each wave takes blocks wave, wave + W, wave + 2W, ... of the split. Software
+  // pipeline over three code buffers: while block n is processed, block n+1's K codes
+  // are requested into the free buffer before n's scores, and its V codes into n's K
+  // buffer once the scores are done. The roles (K, V, free) rotate with period three,
+  // so only three 16-byte-per-lane buffers per token are ever live.
+  uint4 r0[TPL], r1[TPL], r2[TPL];
+  float p[TPL];
+  auto step = [&](int blk, uint4 (&kcur)[TPL], uint4 (&vcur)[TPL], uint4 (&kfree)[TPL]) {
+    const int next = blk + kSplitWaves;
+    const bool more = next < blk_end;
+    if (more) load_codes(kbase, next, kfree);
+    block_weights(blk, kcur, p);
+    if (more) load_codes(vbase, next, kcur);
+    block_accumulate(blk, vcur, p);
+    return more;
+  };
   int blk = blk_begin + wave;
-  if (blk < blk_end) load_block(blk, ka, va);
-  while (blk < blk_end) {
-    int next = blk + kSplitWaves;
-    if (next < blk_end) load_block(next, kb, vb);
-    process_block(blk, ka, va);
-    blk = next;
-    if (blk >= blk_end) break;
-    next = blk + kSplitWaves;
-    if (next < blk_end) load_block(next, ka, va);
-    process_block(blk, kb, vb);
-    blk = next;
+  if (blk < blk_end) {
+    load_codes(kbase, blk, r0);
+    load_codes(vbase, blk, r1);
+    while (true) {
+      if (!step(blk, r0, r1, r2)) break;
+      blk += kSplitWaves;
+      if (!step(blk, r2, r0, r1)) break;
+      blk += kSplitWaves;
+      if (!step(blk, r1, r2, r0)) break;
+      blk += kSplitWaves;
+    }
   }
 
   // Per-lane result in true units: o_true[k] = o[k] * unit(k).
