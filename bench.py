@@ -3,9 +3,10 @@
 
 One step = one decode step of the whole hot path on the 8K int4 workload (batch 8,
 32 heads, head_dim 128, context 8192 per sequence, 4-bit block codes, 64-token blocks):
-kv_append quantizes one new token per sequence into its row's tail block, then
-decode_attn_split + decode_attn_combine (the two kernels of decode_attn_qkv) attend
-one fp16 query per (sequence, head) over the whole compressed cache.
+kv_append quantizes one new token per sequence into its row's tail block (one kernel),
+then decode_attn_qkv attends one fp16 query per (sequence, head) over the whole
+compressed cache (one kernel: split-K over the context, the last workgroup of each row
+merges its splits).
 
 Inputs are synthetic and seeded (decode_attention_block_amd.workloads), already
 resident in HBM when timing starts. Steps rotate over enough copies of the cache
@@ -66,11 +67,6 @@ def attention_bytes(w, lens):
         total += w.heads * (2 * int(n) * code_bytes_per_token(w) + nb * per_block_scalars)
     total += 2 * w.batch * w.heads * w.head_dim * 2  # q in, out
     return total
-
-
-def split_bytes(w, lens):
-    """Algorithmic bytes of the split kernel: codes, scales and q (out is the combine's)."""
-    return attention_bytes(w, lens) - w.batch * w.heads * w.head_dim * 2
 
 
 def append_bytes(w):
@@ -177,7 +173,7 @@ def main():
     max_len_all = w.context + growth
     ws_bytes = max(kvq.decode_attn_workspace_bytes(caches[0], L, args.blocks_per_split)
                    for L in range(w.context, max_len_all + 1))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")  # counters start at zero
     out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
     sm = wl.softmax_scale(w)
     lens_host = [w.context] * copies
@@ -185,9 +181,9 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
-    ev_split = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(args.steps)]
-    step_bytes, step_split_bytes = [], []
+    ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    step_bytes, step_attn_bytes = [], []
 
     def step(i, timed_index):
         ci = i % copies
@@ -197,14 +193,13 @@ def main():
         lens_host[ci] += 1
         L = lens_host[ci]
         if timed_index is not None:
-            ev_split[timed_index][0].record()
-        kvq.decode_attn_split(c, queries[i], sm, ws, L, args.blocks_per_split)
+            ev_attn[timed_index][0].record()
+        kvq.decode_attn_qkv(c, queries[i], sm, out, ws, L, args.blocks_per_split)
         if timed_index is not None:
-            ev_split[timed_index][1].record()
+            ev_attn[timed_index][1].record()
             lens = [L] * B
-            step_split_bytes.append(split_bytes(w, lens))
+            step_attn_bytes.append(attention_bytes(w, lens))
             step_bytes.append(attention_bytes(w, lens) + append_bytes(w))
-        kvq.decode_attn_combine(c, out, ws, L, args.blocks_per_split)
 
     for i in range(args.warmup):
         step(i, None)
@@ -219,12 +214,12 @@ def main():
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
-    split_ms = [a.elapsed_time(b) for a, b in ev_split]
-    avg_split_ms = float(np.mean(split_ms))
+    attn_ms = [a.elapsed_time(b) for a, b in ev_attn]
+    avg_attn_ms = float(np.mean(attn_ms))
 
     ms_per_step = total_ms / args.steps
     value = sum(step_bytes) / (total_ms / 1e3) / 1e9
-    achieved = float(np.mean(step_split_bytes)) / (avg_split_ms / 1e3) / 1e9
+    achieved = float(np.mean(step_attn_bytes)) / (avg_attn_ms / 1e3) / 1e9
     bps, n_split = kvq.decode_attn_plan(caches[0], max_len_all, args.blocks_per_split)
     result = {
         "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s, int4 KV, B=8 ctx 8K",
@@ -245,13 +240,14 @@ def main():
                    "context": w.context, "context_growth_max": growth,
                    "kv_format": "int4 block-64 symmetric" if w.scheme == 0
                    else "uint8 block-64 asymmetric",
-                   "step": "kv_append + decode_attn_split + decode_attn_combine",
+                   "step": "kv_append + decode_attn_qkv",
                    "cache_copies_rotated": copies, "blocks_per_split": bps,
                    "splits_per_row": n_split, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "attn_split_kernel", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "avg_kernel_us": avg_split_ms * 1e3,
-                     "algorithmic_bytes_per_launch": float(np.mean(step_split_bytes))},
+        "roofline": {"bound": "hbm", "kernel": "attn_split_int4_kernel<128> (decode_attn_qkv)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "avg_kernel_us": avg_attn_ms * 1e3,
+                     "algorithmic_bytes_per_launch": float(np.mean(step_attn_bytes))},
         "prefill_quantize": {"ms": float(np.median(prefill_ms)),
                              "gbs": (2 * B * w.context * H * D * 2 + per_cache)
                              / (float(np.median(prefill_ms)) / 1e3) / 1e9},

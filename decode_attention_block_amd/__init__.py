@@ -141,6 +141,14 @@ def decode_attn_workspace_bytes(cache, max_len, blocks_per_split=0):
                                                       int(blocks_per_split))
 
 
+def make_workspace(cache, max_len, blocks_per_split=0, device="cuda"):
+    """A zero-filled device workspace of decode_attn_workspace_bytes(...) bytes (its
+    arrival counters must start at zero; the library leaves them zero)."""
+    import torch
+    n = decode_attn_workspace_bytes(cache, max_len, blocks_per_split)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
 def decode_attn_qkv(cache, q, softmax_scale, out, workspace, max_len, blocks_per_split=0,
                     stream=None):
     """q, out: fp16 CUDA tensors [B][H][D] contiguous; workspace: CUDA tensor of at least
@@ -203,11 +211,17 @@ class KVCache:
     def capacity(self):
         return self.max_blocks * BLOCK_TOKENS
 
-    def host_arrays(self):
-        """The cache buffers copied to numpy, keyed like the oracle's cache dicts."""
+    def host_arrays(self, natural=True):
+        """The cache buffers copied to numpy, keyed like the oracle's cache dicts. With
+        natural=True int4 codes are returned in natural [token][channel] order (see
+        layout.py); otherwise as stored."""
+        from . import layout
         out = {"scheme": self.scheme, "B": self.batch, "H": self.heads, "D": self.head_dim,
                "max_blocks": self.max_blocks}
         for key in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
             t = getattr(self, key)
             out[key] = None if t is None else t.cpu().numpy()
+        if natural and self.scheme == INT4_SYM:
+            out["k_codes"] = layout.int4_to_natural(out["k_codes"], "k")
+            out["v_codes"] = layout.int4_to_natural(out["v_codes"], "v")
         return out

@@ -1,5 +1,6 @@
 // kvq_api.hip — the C ABI of libkvq (declared in include/kvq.h): argument validation,
-// the split plan and kernel launches. No allocation, no state between calls.
+// the split plan and kernel launches. No allocation; nothing kept between calls except
+// what lives in caller-owned buffers (the workspace's arrival counters).
 #include <stdint.h>
 
 #include "kvq.h"
@@ -9,7 +10,7 @@ namespace {
 
 constexpr int kBlockTokens = KVQ_BLOCK_TOKENS;
 constexpr int kSplitWavesHost = 4;      // waves per split workgroup (kvq_attn.hip)
-constexpr int64_t kTargetSplitGroups = 1024;  // workgroups the automatic plan aims for
+constexpr int64_t kTargetSplitGroups = 512;  // automatic plan: ~2 workgroups per MI355X CU
 constexpr int kMaxAutoBlocksPerSplit = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -39,18 +40,20 @@ int check_len(const kvq_cache* c, int32_t max_len) {
 
 int n_blocks_for(int32_t len) { return (len + kBlockTokens - 1) / kBlockTokens; }
 
-// Blocks per split when the caller leaves it to the library: enough splits per row
-// that the launch has about kTargetSplitGroups workgroups, each split a whole number
-// of blocks per wave, at most kMaxAutoBlocksPerSplit blocks.
+// Blocks per split when the caller leaves it to the library: the context of all rows
+// spread over about kTargetSplitGroups workgroups (each split's merge costs a few
+// microseconds of latency, so fewer, longer splits win once the GPU is full), a whole
+// number of blocks per wave, between 4 and kMaxAutoBlocksPerSplit blocks.
 int auto_blocks_per_split(const kvq_cache* c, int nb) {
   const int64_t rows = static_cast<int64_t>(c->batch) * c->heads;
-  int64_t splits = (kTargetSplitGroups + rows - 1) / rows;
-  if (splits < 1) splits = 1;
-  int64_t bps = (nb + splits - 1) / splits;
-  bps = (bps + kSplitWavesHost - 1) / kSplitWavesHost * kSplitWavesHost;
+  int64_t bps = (rows * nb + kTargetSplitGroups - 1) / kTargetSplitGroups;
   if (bps < kSplitWavesHost) bps = kSplitWavesHost;
   if (bps > kMaxAutoBlocksPerSplit) bps = kMaxAutoBlocksPerSplit;
-  return static_cast<int>(bps);
+  // even out the splits of a row (no short last split), whole blocks per wave
+  const int64_t splits = (nb + bps - 1) / bps;
+  if (splits > 0) bps = (nb + splits - 1) / splits;
+  bps = (bps + kSplitWavesHost - 1) / kSplitWavesHost * kSplitWavesHost;
+  return static_cast<int>(bps < kSplitWavesHost ? kSplitWavesHost : bps);
 }
 
 int plan(const kvq_cache* c, int32_t max_len, int32_t bps_req, int* bps, int* n_split) {
@@ -65,15 +68,22 @@ int plan(const kvq_cache* c, int32_t max_len, int32_t bps_req, int* bps, int* n_
   return KVQ_OK;
 }
 
+// Workspace layout: [rows] uint32 arrival counters (padded to 256 bytes), then the
+// partial outputs [rows][n_split][D] and partial (max, sum) [rows][n_split][2] floats.
+size_t counter_bytes(const kvq_cache* c) {
+  const size_t rows = static_cast<size_t>(c->batch) * c->heads;
+  return (rows * sizeof(uint32_t) + 255) / 256 * 256;
+}
+
 size_t workspace_bytes(const kvq_cache* c, int n_split) {
   const size_t parts = static_cast<size_t>(c->batch) * c->heads * n_split;
-  return parts * (static_cast<size_t>(c->head_dim) + 2) * sizeof(float);
+  return counter_bytes(c) + parts * (static_cast<size_t>(c->head_dim) + 2) * sizeof(float);
 }
 
 // Fills the attention launch descriptor after validating the workspace.
 int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
               void* workspace, size_t workspace_bytes_given, int32_t max_len, int32_t bps_req,
-              kvq::AttnArgs* a) {
+              int fused, kvq::AttnArgs* a) {
   int bps, n_split;
   int rc = plan(c, max_len, bps_req, &bps, &n_split);
   if (rc != KVQ_OK) return rc;
@@ -92,8 +102,11 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
   a->seq_lens = c->seq_lens;
   a->q = static_cast<const uint16_t*>(q);
   a->out = static_cast<uint16_t*>(out);
-  a->ws_o = static_cast<float*>(workspace);
-  a->ws_ml = n_split > 0 ? static_cast<float*>(workspace) + parts * c->head_dim : nullptr;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a->counters = n_split > 0 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+  a->ws_o = n_split > 0 ? reinterpret_cast<float*>(ws + counter_bytes(c)) : nullptr;
+  a->ws_ml = n_split > 0 ? a->ws_o + parts * c->head_dim : nullptr;
+  a->fused = fused;
   a->heads = c->heads;
   a->max_blocks = c->max_blocks;
   a->max_len = max_len;
@@ -152,6 +165,9 @@ int kv_append(const kvq_cache* cache, const void* k_new, const void* v_new,
   if (rc != KVQ_OK) return rc;
   if (!cache->k_tail || !cache->v_tail || !k_new || !v_new) return KVQ_EINVAL;
   if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_EALIGN;
+  // the arrival ticket lives in the top 8 bits of each length
+  if (cache->heads > 255 || static_cast<int64_t>(cache->max_blocks) * kBlockTokens >= (1 << 24))
+    return KVQ_ENOTSUP;
   kvq::AppendArgs a;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
@@ -196,7 +212,7 @@ int decode_attn_split(const kvq_cache* cache, const void* q, float softmax_scale
   if (!aligned16(q)) return KVQ_EALIGN;
   kvq::AttnArgs a;
   const int rc = attn_args(cache, q, softmax_scale, nullptr, workspace, workspace_bytes_given,
-                           max_len, blocks_per_split, &a);
+                           max_len, blocks_per_split, 0, &a);
   if (rc != KVQ_OK) return rc;
   if (a.n_split == 0) return KVQ_OK;
   const hipError_t e = kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a,
@@ -211,7 +227,7 @@ int decode_attn_combine(const kvq_cache* cache, void* out, void* workspace,
   if (!aligned16(out)) return KVQ_EALIGN;
   kvq::AttnArgs a;
   const int rc = attn_args(cache, nullptr, 1.0f, out, workspace, workspace_bytes_given, max_len,
-                           blocks_per_split, &a);
+                           blocks_per_split, 0, &a);
   if (rc != KVQ_OK) return rc;
   const hipError_t e = kvq::launch_attn_combine(cache->head_dim, cache->batch, a,
                                                 static_cast<hipStream_t>(stream));
@@ -225,15 +241,14 @@ int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, 
   if (!aligned16(q) || !aligned16(out)) return KVQ_EALIGN;
   kvq::AttnArgs a;
   const int rc = attn_args(cache, q, softmax_scale, out, workspace, workspace_bytes_given,
-                           max_len, blocks_per_split, &a);
+                           max_len, blocks_per_split, 1, &a);
   if (rc != KVQ_OK) return rc;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.n_split > 0) {
-    if (kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a, s) != hipSuccess)
-      return KVQ_EHIP;
-  }
-  return kvq::launch_attn_combine(cache->head_dim, cache->batch, a, s) == hipSuccess ? KVQ_OK
-                                                                                      : KVQ_EHIP;
+  // One launch: the last workgroup of each row merges its splits. With no context at all
+  // a single split column still runs so that every row's zeros are written.
+  if (a.n_split == 0) a.n_split = 1;
+  return kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a,
+                                static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK
+                                                                                : KVQ_EHIP;
 }
 
 const char* kvq_strerror(int status) {

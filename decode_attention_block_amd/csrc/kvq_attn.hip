@@ -27,7 +27,9 @@
 //  * online softmax in base 2 with a wave-uniform running max: the rescale of the
 //    accumulators happens only when a block raises the max;
 //  * at the end of a split the waves' states are merged through LDS into one partial
-//    (max, sum, o[D]) per split.
+//    (max, sum, o[D]) per split; in fused mode (decode_attn_qkv) the last workgroup of
+//    each row to finish merges the row's partials itself, otherwise the combine kernel
+//    does (decode_attn_split + decode_attn_combine).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -48,6 +50,90 @@ struct AGeo {
 
 __device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
 
+// 16-byte load of codes that are read once per call: non-temporal, so the stream does
+// not evict what is reused (scales, partials) from the caches.
+__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Partial states cross workgroups (and L2 slices: the eight XCDs do not share an L2)
+// through agent-scope atomic stores and loads, which go to memory instead of a
+// possibly stale L2 line; a full device-scope fence would write back and invalidate
+// the whole L2 in every workgroup.
+__device__ __forceinline__ void store_shared(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Log-sum-exp merge of the n partial states of one row into its fp16 output channel d:
+// M = max_j m_j, o = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M); zeros when n = 0.
+template <int D, bool kCoherent>
+__device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t row, int n, int d) {
+  auto ld = [](const float* p) { return kCoherent ? load_shared(p) : *p; };
+  _Float16 r = 0;
+  if (n > 0) {
+    const float* ml = a.ws_ml + row * a.n_split * 2;
+    const float* po = a.ws_o + row * a.n_split * D + d;
+    float M = ld(ml);
+    for (int j = 1; j < n; ++j) M = fmaxf(M, ld(ml + 2 * j));
+    float L = 0.0f, acc = 0.0f;
+    for (int j = 0; j < n; ++j) {
+      const float w = __builtin_amdgcn_exp2f(ld(ml + 2 * j) - M);
+      L = __builtin_fmaf(w, ld(ml + 2 * j + 1), L);
+      acc = __builtin_fmaf(w, ld(po + j * D), acc);
+    }
+    r = static_cast<_Float16>(acc / L);
+  }
+  a.out[row * D + d] = __builtin_bit_cast(uint16_t, r);
+}
+
+// End of a split: thread d < D holds channel d of the split's merged (unnormalised)
+// output, M and L its max and weight sum. A single-split row in fused mode is written
+// out directly. Otherwise the partial goes to the workspace; in fused mode the
+// workgroup then waits until its stores have reached memory, takes an arrival ticket
+// for its row, and the last workgroup to arrive merges all of the row's partials and
+// resets the row's counter.
+template <int D>
+__device__ __forceinline__ void finish_split(const AttnArgs& a, int64_t row, int split, int n_row,
+                                             float od, float M, float L) {
+  const int tid = threadIdx.x;
+  if (a.fused && n_row == 1) {
+    if (tid < D) a.out[row * D + tid] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(od / L));
+    return;
+  }
+  float* po = a.ws_o + (row * a.n_split + split) * D;
+  float* ml = a.ws_ml + (row * a.n_split + split) * 2;
+  if (!a.fused) {
+    if (tid < D) po[tid] = od;
+    if (tid == 0) {
+      ml[0] = M;
+      ml[1] = L;
+    }
+    return;
+  }
+  if (tid < D) store_shared(po + tid, od);
+  if (tid == 0) {
+    store_shared(ml, M);
+    store_shared(ml + 1, L);
+  }
+  __shared__ uint32_t ticket;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores completed
+  __syncthreads();
+  // system scope: the read-modify-write is performed at memory, past the per-XCD L2s
+  if (tid == 0)
+    ticket = __hip_atomic_fetch_add(a.counters + row, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  if (ticket == static_cast<uint32_t>(n_row - 1)) {
+    if (tid < D) merge_row<D, true>(a, row, n_row, tid);
+    if (tid == 0)
+      __hip_atomic_store(a.counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
 
 template <int SCHEME, int D>
 struct Query {
@@ -188,7 +274,12 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   len = len < 0 ? 0 : min(len, min(a.max_len, cap));
   const int nb = (len + kBlock - 1) / kBlock;
   const int blk_begin = split * a.bps;
-  if (blk_begin >= nb) return;  // uniform over the workgroup
+  if (blk_begin >= nb) {  // uniform over the workgroup
+    // an empty row has no split to merge: in fused mode split 0 writes its zeros
+    if (a.fused && nb == 0 && split == 0 && threadIdx.x < D)
+      a.out[(static_cast<int64_t>(b) * a.heads + h) * D + threadIdx.x] = 0;
+    return;
+  }
   const int blk_end = min(blk_begin + a.bps, nb);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -219,8 +310,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   auto load_codes = [&](const uint8_t* base, int blk, uint4 (&r)[TPL]) {
     const uint8_t* blk_base = base + static_cast<int64_t>(blk) * kBlock * G::kRowBytes;
 #pragma unroll
-    for (int i = 0; i < TPL; ++i)
-      r[i] = *reinterpret_cast<const uint4*>(blk_base + (lane_off + i * kWave * 16));
+    for (int i = 0; i < TPL; ++i) r[i] = load_stream(blk_base + (lane_off + i * kWave * 16));
   };
 
   // Scores of the lane's TPL tokens of block blk (base-2 logits), then the online
@@ -322,31 +412,288 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
 #pragma unroll
   for (int w = 0; w < kSplitWaves; ++w) alpha[w] = __builtin_amdgcn_exp2f(red_m[w] - M);
 
-  float* ws_o = a.ws_o + (row * a.n_split + split) * D;
-  for (int d = threadIdx.x; d < D; d += kSplitWaves * kWave) {
-    const int c = d / DPL, k = d % DPL;
-    float acc = 0.0f;
+  float od = 0.0f;
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x, c = d / DPL, k = d % DPL;
 #pragma unroll
     for (int w = 0; w < kSplitWaves; ++w) {
       float sw = 0.0f;
 #pragma unroll
       for (int g = 0; g < GROUPS; ++g) sw += red_o[w][g * LPT + c][k];
-      acc = __builtin_fmaf(alpha[w], sw, acc);
+      od = __builtin_fmaf(alpha[w], sw, od);
     }
-    ws_o[d] = acc;
   }
-  if (threadIdx.x == 0) {
-    float L = 0.0f;
+  float L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kSplitWaves; ++w) {
-      float sw = 0.0f;
-      for (int g = 0; g < GROUPS; ++g) sw += red_l[w][g * LPT];
-      L = __builtin_fmaf(alpha[w], sw, L);
-    }
-    float* ml = a.ws_ml + (row * a.n_split + split) * 2;
-    ml[0] = M;
-    ml[1] = L;
+  for (int w = 0; w < kSplitWaves; ++w) {
+    float sw = 0.0f;
+    for (int g = 0; g < GROUPS; ++g) sw += red_l[w][g * LPT];
+    L = __builtin_fmaf(alpha[w], sw, L);
   }
+  finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
+}
+
+// ---- int4 split kernel on the matrix cores --------------------------------------------
+// The int4 cache is stored in the operand order of v_mfma_f32_16x16x32_f16 (see
+// kvq_device.h): a lane's 16-byte loads are its B fragments. One dword of 8 nibbles
+// becomes 8 fp16 operands with a mask, an OR with the fp16 exponent of 1024 and one
+// packed fp16 subtract per pair (exact), so the matrix cores see normal fp16 integers
+// (they round fp16 subnormal inputs too coarsely for scores). QK^T: A = the query in
+// row 0 (other rows zero), N = 16 tokens per tile. P.V: A = the weights split into an
+// fp16 high part (row 0) and low part (row 1), K = 32 tokens per step, N = 16 channels
+// per tile; the weights reach the A layout through a 2 KiB per-wave LDS image. The
+// weights p <= 1 (relative to the running max) are scaled by 2^14 before the split so
+// that the low part of small weights is still a normal fp16 (a subnormal low part
+// would leave weights of 1e-4 with only ~11 significant bits).
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// nibble of a dword held by operand slot j, and the slot of nibble q
+__device__ constexpr int kSlotNibble[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+__device__ constexpr int kNibbleSlot[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+
+// 8 stored nibbles -> fp16 operands in slot order: slots 2, 3, 6, 7 hold 16*c * 2^-10,
+// the others c * 2^-10 (c = nibble - 8). A mask leaves each nibble pair as fp16
+// subnormals u * 2^-24 (or 16u * 2^-24); one packed fp16 FMA scales them by 2^14 and
+// removes the offset, which is exact and lands on normal fp16 values (or zero).
+__device__ __forceinline__ half8_t int4_operand(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  const half2_t scale = as_h2(0x74007400u);    // 2^14
+  const half2_t lo_bias = as_h2(0xA000A000u);  // -8 * 2^-10
+  const half2_t hi_bias = as_h2(0xB000B000u);  // -128 * 2^-10
+  const half2_t a = as_h2(w & 0x000F000Fu) * scale + lo_bias;   // nibbles 0, 4
+  const half2_t b = as_h2(w & 0x00F000F0u) * scale + hi_bias;   // nibbles 1, 5
+  const half2_t c = as_h2(w8 & 0x000F000Fu) * scale + lo_bias;  // nibbles 2, 6
+  const half2_t d = as_h2(w8 & 0x00F000F0u) * scale + hi_bias;  // nibbles 3, 7
+  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+template <int N>
+__device__ __forceinline__ uint32_t dword_of(const uint4 (&r)[N], int f) {
+  const uint4 v = r[f >> 2];
+  switch (f & 3) {
+    case 0: return v.x;
+    case 1: return v.y;
+    case 2: return v.z;
+    default: return v.w;
+  }
+}
+
+// Maximum over lanes 0..15 (row 0 of the MFMA output), returned uniformly.
+__device__ __forceinline__ float row0_max(float v) {
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+}
+
+__device__ __forceinline__ float row0_sum(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+}
+
+template <int D>
+__global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;               // 32-channel K steps of QK^T
+  constexpr int NTV = D / 16;              // 16-channel N tiles of P.V
+  constexpr int LOADS = D / 32;            // 16-byte loads per lane per region
+  constexpr int kRegionBytes = 32 * D;     // one tensor's codes of one block
+  __shared__ __align__(16) _Float16 pimg[kSplitWaves][2][4][16][8];
+  __shared__ float red_o[kSplitWaves][D];
+  __shared__ float red_l[kSplitWaves];
+  __shared__ float red_m[kSplitWaves];
+
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int cap = a.max_blocks * kBlock;
+  int len = a.seq_lens[b];
+  len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+  const int nb = (len + kBlock - 1) / kBlock;
+  const int blk_begin = split * a.bps;
+  if (blk_begin >= nb) {  // uniform over the workgroup
+    // an empty row has no split to merge: in fused mode split 0 writes its zeros
+    if (a.fused && nb == 0 && split == 0 && threadIdx.x < D)
+      a.out[(static_cast<int64_t>(b) * a.heads + h) * D + threadIdx.x] = 0;
+    return;
+  }
+  const int blk_end = min(blk_begin + a.bps, nb);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r16 = lane % 16;  // A row / output column of this lane
+  const int grp = lane / 16;  // 8-element K group of this lane's fragments
+  const int64_t row = static_cast<int64_t>(b) * a.heads + h;
+
+  // This wave's P image: rows 2..15 stay zero, rows 0 and 1 are rewritten per block.
+  {
+    uint4* img = reinterpret_cast<uint4*>(&pimg[wave][0][0][0][0]);
+    img[lane] = make_uint4(0u, 0u, 0u, 0u);
+    img[lane + kWave] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // Query operand: row 0 holds q in slot order, x16 slots pre-divided by 16.
+  half8_t aq[KS];
+  {
+    const uint16_t* qrow = a.q + row * D;
+    const float keep = r16 == 0 ? 1.0f : 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint16_t bits = qrow[32 * ks + 8 * grp + kSlotNibble[j]];
+        float x = static_cast<float>(__builtin_bit_cast(_Float16, bits)) * keep;
+        if (j & 2) x *= 0.0625f;
+        aq[ks][j] = static_cast<_Float16>(x);
+      }
+  }
+
+  const uint8_t* kbase = a.k_codes + row * a.max_blocks * kRegionBytes;
+  const uint8_t* vbase = a.v_codes + row * a.max_blocks * kRegionBytes;
+  const uint32_t lane_off = static_cast<uint32_t>(lane) * 16u;
+  const float* ks_ptr = a.k_scale + row * a.max_blocks;
+  const float* vs_ptr = a.v_scale + row * a.max_blocks;
+
+  float o[NTV];
+#pragma unroll
+  for (int n = 0; n < NTV; ++n) o[n] = 0.0f;
+  float m = -__builtin_inff();  // running max of the base-2 scores (wave-uniform)
+  float l = 0.0f;               // lanes 0..15: sum of their tokens' weights
+
+  auto load_codes = [&](const uint8_t* base, int blk, uint4 (&r)[LOADS]) {
+    const uint8_t* blk_base = base + static_cast<int64_t>(blk) * kRegionBytes;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) r[i] = load_stream(blk_base + (lane_off + i * kWave * 16));
+  };
+
+  // Scores of the block's 64 tokens (lanes 0..15 hold tokens 16*nt + lane), the
+  // online-softmax update, and the weights p (relative to the running max).
+  auto block_weights = [&](int blk, const uint4 (&kr)[LOADS], float (&p)[4]) {
+    const float sk = ks_ptr[blk] * a.qk_scale * 1024.0f;  // operands carry 2^-10
+    float4_t acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            aq[ks], int4_operand(dword_of(kr, nt * KS + ks)), acc[nt], 0, 0, 0);
+    float s[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) s[nt] = acc[nt][0] * sk;
+    if (blk == nb - 1) {  // tokens past the length in the last block weigh nothing
+      const int valid = len - blk * kBlock;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        if (16 * nt + r16 >= valid) s[nt] = -__builtin_inff();
+    }
+    float mb = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mb = row0_max(mb);
+    if (mb > m) {  // wave-uniform
+      const float alpha = __builtin_amdgcn_exp2f(m - mb);
+      l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NTV; ++n) o[n] *= alpha;
+      m = mb;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      p[nt] = __builtin_amdgcn_exp2f(s[nt] - m);
+      l += p[nt];
+    }
+  };
+
+  // o[n] += sv * sum_t p_t * c(t, 16n + lane) for the block (lanes 0..15).
+  auto block_accumulate = [&](int blk, const uint4 (&vr)[LOADS], const float (&p)[4]) {
+    // Operands carry 2^-10 (codes) and 2^14 (weights): p <= 1 is split as p * 2^14 into
+    // fp16 high and low parts so that the low part of small weights stays a normal fp16.
+    const float sv = vs_ptr[blk] * (1024.0f / 16384.0f);
+    if (lane < 16) {
+      const int slot = kNibbleSlot[lane & 7];
+      const float scale = (slot & 2) ? 1024.0f : 16384.0f;  // x16 slots: 2^14 / 16
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float x = p[nt] * scale;
+        const _Float16 hi = static_cast<_Float16>(x);
+        const _Float16 lo = static_cast<_Float16>(x - static_cast<float>(hi));
+        const int kstep = nt >> 1, kgrp = (nt & 1) * 2 + (lane >> 3);
+        pimg[wave][kstep][kgrp][0][slot] = hi;
+        pimg[wave][kstep][kgrp][1][slot] = lo;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const half8_t ap0 = *reinterpret_cast<const half8_t*>(&pimg[wave][0][grp][r16][0]);
+    const half8_t ap1 = *reinterpret_cast<const half8_t*>(&pimg[wave][1][grp][r16][0]);
+#pragma unroll
+    for (int n = 0; n < NTV; ++n) {
+      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap0, int4_operand(dword_of(vr, 2 * n)), acc, 0,
+                                                   0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap1, int4_operand(dword_of(vr, 2 * n + 1)), acc,
+                                                   0, 0, 0);
+      o[n] = __builtin_fmaf(sv, acc[0] + acc[1], o[n]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // Software pipeline over three code buffers (as in the uint8 kernel).
+  uint4 r0[LOADS], r1[LOADS], r2[LOADS];
+  float p[4];
+  auto step = [&](int blk, uint4 (&kcur)[LOADS], uint4 (&vcur)[LOADS], uint4 (&kfree)[LOADS]) {
+    const int next = blk + kSplitWaves;
+    const bool more = next < blk_end;
+    if (more) load_codes(kbase, next, kfree);
+    block_weights(blk, kcur, p);
+    if (more) load_codes(vbase, next, kcur);
+    block_accumulate(blk, vcur, p);
+    return more;
+  };
+  int blk = blk_begin + wave;
+  if (blk < blk_end) {
+    load_codes(kbase, blk, r0);
+    load_codes(vbase, blk, r1);
+    while (true) {
+      if (!step(blk, r0, r1, r2)) break;
+      blk += kSplitWaves;
+      if (!step(blk, r2, r0, r1)) break;
+      blk += kSplitWaves;
+      if (!step(blk, r1, r2, r0)) break;
+      blk += kSplitWaves;
+    }
+  }
+
+  const float lw = row0_sum(lane < 16 ? l : 0.0f);
+  if (lane < 16) {
+#pragma unroll
+    for (int n = 0; n < NTV; ++n) red_o[wave][16 * n + lane] = o[n];
+  }
+  if (lane == 0) {
+    red_l[wave] = lw;
+    red_m[wave] = m;
+  }
+  __syncthreads();
+
+  float M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kSplitWaves; ++w) M = fmaxf(M, red_m[w]);
+  float alpha[kSplitWaves];
+#pragma unroll
+  for (int w = 0; w < kSplitWaves; ++w) alpha[w] = __builtin_amdgcn_exp2f(red_m[w] - M);
+  float od = 0.0f;
+  if (threadIdx.x < D) {
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) od = __builtin_fmaf(alpha[w], red_o[w][threadIdx.x], od);
+  }
+  float L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kSplitWaves; ++w) L = __builtin_fmaf(alpha[w], red_l[w], L);
+  finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
 }
 
 // ---- combine kernel: grid (heads, batch), D threads ---------------------------------
@@ -361,21 +708,7 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   const int nb = (len + kBlock - 1) / kBlock;
   const int n = (nb + a.bps - 1) / a.bps;
   const int64_t row = static_cast<int64_t>(b) * a.heads + h;
-  _Float16 r = 0;
-  if (n > 0) {
-    const float* ml = a.ws_ml + row * a.n_split * 2;
-    const float* po = a.ws_o + row * a.n_split * D + d;
-    float M = ml[0];
-    for (int j = 1; j < n; ++j) M = fmaxf(M, ml[2 * j]);
-    float L = 0.0f, acc = 0.0f;
-    for (int j = 0; j < n; ++j) {
-      const float w = __builtin_amdgcn_exp2f(ml[2 * j] - M);
-      L = __builtin_fmaf(w, ml[2 * j + 1], L);
-      acc = __builtin_fmaf(w, po[j * D], acc);
-    }
-    r = static_cast<_Float16>(acc / L);
-  }
-  a.out[row * D + d] = __builtin_bit_cast(uint16_t, r);
+  merge_row<D, false>(a, row, n, d);
 }
 
 template <int SCHEME, int D>
@@ -387,11 +720,17 @@ hipError_t split_t(int batch, const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+template <int D>
+hipError_t split_int4_t(int batch, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.n_split, a.heads, batch);
+  hipLaunchKernelGGL((attn_split_int4_kernel<D>), grid, dim3(kSplitWaves * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_split(int scheme, int head_dim, int batch, const AttnArgs& a,
                              hipStream_t s) {
   if (scheme == KVQ_INT4_SYM)
-    return head_dim == 128 ? split_t<KVQ_INT4_SYM, 128>(batch, a, s)
-                           : split_t<KVQ_INT4_SYM, 64>(batch, a, s);
+    return head_dim == 128 ? split_int4_t<128>(batch, a, s) : split_int4_t<64>(batch, a, s);
   return head_dim == 128 ? split_t<KVQ_UINT8_ASYM, 128>(batch, a, s)
                          : split_t<KVQ_UINT8_ASYM, 64>(batch, a, s);
 }

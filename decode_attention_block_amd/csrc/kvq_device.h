@@ -125,4 +125,18 @@ __device__ __forceinline__ uint2 pack_uint8x8(const float (&x)[8], float s, int 
   return r;
 }
 
+// ---- int4 cache block layout ---------------------------------------------------------
+// An int4 block (64 tokens x D channels, one K and one V region of 32*D bytes each) is
+// stored in the operand order of v_mfma_f32_16x16x32_f16, so that a lane's 16-byte
+// loads are exactly its matrix-core fragments. Lane l (0..63) owns F = D/8 dwords per
+// region, dword f at byte ((f / 4) * 64 + l) * 16 + (f % 4) * 4; each dword holds 8
+// offset-binary nibbles (code + 8), nibble q in bits 4q..4q+3.
+//   K (B operand of QK^T, K = channels, N = tokens): f = nt * (D/32) + ks,
+//     nibble q = channel 32*ks + 8*(l/16) + q of token 16*nt + (l%16).
+//   V (B operand of P.V, K = tokens, N = channels): f = 2*nt + ks,
+//     nibble q = token 32*ks + 8*(l/16) + q of channel 16*nt + (l%16).
+__device__ __forceinline__ uint32_t int4_dword_offset(int lane, int f) {
+  return static_cast<uint32_t>(((f >> 2) * 64 + lane) * 16 + (f & 3) * 4);
+}
+
 }  // namespace kvq

@@ -49,10 +49,12 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const uint16_t* q;
   uint16_t* out;
-  float* ws_o;   // [rows][n_split][D] unnormalised partial outputs
-  float* ws_ml;  // [rows][n_split][2]  (running max in log2 units, sum of weights)
+  uint32_t* counters;  // [rows] arrival counters of the fused combine (zero between calls)
+  float* ws_o;         // [rows][n_split][D] unnormalised partial outputs
+  float* ws_ml;        // [rows][n_split][2]  (running max in log2 units, sum of weights)
   int heads, max_blocks, max_len, bps, n_split;
-  float qk_scale;  // softmax_scale * log2(e)
+  int fused;           // 1: the last workgroup of each row merges the splits and writes out
+  float qk_scale;      // softmax_scale * log2(e)
 };
 
 // Launchers (return hipError_t of the launch).

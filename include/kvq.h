@@ -15,8 +15,9 @@
  * Conventions shared by every call:
  *   * Ownership: the caller allocates every buffer (device memory unless stated) and
  *     keeps it alive until the work queued on `stream` has finished. The library
- *     allocates nothing and keeps no state between calls; calls on different streams
- *     that touch different buffers may run concurrently.
+ *     allocates nothing and keeps no state of its own between calls; calls on different
+ *     streams that touch different buffers may run concurrently, calls that share a
+ *     buffer must be ordered by the caller (one stream).
  *   * Execution: every call validates its arguments on the host, then queues its
  *     kernels on `stream` (a hipStream_t; NULL means the null stream) and returns
  *     without waiting. Faults inside kernels surface at the caller's next
@@ -44,9 +45,9 @@ extern "C" {
 /* Cache formats. */
 enum kvq_scheme {
   /* [Pg2] §2.1: s = RN(absmax / 7.5f) (s = 0 for an all-zero block);
-   * code = clamp(rint(RN(x / s)), -8, 7), stored as a 4-bit two's-complement nibble.
-   * Byte k of a token's D/2-byte row holds channel 2k in bits 0-3 and 2k+1 in bits 4-7.
-   * Zero points (if the buffers are given) are written +0.0f. */
+   * code = clamp(rint(RN(x / s)), -8, 7) (0 when s = 0), stored as the offset-binary
+   * nibble code + 8 (order: see k_codes below). Zero points (if the buffers are given)
+   * are written +0.0f. */
   KVQ_INT4_SYM = 0,
   /* [Pg1] §2.2, asymmetric per-chunk reading: s = RN(RN(max - min) / 255f),
    * zp = rint(RN(-min / s)) + 0.0f, code = clamp(rint(RN(x / s)) + (int)zp, 0, 255).
@@ -59,7 +60,7 @@ enum kvq_scheme {
 enum kvq_status {
   KVQ_OK = 0,
   KVQ_EINVAL = -1,     /* null pointer, bad scheme/shape/count, negative length */
-  KVQ_ENOTSUP = -2,    /* head_dim other than 64 or 128 */
+  KVQ_ENOTSUP = -2,    /* head_dim other than 64 or 128; kv_append limits (see there) */
   KVQ_ECAPACITY = -3,  /* a length bound exceeds max_blocks * 64 */
   KVQ_EALIGN = -4,     /* a pointer or stride breaks the 16-byte alignment rule */
   KVQ_EWORKSPACE = -5, /* workspace missing or smaller than decode_attn_workspace_bytes */
@@ -68,9 +69,16 @@ enum kvq_status {
 
 /* Cache descriptor. Plain data; every pointer is device memory owned by the caller.
  * B = batch, H = heads, D = head_dim, MB = max_blocks (capacity MB * 64 tokens/row).
- *   k_codes, v_codes : uint8 [B][H][MB][64][D/2 (int4) | D (uint8)], 16-byte aligned.
- *                      Bytes of tokens at or past a row's length inside its last block
- *                      are written 0 by the quantizing calls.
+ *   k_codes, v_codes : uint8 [B][H][MB][64][D/2 (int4) | D (uint8)], 16-byte aligned;
+ *                      each block of a row is one contiguous 32*D (int4) or 64*D
+ *                      (uint8) byte region. uint8 codes are stored [token][channel].
+ *                      int4 codes are stored in matrix-core operand order: the region
+ *                      is 64 lanes x F = D/8 dwords, dword f of lane l at byte
+ *                      ((f/4)*64 + l)*16 + (f%4)*4, nibble q (bits 4q..4q+3) =
+ *                      K: channel 32*ks + 8*(l/16) + q of token 16*nt + l%16, f = nt*D/32 + ks;
+ *                      V: token 32*ks + 8*(l/16) + q of channel 16*nt + l%16, f = 2*nt + ks.
+ *                      Codes of tokens at or past a row's length inside its last block
+ *                      are written as zero nibbles / bytes by the quantizing calls.
  *   k_scale, v_scale : float [B][H][MB].
  *   k_zero,  v_zero  : float [B][H][MB]; required for KVQ_UINT8_ASYM, may be NULL for
  *                      KVQ_INT4_SYM.
@@ -119,7 +127,11 @@ int kv_quantize_blocks(const kvq_cache* cache, const void* k, const void* v,
  * block's statistic (absmax, or min and max) unchanged only its own codes are written;
  * otherwise the whole tail block is re-quantized from the staged fp16 values.
  * Sequences with seq_lens[b] >= MB*64 are left unchanged. The tail staging (written
- * by kv_quantize_blocks or earlier appends) must be present.
+ * by kv_quantize_blocks or earlier appends) must be present. One kernel does all of
+ * it: the workgroups of a sequence count their arrivals in the top 8 bits of
+ * seq_lens[b] while it runs, and the last one stores the new length; hence
+ * heads <= 255 and MB*64 < 2^24 (KVQ_ENOTSUP otherwise), entries of seq_lens must lie
+ * in [0, MB*64], and nothing else may read seq_lens while the append runs.
  *   k_new, v_new  : fp16 [B][H][D] contiguous, 16-byte aligned.
  *   max_len_after : host-side bound on the lengths after the append; must be
  *                   <= MB*64 (KVQ_ECAPACITY otherwise).
@@ -135,8 +147,10 @@ int decode_attn_plan(const kvq_cache* cache, int32_t max_len, int32_t blocks_per
                      int32_t* blocks_per_split_out, int32_t* splits_per_row_out);
 
 /* Bytes of device workspace decode_attn_qkv needs for these arguments (0 on invalid
- * arguments). The workspace holds per-split partial softmax states; its contents
- * need not be initialised and are overwritten by every call. */
+ * arguments). The workspace holds, first, one uint32 arrival counter per row (B*H,
+ * padded to 256 bytes), then the per-split partial softmax states. The counters must
+ * be zero before the first call that uses the workspace (allocate it zero-filled);
+ * every call leaves them zero again. The partial states need no initialisation. */
 size_t decode_attn_workspace_bytes(const kvq_cache* cache, int32_t max_len,
                                    int32_t blocks_per_split);
 
@@ -145,10 +159,11 @@ size_t decode_attn_workspace_bytes(const kvq_cache* cache, int32_t max_len,
  * with K^, V^ the dequantized cache (c*s, or (c - zp)*s), n_b = min(seq_lens[b],
  * max_len). Codes are dequantized in registers; QK^T, an online softmax (base 2,
  * softmax_scale*log2(e) folded into the scores) and the weighted sum of V accumulate
- * in binary32 per split of the context; a second kernel merges the splits by their
- * log-sum-exp and rounds to fp16. Rows with n_b = 0 get zeros. (Attention is the
- * textbook scaled dot product; splitting it into schedulable pieces follows [Pg1]
- * chapter 1's chunked attention.)
+ * in binary32 per split of the context; the splits are merged by their log-sum-exp
+ * and rounded to fp16. One kernel launch: the last workgroup of each row to finish
+ * (counted with the workspace's arrival counters) merges that row. Rows with n_b = 0
+ * get zeros. (Attention is the textbook scaled dot product; splitting it into
+ * schedulable pieces follows [Pg1] chapter 1's chunked attention.)
  *   q               : fp16 [B][H][D] contiguous, 16-byte aligned.
  *   out             : fp16 [B][H][D] contiguous, 16-byte aligned.
  *   workspace       : device buffer of >= decode_attn_workspace_bytes(...) bytes,
@@ -160,10 +175,11 @@ int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, 
                     void* workspace, size_t workspace_bytes, int32_t max_len,
                     int32_t blocks_per_split, void* stream);
 
-/* The two kernels of decode_attn_qkv, queued separately (same arguments and same
- * plan). decode_attn_split writes the partial states to the workspace;
- * decode_attn_combine reads them and writes `out`. Running split then combine on one
- * stream is exactly decode_attn_qkv. */
+/* The same attention as two kernels, queued separately (same arguments, same plan):
+ * decode_attn_split writes every split's partial state to the workspace (it does not
+ * touch the counters), decode_attn_combine merges them into `out` with the same
+ * arithmetic in the same order. Running split then combine on one stream gives
+ * bitwise the result of decode_attn_qkv. */
 int decode_attn_split(const kvq_cache* cache, const void* q, float softmax_scale,
                       void* workspace, size_t workspace_bytes, int32_t max_len,
                       int32_t blocks_per_split, void* stream);

@@ -82,8 +82,7 @@ def gpu_attention(cache, q, sm_scale, max_len, blocks_per_split=0):
     B, H, D = q.shape
     qt = to_gpu(q)
     out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
-    nbytes = kvq.decode_attn_workspace_bytes(cache, max_len, blocks_per_split)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = kvq.make_workspace(cache, max_len, blocks_per_split)
     kvq.decode_attn_qkv(cache, qt, sm_scale, out, ws, max_len, blocks_per_split)
     torch.cuda.synchronize()
     return out.cpu().numpy()

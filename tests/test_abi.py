@@ -94,13 +94,15 @@ def test_capacity_and_lengths():
     assert rc_append(cache(MB=3), max_len_after=193) == ECAP
     assert rc_append(cache(), max_len_after=0) == EINVAL
     assert rc_append(cache(k_tail=0)) == EINVAL
+    assert rc_append(cache(H=256)) == ENOTSUP           # arrival count must fit 8 bits
+    assert rc_append(cache(MB=1 << 18), max_len_after=100) == ENOTSUP  # lengths < 2^24
 
 
 @no_gpu_only
 def test_workspace_rules():
     c = cache(B=2, H=4, D=128, MB=3)
     need = kvq.decode_attn_workspace_bytes(c, 192, 1)
-    assert need == 2 * 4 * 3 * (128 + 2) * 4
+    assert need == 256 + 2 * 4 * 3 * (128 + 2) * 4      # counters (padded) + partials
     assert rc_attn(c, ws_bytes=need - 1, max_len=192, bps=1) == EWS
     assert rc_attn(c, ws=0, max_len=192, bps=1) == EWS
     assert rc_attn(c, ws=FAKE + 4, ws_bytes=need, max_len=192, bps=1) == EALIGN

@@ -95,13 +95,19 @@ def test_padding_poison_and_determinism(scheme):
     base = gpu_attention(c, q, sm, int(lens.max()))
     for _ in range(3):
         assert np.array_equal(gpu_attention(c, q, sm, int(lens.max())), base)
+    from decode_attention_block_amd import layout
     rs = np.random.default_rng(1)
     for b, n in enumerate(lens):
         j, t = divmod(int(n), 64)
         if t:
-            for codes in (c.k_codes, c.v_codes):
-                junk = rs.integers(0, 256, codes[b, :, j, t:].shape, dtype=np.uint8)
-                codes[b, :, j, t:] = torch.from_numpy(junk).cuda()
+            for which, codes in (("k", c.k_codes), ("v", c.v_codes)):
+                blk = codes[b, :, j].cpu().numpy()          # [H][64][row bytes] as stored
+                if scheme == INT4:
+                    blk = layout.int4_to_natural(blk, which)
+                blk[:, t:] = rs.integers(0, 256, blk[:, t:].shape, dtype=np.uint8)
+                if scheme == INT4:
+                    blk = layout.int4_from_natural(blk, which)
+                codes[b, :, j] = torch.from_numpy(blk).cuda()
     torch.cuda.synchronize()
     assert np.array_equal(gpu_attention(c, q, sm, int(lens.max())), base)
 
@@ -117,18 +123,38 @@ def test_empty_and_single_token_rows():
     assert norm_err <= ATTN_TOL
 
 
-def test_split_and_combine_phases_equal_fused_call():
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+def test_split_and_combine_phases_equal_fused_call(scheme):
+    """decode_attn_split + decode_attn_combine give bitwise the fused result, and the
+    fused call leaves the workspace's arrival counters at zero after every call."""
     import decode_attention_block_amd as kvq
     import torch
-    k, v, q, lens = _small_case(UINT8, 64, seed=8)
-    c = gpu_quantize(UINT8, k, v, lens, 11)
-    say("phases")
-    fused = gpu_attention(c, q, 0.125, int(lens.max()), 2)
+    k, v, q, lens = _small_case(scheme, 64, seed=8)
+    c = gpu_quantize(scheme, k, v, lens, 11)
+    say("phases", scheme)
+    L = int(lens.max())
     qt = to_gpu(q)
+    ws = kvq.make_workspace(c, L, 2)
+    fused = torch.empty_like(qt)
+    for _ in range(3):
+        kvq.decode_attn_qkv(c, qt, 0.125, fused, ws, L, 2)
+        torch.cuda.synchronize()
+        assert not ws[:4 * c.batch * c.heads].any()
     out = torch.empty_like(qt)
-    ws = torch.empty(kvq.decode_attn_workspace_bytes(c, int(lens.max()), 2), dtype=torch.uint8,
-                     device="cuda")
-    kvq.decode_attn_split(c, qt, 0.125, ws, int(lens.max()), 2)
-    kvq.decode_attn_combine(c, out, ws, int(lens.max()), 2)
+    kvq.decode_attn_split(c, qt, 0.125, ws, L, 2)
+    kvq.decode_attn_combine(c, out, ws, L, 2)
     torch.cuda.synchronize()
-    assert np.array_equal(out.cpu().numpy(), fused)
+    assert np.array_equal(out.cpu().numpy(), fused.cpu().numpy())
+
+
+def test_zero_context_call_writes_zeros():
+    import decode_attention_block_amd as kvq
+    import torch
+    k, v, q, lens = _small_case(INT4, 128, seed=9, B=2, S=64, lens=(0, 0))
+    c = gpu_quantize(INT4, k, v, lens, 1, max_len=0)
+    say("zero context")
+    qt = to_gpu(q)
+    out = torch.full_like(qt, 7.0)
+    kvq.decode_attn_qkv(c, qt, 0.1, out, None, 0)
+    torch.cuda.synchronize()
+    assert not out.cpu().numpy().any()

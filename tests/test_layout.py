@@ -1,0 +1,47 @@
+"""The host-side description of the int4 storage order (decode_attention_block_amd.layout)
+against the formula in its docstring, worked by hand for single nibbles."""
+import numpy as np
+import pytest
+
+from decode_attention_block_amd import layout
+
+
+def one_hot_natural(D, t, d, value=0xB):
+    nat = np.zeros((64, D // 2), np.uint8)
+    nat[t, d // 2] = value << (4 * (d % 2))
+    return nat
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_round_trip(D, which):
+    rs = np.random.default_rng(0)
+    nat = rs.integers(0, 256, (2, 3, 64, D // 2), dtype=np.uint8)
+    st = layout.int4_from_natural(nat, which)
+    assert np.array_equal(layout.int4_to_natural(st, which), nat)
+    assert sorted(st.ravel().tolist()) != [] and st.shape == nat.shape
+
+
+def test_k_nibble_position_by_hand():
+    # D=128, token 37, channel 77: nt = 2, lane%16 = 5; ks = 2, lane//16 = (77-64)//8 = 1,
+    # q = 13 - 8 = 5 -> lane 21, f = 2*4 + 2 = 10 -> byte ((10//4)*64 + 21)*16 + (10%4)*4 + 2
+    # = (128 + 21)*16 + 8 + 2 = 2394, high nibble (q odd).
+    st = layout.int4_from_natural(one_hot_natural(128, 37, 77), "k").ravel()
+    assert np.flatnonzero(st).tolist() == [2394] and st[2394] == 0xB0
+
+
+def test_v_nibble_position_by_hand():
+    # D=128, token 45, channel 100: nt = 6, lane%16 = 4; ks = 1, lane//16 = (45-32)//8 = 1,
+    # q = 5 -> lane 20, f = 2*6 + 1 = 13 -> byte ((13//4)*64 + 20)*16 + (13%4)*4 + 2
+    # = (192 + 20)*16 + 4 + 2 = 3398, high nibble.
+    st = layout.int4_from_natural(one_hot_natural(128, 45, 100), "v").ravel()
+    assert np.flatnonzero(st).tolist() == [3398] and st[3398] == 0xB0
+
+
+def test_v_first_dword_holds_eight_tokens_of_channel_zero():
+    D = 64
+    nat = np.zeros((64, D // 2), np.uint8)
+    for t in range(8):
+        nat[t, 0] = t + 1            # channel 0 of tokens 0..7 (low nibble)
+    st = layout.int4_from_natural(nat, "v").ravel()
+    assert st[:4].tolist() == [0x21, 0x43, 0x65, 0x87]
