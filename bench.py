@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_int4_b8h32d128_ctx8k_traffic.json")
 CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 
@@ -74,6 +75,25 @@ def append_bytes(w):
     staged fp16 copy and their codes out."""
     rows = w.batch * w.heads
     return rows * 2 * (w.head_dim * 2 * 2 + code_bytes_per_token(w))
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (scaled by the counters' reading for a 1 GiB copy), or None once the kernel's
+    sources differ from the ones the counters were taken on."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return rec["traffic_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def copy_probe():
@@ -245,7 +265,8 @@ def main():
                    "splits_per_row": n_split, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "attn_split_int4_kernel<128> (decode_attn_qkv)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if w.name == HEADLINE else None,
                      "avg_kernel_us": avg_attn_ms * 1e3,
                      "algorithmic_bytes_per_launch": float(np.mean(step_attn_bytes))},
         "prefill_quantize": {"ms": float(np.median(prefill_ms)),
