@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the block-quantized KV cache on one MI355X.
 
-One step = one decode step of the whole hot path on the 8K int4 workload (batch 8,
+Headline step = one decode step of the whole hot path on the 8K int4 workload (batch 8,
 32 heads, head_dim 128, context 8192 per sequence, 4-bit block codes, 64-token blocks):
 kv_append quantizes one new token per sequence into its row's tail block (one kernel),
 then decode_attn_qkv attends one fp16 query per (sequence, head) over the whole
@@ -15,9 +15,18 @@ reads its cache from HBM. Each copy gains one token per use, so the context grow
 from 8192 by at most ceil((warmup + steps) / copies) tokens; bytes are counted from
 the actual lengths.
 
-Prints one JSON line (see the keys below). --profile-loop runs only the timed loop
-(for rocprofv3), --copy-probe times a plain device copy of known size (the
-calibration kernel for the FETCH_SIZE / WRITE_SIZE counters).
+The same run also measures the other workloads (unless --headline-only) and reports
+them under "workloads":
+  * the 8K uint8 workload, with the same step and rotation;
+  * the 32K workload (batch 16, context 32768): its 64-step decode loop of kv_append +
+    decode_attn_qkv, repeated from the same prefill (lengths reset between loops,
+    outside the timed region);
+  * the 32-layer ragged workload: one step is decode_attn_qkv over each of the 32
+    layers' caches (per-sequence lengths 1024..8192, no append in this workload).
+
+Prints one JSON line. --profile-loop runs only the timed loop of --workload (for
+rocprofv3), --copy-probe times a plain device copy of known size (the calibration
+kernel for the FETCH_SIZE / WRITE_SIZE counters).
 """
 import argparse
 import json
@@ -35,6 +44,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_int4_b8h32d128_ctx8k_traffic.json")
 CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
+OTHERS = ("llama7b_b8_h32_d128_ctx8k_uint8", "long_b16_h32_d128_ctx32k_append64_int4",
+          "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4")
 
 
 def parse():
@@ -47,8 +58,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate host time spent timing the oracle")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--headline-only", action="store_true",
+                   help="measure only --workload, not the other workloads")
     p.add_argument("--profile-loop", action="store_true",
-                   help="only the timed loop (for rocprofv3); no oracle, no copy probe")
+                   help="only the timed loop of --workload (for rocprofv3); no oracle, "
+                        "no other workloads")
     p.add_argument("--copy-probe", action="store_true",
                    help="only a 1 GiB device-to-device copy (counter calibration)")
     return p.parse_args()
@@ -138,6 +152,243 @@ def cpu_baseline(w, host_cache, q, lens, budget_s):
             "tokens_per_s": w.batch * passes / elapsed}
 
 
+class Timer:
+    """HIP events around each attention launch and around each timed segment, all on
+    the current stream (the one the library's kernels are queued on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.attn = []       # (start, end) event pairs
+        self.segments = []
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def attn_ms(self):
+        return [a.elapsed_time(b) for a, b in self.attn]
+
+    def total_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.segments)
+
+
+def quantized_copies(kvq, torch, w, layer, lens, max_blocks, n_copies, device_inputs):
+    """n_copies caches holding the quantized prefill of one layer; returns them and the
+    prefill kernel times (ms). device_inputs: draw K and V with the device-side recipe
+    (same distributions, other values) instead of the host recipe."""
+    n = int(np.max(lens))
+    wl = wl_mod()
+    if device_inputs:
+        k = wl.prefill_batch_device(w, layer, 0, n_tokens=n)
+        v = wl.prefill_batch_device(w, layer, 1, n_tokens=n)
+    else:
+        k = torch.from_numpy(wl.prefill_batch(w, layer, 0, n_tokens=n)).cuda()
+        v = torch.from_numpy(wl.prefill_batch(w, layer, 1, n_tokens=n)).cuda()
+    caches, ms = [], []
+    for _ in range(n_copies):
+        c = kvq.KVCache(w.scheme, w.batch, w.heads, w.head_dim, max_blocks)
+        c.seq_lens.copy_(torch.from_numpy(np.asarray(lens, np.int32)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.kv_quantize_blocks(c, k, v, n)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        caches.append(c)
+    del k, v
+    return caches, ms
+
+
+def wl_mod():
+    from decode_attention_block_amd import workloads
+    return workloads
+
+
+def workspace(kvq, torch, cache, lengths, bps):
+    n = max(kvq.decode_attn_workspace_bytes(cache, int(L), bps) for L in lengths)
+    return torch.zeros(n, dtype=torch.uint8, device="cuda")   # counters start at zero
+
+
+def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs):
+    """Single-layer fixed-length workloads; step = kv_append + decode_attn_qkv.
+
+    Without decode steps of its own (the 8K workloads) the step rotates over cache
+    copies; with them (the 32K workload) the workload's decode loop runs from the same
+    prefill, lengths reset between loops (untimed), until `steps` steps are timed."""
+    wl = wl_mod()
+    B, H, D = w.batch, w.heads, w.head_dim
+    per_cache = 2 * B * H * w.context * code_bytes_per_token(w)
+    if w.decode_steps:
+        copies, growth = 1, w.decode_steps
+    else:
+        copies = max(1, math.ceil(CACHE_BYTES_TARGET / per_cache))
+        growth = math.ceil((warmup + steps) / copies)
+    max_blocks = (w.context + growth + 63) // 64
+    t_setup = time.perf_counter()
+    caches, prefill_ms = quantized_copies(kvq, torch, w, 0, wl.lengths(w), max_blocks, copies,
+                                          device_inputs)
+    kn = np.stack([wl.appended_kv(w, 0, s, 0, growth) for s in range(B)], axis=1)
+    vn = np.stack([wl.appended_kv(w, 0, s, 1, growth) for s in range(B)], axis=1)
+    k_new = torch.from_numpy(kn).cuda()          # [growth][B][H][D]
+    v_new = torch.from_numpy(vn).cuda()
+    n_q = warmup + steps
+    queries = torch.from_numpy(np.stack([wl.query(w, 0, s % max(growth, 1) if w.decode_steps
+                                                  else s) for s in range(n_q)])).cuda()
+    host_cache = caches[0].host_arrays() if keep_host else None
+    ws = workspace(kvq, torch, caches[0], range(w.context, w.context + growth + 1), bps)
+    out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
+    sm = wl.softmax_scale(w)
+    lens_host = [w.context] * copies
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    timer = Timer(torch)
+    attn_bytes, step_bytes = [], []
+
+    def step(i, timed):
+        ci = i % copies
+        c = caches[ci]
+        used = lens_host[ci] - w.context
+        kvq.kv_append(c, k_new[used], v_new[used], lens_host[ci] + 1)
+        lens_host[ci] += 1
+        L = lens_host[ci]
+        if timed:
+            e0 = timer.event()
+        kvq.decode_attn_qkv(c, queries[i], sm, out, ws, L, bps)
+        if timed:
+            timer.attn.append((e0, timer.event()))
+            attn_bytes.append(attention_bytes(w, [L] * B))
+            step_bytes.append(attn_bytes[-1] + append_bytes(w))
+
+    def reset():
+        for ci, c in enumerate(caches):
+            c.seq_lens.fill_(w.context)
+            lens_host[ci] = w.context
+        torch.cuda.synchronize()
+
+    wall0 = time.perf_counter()
+    if w.decode_steps:
+        # warm up on attention alone (appends would consume the loop's tokens)
+        for i in range(warmup):
+            kvq.decode_attn_qkv(caches[0], queries[0], sm, out, ws, w.context, bps)
+        torch.cuda.synchronize()
+        done = 0
+        while done < steps:
+            reset()
+            n = min(w.decode_steps, steps - done)
+            t0 = timer.event()
+            for j in range(n):
+                step(j, True)
+            timer.segments.append((t0, timer.event()))
+            done += n
+    else:
+        for i in range(warmup):
+            step(i, False)
+        torch.cuda.synchronize()
+        t0 = timer.event()
+        for j in range(steps):
+            step(warmup + j, True)
+        timer.segments.append((t0, timer.event()))
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - wall0
+    total_ms = timer.total_ms()
+    attn_ms = timer.attn_ms()
+    bps_eff, n_split = kvq.decode_attn_plan(caches[0], w.context + growth, bps)
+    res = {
+        "workload": w.name,
+        "step": "kv_append + decode_attn_qkv",
+        "steps": steps, "warmup": warmup,
+        "ms_per_step": total_ms / steps,
+        "gbs": sum(step_bytes) / (total_ms / 1e3) / 1e9,
+        "tokens_per_s": B * steps / (total_ms / 1e3),
+        "attn_avg_us": float(np.mean(attn_ms)) * 1e3,
+        "attn_gbs": float(np.mean(attn_bytes)) / (float(np.mean(attn_ms)) / 1e3) / 1e9,
+        "attn_bytes_per_launch": float(np.mean(attn_bytes)),
+        "context": [w.context + 1, w.context + growth],
+        "cache_copies_rotated": copies, "blocks_per_split": bps_eff,
+        "splits_per_row": n_split,
+        "prefill_quantize_ms": float(np.median(prefill_ms)),
+        "prefill_quantize_gbs": (2 * B * w.context * H * D * 2 + per_cache)
+        / (float(np.median(prefill_ms)) / 1e3) / 1e9,
+        "host_wall_s": wall_s, "setup_s": setup_s,
+    }
+    res["attn_frac"] = res["attn_gbs"] / HBM_PEAK_GBS
+    return res, host_cache
+
+
+def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
+    """The 32-layer ragged workload: one step is decode_attn_qkv over every layer's
+    cache, each layer with its own K, V and query."""
+    wl = wl_mod()
+    B, H, D = w.batch, w.heads, w.head_dim
+    lens = wl.lengths(w)
+    L = int(lens.max())
+    t_setup = time.perf_counter()
+    caches, prefill_ms, queries = [], [], []
+    for layer in range(w.layers):
+        c, ms = quantized_copies(kvq, torch, w, layer, lens, w.max_blocks, 1, device_inputs)
+        caches += c
+        prefill_ms += ms
+        queries.append(torch.from_numpy(wl.query(w, layer)).cuda())
+    ws = workspace(kvq, torch, caches[0], [L], bps)
+    out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
+    sm = wl.softmax_scale(w)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    timer = Timer(torch)
+
+    def step(timed):
+        for layer in range(w.layers):
+            if timed:
+                e0 = timer.event()
+            kvq.decode_attn_qkv(caches[layer], queries[layer], sm, out, ws, L, bps)
+            if timed:
+                timer.attn.append((e0, timer.event()))
+
+    wall0 = time.perf_counter()
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = timer.event()
+    for _ in range(steps):
+        step(True)
+    timer.segments.append((t0, timer.event()))
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - wall0
+    total_ms = timer.total_ms()
+    per_launch = attention_bytes(w, lens)
+    attn_ms = timer.attn_ms()
+    bps_eff, n_split = kvq.decode_attn_plan(caches[0], L, bps)
+    res = {
+        "workload": w.name,
+        "step": f"decode_attn_qkv over {w.layers} layers",
+        "steps": steps, "warmup": warmup,
+        "ms_per_step": total_ms / steps,
+        "gbs": per_launch * w.layers * steps / (total_ms / 1e3) / 1e9,
+        "tokens_per_s": B * steps / (total_ms / 1e3),
+        "attn_avg_us": float(np.mean(attn_ms)) * 1e3,
+        "attn_gbs": per_launch / (float(np.mean(attn_ms)) / 1e3) / 1e9,
+        "attn_bytes_per_launch": float(per_launch),
+        "context": [int(lens.min()), L], "mean_context": float(lens.mean()),
+        "blocks_per_split": bps_eff, "splits_per_row": n_split,
+        "prefill_quantize_ms_per_layer": float(np.median(prefill_ms)),
+        "host_wall_s": wall_s, "setup_s": setup_s,
+    }
+    res["attn_frac"] = res["attn_gbs"] / HBM_PEAK_GBS
+    return res
+
+
+def measure(kvq, torch, w, steps, warmup, bps, keep_host=False, device_inputs=False):
+    if w.layers > 1:
+        res = run_layers(kvq, torch, w, steps, warmup, bps, device_inputs), None
+    else:
+        res = run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs)
+    res[0]["inputs"] = ("K/V drawn on the device (torch generator, same distributions)"
+                        if device_inputs else "K/V from the seeded host recipe")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -148,7 +399,6 @@ def main():
     import torch
 
     import decode_attention_block_amd as kvq
-    from decode_attention_block_amd import workloads as wl
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
@@ -157,129 +407,73 @@ def main():
         print(json.dumps(copy_probe()), flush=True)
         return
 
+    wl = wl_mod()
     w = wl.BY_NAME[args.workload]
-    if w.ragged is not None or w.layers != 1:
-        sys.exit("bench.py times single-layer, fixed-length workloads")
+    with_cpu = not (args.no_cpu or args.profile_loop)
+    print(f"[bench] {w.name}: {args.steps} steps after {args.warmup} warm-up",
+          file=sys.stderr, flush=True)
+    big = w.decode_steps > 0 or w.layers > 1
+    res, host_cache = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
+                              keep_host=with_cpu and not big, device_inputs=big)
+    if args.profile_loop:
+        print(json.dumps(res), flush=True)
+        return
+
     B, H, D = w.batch, w.heads, w.head_dim
-    per_cache = 2 * B * H * w.context * code_bytes_per_token(w)
-    copies = max(1, math.ceil(CACHE_BYTES_TARGET / per_cache))
-    total_steps = args.warmup + args.steps
-    growth = math.ceil(total_steps / copies)
-    max_blocks = (w.context + growth + 63) // 64
-
-    # ---- untimed setup: inputs, prefill quantization into every copy ----------------
-    t_setup = time.perf_counter()
-    k = torch.from_numpy(wl.prefill_batch(w, 0, 0)).cuda()
-    v = torch.from_numpy(wl.prefill_batch(w, 0, 1)).cuda()
-    kn = np.stack([wl.appended_kv(w, 0, s, 0, growth) for s in range(B)], axis=1)
-    vn = np.stack([wl.appended_kv(w, 0, s, 1, growth) for s in range(B)], axis=1)
-    k_new = torch.from_numpy(kn).cuda()          # [growth][B][H][D]
-    v_new = torch.from_numpy(vn).cuda()
-    queries = torch.from_numpy(np.stack([wl.query(w, 0, s) for s in range(total_steps)])).cuda()
-    caches = []
-    prefill_ms = []
-    for _ in range(copies):
-        c = kvq.KVCache(w.scheme, B, H, D, max_blocks)
-        c.seq_lens.fill_(w.context)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        kvq.kv_quantize_blocks(c, k, v, w.context)
-        e1.record()
-        torch.cuda.synchronize()
-        prefill_ms.append(e0.elapsed_time(e1))
-        caches.append(c)
-    del k, v
-    host_cache = caches[0].host_arrays() if not (args.no_cpu or args.profile_loop) else None
-    max_len_all = w.context + growth
-    ws_bytes = max(kvq.decode_attn_workspace_bytes(caches[0], L, args.blocks_per_split)
-                   for L in range(w.context, max_len_all + 1))
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")  # counters start at zero
-    out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
-    sm = wl.softmax_scale(w)
-    lens_host = [w.context] * copies
-    uses = [0] * copies
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t_setup
-
-    ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    step_bytes, step_attn_bytes = [], []
-
-    def step(i, timed_index):
-        ci = i % copies
-        c = caches[ci]
-        kvq.kv_append(c, k_new[uses[ci]], v_new[uses[ci]], lens_host[ci] + 1)
-        uses[ci] += 1
-        lens_host[ci] += 1
-        L = lens_host[ci]
-        if timed_index is not None:
-            ev_attn[timed_index][0].record()
-        kvq.decode_attn_qkv(c, queries[i], sm, out, ws, L, args.blocks_per_split)
-        if timed_index is not None:
-            ev_attn[timed_index][1].record()
-            lens = [L] * B
-            step_attn_bytes.append(attention_bytes(w, lens))
-            step_bytes.append(attention_bytes(w, lens) + append_bytes(w))
-
-    for i in range(args.warmup):
-        step(i, None)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record()
-    for j in range(args.steps):
-        step(args.warmup + j, j)
-    t1.record()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
-    attn_ms = [a.elapsed_time(b) for a, b in ev_attn]
-    avg_attn_ms = float(np.mean(attn_ms))
-
-    ms_per_step = total_ms / args.steps
-    value = sum(step_bytes) / (total_ms / 1e3) / 1e9
-    achieved = float(np.mean(step_attn_bytes)) / (avg_attn_ms / 1e3) / 1e9
-    bps, n_split = kvq.decode_attn_plan(caches[0], max_len_all, args.blocks_per_split)
+    kernel = ("attn_split_int4_kernel<%d>" if w.scheme == 0 else "attn_split_kernel<1,%d>") % D
     result = {
         "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s, int4 KV, B=8 ctx 8K",
-        "value": value,
+        "value": res["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded N(0,1) K/V with 0.1% x20 outliers, N(0,1) queries)",
-        "pct_of_hbm_peak": 100.0 * value / HBM_PEAK_GBS,
-        "tokens_per_s": B * args.steps / (total_ms / 1e3),
+        "data": "synthetic (seeded; see decode_attention_block_amd/workloads.py)",
+        "pct_of_hbm_peak": 100.0 * res["gbs"] / HBM_PEAK_GBS,
+        "tokens_per_s": res["tokens_per_s"],
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D,
-                   "context": w.context, "context_growth_max": growth,
+                   "context": w.context, "context_range_timed": res["context"],
                    "kv_format": "int4 block-64 symmetric" if w.scheme == 0
                    else "uint8 block-64 asymmetric",
-                   "step": "kv_append + decode_attn_qkv",
-                   "cache_copies_rotated": copies, "blocks_per_split": bps,
-                   "splits_per_row": n_split, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "attn_split_int4_kernel<128> (decode_attn_qkv)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
+                   "step": res["step"],
+                   "cache_copies_rotated": res.get("cache_copies_rotated"),
+                   "blocks_per_split": res["blocks_per_split"],
+                   "splits_per_row": res["splits_per_row"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": kernel + " (decode_attn_qkv)",
+                     "achieved": res["attn_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": res["attn_gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic() if w.name == HEADLINE else None,
-                     "avg_kernel_us": avg_attn_ms * 1e3,
-                     "algorithmic_bytes_per_launch": float(np.mean(step_attn_bytes))},
-        "prefill_quantize": {"ms": float(np.median(prefill_ms)),
-                             "gbs": (2 * B * w.context * H * D * 2 + per_cache)
-                             / (float(np.median(prefill_ms)) / 1e3) / 1e9},
-        "host_wall_s": wall_s,
-        "setup_s": setup_s,
+                     "avg_kernel_us": res["attn_avg_us"],
+                     "algorithmic_bytes_per_launch": res["attn_bytes_per_launch"]},
+        "prefill_quantize": {"ms": res.get("prefill_quantize_ms"),
+                             "gbs": res.get("prefill_quantize_gbs")},
+        "host_wall_s": res["host_wall_s"],
+        "setup_s": res["setup_s"],
     }
-    if not (args.no_cpu or args.profile_loop):
+    if with_cpu and host_cache is not None:
         lens0 = np.full(B, w.context, np.int32)
-        host_cache["B"] = B
         result["cpu_baseline"] = cpu_baseline(w, host_cache, wl.query(w, 0), lens0,
                                               args.cpu_seconds)
+        del host_cache
+    if not args.headline_only:
+        others = []
+        for name in OTHERS:
+            if name == w.name:
+                continue
+            ow = wl.BY_NAME[name]
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            steps = 64 * 3 if ow.decode_steps else (20 if ow.layers > 1 else args.steps)
+            warm = 3 if ow.layers > 1 else args.warmup
+            r, _ = measure(kvq, torch, ow, steps, warm, args.blocks_per_split,
+                           device_inputs=ow.decode_steps > 0 or ow.layers > 1)
+            others.append(r)
+            torch.cuda.empty_cache()
+        result["workloads"] = others
     print(json.dumps(result), flush=True)
 
 

@@ -10,6 +10,8 @@ raises. PyTorch provides device memory and streams.
 import ctypes
 import os
 
+import numpy as np
+
 from . import build as _build
 
 INT4_SYM = 0
@@ -211,16 +213,23 @@ class KVCache:
     def capacity(self):
         return self.max_blocks * BLOCK_TOKENS
 
-    def host_arrays(self, natural=True):
+    def host_arrays(self, natural=True, seqs=None, blocks=None):
         """The cache buffers copied to numpy, keyed like the oracle's cache dicts. With
         natural=True int4 codes are returned in natural [token][channel] order (see
-        layout.py); otherwise as stored."""
+        layout.py); otherwise as stored. `seqs` (a list of sequence indices) and `blocks`
+        (a slice of block indices) restrict the copy; "B" and "max_blocks" then give the
+        sizes of what was copied."""
         from . import layout
-        out = {"scheme": self.scheme, "B": self.batch, "H": self.heads, "D": self.head_dim,
-               "max_blocks": self.max_blocks}
+        sel_b = slice(None) if seqs is None else list(seqs)
+        sel_j = slice(None) if blocks is None else blocks
+        n_b = self.batch if seqs is None else len(sel_b)
+        n_j = len(range(self.max_blocks)[sel_j])
+        out = {"scheme": self.scheme, "B": n_b, "H": self.heads, "D": self.head_dim,
+               "max_blocks": n_j}
         for key in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
             t = getattr(self, key)
-            out[key] = None if t is None else t.cpu().numpy()
+            out[key] = None if t is None else np.ascontiguousarray(
+                t[sel_b][:, :, sel_j].cpu().numpy())
         if natural and self.scheme == INT4_SYM:
             out["k_codes"] = layout.int4_to_natural(out["k_codes"], "k")
             out["v_codes"] = layout.int4_to_natural(out["v_codes"], "v")

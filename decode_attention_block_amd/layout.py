@@ -14,29 +14,51 @@ Natural order packs channel 2k of a token in the low nibble of byte k. These hel
 only move nibbles (reading a cache back, or writing test patterns into it); no part
 of the computation runs here.
 """
-import functools
-
 import numpy as np
 
 BLOCK = 64
 
 
-@functools.lru_cache(maxsize=None)
-def _maps(D):
-    """For one region: stored byte, nibble-in-byte and natural (token, channel) of every
-    stored nibble, each shaped [64 lanes][F dwords][8 nibbles]."""
+def _unpack(b):
+    """uint8 [..., n] -> nibbles [..., n, 2] (low nibble first)."""
+    return np.stack([b & 0xF, b >> 4], axis=-1)
+
+
+def _pack(n):
+    """nibbles [..., n, 2] -> uint8 [..., n]."""
+    return (n[..., 0] | (n[..., 1] << 4)).astype(np.uint8)
+
+
+def _stored_to_fl(stored, D):
+    """[..., 64, D/2] stored bytes -> nibbles [..., F, 64 lanes, 8]: dword f of lane l."""
     F = D // 8
-    ks_k = D // 32
-    lane = np.arange(64).reshape(64, 1, 1)
-    f = np.arange(F).reshape(1, F, 1)
-    q = np.arange(8).reshape(1, 1, 8)
-    byte = ((f // 4) * 64 + lane) * 16 + (f % 4) * 4 + q // 2
-    nib = np.broadcast_to(q % 2, byte.shape)
-    t_k = np.broadcast_to(16 * (f // ks_k) + lane % 16, byte.shape)
-    d_k = 32 * (f % ks_k) + 8 * (lane // 16) + q
-    d_v = np.broadcast_to(16 * (f // 2) + lane % 16, byte.shape)
-    t_v = 32 * (f % 2) + 8 * (lane // 16) + q
-    return byte, nib, (t_k, d_k), (t_v, d_v)
+    lead = stored.shape[:-2]
+    # byte ((f//4)*64 + l)*16 + (f%4)*4 + q//2  ->  [f//4][l][f%4][q]
+    nib = _unpack(stored.reshape(lead + (F // 4, 64, 4, 4))).reshape(lead + (F // 4, 64, 4, 8))
+    n = len(lead)
+    nib = nib.transpose(tuple(range(n)) + (n, n + 2, n + 1, n + 3))   # [g][r][l][q]
+    return nib.reshape(lead + (F, 64, 8))
+
+
+def _fl_to_stored(fl, D):
+    F = D // 8
+    lead = fl.shape[:-3]
+    n = len(lead)
+    nib = fl.reshape(lead + (F // 4, 4, 64, 8))
+    nib = nib.transpose(tuple(range(n)) + (n, n + 2, n + 1, n + 3))   # [g][l][r][q]
+    return _pack(nib.reshape(lead + (F // 4, 64, 4, 4, 2))).reshape(lead + (BLOCK, D // 2))
+
+
+# Axis orders. K: dword f = nt*(D/32) + ks and lane l = 16*lh + ll give the 5-d index
+# [nt][ks][lh][ll][q]; token 16*nt + ll, channel 32*ks + 8*lh + q, so natural order
+# [token][channel] = [nt][ll][ks][lh][q]. V: f = 2*nt + ks gives [nt][ks][lh][ll][q];
+# token 32*ks + 8*lh + q, channel 16*nt + ll, so natural order = [ks][lh][q][nt][ll].
+_K_TO_NAT = (0, 3, 1, 2, 4)
+_V_TO_NAT = (1, 2, 4, 0, 3)
+
+
+def _split_shape(which, D):
+    return (4, D // 32, 4, 16, 8) if which == "k" else (D // 16, 2, 4, 16, 8)
 
 
 def int4_to_natural(stored, which):
@@ -46,13 +68,11 @@ def int4_to_natural(stored, which):
     stored = np.asarray(stored, np.uint8)
     D = stored.shape[-1] * 2
     lead = stored.shape[:-2]
-    region = stored.reshape(lead + (32 * D,))
-    byte, nib, kmap, vmap = _maps(D)
-    t, d = kmap if which == "k" else vmap
-    nibbles = (region[..., byte] >> (4 * nib).astype(np.uint8)) & 0xF
-    nat = np.zeros(lead + (BLOCK, D), np.uint8)
-    nat[..., t, d] = nibbles
-    return (nat[..., 0::2] | (nat[..., 1::2] << 4)).astype(np.uint8)
+    n = len(lead)
+    fl = _stored_to_fl(stored, D).reshape(lead + _split_shape(which, D))
+    perm = _K_TO_NAT if which == "k" else _V_TO_NAT
+    nat = fl.transpose(tuple(range(n)) + tuple(n + p for p in perm))
+    return _pack(nat.reshape(lead + (BLOCK, D // 2, 2)))
 
 
 def int4_from_natural(natural, which):
@@ -60,12 +80,10 @@ def int4_from_natural(natural, which):
     natural = np.asarray(natural, np.uint8)
     D = natural.shape[-1] * 2
     lead = natural.shape[:-2]
-    nat = np.empty(lead + (BLOCK, D), np.uint8)
-    nat[..., 0::2] = natural & 0xF
-    nat[..., 1::2] = natural >> 4
-    byte, nib, kmap, vmap = _maps(D)
-    t, d = kmap if which == "k" else vmap
-    nibbles = nat[..., t, d]                      # [..., 64, F, 8]
-    region = np.zeros(lead + (32 * D,), np.uint8)
-    region[..., byte[..., 0::2]] = nibbles[..., 0::2] | (nibbles[..., 1::2] << 4)
-    return region.reshape(lead + (BLOCK, D // 2))
+    n = len(lead)
+    perm = _K_TO_NAT if which == "k" else _V_TO_NAT
+    split = _split_shape(which, D)
+    nat = _unpack(natural).reshape(lead + tuple(split[p] for p in perm))
+    inv = tuple(int(i) for i in np.argsort(perm))
+    fl = nat.transpose(tuple(range(n)) + tuple(n + p for p in inv))
+    return _fl_to_stored(np.ascontiguousarray(fl).reshape(lead + (D // 8, 64, 8)), D)

@@ -155,3 +155,46 @@ def prefill_batch(w, layer, which, n_tokens=None, seqs=None):
 def softmax_scale(w):
     """binary32 1/sqrt(head_dim), the query scaling the workloads use."""
     return float(np.float32(1.0) / np.sqrt(np.float32(w.head_dim)))
+
+
+def device_seed(w, layer, stream, seq):
+    """63-bit seed of the device-side generator for one (workload, layer, stream,
+    sequence)."""
+    ss = np.random.SeedSequence([SEED, w.index, layer, stream, seq, 1 << 20])
+    return int(ss.generate_state(1, np.uint64)[0] & ((1 << 63) - 1))
+
+
+def prefill_batch_device(w, layer, which, n_tokens=None, device="cuda"):
+    """float16 torch tensor [B][S][H][D] drawn on the device with torch's seeded
+    generator, one stream per sequence: the same distributions as prefill_batch
+    (outliers as an independent 0.1% mask; Student-t(3) as
+    Z / sqrt((Z1^2 + Z2^2 + Z3^2) / 3)), different random streams, so different values.
+    Used where drawing on the host would take minutes (timing the 32K and 32-layer
+    workloads); the parity tests use the host recipe."""
+    import torch
+    n = w.context if n_tokens is None else n_tokens
+    shape = (n, w.heads, w.head_dim)
+    dist = w.k_dist if which == 0 else w.v_dist
+    stream = STREAM_K if which == 0 else STREAM_V
+    out = torch.empty((w.batch,) + shape, dtype=torch.float16, device=device)
+    g = torch.Generator(device=device)
+    for b in range(w.batch):
+        g.manual_seed(device_seed(w, layer, stream, b))
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if dist == "normal_outliers":
+            u = torch.rand(shape, generator=g, device=device)
+            x.mul_(torch.where(u < 0.001, 20.0, 1.0))
+        elif dist.startswith("normal"):
+            mu = float(dist[len("normal"):] or 0.0)
+            if mu:
+                x += mu
+        elif dist == "student_t3_half":
+            chi2 = torch.zeros_like(x)
+            for _ in range(3):
+                z = torch.randn(shape, generator=g, device=device)
+                chi2.addcmul_(z, z)
+            x.mul_(0.5).div_(torch.sqrt(chi2 / 3.0))
+        else:
+            raise ValueError(dist)
+        out[b] = x
+    return out

@@ -1,0 +1,102 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark
+times: prefill with kv_quantize_blocks, then decode steps of kv_append (one token per
+sequence) followed by the fused decode_attn_qkv with the automatic split plan.
+
+The oracle checks sampled outputs it can compute one by one:
+  * the prefill blocks of the sampled sequences, bitwise;
+  * after every step, seq_lens and the block the appended tokens fill. The prefill
+    lengths are multiples of 64, so the appended tokens form one block of their own,
+    which the oracle quantizes from those tokens alone;
+  * attention at the listed steps, for every head of the sampled sequences, within the
+    2e-3 normwise bound, against the oracle's fp64 attention over the GPU cache."""
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_block_amd import workloads as wl
+from helpers import ATTN_TOL, attn_errors, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_steps(w, n_steps, attn_steps, seqs, prefill_seqs):
+    import decode_attention_block_amd as kvq
+    import torch
+    B, H, D = w.batch, w.heads, w.head_dim
+    L0 = w.context
+    assert L0 % 64 == 0
+    j_new = L0 // 64
+    max_blocks = (L0 + n_steps + 63) // 64
+    say(w.name, "generating inputs")
+    c = kvq.KVCache(w.scheme, B, H, D, max_blocks)
+    c.seq_lens.fill_(L0)
+    k = wl.prefill_batch(w, 0, 0)
+    v = wl.prefill_batch(w, 0, 1)
+    say(w.name, "prefill")
+    kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    kvq.kv_quantize_blocks(c, kt, vt, L0)
+    torch.cuda.synchronize()
+    del kt, vt
+    host = c.host_arrays(seqs=seqs)
+    pre = c.host_arrays(seqs=prefill_seqs, blocks=slice(0, j_new))
+    ref = oracle.quantize_cache(w.scheme, k[prefill_seqs], v[prefill_seqs],
+                                np.full(len(prefill_seqs), L0, np.int32), j_new)
+    del k, v
+    for key in ("k_codes", "v_codes"):
+        assert np.array_equal(pre[key], ref[key]), key
+    for key in ("k_scale", "v_scale") + (("k_zero", "v_zero") if w.scheme else ()):
+        assert np.array_equal(pre[key].view(np.uint32), ref[key].view(np.uint32)), key
+    del pre, ref
+
+    kn = np.stack([wl.appended_kv(w, 0, s, 0, n_steps) for s in range(B)], axis=1)
+    vn = np.stack([wl.appended_kv(w, 0, s, 1, n_steps) for s in range(B)], axis=1)
+    k_new, v_new = torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda()
+    sm = wl.softmax_scale(w)
+    out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
+    max_len_all = L0 + n_steps
+    ws_bytes = max(kvq.decode_attn_workspace_bytes(c, L, 0) for L in range(L0, max_len_all + 1))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    worst = 0.0
+    for s in range(1, n_steps + 1):
+        L = L0 + s
+        kvq.kv_append(c, k_new[s - 1], v_new[s - 1], L)
+        q = wl.query(w, 0, s - 1)
+        kvq.decode_attn_qkv(c, torch.from_numpy(q).cuda(), sm, out, ws, L, 0)
+        torch.cuda.synchronize()
+        assert (c.seq_lens.cpu().numpy() == L).all(), s
+        tail = c.host_arrays(blocks=slice(j_new, j_new + 1))
+        tref = oracle.quantize_cache(w.scheme, np.ascontiguousarray(kn[:s].transpose(1, 0, 2, 3)),
+                                     np.ascontiguousarray(vn[:s].transpose(1, 0, 2, 3)),
+                                     np.full(B, s, np.int32), 1)
+        for key in ("k_codes", "v_codes"):
+            assert np.array_equal(tail[key], tref[key]), (s, key)
+        for key in ("k_scale", "v_scale") + (("k_zero", "v_zero") if w.scheme else ()):
+            assert np.array_equal(tail[key].view(np.uint32), tref[key].view(np.uint32)), (s, key)
+        if s in attn_steps:
+            say(w.name, "attention step", s)
+            for key in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
+                host[key][:, :, j_new] = tail[key][seqs, :, 0]
+            bps, n_split = kvq.decode_attn_plan(c, L, 0)
+            o = out.cpu().numpy()[seqs]
+            r = oracle.attention(host, q[seqs], np.full(len(seqs), L, np.int32), sm)
+            norm_err, elem_err = attn_errors(o, r)
+            print(f"{w.name} step {s} len {L} plan ({bps},{n_split}): normwise {norm_err:.3e} "
+                  f"elementwise(floored) {elem_err:.3e}")
+            worst = max(worst, norm_err)
+    assert worst <= ATTN_TOL
+
+
+@pytest.mark.parametrize("index,n_steps", [(1, 28), (2, 55)])
+def test_ctx8k_decode_steps_as_benchmarked(index, n_steps):
+    """The 8K workloads over the context growth the benchmark's rotation reaches;
+    attention of all 256 rows checked at the first and last step, the prefill of
+    sequence 3 bitwise."""
+    w = wl.WORKLOADS[index]
+    _decode_steps(w, n_steps, {1, n_steps}, list(range(w.batch)), [3])
+
+
+def test_long_32k_64_decode_steps():
+    """Batch 16 at context 32768 with 64 appended tokens (the tail block passes through
+    every fill level); attention of sequences 0 and 15 at steps 1, 2, 32, 63, 64."""
+    w = wl.WORKLOADS[3]
+    _decode_steps(w, w.decode_steps, {1, 2, 32, 63, 64}, [0, w.batch - 1], [0, w.batch - 1])

@@ -45,3 +45,31 @@ def test_v_first_dword_holds_eight_tokens_of_channel_zero():
         nat[t, 0] = t + 1            # channel 0 of tokens 0..7 (low nibble)
     st = layout.int4_from_natural(nat, "v").ravel()
     assert st[:4].tolist() == [0x21, 0x43, 0x65, 0x87]
+
+
+def _brute_force_to_natural(region, D, which):
+    """One nibble at a time, straight from the storage formula: dword f of lane l at
+    byte ((f//4)*64 + l)*16 + (f%4)*4, nibble q in bits 4q..4q+3 of that dword."""
+    nat = np.zeros((64, D), np.uint8)
+    F, ks_k = D // 8, D // 32
+    for lane in range(64):
+        for f in range(F):
+            for q in range(8):
+                byte = ((f // 4) * 64 + lane) * 16 + (f % 4) * 4 + q // 2
+                val = (int(region[byte]) >> (4 * (q % 2))) & 0xF
+                if which == "k":
+                    t, d = 16 * (f // ks_k) + lane % 16, 32 * (f % ks_k) + 8 * (lane // 16) + q
+                else:
+                    t, d = 32 * (f % 2) + 8 * (lane // 16) + q, 16 * (f // 2) + lane % 16
+                nat[t, d] = val
+    return nat[:, 0::2] | (nat[:, 1::2] << 4)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_converters_match_nibble_by_nibble_formula(D, which):
+    rs = np.random.default_rng(D + len(which))
+    st = rs.integers(0, 256, (2, 64, D // 2), dtype=np.uint8)
+    nat = layout.int4_to_natural(st, which)
+    for i in range(2):
+        assert np.array_equal(nat[i], _brute_force_to_natural(st[i].ravel(), D, which))
