@@ -9,9 +9,7 @@
 namespace {
 
 constexpr int kBlockTokens = KVQ_BLOCK_TOKENS;
-constexpr int kSplitWavesHost = 4;      // waves per split workgroup (kvq_attn.hip)
-constexpr int64_t kTargetSplitGroups = 512;  // automatic plan: ~2 workgroups per MI355X CU
-constexpr int kMaxAutoBlocksPerSplit = 64;
+constexpr int64_t kTargetWorkgroups = 256;  // automatic plan: one workgroup per MI355X CU
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -40,20 +38,14 @@ int check_len(const kvq_cache* c, int32_t max_len) {
 
 int n_blocks_for(int32_t len) { return (len + kBlockTokens - 1) / kBlockTokens; }
 
-// Blocks per split when the caller leaves it to the library: the context of all rows
-// spread over about kTargetSplitGroups workgroups (each split's merge costs a few
-// microseconds of latency, so fewer, longer splits win once the GPU is full), a whole
-// number of blocks per wave, between 4 and kMaxAutoBlocksPerSplit blocks.
+// Blocks per split when the caller leaves it to the library: as few splits per row as
+// fill the GPU with about one workgroup per CU. Long unbroken runs of one row's codes
+// stream from HBM faster than many short ones, and every extra split costs a merge.
 int auto_blocks_per_split(const kvq_cache* c, int nb) {
   const int64_t rows = static_cast<int64_t>(c->batch) * c->heads;
-  int64_t bps = (rows * nb + kTargetSplitGroups - 1) / kTargetSplitGroups;
-  if (bps < kSplitWavesHost) bps = kSplitWavesHost;
-  if (bps > kMaxAutoBlocksPerSplit) bps = kMaxAutoBlocksPerSplit;
-  // even out the splits of a row (no short last split), whole blocks per wave
-  const int64_t splits = (nb + bps - 1) / bps;
-  if (splits > 0) bps = (nb + splits - 1) / splits;
-  bps = (bps + kSplitWavesHost - 1) / kSplitWavesHost * kSplitWavesHost;
-  return static_cast<int>(bps < kSplitWavesHost ? kSplitWavesHost : bps);
+  const int64_t splits = (kTargetWorkgroups + rows - 1) / rows;
+  const int64_t bps = (nb + splits - 1) / splits;
+  return static_cast<int>(bps < 1 ? 1 : bps);
 }
 
 int plan(const kvq_cache* c, int32_t max_len, int32_t bps_req, int* bps, int* n_split) {
@@ -87,6 +79,10 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
   int bps, n_split;
   int rc = plan(c, max_len, bps_req, &bps, &n_split);
   if (rc != KVQ_OK) return rc;
+  // int4 kernels address a row's codes with 32-bit buffer offsets
+  if (c->scheme == KVQ_INT4_SYM &&
+      static_cast<int64_t>(c->max_blocks) * 32 * c->head_dim > INT32_MAX)
+    return KVQ_ENOTSUP;
   if (n_split > 0) {
     if (!workspace || workspace_bytes_given < workspace_bytes(c, n_split))
       return KVQ_EWORKSPACE;

@@ -58,6 +58,18 @@ __device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no
+// swizzle); loads past num_records return zeros instead of faulting.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// The same non-temporal 16-byte load through a buffer resource: voffset per lane,
+// soffset uniform.
+__device__ __forceinline__ uint4 load_stream(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, 2 /* nt */);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Partial states cross workgroups (and L2 slices: the eight XCDs do not share an L2)
 // through agent-scope atomic stores and loads, which go to memory instead of a
 // possibly stale L2 line; a full device-scope fence would write back and invalidate
@@ -257,6 +269,67 @@ __device__ __forceinline__ void chunk_axpy(const uint4& raw, float p, half2_t of
   }
 }
 
+// ---- the load pipeline shared by the split kernels -----------------------------------
+// Streams one wave's share of a split [blk_begin, blk_end) of n blocks: the blocks
+// blk_begin + (wave + 4i + rot) mod n, i = 0, 1, ..., where rot is a per-row offset so
+// that workgroups streaming different rows are not in step across memory (rows a
+// power-of-two-ish stride apart measured up to 20% slower in lock step). Each block's K
+// codes, then its V codes, pass through two buffers: block i's V codes are requested
+// before its K codes are consumed, block i+1's K codes before its V codes are. No load
+// is ever skipped (a chunk's last K request repeats the last block, a cache hit that is
+// never consumed), so every path issues the same loads and the compiler's wait counts
+// stay exact: a conditional load makes it drain the whole pipeline instead. Per-block
+// parameters (scales, zero points) are loaded one block per lane, 64 blocks at a time,
+// and handed out by readlane: a vector load per block would sit behind the prefetched
+// codes, and waiting for it would drain the pipeline too.
+__device__ __forceinline__ float lane_value(float v, int i) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
+}
+
+template <int LOADS, class LoadParams, class Load, class OnK, class OnV>
+__device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, int wave, int lane,
+                                                   int64_t row, LoadParams load_params, Load load,
+                                                   OnK on_k, OnV on_v) {
+  const int n = blk_end - blk_begin;
+  const int rot = static_cast<int>((static_cast<uint32_t>(row) * 2654435761u) >> 8) % n;
+  const int n_wave = wave < n ? (n - wave + kSplitWaves - 1) / kSplitWaves : 0;
+  auto blk_of = [&](int i) {
+    const int b = wave + kSplitWaves * i + rot;
+    return blk_begin + (b >= n ? b - n : b);
+  };
+  uint4 kbuf[LOADS], vbuf[LOADS];
+  for (int i0 = 0; i0 < n_wave; i0 += kWave) {
+    const int i1 = min(n_wave, i0 + kWave);
+    const auto params = load_params(blk_of(min(i0 + lane, i1 - 1)));
+    load(false, blk_of(i0), kbuf);
+    for (int i = i0; i < i1; ++i) {
+      const int blk = blk_of(i);
+      load(true, blk, vbuf);
+      // keep each request where it is: the scheduler would otherwise sink it below the
+      // work it is meant to overlap, to shorten its registers' lifetime
+      __builtin_amdgcn_sched_barrier(0);
+      const auto pb = params.at(i - i0);
+      on_k(blk, pb, kbuf);
+      load(false, blk_of(min(i + 1, i1 - 1)), kbuf);
+      __builtin_amdgcn_sched_barrier(0);
+      on_v(blk, pb, vbuf);
+    }
+  }
+}
+
+struct ScaleParams {  // block scales of K and V
+  float ks, vs;
+  __device__ __forceinline__ ScaleParams at(int j) const {
+    return {lane_value(ks, j), lane_value(vs, j)};
+  }
+};
+struct ScaleZeroParams {  // block scales and zero points of K and V
+  float ks, kz, vs, vz;
+  __device__ __forceinline__ ScaleZeroParams at(int j) const {
+    return {lane_value(ks, j), lane_value(kz, j), lane_value(vs, j), lane_value(vz, j)};
+  }
+};
+
 // ---- split kernel: grid (n_split, heads, batch), kSplitWaves waves ------------------
 template <int SCHEME, int D>
 __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArgs a) {
@@ -292,10 +365,16 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   q.load(a.q + row * D + chunk * DPL);
   const float qsum_row = group_sum<LPT>(q.sum);
 
-  // Row bases are wave-uniform (scalar registers); each lane adds only its 32-bit offset.
-  const uint8_t* kbase = a.k_codes + row * a.max_blocks * kBlock * G::kRowBytes;
-  const uint8_t* vbase = a.v_codes + row * a.max_blocks * kBlock * G::kRowBytes;
-  const uint32_t lane_off = static_cast<uint32_t>(lane) * 16u;
+  // The row's code regions as buffer resources (uniform base and block offset, the
+  // lane's 16-byte slot as the only per-lane address). The host keeps the row below 2^31
+  // bytes.
+  constexpr int kRegionBytes = kBlock * G::kRowBytes;
+  const int row_bytes = a.max_blocks * kRegionBytes;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.k_codes + row * row_bytes), 0, row_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.v_codes + row * row_bytes), 0, row_bytes, kBufferRsrcWord3);
+  const int lane_off = lane * 16;
   const float* ks = a.k_scale + row * a.max_blocks;
   const float* vs = a.v_scale + row * a.max_blocks;
   const float* kz = a.k_zero + row * a.max_blocks;
@@ -307,17 +386,18 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   float m = -__builtin_inff();  // running max of the base-2 scores (wave-uniform)
   float l = 0.0f;               // sum of weights over this lane's tokens
 
-  auto load_codes = [&](const uint8_t* base, int blk, uint4 (&r)[TPL]) {
-    const uint8_t* blk_base = base + static_cast<int64_t>(blk) * kBlock * G::kRowBytes;
+  auto load_codes = [&](bool is_v, int blk, uint4 (&r)[TPL]) {
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) r[i] = load_stream(blk_base + (lane_off + i * kWave * 16));
+    for (int i = 0; i < TPL; ++i)
+      r[i] = load_stream(is_v ? vrsrc : krsrc, lane_off, blk * kRegionBytes + i * kWave * 16);
   };
 
   // Scores of the lane's TPL tokens of block blk (base-2 logits), then the online
   // softmax update; returns the weights p (relative to the running max m).
-  auto block_weights = [&](int blk, const uint4 (&kr)[TPL], float (&p)[TPL]) {
-    const float sk = ks[blk] * a.qk_scale;
-    const float bias_k = (SCHEME == KVQ_INT4_SYM ? 8.0f : kz[blk]) * qsum_row;
+  auto block_weights = [&](int blk, float kscale, float kzero, const uint4 (&kr)[TPL],
+                           float (&p)[TPL]) {
+    const float sk = kscale * a.qk_scale;
+    const float bias_k = (SCHEME == KVQ_INT4_SYM ? 8.0f : kzero) * qsum_row;
     float s[TPL];
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
@@ -349,14 +429,15 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   };
 
   // o += sum_i p_i * sv * (V code - offset) over the lane's TPL tokens of block blk.
-  auto block_accumulate = [&](int blk, const uint4 (&vr)[TPL], const float (&p)[TPL]) {
-    const float sv = vs[blk];
+  auto block_accumulate = [&](float vscale, float vzero, const uint4 (&vr)[TPL],
+                              const float (&p)[TPL]) {
+    const float sv = vscale;
     half2_t off_lo, off_hi;
     if constexpr (SCHEME == KVQ_INT4_SYM) {
       off_lo = as_h2(0x80088008u);  // -8 * 2^-24 in both halves
       off_hi = as_h2(0x80808080u);  // -8 * 2^-20 = -128 * 2^-24
     } else {
-      const _Float16 zh = static_cast<_Float16>(vz[blk] * -5.9604644775390625e-08f);
+      const _Float16 zh = static_cast<_Float16>(vzero * -5.9604644775390625e-08f);
       off_lo = half2_t{zh, zh};
       off_hi = off_lo;
     }
@@ -364,35 +445,16 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
     for (int i = 0; i < TPL; ++i) chunk_axpy<SCHEME>(vr[i], p[i] * sv, off_lo, off_hi, o);
   };
 
-  // Each wave takes blocks wave, wave + W, wave + 2W, ... of the split. Software
-  // pipeline over three code buffers: while block n is processed, block n+1's K codes
-  // are requested into the free buffer before n's scores, and its V codes into n's K
-  // buffer once the scores are done. The roles (K, V, free) rotate with period three,
-  // so only three 16-byte-per-lane buffers per token are ever live.
-  uint4 r0[TPL], r1[TPL], r2[TPL];
   float p[TPL];
-  auto step = [&](int blk, uint4 (&kcur)[TPL], uint4 (&vcur)[TPL], uint4 (&kfree)[TPL]) {
-    const int next = blk + kSplitWaves;
-    const bool more = next < blk_end;
-    if (more) load_codes(kbase, next, kfree);
-    block_weights(blk, kcur, p);
-    if (more) load_codes(vbase, next, kcur);
-    block_accumulate(blk, vcur, p);
-    return more;
-  };
-  int blk = blk_begin + wave;
-  if (blk < blk_end) {
-    load_codes(kbase, blk, r0);
-    load_codes(vbase, blk, r1);
-    while (true) {
-      if (!step(blk, r0, r1, r2)) break;
-      blk += kSplitWaves;
-      if (!step(blk, r2, r0, r1)) break;
-      blk += kSplitWaves;
-      if (!step(blk, r1, r2, r0)) break;
-      blk += kSplitWaves;
-    }
-  }
+  stream_wave_blocks<TPL>(
+      blk_begin, blk_end, wave, lane, row,
+      [&](int blk) { return ScaleZeroParams{ks[blk], kz[blk], vs[blk], vz[blk]}; }, load_codes,
+      [&](int blk, const ScaleZeroParams& pb, const uint4 (&kr)[TPL]) {
+        block_weights(blk, pb.ks, pb.kz, kr, p);
+      },
+      [&](int, const ScaleZeroParams& pb, const uint4 (&vr)[TPL]) {
+        block_accumulate(pb.vs, pb.vz, vr, p);
+      });
 
   // Per-lane result in true units: o_true[k] = o[k] * unit(k).
 #pragma unroll
@@ -447,11 +509,14 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
 // would leave weights of 1e-4 with only ~11 significant bits).
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// nibble of a dword held by operand slot j, and the slot of nibble q
-__device__ constexpr int kSlotNibble[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-__device__ constexpr int kNibbleSlot[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+// Nibble of a dword held by operand slot j (0, 4, 1, 5, 2, 6, 3, 7 for j = 0..7), and
+// the slot of nibble q (the inverse). Arithmetic rather than a table: a table indexed by
+// lane would be read from memory.
+__device__ __forceinline__ constexpr int slot_nibble(int j) { return (j >> 1) | ((j & 1) << 2); }
+__device__ __forceinline__ constexpr int nibble_slot(int q) { return ((q & 3) << 1) | (q >> 2); }
 
 // 8 stored nibbles -> fp16 operands in slot order: slots 2, 3, 6, 7 hold 16*c * 2^-10,
 // the others c * 2^-10 (c = nibble - 8). A mask leaves each nibble pair as fp16
@@ -546,16 +611,22 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(At
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint16_t bits = qrow[32 * ks + 8 * grp + kSlotNibble[j]];
+        const uint16_t bits = qrow[32 * ks + 8 * grp + slot_nibble(j)];
         float x = static_cast<float>(__builtin_bit_cast(_Float16, bits)) * keep;
         if (j & 2) x *= 0.0625f;
         aq[ks][j] = static_cast<_Float16>(x);
       }
   }
 
-  const uint8_t* kbase = a.k_codes + row * a.max_blocks * kRegionBytes;
-  const uint8_t* vbase = a.v_codes + row * a.max_blocks * kRegionBytes;
-  const uint32_t lane_off = static_cast<uint32_t>(lane) * 16u;
+  // The row's code regions as buffer resources: a load's address is then the uniform
+  // block offset (a scalar register) plus the lane's 16-byte slot, with no per-lane
+  // 64-bit address arithmetic. The host keeps max_blocks * 32 * D below 2^31.
+  const int row_bytes = a.max_blocks * kRegionBytes;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.k_codes + row * row_bytes), 0, row_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.v_codes + row * row_bytes), 0, row_bytes, kBufferRsrcWord3);
+  const int lane_off = lane * 16;
   const float* ks_ptr = a.k_scale + row * a.max_blocks;
   const float* vs_ptr = a.v_scale + row * a.max_blocks;
 
@@ -565,16 +636,17 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(At
   float m = -__builtin_inff();  // running max of the base-2 scores (wave-uniform)
   float l = 0.0f;               // lanes 0..15: sum of their tokens' weights
 
-  auto load_codes = [&](const uint8_t* base, int blk, uint4 (&r)[LOADS]) {
-    const uint8_t* blk_base = base + static_cast<int64_t>(blk) * kRegionBytes;
+  auto load_codes = [&](__amdgpu_buffer_rsrc_t rsrc, int blk, uint4 (&r)[LOADS]) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) r[i] = load_stream(blk_base + (lane_off + i * kWave * 16));
+    for (int i = 0; i < LOADS; ++i)
+      r[i] = load_stream(rsrc, lane_off, blk * kRegionBytes + i * kWave * 16);
   };
+
 
   // Scores of the block's 64 tokens (lanes 0..15 hold tokens 16*nt + lane), the
   // online-softmax update, and the weights p (relative to the running max).
-  auto block_weights = [&](int blk, const uint4 (&kr)[LOADS], float (&p)[4]) {
-    const float sk = ks_ptr[blk] * a.qk_scale * 1024.0f;  // operands carry 2^-10
+  auto block_weights = [&](int blk, float kscale, const uint4 (&kr)[LOADS], float (&p)[4]) {
+    const float sk = kscale * a.qk_scale * 1024.0f;  // operands carry 2^-10
     float4_t acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -610,13 +682,15 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(At
   };
 
   // o[n] += sv * sum_t p_t * c(t, 16n + lane) for the block (lanes 0..15).
-  auto block_accumulate = [&](int blk, const uint4 (&vr)[LOADS], const float (&p)[4]) {
+  const int p_slot = nibble_slot(lane & 7);                    // this lane's weights' slot
+  const float p_unit = (p_slot & 2) ? 1024.0f : 16384.0f;      // x16 slots: 2^14 / 16
+  auto block_accumulate = [&](float vscale, const uint4 (&vr)[LOADS], const float (&p)[4]) {
     // Operands carry 2^-10 (codes) and 2^14 (weights): p <= 1 is split as p * 2^14 into
     // fp16 high and low parts so that the low part of small weights stays a normal fp16.
-    const float sv = vs_ptr[blk] * (1024.0f / 16384.0f);
+    const float sv = vscale * (1024.0f / 16384.0f);
     if (lane < 16) {
-      const int slot = kNibbleSlot[lane & 7];
-      const float scale = (slot & 2) ? 1024.0f : 16384.0f;  // x16 slots: 2^14 / 16
+      const int slot = p_slot;
+      const float scale = p_unit;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const float x = p[nt] * scale;
@@ -642,31 +716,17 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(At
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Software pipeline over three code buffers (as in the uint8 kernel).
-  uint4 r0[LOADS], r1[LOADS], r2[LOADS];
   float p[4];
-  auto step = [&](int blk, uint4 (&kcur)[LOADS], uint4 (&vcur)[LOADS], uint4 (&kfree)[LOADS]) {
-    const int next = blk + kSplitWaves;
-    const bool more = next < blk_end;
-    if (more) load_codes(kbase, next, kfree);
-    block_weights(blk, kcur, p);
-    if (more) load_codes(vbase, next, kcur);
-    block_accumulate(blk, vcur, p);
-    return more;
-  };
-  int blk = blk_begin + wave;
-  if (blk < blk_end) {
-    load_codes(kbase, blk, r0);
-    load_codes(vbase, blk, r1);
-    while (true) {
-      if (!step(blk, r0, r1, r2)) break;
-      blk += kSplitWaves;
-      if (!step(blk, r2, r0, r1)) break;
-      blk += kSplitWaves;
-      if (!step(blk, r1, r2, r0)) break;
-      blk += kSplitWaves;
-    }
-  }
+  stream_wave_blocks<LOADS>(
+      blk_begin, blk_end, wave, lane, row,
+      [&](int blk) { return ScaleParams{ks_ptr[blk], vs_ptr[blk]}; },
+      [&](bool is_v, int blk, uint4 (&r)[LOADS]) { load_codes(is_v ? vrsrc : krsrc, blk, r); },
+      [&](int blk, const ScaleParams& pb, const uint4 (&kr)[LOADS]) {
+        block_weights(blk, pb.ks, kr, p);
+      },
+      [&](int, const ScaleParams& pb, const uint4 (&vr)[LOADS]) {
+        block_accumulate(pb.vs, vr, p);
+      });
 
   const float lw = row0_sum(lane < 16 ? l : 0.0f);
   if (lane < 16) {
