@@ -79,10 +79,10 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
   int bps, n_split;
   int rc = plan(c, max_len, bps_req, &bps, &n_split);
   if (rc != KVQ_OK) return rc;
-  // int4 kernels address a row's codes with 32-bit buffer offsets
-  if (c->scheme == KVQ_INT4_SYM &&
-      static_cast<int64_t>(c->max_blocks) * 32 * c->head_dim > INT32_MAX)
-    return KVQ_ENOTSUP;
+  // the split kernels address a row's codes with 32-bit buffer offsets
+  const int64_t row_code_bytes = static_cast<int64_t>(c->max_blocks) * kBlockTokens *
+                                 (c->scheme == KVQ_INT4_SYM ? c->head_dim / 2 : c->head_dim);
+  if (row_code_bytes > INT32_MAX) return KVQ_ENOTSUP;
   if (n_split > 0) {
     if (!workspace || workspace_bytes_given < workspace_bytes(c, n_split))
       return KVQ_EWORKSPACE;

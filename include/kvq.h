@@ -170,8 +170,9 @@ size_t decode_attn_workspace_bytes(const kvq_cache* cache, int32_t max_len,
  *                     16-byte aligned; must not be shared by concurrent calls.
  *   max_len         : host-side bound on seq_lens, sizes the launch; <= MB*64.
  *   blocks_per_split: 0 = automatic, else the split size in blocks.
- * int4 caches need MB*32*D < 2^31 (a row's codes are addressed with 32-bit offsets;
- * KVQ_ENOTSUP otherwise, also from decode_attn_split / decode_attn_combine).
+ * A row's codes must stay below 2^31 bytes (MB*64*D/2 for int4, MB*64*D for uint8):
+ * they are addressed with 32-bit offsets (KVQ_ENOTSUP otherwise, also from
+ * decode_attn_split / decode_attn_combine).
  * Returns KVQ_OK or a negative kvq_status. */
 int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, void* out,
                     void* workspace, size_t workspace_bytes, int32_t max_len,

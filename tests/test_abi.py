@@ -96,9 +96,11 @@ def test_capacity_and_lengths():
     assert rc_append(cache(k_tail=0)) == EINVAL
     assert rc_append(cache(H=256)) == ENOTSUP           # arrival count must fit 8 bits
     assert rc_append(cache(MB=1 << 18), max_len_after=100) == ENOTSUP  # lengths < 2^24
-    # int4 rows are addressed with 32-bit offsets: MB * 32 * D < 2^31
-    assert rc_attn(cache(MB=(1 << 19) + 1, D=128)) == ENOTSUP
-    assert rc_attn(cache(scheme=1, MB=(1 << 19) + 1, D=128), ws=0) == EWS  # uint8: no limit
+    # a row's codes are addressed with 32-bit offsets: below 2^31 bytes
+    assert rc_attn(cache(MB=(1 << 19) + 1, D=128)) == ENOTSUP            # int4: 4 KiB blocks
+    assert rc_attn(cache(MB=(1 << 19) - 1, D=128), ws=0) == EWS           # just fits
+    assert rc_attn(cache(scheme=1, MB=(1 << 18) + 1, D=128)) == ENOTSUP  # uint8: 8 KiB
+    assert rc_attn(cache(scheme=1, MB=1 << 18, D=64), ws=0) == EWS
 
 
 @no_gpu_only
