@@ -12,8 +12,9 @@ Inputs are synthetic and seeded (decode_attention_block_amd.workloads), already
 resident in HBM when timing starts. Steps rotate over enough copies of the cache
 (>= 1 GiB in all) that the 256 MB Infinity Cache cannot hold them, so every step
 reads its cache from HBM. Each copy gains one token per use, so the context grows
-from 8192 by at most ceil((warmup + steps) / copies) tokens; bytes are counted from
-the actual lengths.
+from 8192 by at most ceil(steps / copies) tokens; bytes are counted from the actual
+lengths. Warm-up steps (the GPU takes a few milliseconds of load to reach steady
+clocks) run first, from the same prefill lengths, which are restored before timing.
 
 The same run also measures the other workloads (unless --headline-only) and reports
 them under "workloads":
@@ -51,8 +52,8 @@ OTHERS = ("llama7b_b8_h32_d128_ctx8k_uint8", "long_b16_h32_d128_ctx32k_append64_
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--blocks-per-split", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -213,9 +214,10 @@ def workspace(kvq, torch, cache, lengths, bps):
 def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs):
     """Single-layer fixed-length workloads; step = kv_append + decode_attn_qkv.
 
-    Without decode steps of its own (the 8K workloads) the step rotates over cache
-    copies; with them (the 32K workload) the workload's decode loop runs from the same
-    prefill, lengths reset between loops (untimed), until `steps` steps are timed."""
+    Steps run in segments that start from the prefill lengths (reset between segments,
+    untimed): the 32K workload's segments are its 64-step decode loop on one cache; the
+    8K workloads rotate over cache copies, each gaining one token per use. Warm-up steps
+    are whole steps too, in segments of their own."""
     wl = wl_mod()
     B, H, D = w.batch, w.heads, w.head_dim
     per_cache = 2 * B * H * w.context * code_bytes_per_token(w)
@@ -223,7 +225,8 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
         copies, growth = 1, w.decode_steps
     else:
         copies = max(1, math.ceil(CACHE_BYTES_TARGET / per_cache))
-        growth = math.ceil((warmup + steps) / copies)
+        growth = math.ceil(steps / copies)
+    seg_cap = copies * growth                # steps before lengths must be reset
     max_blocks = (w.context + growth + 63) // 64
     t_setup = time.perf_counter()
     caches, prefill_ms = quantized_copies(kvq, torch, w, 0, wl.lengths(w), max_blocks, copies,
@@ -232,65 +235,49 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
     vn = np.stack([wl.appended_kv(w, 0, s, 1, growth) for s in range(B)], axis=1)
     k_new = torch.from_numpy(kn).cuda()          # [growth][B][H][D]
     v_new = torch.from_numpy(vn).cuda()
-    n_q = warmup + steps
-    queries = torch.from_numpy(np.stack([wl.query(w, 0, s % max(growth, 1) if w.decode_steps
-                                                  else s) for s in range(n_q)])).cuda()
+    queries = torch.from_numpy(np.stack([wl.query(w, 0, s) for s in range(seg_cap)])).cuda()
     host_cache = caches[0].host_arrays() if keep_host else None
     ws = workspace(kvq, torch, caches[0], range(w.context, w.context + growth + 1), bps)
     out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
     sm = wl.softmax_scale(w)
-    lens_host = [w.context] * copies
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
     timer = Timer(torch)
     attn_bytes, step_bytes = [], []
 
-    def step(i, timed):
-        ci = i % copies
-        c = caches[ci]
-        used = lens_host[ci] - w.context
-        kvq.kv_append(c, k_new[used], v_new[used], lens_host[ci] + 1)
-        lens_host[ci] += 1
-        L = lens_host[ci]
+    def step(j, timed):
+        """Step j of a segment: copy j % copies gains its (j // copies)-th token."""
+        c = caches[j % copies]
+        used = j // copies
+        L = w.context + used + 1
+        kvq.kv_append(c, k_new[used], v_new[used], L)
         if timed:
             e0 = timer.event()
-        kvq.decode_attn_qkv(c, queries[i], sm, out, ws, L, bps)
+        kvq.decode_attn_qkv(c, queries[j], sm, out, ws, L, bps)
         if timed:
             timer.attn.append((e0, timer.event()))
             attn_bytes.append(attention_bytes(w, [L] * B))
             step_bytes.append(attn_bytes[-1] + append_bytes(w))
 
-    def reset():
-        for ci, c in enumerate(caches):
-            c.seq_lens.fill_(w.context)
-            lens_host[ci] = w.context
+    def run(n_steps, timed):
+        done = 0
+        while done < n_steps:
+            for c in caches:
+                c.seq_lens.fill_(w.context)
+            torch.cuda.synchronize()
+            n = min(seg_cap, n_steps - done)
+            t0 = timer.event() if timed else None
+            for j in range(n):
+                step(j, timed)
+            if timed:
+                timer.segments.append((t0, timer.event()))
+            done += n
         torch.cuda.synchronize()
 
+    run(warmup, False)
     wall0 = time.perf_counter()
-    if w.decode_steps:
-        # warm up on attention alone (appends would consume the loop's tokens)
-        for i in range(warmup):
-            kvq.decode_attn_qkv(caches[0], queries[0], sm, out, ws, w.context, bps)
-        torch.cuda.synchronize()
-        done = 0
-        while done < steps:
-            reset()
-            n = min(w.decode_steps, steps - done)
-            t0 = timer.event()
-            for j in range(n):
-                step(j, True)
-            timer.segments.append((t0, timer.event()))
-            done += n
-    else:
-        for i in range(warmup):
-            step(i, False)
-        torch.cuda.synchronize()
-        t0 = timer.event()
-        for j in range(steps):
-            step(warmup + j, True)
-        timer.segments.append((t0, timer.event()))
-    torch.cuda.synchronize()
+    run(steps, True)
     wall_s = time.perf_counter() - wall0
     total_ms = timer.total_ms()
     attn_ms = timer.attn_ms()
@@ -306,8 +293,7 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
         "attn_gbs": float(np.mean(attn_bytes)) / (float(np.mean(attn_ms)) / 1e3) / 1e9,
         "attn_bytes_per_launch": float(np.mean(attn_bytes)),
         "context": [w.context + 1, w.context + growth],
-        "cache_copies_rotated": copies, "blocks_per_split": bps_eff,
-        "splits_per_row": n_split,
+        "cache_copies_rotated": copies, "blocks_per_split": bps_eff, "splits_per_row": n_split,
         "prefill_quantize_ms": float(np.median(prefill_ms)),
         "prefill_quantize_gbs": (2 * B * w.context * H * D * 2 + per_cache)
         / (float(np.median(prefill_ms)) / 1e3) / 1e9,
@@ -468,7 +454,7 @@ def main():
             ow = wl.BY_NAME[name]
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             steps = 64 * 3 if ow.decode_steps else (20 if ow.layers > 1 else args.steps)
-            warm = 3 if ow.layers > 1 else args.warmup
+            warm = 10 if ow.layers > 1 else args.warmup
             r, _ = measure(kvq, torch, ow, steps, warm, args.blocks_per_split,
                            device_inputs=ow.decode_steps > 0 or ow.layers > 1)
             others.append(r)

@@ -125,6 +125,16 @@ def test_plan_is_whole_blocks_and_covers_context():
     assert kvq.decode_attn_plan(c, 8192, 5) == (5, (128 + 4) // 5)
 
 
+def test_automatic_plan_fills_the_gpu_with_fewest_splits():
+    # one workgroup per row once the rows alone fill the 256 CUs
+    assert kvq.decode_attn_plan(cache(B=8, H=32, MB=129), 8192) == (128, 1)
+    assert kvq.decode_attn_plan(cache(B=8, H=32, MB=129), 8220) == (129, 1)
+    assert kvq.decode_attn_plan(cache(B=16, H=32, MB=514), 32832) == (513, 1)
+    # fewer rows: just enough splits per row to reach about 256 workgroups
+    assert kvq.decode_attn_plan(cache(B=1, H=32, MB=2048), 131072) == (256, 8)
+    assert kvq.decode_attn_plan(cache(B=1, H=2, MB=4), 256) == (1, 4)
+
+
 def test_strerror_names_every_status():
     for code in range(-6, 1):
         assert kvq.kvq_strerror(code) != "unknown status"

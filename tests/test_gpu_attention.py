@@ -124,27 +124,98 @@ def test_empty_and_single_token_rows():
 
 
 @pytest.mark.parametrize("scheme", [INT4, UINT8])
-def test_split_and_combine_phases_equal_fused_call(scheme):
-    """decode_attn_split + decode_attn_combine give bitwise the fused result, and the
-    fused call leaves the workspace's arrival counters at zero after every call."""
+@pytest.mark.parametrize("bps", [2, 0])
+def test_split_and_combine_phases_equal_fused_call(scheme, bps):
+    """decode_attn_split + decode_attn_combine give bitwise the fused result (several
+    splits per row, and the automatic plan), and the fused call leaves the workspace's
+    arrival counters at zero after every call."""
     import decode_attention_block_amd as kvq
     import torch
     k, v, q, lens = _small_case(scheme, 64, seed=8)
     c = gpu_quantize(scheme, k, v, lens, 11)
-    say("phases", scheme)
+    say("phases", scheme, bps)
     L = int(lens.max())
     qt = to_gpu(q)
-    ws = kvq.make_workspace(c, L, 2)
+    ws = kvq.make_workspace(c, L, bps)
     fused = torch.empty_like(qt)
     for _ in range(3):
-        kvq.decode_attn_qkv(c, qt, 0.125, fused, ws, L, 2)
+        kvq.decode_attn_qkv(c, qt, 0.125, fused, ws, L, bps)
         torch.cuda.synchronize()
         assert not ws[:4 * c.batch * c.heads].any()
     out = torch.empty_like(qt)
-    kvq.decode_attn_split(c, qt, 0.125, ws, L, 2)
-    kvq.decode_attn_combine(c, out, ws, L, 2)
+    kvq.decode_attn_split(c, qt, 0.125, ws, L, bps)
+    kvq.decode_attn_combine(c, out, ws, L, bps)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), fused.cpu().numpy())
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bps", [0, 3])
+def test_ragged_rows(scheme, D, bps):
+    """Ragged rows in one batch: empty, one-token, block-edge and long rows (one split or
+    several). All rows within tolerance of the oracle; split + combine bitwise equal to
+    the fused call; counters back at zero; repeated calls identical."""
+    import decode_attention_block_amd as kvq
+    import torch
+    B, H, S = 13, 3, 700
+    lens = np.array([0, 1, 63, 64, 65, 700, 0, 333, 129, 2, 640, 17, 511], np.int32)
+    k, v, q, _ = _small_case(scheme, D, seed=21, B=B, H=H, S=S, lens=lens)
+    c = gpu_quantize(scheme, k, v, lens, 11)
+    L = int(lens.max())
+    say("ragged", scheme, D, "plan", kvq.decode_attn_plan(c, L, bps))
+    sm = float(np.float32(1) / np.sqrt(np.float32(D)))
+    qt = to_gpu(q)
+    ws = kvq.make_workspace(c, L, bps)
+    fused = torch.full_like(qt, 7.0)
+    kvq.decode_attn_qkv(c, qt, sm, fused, ws, L, bps)
+    torch.cuda.synchronize()
+    o = fused.cpu().numpy()
+    ref = oracle.attention(c.host_arrays(), q, lens, sm)
+    norm_err, _ = attn_errors(o, ref)
+    print(f"ragged scheme {scheme} D {D} bps {bps}: normwise {norm_err:.3e}")
+    assert norm_err <= ATTN_TOL
+    assert not o[0].any() and not o[6].any()                  # empty rows are zeros
+    assert not ws[:4 * B * H].any()
+    for _ in range(2):
+        again = torch.empty_like(qt)
+        kvq.decode_attn_qkv(c, qt, sm, again, ws, L, bps)
+        torch.cuda.synchronize()
+        assert np.array_equal(again.cpu().numpy(), o)
+    out = torch.full_like(qt, 7.0)
+    kvq.decode_attn_split(c, qt, sm, ws, L, bps)
+    kvq.decode_attn_combine(c, out, ws, L, bps)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), o)
+
+
+@pytest.mark.parametrize("lens", [(5, 70), (0, 0, 0), (0, 130, 0)])
+def test_lengths_below_the_launch_bound(lens):
+    """max_len well above every length (the launch sizes for capacity, the rows are
+    shorter), and batches with empty rows only."""
+    import decode_attention_block_amd as kvq
+    import torch
+    lens = np.array(lens, np.int32)
+    B, H, S = len(lens), 2, 130
+    k, v, q, _ = _small_case(INT4, 128, seed=23, B=B, H=H, S=S, lens=lens)
+    c = gpu_quantize(INT4, k, v, lens, 4, max_len=S)
+    say("short rows", lens.tolist())
+    sm = 0.0883883476
+    qt = to_gpu(q)
+    ws = kvq.make_workspace(c, 256)
+    out = torch.full_like(qt, 7.0)
+    kvq.decode_attn_qkv(c, qt, sm, out, ws, 256)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    ref = oracle.attention(c.host_arrays(), q, lens, sm)
+    rows = [(b, h) for b in range(B) for h in range(H) if lens[b] > 0]
+    for b in range(B):
+        if lens[b] == 0:
+            assert not o[b].any()
+    if rows:
+        norm_err, _ = attn_errors(o, ref, rows=rows)
+        assert norm_err <= ATTN_TOL
+    assert not ws[:4 * B * H].any()
 
 
 def test_zero_context_call_writes_zeros():
