@@ -44,6 +44,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_int4_b8h32d128_ctx8k_traffic.json")
 CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
+EVENT_STRIDE = 8               # HIP events around every 8th attention launch: a pair of
+                               # events around every launch adds ~5 us to each step
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 OTHERS = ("llama7b_b8_h32_d128_ctx8k_uint8", "long_b16_h32_d128_ctx32k_append64_int4",
           "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4")
@@ -154,8 +156,9 @@ def cpu_baseline(w, host_cache, q, lens, budget_s):
 
 
 class Timer:
-    """HIP events around each attention launch and around each timed segment, all on
-    the current stream (the one the library's kernels are queued on)."""
+    """HIP events around sampled attention launches (every EVENT_STRIDE-th) and around
+    each timed segment, all on the current stream (the one the library's kernels are
+    queued on). An event pair measures the launch including its dispatch."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -252,13 +255,15 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
         used = j // copies
         L = w.context + used + 1
         kvq.kv_append(c, k_new[used], v_new[used], L)
-        if timed:
+        sample = timed and j % EVENT_STRIDE == 0
+        if sample:
             e0 = timer.event()
         kvq.decode_attn_qkv(c, queries[j], sm, out, ws, L, bps)
-        if timed:
+        if sample:
             timer.attn.append((e0, timer.event()))
             attn_bytes.append(attention_bytes(w, [L] * B))
-            step_bytes.append(attn_bytes[-1] + append_bytes(w))
+        if timed:
+            step_bytes.append(attention_bytes(w, [L] * B) + append_bytes(w))
 
     def run(n_steps, timed):
         done = 0
@@ -326,10 +331,11 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
 
     def step(timed):
         for layer in range(w.layers):
-            if timed:
+            sample = timed and layer % EVENT_STRIDE == 0
+            if sample:
                 e0 = timer.event()
             kvq.decode_attn_qkv(caches[layer], queries[layer], sm, out, ws, L, bps)
-            if timed:
+            if sample:
                 timer.attn.append((e0, timer.event()))
 
     wall0 = time.perf_counter()

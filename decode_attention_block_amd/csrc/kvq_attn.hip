@@ -275,10 +275,10 @@ __device__ __forceinline__ void chunk_axpy(const uint4& raw, float p, half2_t of
 // that workgroups streaming different rows are not in step across memory (rows a
 // power-of-two-ish stride apart measured up to 20% slower in lock step). Each block's K
 // codes, then its V codes, pass through two buffers: block i's V codes are requested
-// before its K codes are consumed, block i+1's K codes before its V codes are. No load
-// is ever skipped (a chunk's last K request repeats the last block, a cache hit that is
-// never consumed), so every path issues the same loads and the compiler's wait counts
-// stay exact: a conditional load makes it drain the whole pipeline instead. Per-block
+// before its K codes are consumed, block i+1's K codes before its V codes are; the last
+// block of a chunk is peeled off the loop, so the loop body's loads are unconditional,
+// every path issues the same loads and the compiler's wait counts stay exact (a
+// conditional load makes it drain the whole pipeline instead). Per-block
 // parameters (scales, zero points) are loaded one block per lane, 64 blocks at a time,
 // and handed out by readlane: a vector load per block would sit behind the prefetched
 // codes, and waiting for it would drain the pipeline too.
@@ -302,7 +302,7 @@ __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, i
     const int i1 = min(n_wave, i0 + kWave);
     const auto params = load_params(blk_of(min(i0 + lane, i1 - 1)));
     load(false, blk_of(i0), kbuf);
-    for (int i = i0; i < i1; ++i) {
+    for (int i = i0; i < i1 - 1; ++i) {
       const int blk = blk_of(i);
       load(true, blk, vbuf);
       // keep each request where it is: the scheduler would otherwise sink it below the
@@ -310,8 +310,16 @@ __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, i
       __builtin_amdgcn_sched_barrier(0);
       const auto pb = params.at(i - i0);
       on_k(blk, pb, kbuf);
-      load(false, blk_of(min(i + 1, i1 - 1)), kbuf);
+      load(false, blk_of(i + 1), kbuf);
       __builtin_amdgcn_sched_barrier(0);
+      on_v(blk, pb, vbuf);
+    }
+    {  // the chunk's last block: nothing further to request
+      const int blk = blk_of(i1 - 1);
+      load(true, blk, vbuf);
+      __builtin_amdgcn_sched_barrier(0);
+      const auto pb = params.at(i1 - 1 - i0);
+      on_k(blk, pb, kbuf);
       on_v(blk, pb, vbuf);
     }
   }
