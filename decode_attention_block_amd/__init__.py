@@ -23,7 +23,7 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_ENOTSUP", -3: "KVQ_ECAPACITY",
 
 EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan",
            "decode_attn_workspace_bytes", "decode_attn_qkv", "decode_attn_split",
-           "decode_attn_combine", "kvq_strerror", "kvq_version"]
+           "decode_attn_combine", "decode_step_qkv", "kvq_strerror", "kvq_version"]
 
 
 class KvqError(RuntimeError):
@@ -70,6 +70,7 @@ def load_library():
         "decode_attn_qkv": ([C, P, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
         "decode_attn_split": ([C, P, ctypes.c_float, P, sz, i32, i32, P], ctypes.c_int),
         "decode_attn_combine": ([C, P, P, sz, i32, i32, P], ctypes.c_int),
+        "decode_step_qkv": ([C, P, P, P, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
         "kvq_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "kvq_version": ([], ctypes.c_int),
     }
@@ -179,6 +180,23 @@ def decode_attn_combine(cache, out, workspace, max_len, blocks_per_split=0, stre
                                             int(max_len), int(blocks_per_split),
                                             _stream(stream))
     _check(rc, "decode_attn_combine")
+
+
+def decode_step_qkv(cache, k_new, v_new, q, softmax_scale, out, workspace, max_len_after,
+                    blocks_per_split=0, stream=None):
+    """kv_append(k_new, v_new) then decode_attn_qkv(q) over the lengths after the append,
+    as one launch when the plan has one split per row. k_new, v_new, q, out: fp16 CUDA
+    tensors [B][H][D] contiguous; workspace: at least
+    decode_attn_workspace_bytes(cache, max_len_after, blocks_per_split) bytes."""
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("q", q), ("out", out)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B][H][D]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().decode_step_qkv(_desc(cache), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                        float(softmax_scale), _ptr(out), _ptr(workspace),
+                                        ws_bytes, int(max_len_after), int(blocks_per_split),
+                                        _stream(stream))
+    _check(rc, "decode_step_qkv")
 
 
 class KVCache:

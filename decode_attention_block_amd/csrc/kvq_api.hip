@@ -112,6 +112,36 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
   return KVQ_OK;
 }
 
+// Validates an append and fills its launch descriptor.
+int append_args(const kvq_cache* c, const void* k_new, const void* v_new, int32_t max_len_after,
+                kvq::AppendArgs* a) {
+  int rc = check_cache(c);
+  if (rc != KVQ_OK) return rc;
+  if (max_len_after < 1) return KVQ_EINVAL;
+  rc = check_len(c, max_len_after);
+  if (rc != KVQ_OK) return rc;
+  if (!c->k_tail || !c->v_tail || !k_new || !v_new) return KVQ_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_EALIGN;
+  // the arrival ticket lives in the top 8 bits of each length
+  if (c->heads > 255 || static_cast<int64_t>(c->max_blocks) * kBlockTokens >= (1 << 24))
+    return KVQ_ENOTSUP;
+  a->k_new = static_cast<const uint16_t*>(k_new);
+  a->v_new = static_cast<const uint16_t*>(v_new);
+  a->k_codes = static_cast<uint8_t*>(c->k_codes);
+  a->v_codes = static_cast<uint8_t*>(c->v_codes);
+  a->k_scale = c->k_scale;
+  a->v_scale = c->v_scale;
+  a->k_zero = c->k_zero;
+  a->v_zero = c->v_zero;
+  a->k_tail = static_cast<uint16_t*>(c->k_tail);
+  a->v_tail = static_cast<uint16_t*>(c->v_tail);
+  a->seq_lens = c->seq_lens;
+  a->batch = c->batch;
+  a->heads = c->heads;
+  a->max_blocks = c->max_blocks;
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,31 +184,9 @@ int kv_quantize_blocks(const kvq_cache* cache, const void* k, const void* v,
 
 int kv_append(const kvq_cache* cache, const void* k_new, const void* v_new,
               int32_t max_len_after, void* stream) {
-  int rc = check_cache(cache);
-  if (rc != KVQ_OK) return rc;
-  if (max_len_after < 1) return KVQ_EINVAL;
-  rc = check_len(cache, max_len_after);
-  if (rc != KVQ_OK) return rc;
-  if (!cache->k_tail || !cache->v_tail || !k_new || !v_new) return KVQ_EINVAL;
-  if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_EALIGN;
-  // the arrival ticket lives in the top 8 bits of each length
-  if (cache->heads > 255 || static_cast<int64_t>(cache->max_blocks) * kBlockTokens >= (1 << 24))
-    return KVQ_ENOTSUP;
   kvq::AppendArgs a;
-  a.k_new = static_cast<const uint16_t*>(k_new);
-  a.v_new = static_cast<const uint16_t*>(v_new);
-  a.k_codes = static_cast<uint8_t*>(cache->k_codes);
-  a.v_codes = static_cast<uint8_t*>(cache->v_codes);
-  a.k_scale = cache->k_scale;
-  a.v_scale = cache->v_scale;
-  a.k_zero = cache->k_zero;
-  a.v_zero = cache->v_zero;
-  a.k_tail = static_cast<uint16_t*>(cache->k_tail);
-  a.v_tail = static_cast<uint16_t*>(cache->v_tail);
-  a.seq_lens = cache->seq_lens;
-  a.batch = cache->batch;
-  a.heads = cache->heads;
-  a.max_blocks = cache->max_blocks;
+  const int rc = append_args(cache, k_new, v_new, max_len_after, &a);
+  if (rc != KVQ_OK) return rc;
   const hipError_t e = kvq::launch_append(cache->scheme, cache->head_dim, a,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
@@ -206,7 +214,7 @@ int decode_attn_split(const kvq_cache* cache, const void* q, float softmax_scale
                       int32_t blocks_per_split, void* stream) {
   if (!q) return KVQ_EINVAL;
   if (!aligned16(q)) return KVQ_EALIGN;
-  kvq::AttnArgs a;
+  kvq::AttnArgs a = {};
   const int rc = attn_args(cache, q, softmax_scale, nullptr, workspace, workspace_bytes_given,
                            max_len, blocks_per_split, 0, &a);
   if (rc != KVQ_OK) return rc;
@@ -221,7 +229,7 @@ int decode_attn_combine(const kvq_cache* cache, void* out, void* workspace,
                         void* stream) {
   if (!out) return KVQ_EINVAL;
   if (!aligned16(out)) return KVQ_EALIGN;
-  kvq::AttnArgs a;
+  kvq::AttnArgs a = {};
   const int rc = attn_args(cache, nullptr, 1.0f, out, workspace, workspace_bytes_given, max_len,
                            blocks_per_split, 0, &a);
   if (rc != KVQ_OK) return rc;
@@ -235,7 +243,7 @@ int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, 
                     int32_t blocks_per_split, void* stream) {
   if (!q || !out) return KVQ_EINVAL;
   if (!aligned16(q) || !aligned16(out)) return KVQ_EALIGN;
-  kvq::AttnArgs a;
+  kvq::AttnArgs a = {};
   const int rc = attn_args(cache, q, softmax_scale, out, workspace, workspace_bytes_given,
                            max_len, blocks_per_split, 1, &a);
   if (rc != KVQ_OK) return rc;
@@ -245,6 +253,29 @@ int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, 
   return kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a,
                                 static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK
                                                                                 : KVQ_EHIP;
+}
+
+int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                    float softmax_scale, void* out, void* workspace,
+                    size_t workspace_bytes_given, int32_t max_len_after,
+                    int32_t blocks_per_split, void* stream) {
+  if (!q || !out) return KVQ_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_EALIGN;
+  kvq::AttnArgs a = {};
+  int rc = append_args(cache, k_new, v_new, max_len_after, &a.ap);
+  if (rc != KVQ_OK) return rc;
+  rc = attn_args(cache, q, softmax_scale, out, workspace, workspace_bytes_given, max_len_after,
+                 blocks_per_split, 1, &a);
+  if (rc != KVQ_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.n_split == 1)  // one workgroup per row: it appends, then attends
+    return kvq::launch_decode_step(cache->scheme, cache->head_dim, cache->batch, a, s) ==
+                   hipSuccess ? KVQ_OK : KVQ_EHIP;
+  // several splits per row: the splits must all see the appended token
+  if (kvq::launch_append(cache->scheme, cache->head_dim, a.ap, s) != hipSuccess) return KVQ_EHIP;
+  return kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a, s) == hipSuccess
+             ? KVQ_OK
+             : KVQ_EHIP;
 }
 
 const char* kvq_strerror(int status) {

@@ -30,8 +30,7 @@
 //    (max, sum, o[D]) per split; in fused mode (decode_attn_qkv) the last workgroup of
 //    each row to finish merges the row's partials itself, otherwise the combine kernel
 //    does (decode_attn_split + decode_attn_combine).
-#include "kvq_device.h"
-#include "kvq_internal.h"
+#include "kvq_append.h"
 
 namespace kvq {
 namespace {
@@ -50,24 +49,11 @@ struct AGeo {
 
 __device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
 
-// 16-byte load of codes that are read once per call: non-temporal, so the stream does
-// not evict what is reused (scales, partials) from the caches.
-__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no
-// swizzle); loads past num_records return zeros instead of faulting.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-
-// The same non-temporal 16-byte load through a buffer resource: voffset per lane,
-// soffset uniform.
+// 16-byte load of codes that are read once per call, through a buffer resource
+// (voffset per lane, soffset uniform): non-temporal, so the stream does not evict what
+// is reused (scales, partials) from the caches.
 __device__ __forceinline__ uint4 load_stream(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, 2 /* nt */);
-  return make_uint4(v.x, v.y, v.z, v.w);
+  return load_b128<2 /* non-temporal */>(rsrc, voffset, soffset);
 }
 
 // Partial states cross workgroups (and L2 slices: the eight XCDs do not share an L2)
@@ -339,7 +325,7 @@ struct ScaleZeroParams {  // block scales and zero points of K and V
 };
 
 // ---- split kernel: grid (n_split, heads, batch), kSplitWaves waves ------------------
-template <int SCHEME, int D>
+template <int SCHEME, int D, bool kAppend>
 __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArgs a) {
   using G = AGeo<SCHEME, D>;
   constexpr int TPL = G::kTPL, DPL = G::kDPL, LPT = G::kLPT, GROUPS = G::kGroups;
@@ -351,7 +337,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int cap = a.max_blocks * kBlock;
-  int len = a.seq_lens[b];
+  int len = kAppend ? append_token<SCHEME, D>(a.ap, b, static_cast<int64_t>(b) * a.heads + h)
+                    : a.seq_lens[b];
   len = len < 0 ? 0 : min(len, min(a.max_len, cap));
   const int nb = (len + kBlock - 1) / kBlock;
   const int blk_begin = split * a.bps;
@@ -570,7 +557,7 @@ __device__ __forceinline__ float row0_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
 }
 
-template <int D>
+template <int D, bool kAppend>
 __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(AttnArgs a) {
   constexpr int KS = D / 32;               // 32-channel K steps of QK^T
   constexpr int NTV = D / 16;              // 16-channel N tiles of P.V
@@ -585,7 +572,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(At
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int cap = a.max_blocks * kBlock;
-  int len = a.seq_lens[b];
+  int len = kAppend ? append_token<KVQ_INT4_SYM, D>(a.ap, b, static_cast<int64_t>(b) * a.heads + h)
+                    : a.seq_lens[b];
   len = len < 0 ? 0 : min(len, min(a.max_len, cap));
   const int nb = (len + kBlock - 1) / kBlock;
   const int blk_begin = split * a.bps;
@@ -779,28 +767,45 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   merge_row<D, false>(a, row, n, d);
 }
 
-template <int SCHEME, int D>
-hipError_t split_t(int batch, const AttnArgs& a, hipStream_t s) {
+template <int D, bool kAppend>
+hipError_t split_int4_t(int batch, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.heads, batch);
-  hipLaunchKernelGGL((attn_split_kernel<SCHEME, D>), grid, dim3(kSplitWaves * kWave), 0, s, a);
+  hipLaunchKernelGGL((attn_split_int4_kernel<D, kAppend>), grid, dim3(kSplitWaves * kWave), 0, s,
+                     a);
   return hipGetLastError();
+}
+
+template <int SCHEME, int D, bool kAppend>
+hipError_t split_t(int batch, const AttnArgs& a, hipStream_t s) {
+  if constexpr (SCHEME == KVQ_INT4_SYM) {
+    return split_int4_t<D, kAppend>(batch, a, s);
+  } else {
+    dim3 grid(a.n_split, a.heads, batch);
+    hipLaunchKernelGGL((attn_split_kernel<SCHEME, D, kAppend>), grid, dim3(kSplitWaves * kWave),
+                       0, s, a);
+    return hipGetLastError();
+  }
+}
+
+template <bool kAppend>
+hipError_t launch(int scheme, int head_dim, int batch, const AttnArgs& a, hipStream_t s) {
+  if (scheme == KVQ_INT4_SYM)
+    return head_dim == 128 ? split_t<KVQ_INT4_SYM, 128, kAppend>(batch, a, s)
+                           : split_t<KVQ_INT4_SYM, 64, kAppend>(batch, a, s);
+  return head_dim == 128 ? split_t<KVQ_UINT8_ASYM, 128, kAppend>(batch, a, s)
+                         : split_t<KVQ_UINT8_ASYM, 64, kAppend>(batch, a, s);
 }
 
 }  // namespace
 
-template <int D>
-hipError_t split_int4_t(int batch, const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.n_split, a.heads, batch);
-  hipLaunchKernelGGL((attn_split_int4_kernel<D>), grid, dim3(kSplitWaves * kWave), 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_attn_split(int scheme, int head_dim, int batch, const AttnArgs& a,
                              hipStream_t s) {
-  if (scheme == KVQ_INT4_SYM)
-    return head_dim == 128 ? split_int4_t<128>(batch, a, s) : split_int4_t<64>(batch, a, s);
-  return head_dim == 128 ? split_t<KVQ_UINT8_ASYM, 128>(batch, a, s)
-                         : split_t<KVQ_UINT8_ASYM, 64>(batch, a, s);
+  return launch<false>(scheme, head_dim, batch, a, s);
+}
+
+hipError_t launch_decode_step(int scheme, int head_dim, int batch, const AttnArgs& a,
+                              hipStream_t s) {
+  return launch<true>(scheme, head_dim, batch, a, s);
 }
 
 hipError_t launch_attn_combine(int head_dim, int batch, const AttnArgs& a, hipStream_t s) {

@@ -139,4 +139,17 @@ __device__ __forceinline__ uint32_t int4_dword_offset(int lane, int f) {
   return static_cast<uint32_t>(((f >> 2) * 64 + lane) * 16 + (f & 3) * 4);
 }
 
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no
+// swizzle): loads past num_records return zeros and access no memory.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// 16-byte load through a buffer resource at voffset (per lane) + soffset (uniform);
+// AUX = cache policy bits (2: non-temporal).
+template <int AUX>
+__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, soffset, AUX);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 }  // namespace kvq

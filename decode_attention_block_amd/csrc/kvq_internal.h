@@ -55,6 +55,7 @@ struct AttnArgs {
   int heads, max_blocks, max_len, bps, n_split;
   int fused;           // 1: the last workgroup of each row merges the splits and writes out
   float qk_scale;      // softmax_scale * log2(e)
+  AppendArgs ap;       // fused decode step: the token each row's workgroup appends first
 };
 
 // Launchers (return hipError_t of the launch).
@@ -63,6 +64,10 @@ hipError_t launch_quantize(int scheme, int head_dim, int batch, int n_blocks,
 hipError_t launch_append(int scheme, int head_dim, const AppendArgs& a, hipStream_t s);
 hipError_t launch_attn_split(int scheme, int head_dim, int batch, const AttnArgs& a,
                              hipStream_t s);
+// Fused decode step (one split per row): each workgroup appends its row's token (a.ap),
+// then attends over the row including it.
+hipError_t launch_decode_step(int scheme, int head_dim, int batch, const AttnArgs& a,
+                              hipStream_t s);
 hipError_t launch_attn_combine(int head_dim, int batch, const AttnArgs& a, hipStream_t s);
 
 }  // namespace kvq

@@ -190,6 +190,23 @@ int decode_attn_combine(const kvq_cache* cache, void* out, void* workspace,
                         size_t workspace_bytes, int32_t max_len, int32_t blocks_per_split,
                         void* stream);
 
+/* One decode step of every row: kv_append of (k_new, v_new) followed by
+ * decode_attn_qkv of q over the lengths after the append, with the results (cache,
+ * seq_lens and out) bitwise those of the two calls made in that order on one stream.
+ * When the plan for max_len_after gives one split per row (the automatic plan does
+ * whenever B*H >= 256), it is one kernel launch: each row's workgroup appends the
+ * row's token, then attends over the row including it, so the append's latency is
+ * not a separate launch; otherwise it queues the two kernels. Arguments and limits are
+ * those of kv_append and decode_attn_qkv (max_len_after bounds the lengths after the
+ * append and sizes the plan; the workspace is sized by
+ * decode_attn_workspace_bytes(cache, max_len_after, blocks_per_split)); the same
+ * status codes. (The step is one iteration of the decode phase, one token generated
+ * per sequence, [Pg1] §3.1; each such token reads the whole cache, [Pg2] §2.1.)
+ * Returns KVQ_OK or a negative kvq_status. */
+int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                    float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                    int32_t max_len_after, int32_t blocks_per_split, void* stream);
+
 /* Human-readable text of a kvq_status (static storage). */
 const char* kvq_strerror(int status);
 

@@ -58,6 +58,12 @@ def rc_append(c, k=FAKE, v=FAKE, max_len_after=100):
     return kvq.load_library().kv_append(ctypes.byref(c), k, v, max_len_after, None)
 
 
+def rc_step(c, k=FAKE, v=FAKE, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30, max_len_after=100,
+            bps=0):
+    return kvq.load_library().decode_step_qkv(ctypes.byref(c), k, v, q, 0.1, out, ws, ws_bytes,
+                                              max_len_after, bps, None)
+
+
 EINVAL, ENOTSUP, ECAP, EALIGN, EWS = -1, -2, -3, -4, -5
 
 
@@ -113,6 +119,30 @@ def test_workspace_rules():
     assert rc_attn(c, ws=FAKE + 4, ws_bytes=need, max_len=192, bps=1) == EALIGN
     assert rc_attn(c, max_len=192, bps=-1) == EINVAL
     assert kvq.decode_attn_workspace_bytes(cache(D=96), 10) == 0
+
+
+@no_gpu_only
+def test_decode_step_validates_like_append_and_attention():
+    # every rule of kv_append and of decode_attn_qkv, checked before anything launches
+    assert rc_step(cache(), q=0) == EINVAL
+    assert rc_step(cache(), out=0) == EINVAL
+    assert rc_step(cache(), k=0) == EINVAL
+    assert rc_step(cache(), v=FAKE + 2) == EALIGN
+    assert rc_step(cache(), q=FAKE + 4) == EALIGN
+    assert rc_step(cache(), out=FAKE + 4) == EALIGN
+    assert rc_step(cache(scheme=2)) == EINVAL
+    assert rc_step(cache(D=96)) == ENOTSUP
+    assert rc_step(cache(v_tail=0)) == EINVAL
+    assert rc_step(cache(H=256)) == ENOTSUP
+    assert rc_step(cache(MB=3), max_len_after=193) == ECAP
+    assert rc_step(cache(), max_len_after=0) == EINVAL
+    assert rc_step(cache(MB=(1 << 19) + 1, D=128, B=1, H=1), max_len_after=100) == ENOTSUP
+    c = cache(B=2, H=4, D=128, MB=3)
+    need = kvq.decode_attn_workspace_bytes(c, 192, 1)
+    assert rc_step(c, ws_bytes=need - 1, max_len_after=192, bps=1) == EWS
+    assert rc_step(c, ws=0, max_len_after=192, bps=1) == EWS
+    assert rc_step(c, ws=FAKE + 4, ws_bytes=need, max_len_after=192, bps=1) == EALIGN
+    assert rc_step(c, max_len_after=192, bps=-1) == EINVAL
 
 
 def test_plan_is_whole_blocks_and_covers_context():
