@@ -3,10 +3,11 @@
 
 Headline step = one decode step of the whole hot path on the 8K int4 workload (batch 8,
 32 heads, head_dim 128, context 8192 per sequence, 4-bit block codes, 64-token blocks):
-kv_append quantizes one new token per sequence into its row's tail block (one kernel),
-then decode_attn_qkv attends one fp16 query per (sequence, head) over the whole
-compressed cache (one kernel: split-K over the context, the last workgroup of each row
-merges its splits).
+decode_step_qkv quantizes one new token per (sequence, head) into its row's tail block
+and attends one fp16 query per (sequence, head) over the whole compressed cache,
+including that token. With one split per row (256 rows fill the GPU) that is one
+kernel launch: each row's workgroup appends, then attends. --separate times the same
+step as two calls, kv_append then decode_attn_qkv.
 
 Inputs are synthetic and seeded (decode_attention_block_amd.workloads), already
 resident in HBM when timing starts. Steps rotate over enough copies of the cache
@@ -19,8 +20,8 @@ clocks) run first, from the same prefill lengths, which are restored before timi
 The same run also measures the other workloads (unless --headline-only) and reports
 them under "workloads":
   * the 8K uint8 workload, with the same step and rotation;
-  * the 32K workload (batch 16, context 32768): its 64-step decode loop of kv_append +
-    decode_attn_qkv, repeated from the same prefill (lengths reset between loops,
+  * the 32K workload (batch 16, context 32768): its 64-step decode loop of
+    decode_step_qkv, repeated from the same prefill (lengths reset between loops,
     outside the timed region);
   * the 32-layer ragged workload: one step is decode_attn_qkv over each of the 32
     layers' caches (per-sequence lengths 1024..8192, no append in this workload).
@@ -42,9 +43,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_int4_b8h32d128_ctx8k_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_int4_b8h32d128_ctx8k_traffic.json")
 CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
-EVENT_STRIDE = 8               # HIP events around every 8th attention launch: a pair of
+EVENT_STRIDE = 8               # HIP events around every 8th step-kernel launch: a pair of
                                # events around every launch adds ~5 us to each step
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 OTHERS = ("llama7b_b8_h32_d128_ctx8k_uint8", "long_b16_h32_d128_ctx32k_append64_int4",
@@ -58,6 +59,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--blocks-per-split", type=int, default=0)
+    p.add_argument("--separate", action="store_true",
+                   help="time the step as kv_append + decode_attn_qkv (two calls)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate host time spent timing the oracle")
     p.add_argument("--no-cpu", action="store_true")
@@ -95,7 +98,7 @@ def append_bytes(w):
 
 
 def measured_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    """HBM bytes per launch of the headline step kernel from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     runs (scaled by the counters' reading for a 1 GiB copy), or None once the kernel's
     sources differ from the ones the counters were taken on."""
     import hashlib
@@ -156,13 +159,13 @@ def cpu_baseline(w, host_cache, q, lens, budget_s):
 
 
 class Timer:
-    """HIP events around sampled attention launches (every EVENT_STRIDE-th) and around
+    """HIP events around sampled kernel launches (every EVENT_STRIDE-th) and around
     each timed segment, all on the current stream (the one the library's kernels are
     queued on). An event pair measures the launch including its dispatch."""
 
     def __init__(self, torch):
         self.torch = torch
-        self.attn = []       # (start, end) event pairs
+        self.kernel = []     # (start, end) event pairs
         self.segments = []
 
     def event(self):
@@ -170,8 +173,8 @@ class Timer:
         e.record()
         return e
 
-    def attn_ms(self):
-        return [a.elapsed_time(b) for a, b in self.attn]
+    def kernel_ms(self):
+        return [a.elapsed_time(b) for a, b in self.kernel]
 
     def total_ms(self):
         return sum(a.elapsed_time(b) for a, b in self.segments)
@@ -214,8 +217,10 @@ def workspace(kvq, torch, cache, lengths, bps):
     return torch.zeros(n, dtype=torch.uint8, device="cuda")   # counters start at zero
 
 
-def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs):
-    """Single-layer fixed-length workloads; step = kv_append + decode_attn_qkv.
+def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs,
+                         separate=False):
+    """Single-layer fixed-length workloads; step = decode_step_qkv (or, with separate,
+    kv_append + decode_attn_qkv; the sampled kernel is then the attention alone).
 
     Steps run in segments that start from the prefill lengths (reset between segments,
     untimed): the 32K workload's segments are its 64-step decode loop on one cache; the
@@ -247,21 +252,26 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
     setup_s = time.perf_counter() - t_setup
 
     timer = Timer(torch)
-    attn_bytes, step_bytes = [], []
+    kernel_bytes, step_bytes = [], []
 
     def step(j, timed):
         """Step j of a segment: copy j % copies gains its (j // copies)-th token."""
         c = caches[j % copies]
         used = j // copies
         L = w.context + used + 1
-        kvq.kv_append(c, k_new[used], v_new[used], L)
+        if separate:
+            kvq.kv_append(c, k_new[used], v_new[used], L)
         sample = timed and j % EVENT_STRIDE == 0
         if sample:
             e0 = timer.event()
-        kvq.decode_attn_qkv(c, queries[j], sm, out, ws, L, bps)
+        if separate:
+            kvq.decode_attn_qkv(c, queries[j], sm, out, ws, L, bps)
+        else:
+            kvq.decode_step_qkv(c, k_new[used], v_new[used], queries[j], sm, out, ws, L, bps)
         if sample:
-            timer.attn.append((e0, timer.event()))
-            attn_bytes.append(attention_bytes(w, [L] * B))
+            timer.kernel.append((e0, timer.event()))
+            kernel_bytes.append(attention_bytes(w, [L] * B) +
+                                (0 if separate else append_bytes(w)))
         if timed:
             step_bytes.append(attention_bytes(w, [L] * B) + append_bytes(w))
 
@@ -285,18 +295,22 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
     run(steps, True)
     wall_s = time.perf_counter() - wall0
     total_ms = timer.total_ms()
-    attn_ms = timer.attn_ms()
+    kernel_ms = timer.kernel_ms()
     bps_eff, n_split = kvq.decode_attn_plan(caches[0], w.context + growth, bps)
+    one_launch = not separate and n_split == 1
     res = {
         "workload": w.name,
-        "step": "kv_append + decode_attn_qkv",
+        "step": ("kv_append + decode_attn_qkv" if separate else
+                 "decode_step_qkv (%s)" % ("append and attention in one launch" if one_launch
+                                           else "append, then attention")),
+        "kernel": kernel_name(w, fused=one_launch),
         "steps": steps, "warmup": warmup,
         "ms_per_step": total_ms / steps,
         "gbs": sum(step_bytes) / (total_ms / 1e3) / 1e9,
         "tokens_per_s": B * steps / (total_ms / 1e3),
-        "attn_avg_us": float(np.mean(attn_ms)) * 1e3,
-        "attn_gbs": float(np.mean(attn_bytes)) / (float(np.mean(attn_ms)) / 1e3) / 1e9,
-        "attn_bytes_per_launch": float(np.mean(attn_bytes)),
+        "kernel_avg_us": float(np.mean(kernel_ms)) * 1e3,
+        "kernel_gbs": float(np.mean(kernel_bytes)) / (float(np.mean(kernel_ms)) / 1e3) / 1e9,
+        "kernel_bytes_per_launch": float(np.mean(kernel_bytes)),
         "context": [w.context + 1, w.context + growth],
         "cache_copies_rotated": copies, "blocks_per_split": bps_eff, "splits_per_row": n_split,
         "prefill_quantize_ms": float(np.median(prefill_ms)),
@@ -304,7 +318,7 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
         / (float(np.median(prefill_ms)) / 1e3) / 1e9,
         "host_wall_s": wall_s, "setup_s": setup_s,
     }
-    res["attn_frac"] = res["attn_gbs"] / HBM_PEAK_GBS
+    res["kernel_frac"] = res["kernel_gbs"] / HBM_PEAK_GBS
     return res, host_cache
 
 
@@ -336,7 +350,7 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
                 e0 = timer.event()
             kvq.decode_attn_qkv(caches[layer], queries[layer], sm, out, ws, L, bps)
             if sample:
-                timer.attn.append((e0, timer.event()))
+                timer.kernel.append((e0, timer.event()))
 
     wall0 = time.perf_counter()
     for _ in range(warmup):
@@ -350,32 +364,44 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
     wall_s = time.perf_counter() - wall0
     total_ms = timer.total_ms()
     per_launch = attention_bytes(w, lens)
-    attn_ms = timer.attn_ms()
+    kernel_ms = timer.kernel_ms()
     bps_eff, n_split = kvq.decode_attn_plan(caches[0], L, bps)
     res = {
         "workload": w.name,
         "step": f"decode_attn_qkv over {w.layers} layers",
+        "kernel": kernel_name(w, fused=False),
         "steps": steps, "warmup": warmup,
         "ms_per_step": total_ms / steps,
         "gbs": per_launch * w.layers * steps / (total_ms / 1e3) / 1e9,
         "tokens_per_s": B * steps / (total_ms / 1e3),
-        "attn_avg_us": float(np.mean(attn_ms)) * 1e3,
-        "attn_gbs": per_launch / (float(np.mean(attn_ms)) / 1e3) / 1e9,
-        "attn_bytes_per_launch": float(per_launch),
+        "kernel_avg_us": float(np.mean(kernel_ms)) * 1e3,
+        "kernel_gbs": per_launch / (float(np.mean(kernel_ms)) / 1e3) / 1e9,
+        "kernel_bytes_per_launch": float(per_launch),
         "context": [int(lens.min()), L], "mean_context": float(lens.mean()),
         "blocks_per_split": bps_eff, "splits_per_row": n_split,
         "prefill_quantize_ms_per_layer": float(np.median(prefill_ms)),
         "host_wall_s": wall_s, "setup_s": setup_s,
     }
-    res["attn_frac"] = res["attn_gbs"] / HBM_PEAK_GBS
+    res["kernel_frac"] = res["kernel_gbs"] / HBM_PEAK_GBS
     return res
 
 
-def measure(kvq, torch, w, steps, warmup, bps, keep_host=False, device_inputs=False):
+def kernel_name(w, fused):
+    """The timed kernel as rocprofv3 lists it (template arguments: head_dim, and whether
+    the workgroup appends the row's token first)."""
+    b = "true" if fused else "false"
+    if w.scheme == 0:
+        return f"attn_split_int4_kernel<{w.head_dim}, {b}>"
+    return f"attn_split_kernel<1, {w.head_dim}, {b}>"
+
+
+def measure(kvq, torch, w, steps, warmup, bps, keep_host=False, device_inputs=False,
+            separate=False):
     if w.layers > 1:
         res = run_layers(kvq, torch, w, steps, warmup, bps, device_inputs), None
     else:
-        res = run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs)
+        res = run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs,
+                                   separate)
     res[0]["inputs"] = ("K/V drawn on the device (torch generator, same distributions)"
                         if device_inputs else "K/V from the seeded host recipe")
     return res
@@ -406,13 +432,14 @@ def main():
           file=sys.stderr, flush=True)
     big = w.decode_steps > 0 or w.layers > 1
     res, host_cache = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
-                              keep_host=with_cpu and not big, device_inputs=big)
+                              keep_host=with_cpu and not big, device_inputs=big,
+                              separate=args.separate)
     if args.profile_loop:
         print(json.dumps(res), flush=True)
         return
 
     B, H, D = w.batch, w.heads, w.head_dim
-    kernel = ("attn_split_int4_kernel<%d>" if w.scheme == 0 else "attn_split_kernel<1,%d>") % D
+    fused = res["kernel"].endswith("true>")
     result = {
         "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s, int4 KV, B=8 ctx 8K",
         "value": res["gbs"],
@@ -436,12 +463,14 @@ def main():
                    "cache_copies_rotated": res.get("cache_copies_rotated"),
                    "blocks_per_split": res["blocks_per_split"],
                    "splits_per_row": res["splits_per_row"], "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": kernel + " (decode_attn_qkv)",
-                     "achieved": res["attn_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": res["attn_gbs"] / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if w.name == HEADLINE else None,
-                     "avg_kernel_us": res["attn_avg_us"],
-                     "algorithmic_bytes_per_launch": res["attn_bytes_per_launch"]},
+        "roofline": {"bound": "hbm",
+                     "kernel": res["kernel"] + (" (decode_step_qkv: append + attention)"
+                                                if fused else " (decode_attn_qkv)"),
+                     "achieved": res["kernel_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": res["kernel_gbs"] / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if w.name == HEADLINE and fused else None,
+                     "avg_kernel_us": res["kernel_avg_us"],
+                     "algorithmic_bytes_per_launch": res["kernel_bytes_per_launch"]},
         "prefill_quantize": {"ms": res.get("prefill_quantize_ms"),
                              "gbs": res.get("prefill_quantize_gbs")},
         "host_wall_s": res["host_wall_s"],
@@ -462,7 +491,8 @@ def main():
             steps = 64 * 3 if ow.decode_steps else (20 if ow.layers > 1 else args.steps)
             warm = 10 if ow.layers > 1 else args.warmup
             r, _ = measure(kvq, torch, ow, steps, warm, args.blocks_per_split,
-                           device_inputs=ow.decode_steps > 0 or ow.layers > 1)
+                           device_inputs=ow.decode_steps > 0 or ow.layers > 1,
+                           separate=args.separate)
             others.append(r)
             torch.cuda.empty_cache()
         result["workloads"] = others
