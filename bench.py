@@ -45,8 +45,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_int4_b8h32d128_ctx8k_traffic.json")
 CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
-EVENT_STRIDE = 8               # HIP events around every 8th step-kernel launch: a pair of
-                               # events around every launch adds ~5 us to each step
+EVENT_STRIDE = 8               # HIP events around every 8th attention launch when a step
+                               # has several launches: a pair of events around a launch
+                               # adds ~5 us to its step
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 OTHERS = ("llama7b_b8_h32_d128_ctx8k_uint8", "long_b16_h32_d128_ctx32k_append64_int4",
           "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4")
@@ -253,6 +254,11 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
 
     timer = Timer(torch)
     kernel_bytes, step_bytes = [], []
+    # One launch per step: the kernel's average duration is the timed segments' total
+    # over the steps (HIP events bracket the segments); several launches per step: HIP
+    # events around every EVENT_STRIDE-th launch of the attention kernel.
+    bps_eff, n_split = kvq.decode_attn_plan(caches[0], w.context + growth, bps)
+    one_launch = not separate and n_split == 1
 
     def step(j, timed):
         """Step j of a segment: copy j % copies gains its (j // copies)-th token."""
@@ -261,7 +267,7 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
         L = w.context + used + 1
         if separate:
             kvq.kv_append(c, k_new[used], v_new[used], L)
-        sample = timed and j % EVENT_STRIDE == 0
+        sample = timed and not one_launch and j % EVENT_STRIDE == 0
         if sample:
             e0 = timer.event()
         if separate:
@@ -274,6 +280,8 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
                                 (0 if separate else append_bytes(w)))
         if timed:
             step_bytes.append(attention_bytes(w, [L] * B) + append_bytes(w))
+            if one_launch:
+                kernel_bytes.append(step_bytes[-1])
 
     def run(n_steps, timed):
         done = 0
@@ -295,9 +303,7 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
     run(steps, True)
     wall_s = time.perf_counter() - wall0
     total_ms = timer.total_ms()
-    kernel_ms = timer.kernel_ms()
-    bps_eff, n_split = kvq.decode_attn_plan(caches[0], w.context + growth, bps)
-    one_launch = not separate and n_split == 1
+    kernel_ms = [total_ms / steps] if one_launch else timer.kernel_ms()
     res = {
         "workload": w.name,
         "step": ("kv_append + decode_attn_qkv" if separate else
@@ -311,6 +317,8 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
         "kernel_avg_us": float(np.mean(kernel_ms)) * 1e3,
         "kernel_gbs": float(np.mean(kernel_bytes)) / (float(np.mean(kernel_ms)) / 1e3) / 1e9,
         "kernel_bytes_per_launch": float(np.mean(kernel_bytes)),
+        "kernel_timing": ("timed segments / steps (one launch per step)" if one_launch else
+                          f"HIP event pairs around every {EVENT_STRIDE}th attention launch"),
         "context": [w.context + 1, w.context + growth],
         "cache_copies_rotated": copies, "blocks_per_split": bps_eff, "splits_per_row": n_split,
         "prefill_quantize_ms": float(np.median(prefill_ms)),
@@ -344,13 +352,10 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
     timer = Timer(torch)
 
     def step(timed):
+        # one launch per layer and nothing else: the kernel's average duration is the
+        # timed segment over the launches
         for layer in range(w.layers):
-            sample = timed and layer % EVENT_STRIDE == 0
-            if sample:
-                e0 = timer.event()
             kvq.decode_attn_qkv(caches[layer], queries[layer], sm, out, ws, L, bps)
-            if sample:
-                timer.kernel.append((e0, timer.event()))
 
     wall0 = time.perf_counter()
     for _ in range(warmup):
@@ -364,7 +369,7 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
     wall_s = time.perf_counter() - wall0
     total_ms = timer.total_ms()
     per_launch = attention_bytes(w, lens)
-    kernel_ms = timer.kernel_ms()
+    kernel_ms = [total_ms / (steps * w.layers)]
     bps_eff, n_split = kvq.decode_attn_plan(caches[0], L, bps)
     res = {
         "workload": w.name,
@@ -377,6 +382,7 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
         "kernel_avg_us": float(np.mean(kernel_ms)) * 1e3,
         "kernel_gbs": per_launch / (float(np.mean(kernel_ms)) / 1e3) / 1e9,
         "kernel_bytes_per_launch": float(per_launch),
+        "kernel_timing": "timed segment / launches (one launch per layer)",
         "context": [int(lens.min()), L], "mean_context": float(lens.mean()),
         "blocks_per_split": bps_eff, "splits_per_row": n_split,
         "prefill_quantize_ms_per_layer": float(np.median(prefill_ms)),
@@ -469,7 +475,7 @@ def main():
                      "achieved": res["kernel_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": res["kernel_gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic() if w.name == HEADLINE and fused else None,
-                     "avg_kernel_us": res["kernel_avg_us"],
+                     "avg_kernel_us": res["kernel_avg_us"], "timing": res["kernel_timing"],
                      "algorithmic_bytes_per_launch": res["kernel_bytes_per_launch"]},
         "prefill_quantize": {"ms": res.get("prefill_quantize_ms"),
                              "gbs": res.get("prefill_quantize_gbs")},

@@ -19,26 +19,35 @@ namespace kvq {
 constexpr int kThreads = 256;  // threads of one block's quantizer
 constexpr int kWaves = kThreads / kWave;
 
-// Maxima of N values over a group of kThreads threads (the workgroup, or one half of a
-// two-group workgroup, each half with its own lds); every thread of the group receives
-// the results. Contains one workgroup barrier.
-template <int N>
-__device__ __forceinline__ void block_max(float (&v)[N], float* lds /* [N * kWaves] */) {
+// Maxima of N values over a group of NT threads (one wave, or a workgroup of NT
+// threads); every thread of the group receives the results. For NT > kWave it contains
+// one workgroup barrier (lds: N * NT / kWave floats); a single wave needs no LDS.
+template <int N, int NT>
+__device__ __forceinline__ void group_max(float (&v)[N], float* lds) {
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = wave_max(v[i]);
-  const int w = (threadIdx.x % kThreads) / kWave;
-  if ((threadIdx.x % kWave) == 0) {
+  if constexpr (NT > kWave) {
+    constexpr int W = NT / kWave;
+    const int w = (threadIdx.x % NT) / kWave;
+    if ((threadIdx.x % kWave) == 0) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) lds[i * kWaves + w] = v[i];
+      for (int i = 0; i < N; ++i) lds[i * W + w] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      float r = lds[i * W];
+#pragma unroll
+      for (int k = 1; k < W; ++k) r = fmaxf(r, lds[i * W + k]);
+      v[i] = r;
+    }
   }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    float r = lds[i * kWaves];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) r = fmaxf(r, lds[i * kWaves + k]);
-    v[i] = r;
-  }
+}
+
+// The same over the kThreads threads of a block quantizer workgroup.
+template <int N>
+__device__ __forceinline__ void block_max(float (&v)[N], float* lds /* [N * kWaves] */) {
+  group_max<N, kThreads>(v, lds);
 }
 
 template <int SCHEME, int D>
@@ -63,12 +72,13 @@ __device__ __forceinline__ void store_codes(uint8_t* token_row, int chunk, const
 
 // int4: writes one block region (K or V) in fragment order from the block's fp16 values
 // staged in LDS (xs[t * D + d], natural order); tokens t >= ntok give zero nibbles.
-template <int D>
+// Called by NT threads (tid = 0 .. NT-1).
+template <int D, int NT = kThreads>
 __device__ __forceinline__ void int4_write_block_from(const _Float16* xs, int ntok, float s,
                                                       bool is_v, uint8_t* out, int tid) {
   constexpr int KS = D / 32;      // 32-channel K steps
   constexpr int kChunks = 2 * D;  // 16-byte chunks per region (32 * D bytes)
-  for (int c = tid; c < kChunks; c += kThreads) {
+  for (int c = tid; c < kChunks; c += NT) {
     const int lane = c % kWave, i = c / kWave;
     uint32_t w[4];
 #pragma unroll
@@ -98,59 +108,63 @@ __device__ __forceinline__ void int4_write_block_from(const _Float16* xs, int nt
 }
 
 // ---- append one token to one row (K and V) -----------------------------------------
-// Called by all kThreads threads of a workgroup (contains one workgroup barrier).
-// len = the row's length before the token (< capacity); fresh[kv] = this thread's 16
-// bytes of the new K (kv = 0) or V (kv = 1) token, channels chunk*8 .. +7. The new
-// token's fp16 values go to the row's tail staging. A block whose statistic (absmax, or
-// min and max) the token leaves unchanged keeps its scale and gets only the new
-// token's codes; otherwise (and for a block the token opens) the whole block is
-// re-quantized from the staged values and its scale (and zero point) rewritten. Both
-// tensors are reduced in one pass so that their loads and barriers overlap.
-// xs: 2 * kBlock * D fp16 of LDS, 16-byte aligned (int4 only; unused for uint8);
-// red: kAppendStats<SCHEME> * kWaves floats of LDS.
+// The append of one token to row `row` (length len before it, len < capacity) runs in
+// three phases, each called by the NT threads (tid = 0 .. NT-1: a whole workgroup of NT
+// threads, or one wave) that take part:
+//   append_stage:  stages tokens 0..slot of the open block of both tensors in LDS (the
+//                  new token from `fresh`, zeros after it) and reduces the block
+//                  statistics before and after the token joins;
+//   code writes:   a block whose statistic (absmax, or min and max) the token leaves
+//                  unchanged keeps its scale and gets only the new token's codes;
+//                  otherwise (and for a block the token opens) the whole block is
+//                  re-quantized from the staged values (append_write_codes, or the
+//                  register-resident variant of the fused decode step);
+//   append_finish: the new token's fp16 staging and the changed scales (zero points).
+// fresh[kv] = this thread's 16 bytes of the new K (kv = 0) or V (kv = 1) token,
+// channels (tid % (D/8)) * 8 .. +7. xs: 2 * kBlock * D fp16 of LDS, 16-byte aligned;
+// red: kAppendStats<SCHEME> * NT / kWave floats of LDS (unused for one wave).
 template <int SCHEME>
 constexpr int kAppendStats = SCHEME == KVQ_INT4_SYM ? 4 : 8;  // old and new, K and V
 
-template <int SCHEME, int D>
-__device__ __forceinline__ void append_row(const AppendArgs& a, int64_t row, int len,
-                                           const uint4 (&fresh)[2], _Float16* xs, float* red) {
-  using G = QGeo<SCHEME, D>;
-  constexpr int NS = kAppendStats<SCHEME> / 2;  // statistics per tensor
-  const int tid = threadIdx.x % kThreads;
-  const int tr = tid / G::kThreadsPerToken;
-  const int chunk = tid % G::kThreadsPerToken;
-  const int slot = len % kBlock;
-  const int64_t blk = row * a.max_blocks + len / kBlock;
+struct AppendPlan {  // one tensor's outcome: the block's scale, zero point, re-quantized?
+  float s, zp;
+  bool full;
+};
 
-  // The staged tokens 0..slot-1 through buffer resources that end at token `slot`:
+struct BlockScales {
+  float ks, kz, vs, vz;
+};
+
+template <int SCHEME, int D, int NT>
+__device__ __forceinline__ void append_stage(const AppendArgs& a, int64_t row, int len, int tid,
+                                             const uint4 (&fresh)[2], _Float16* xs, float* red,
+                                             AppendPlan (&plan)[2]) {
+  constexpr int TPT = D / 8;             // threads per token row (16 bytes each)
+  constexpr int TPP = NT / TPT;          // tokens per pass
+  constexpr int PASSES = kBlock / TPP;
+  constexpr int NS = kAppendStats<SCHEME> / 2;  // statistics per tensor
+  const int tr = tid / TPT;
+  const int chunk = tid % TPT;
+  const int slot = len % kBlock;
+
+  // The staged tokens are read through buffer resources that end at token `slot`:
   // every lane loads unconditionally and the loads past the end return zeros without
-  // touching memory (no divergent branches around the loads).
-  uint4 raw[2][G::kPasses];
+  // touching memory.
+  float st[2 * NS];
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (kv ? a.v_tail : a.k_tail) + row * kBlock * D, 0, slot * D * 2, kBufferRsrcWord3);
-#pragma unroll
-    for (int p = 0; p < G::kPasses; ++p) {
-      const int t = p * G::kTokensPerPass + tr;
-      const uint4 staged = load_b128<0>(rs, (t * D + chunk * 8) * 2, 0);
-      raw[kv][p] = t == slot ? fresh[kv] : staged;
-    }
-  }
-
-  // statistics of each block before (old) and after (new) the token joins it
-  float st[2 * NS];
-#pragma unroll
-  for (int kv = 0; kv < 2; ++kv) {
     float amax_o = 0.0f, mn_o = __builtin_inff(), mx_o = -__builtin_inff();
     float amax_n = 0.0f, mn_n = __builtin_inff(), mx_n = -__builtin_inff();
 #pragma unroll
-    for (int p = 0; p < G::kPasses; ++p) {
-      const int t = p * G::kTokensPerPass + tr;
+    for (int p = 0; p < PASSES; ++p) {
+      const int t = p * TPP + tr;
+      const uint4 staged = load_b128<0>(rs, (t * D + chunk * 8) * 2, 0);
+      const uint4 raw = t == slot ? fresh[kv] : staged;
+      *reinterpret_cast<uint4*>(xs + kv * kBlock * D + t * D + chunk * 8) = raw;
       float x[8];
-      unpack8(raw[kv][p], x);
-      if constexpr (SCHEME == KVQ_INT4_SYM)
-        *reinterpret_cast<uint4*>(xs + kv * kBlock * D + t * D + chunk * 8) = raw[kv][p];
+      unpack8(raw, x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (t < slot) {
@@ -175,31 +189,51 @@ __device__ __forceinline__ void append_row(const AppendArgs& a, int64_t row, int
       st[kv * NS + 3] = mx_n;
     }
   }
-  block_max<2 * NS>(st, red);  // also makes the xs stores visible to the workgroup
+  // Makes the LDS stores visible to the group: the workgroup barrier inside group_max,
+  // or for one wave the in-order execution of its LDS requests (the wave barrier keeps
+  // the compiler from moving reads of other lanes' values above the stores).
+  if constexpr (NT == kWave) __builtin_amdgcn_wave_barrier();
+  group_max<2 * NS, NT>(st, red);
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const float* sv = st + kv * NS;
+    plan[kv].zp = 0.0f;
+    if constexpr (SCHEME == KVQ_INT4_SYM) {
+      plan[kv].full = slot == 0 || sv[0] != sv[1];
+      plan[kv].s = int4_scale(sv[1]);
+    } else {
+      plan[kv].full = slot == 0 || sv[0] != sv[2] || sv[1] != sv[3];
+      uint8_scale_zero(-sv[2], sv[3], plan[kv].s, plan[kv].zp);
+    }
+  }
+}
 
+// Code writes through memory (see above): the whole block, or the new token's codes.
+template <int SCHEME, int D, int NT>
+__device__ __forceinline__ void append_write_codes(const AppendArgs& a, int64_t row, int len,
+                                                   int tid, const _Float16* xs,
+                                                   const AppendPlan (&plan)[2]) {
+  constexpr int TPT = D / 8;
+  constexpr int TPP = NT / TPT;
+  constexpr int PASSES = kBlock / TPP;
+  constexpr int RB = SCHEME == KVQ_INT4_SYM ? D / 2 : D;  // code bytes per token
+  const int tr = tid / TPT;
+  const int chunk = tid % TPT;
+  const int slot = len % kBlock;
+  const int64_t blk = row * a.max_blocks + len / kBlock;
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     const bool is_v = kv != 0;
-    const float* sv = st + kv * NS;
-    float s, zp = 0.0f;
-    bool full;
+    const float s = plan[kv].s;
+    uint8_t* codes = (is_v ? a.v_codes : a.k_codes) + blk * kBlock * RB;
+    const _Float16* xt = xs + kv * kBlock * D;  // tokens 0..slot, zeros after
     if constexpr (SCHEME == KVQ_INT4_SYM) {
-      full = slot == 0 || sv[0] != sv[1];
-      s = int4_scale(sv[1]);
-    } else {
-      full = slot == 0 || sv[0] != sv[2] || sv[1] != sv[3];
-      uint8_scale_zero(-sv[2], sv[3], s, zp);
-    }
-    uint8_t* codes = (is_v ? a.v_codes : a.k_codes) + blk * kBlock * G::kRowBytes;
-    uint16_t* tail = (is_v ? a.v_tail : a.k_tail) + row * kBlock * D + chunk * 8;
-    if constexpr (SCHEME == KVQ_INT4_SYM) {
-      const _Float16* xt = xs + kv * kBlock * D;  // tokens 0..slot, zeros after
-      if (full) {
-        int4_write_block_from<D>(xt, slot + 1, s, is_v, codes, tid);
+      if (plan[kv].full) {
+        int4_write_block_from<D, NT>(xt, slot + 1, s, is_v, codes, tid);
       } else if (!is_v) {
         // K: the new token's D/8 dwords (8 channels each)
         constexpr int KS = D / 32;
-        for (int idx = tid; idx < D / 8; idx += kThreads) {
+        for (int idx = tid; idx < D / 8; idx += NT) {
           const int ks = idx / 4, g = idx % 4;
           uint32_t word = 0;
 #pragma unroll
@@ -213,7 +247,7 @@ __device__ __forceinline__ void append_row(const AppendArgs& a, int64_t row, int
         // scale unchanged, rebuilding the dword from the staged values reproduces the
         // stored nibbles (and zeros past the token), so the cache is never read back
         const int ks = slot / 32, g = (slot % 32) / 8, t0 = 32 * ks + 8 * g;
-        for (int d = tid; d < D; d += kThreads) {
+        for (int d = tid; d < D; d += NT) {
           uint32_t word = 0;
 #pragma unroll
           for (int q = 0; q < 8; ++q)
@@ -223,28 +257,142 @@ __device__ __forceinline__ void append_row(const AppendArgs& a, int64_t row, int
           *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(16 * g + d % 16, f)) = word;
         }
       }
-#pragma unroll
-      for (int p = 0; p < G::kPasses; ++p) {
-        const int t = p * G::kTokensPerPass + tr;
-        if (t == slot) *reinterpret_cast<uint4*>(tail + t * D) = raw[kv][p];
-      }
     } else {
-      const int zpi = static_cast<int>(zp);
+      // natural order: each thread codes its own staged 8 channels of each token
+      const int zpi = static_cast<int>(plan[kv].zp);
 #pragma unroll
-      for (int p = 0; p < G::kPasses; ++p) {
-        const int t = p * G::kTokensPerPass + tr;
-        if (full || t == slot) {
+      for (int p = 0; p < PASSES; ++p) {
+        const int t = p * TPP + tr;
+        if (plan[kv].full || t == slot) {
           float x[8];
-          unpack8(raw[kv][p], x);
-          store_codes<SCHEME, D>(codes + t * G::kRowBytes, chunk, x, s, zpi, t <= slot);
+          unpack8(*reinterpret_cast<const uint4*>(xt + t * D + chunk * 8), x);
+          store_codes<SCHEME, D>(codes + t * RB, chunk, x, s, zpi, t <= slot);
         }
-        if (t == slot) *reinterpret_cast<uint4*>(tail + t * D) = raw[kv][p];
       }
     }
-    if (tid == 0 && full) {
-      (is_v ? a.v_scale : a.k_scale)[blk] = s;
-      float* zero = is_v ? a.v_zero : a.k_zero;
-      if (zero) zero[blk] = zp;
+  }
+}
+
+// The new token's fp16 staging and the scales (zero points) of re-quantized blocks.
+template <int D, int NT>
+__device__ __forceinline__ BlockScales append_finish(const AppendArgs& a, int64_t row, int len,
+                                                     int tid, const uint4 (&fresh)[2],
+                                                     const AppendPlan (&plan)[2]) {
+  constexpr int TPT = D / 8;
+  constexpr int TPP = NT / TPT;
+  const int slot = len % kBlock;
+  const int64_t blk = row * a.max_blocks + len / kBlock;
+  if (tid / TPT == slot % TPP) {
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      uint16_t* tail = (kv ? a.v_tail : a.k_tail) + row * kBlock * D;
+      *reinterpret_cast<uint4*>(tail + slot * D + (tid % TPT) * 8) = fresh[kv];
+    }
+  }
+  if (tid == 0) {
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      if (!plan[kv].full) continue;
+      (kv ? a.v_scale : a.k_scale)[blk] = plan[kv].s;
+      float* zero = kv ? a.v_zero : a.k_zero;
+      if (zero) zero[blk] = plan[kv].zp;
+    }
+  }
+  return {plan[0].s, plan[0].zp, plan[1].s, plan[1].zp};
+}
+
+template <int SCHEME, int D, int NT>
+__device__ __forceinline__ BlockScales append_row(const AppendArgs& a, int64_t row, int len,
+                                                  int tid, const uint4 (&fresh)[2],
+                                                  _Float16* xs, float* red) {
+  AppendPlan plan[2];
+  append_stage<SCHEME, D, NT>(a, row, len, tid, fresh, xs, red, plan);
+  append_write_codes<SCHEME, D, NT>(a, row, len, tid, xs, plan);
+  return append_finish<D, NT>(a, row, len, tid, fresh, plan);
+}
+
+// ---- int4 tail block kept in registers (fused decode step) ---------------------------
+// One wave's view of an int4 block region: lane l holds chunk i (i < D/32) = bytes
+// ((i * 64) + l) * 16 .. +15, i.e. its matrix-core fragments. Dword f of the lane is
+// component f % 4 of chunk f / 4 (selected without indexing the array at run time).
+template <int N>
+__device__ __forceinline__ uint32_t get_dword(const uint4 (&r)[N], int f) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    v = f == 4 * i + 0 ? r[i].x : v;
+    v = f == 4 * i + 1 ? r[i].y : v;
+    v = f == 4 * i + 2 ? r[i].z : v;
+    v = f == 4 * i + 3 ? r[i].w : v;
+  }
+  return v;
+}
+
+// Code writes of one int4 tensor by one wave that also leaves the block's new codes in
+// registers, so the wave can attend the block without reading it back: r receives
+// chunk i (i < D/32) of the lane, i.e. bytes ((i * 64) + lane) * 16 .. +15 of the
+// region, computed from the staged values (tokens 0..slot, zeros after). The cache gets
+// the same bytes as from append_write_codes, except that a V append writes only the
+// byte holding the token's nibble: stores into the code buffer cost the concurrent
+// code stream far more than their size, so they are kept to what changes (the whole
+// block, or the token's D/2 bytes of K and D bytes of V).
+template <int D>
+__device__ __forceinline__ void int4_tail_fragments(const _Float16* xt, int slot,
+                                                    const AppendPlan& pl, bool is_v, int lane,
+                                                    uint4 (&r)[D / 32], uint8_t* codes) {
+  constexpr int LOADS = D / 32;  // chunks per lane
+  constexpr int KS = D / 32;     // K: dwords per token per lane group
+  const float s = pl.s;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    uint32_t w[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int f = 4 * i + c;
+      uint32_t word = 0;
+      if (!is_v) {
+        const int t = 16 * (f / KS) + lane % 16;
+        const int d0 = 32 * (f % KS) + 8 * (lane / 16);
+        if (t <= slot) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            word |= int4_code(static_cast<float>(xt[t * D + d0 + q]), s) << (4 * q);
+        }
+      } else {
+        const int d = 16 * (f / 2) + lane % 16;
+        const int t0 = 32 * (f % 2) + 8 * (lane / 16);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (t0 + q <= slot)
+            word |= int4_code(static_cast<float>(xt[(t0 + q) * D + d]), s) << (4 * q);
+      }
+      w[c] = word;
+    }
+    r[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    if (pl.full) store_b128(codes + (i * kWave + lane) * 16, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  if (pl.full) return;
+  if (!is_v) {
+    // lane 16g + slot % 16 holds the token's 8-channel group g of each 32-channel step
+    // ks: dwords (slot / 16) * KS + ks
+    if (lane % 16 == slot % 16) {
+      const int f0 = (slot / 16) * KS;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(lane, f0 + ks)) =
+            get_dword(r, f0 + ks);
+    }
+  } else {
+    // lanes 16g .. 16g + 15 (g = (slot % 32) / 8) hold the token in nibble slot % 8 of
+    // dword 2 * nt + slot / 32 for channel 16 * nt + lane % 16
+    if (lane / 16 == (slot % 32) / 8) {
+      const int ks = slot / 32, q = slot % 8;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) {
+        const int f = 2 * nt + ks;
+        codes[int4_dword_offset(lane, f) + q / 2] =
+            static_cast<uint8_t>(get_dword(r, f) >> (8 * (q / 2)));
+      }
     }
   }
 }
@@ -264,29 +412,23 @@ __device__ __forceinline__ int append_ticket(int32_t* seq_lens, int b, int arriv
   return len0;
 }
 
-// One decode step's append for row (b, h) = `row`: takes the sequence's arrival ticket
-// (`arrivals` = heads workgroups per sequence, one per row) and appends the row's new
-// K and V token. Called by all kThreads threads of the workgroup; returns the row's
-// length after the append (unchanged when the row is at capacity, which the append
-// leaves untouched). On return the new codes, scales and staging are visible to every
-// thread of the workgroup (a workgroup barrier follows the stores).
+// The append of row (b, h) = `row` by the kThreads threads of a workgroup: takes the
+// sequence's arrival ticket (`heads` workgroups per sequence, one per row) and appends
+// the row's new K and V token (nothing for a row at capacity).
 template <int SCHEME, int D>
-__device__ __forceinline__ int append_token(const AppendArgs& a, int b, int64_t row) {
-  using G = QGeo<SCHEME, D>;
-  __shared__ __align__(16) _Float16 xs[SCHEME == KVQ_INT4_SYM ? 2 * kBlock * D : 8];
+__device__ __forceinline__ void append_token(const AppendArgs& a, int b, int64_t row) {
+  __shared__ __align__(16) _Float16 xs[2 * kBlock * D];
   __shared__ float red[kAppendStats<SCHEME> * kWaves];
   __shared__ int len_shared;
   const int cap = a.max_blocks * kBlock;
-  const int off = (threadIdx.x % G::kThreadsPerToken) * 8;
+  const int off = (threadIdx.x % (D / 8)) * 8;
   const uint4 fresh[2] = {*reinterpret_cast<const uint4*>(a.k_new + row * D + off),
                           *reinterpret_cast<const uint4*>(a.v_new + row * D + off)};
   if (threadIdx.x == 0) len_shared = append_ticket(a.seq_lens, b, a.heads, cap);
   __syncthreads();
   const int len = len_shared;
-  if (len >= cap) return len;  // uniform over the workgroup
-  append_row<SCHEME, D>(a, row, len, fresh, xs, red);
-  __syncthreads();
-  return len + 1;
+  if (len >= cap) return;  // uniform over the workgroup
+  append_row<SCHEME, D, kThreads>(a, row, len, threadIdx.x, fresh, xs, red);
 }
 
 }  // namespace kvq

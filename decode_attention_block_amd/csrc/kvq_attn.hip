@@ -277,6 +277,7 @@ __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, i
                                                    int64_t row, LoadParams load_params, Load load,
                                                    OnK on_k, OnV on_v) {
   const int n = blk_end - blk_begin;
+  if (n <= 0) return;  // uniform (a decode step's streaming waves may have no block)
   const int rot = static_cast<int>((static_cast<uint32_t>(row) * 2654435761u) >> 8) % n;
   const int n_wave = wave < n ? (n - wave + kSplitWaves - 1) / kSplitWaves : 0;
   auto blk_of = [&](int i) {
@@ -324,31 +325,106 @@ struct ScaleZeroParams {  // block scales and zero points of K and V
   }
 };
 
+// ---- fused decode step ----------------------------------------------------------------
+// In a decode step (kAppend) the workgroup of row (b, h) has one wave more than the
+// attention: waves 0 .. kSplitWaves-1 attend the blocks the append leaves untouched
+// while the last wave appends the row's new token (append_stage .. append_finish) and
+// then attends the block that holds it. The row's length is read once, before anything else; the append
+// wave then takes the sequence's arrival ticket (1 << 24 added to seq_lens[b], as in
+// kv_append) and the last of the sequence's `heads` workgroups stores the new length.
+// Since every workgroup of the sequence reads the length before it takes its ticket,
+// none can see the new length, and the ticket's latency hides behind the append instead
+// of delaying the attention.
+constexpr int kStepWaves = kSplitWaves + 1;
+
+struct StepLens {
+  int len0;          // the row's length before the append
+  int len;           // attended length: after the append, within max_len and capacity
+  int tail_blk;      // the block the append wave attends (holding the new token), or -1
+  int len_streamed;  // tokens in the blocks the other waves attend
+};
+
+__device__ __forceinline__ StepLens step_lengths(const AttnArgs& a, int b, int cap) {
+  __shared__ int len_shared;
+  if (threadIdx.x == 0)
+    len_shared = static_cast<int>(
+        __hip_atomic_load(reinterpret_cast<uint32_t*>(a.ap.seq_lens) + b, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_SYSTEM) & 0xFFFFFFu);  // low 24 bits: the length
+  __syncthreads();
+  StepLens r;
+  r.len0 = len_shared;
+  r.len = min(r.len0 < cap ? r.len0 + 1 : r.len0, min(a.max_len, cap));
+  const int j = r.len0 / kBlock;
+  r.tail_blk = r.len0 < cap && r.len > j * kBlock ? j : -1;
+  r.len_streamed = r.tail_blk >= 0 ? j * kBlock : r.len;
+  return r;
+}
+
+// The append wave's part of the step before it attends: ticket, append, and (by the
+// last arrival of the sequence) the new length. write_codes(plan) does the code writes
+// (after append_stage, before append_finish). Returns the scales (and zero points) of
+// the block holding the new token.
+template <int SCHEME, int D, class WriteCodes>
+__device__ __forceinline__ BlockScales step_append(const AttnArgs& a, const StepLens& sl, int b,
+                                                   int64_t row, int cap, int lane, _Float16* xs,
+                                                   WriteCodes write_codes) {
+  uint32_t* lens = reinterpret_cast<uint32_t*>(a.ap.seq_lens);
+  uint32_t ticket = 0;
+  if (lane == 0)
+    ticket = __hip_atomic_fetch_add(lens + b, 1u << 24, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM);
+  BlockScales sc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (sl.len0 < cap) {
+    const int off = (lane % (D / 8)) * 8;
+    const uint4 fresh[2] = {*reinterpret_cast<const uint4*>(a.ap.k_new + row * D + off),
+                            *reinterpret_cast<const uint4*>(a.ap.v_new + row * D + off)};
+    AppendPlan plan[2];
+    append_stage<SCHEME, D, kWave>(a.ap, row, sl.len0, lane, fresh, xs, nullptr, plan);
+    write_codes(plan);
+    sc = append_finish<D, kWave>(a.ap, row, sl.len0, lane, fresh, plan);
+  }
+  if (lane == 0 && (ticket >> 24) == static_cast<uint32_t>(a.heads - 1))
+    __hip_atomic_exchange(lens + b, static_cast<uint32_t>(sl.len0 < cap ? sl.len0 + 1 : sl.len0),
+                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return sc;
+}
+
 // ---- split kernel: grid (n_split, heads, batch), kSplitWaves waves ------------------
 template <int SCHEME, int D, bool kAppend>
-__global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void attn_split_kernel(
+    AttnArgs a) {
   using G = AGeo<SCHEME, D>;
   constexpr int TPL = G::kTPL, DPL = G::kDPL, LPT = G::kLPT, GROUPS = G::kGroups;
-  __shared__ float red_o[kSplitWaves][kWave][DPL + 1];
-  __shared__ float red_l[kSplitWaves][kWave];
-  __shared__ float red_m[kSplitWaves];
+  constexpr int kStates = kAppend ? kStepWaves : kSplitWaves;  // waves' partial states
+  __shared__ float red_o[kStates][kWave][DPL + 1];
+  __shared__ float red_l[kStates][kWave];
+  __shared__ float red_m[kStates];
+  __shared__ __align__(16) _Float16 xs[kAppend ? 2 * kBlock * D : 8];  // append staging
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int cap = a.max_blocks * kBlock;
-  int len = kAppend ? append_token<SCHEME, D>(a.ap, b, static_cast<int64_t>(b) * a.heads + h)
-                    : a.seq_lens[b];
-  len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+  StepLens sl = {0, 0, -1, 0};
+  int len;
+  if constexpr (kAppend) {
+    sl = step_lengths(a, b, cap);
+    len = sl.len;
+  } else {
+    len = a.seq_lens[b];
+    len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+    sl.len_streamed = len;
+  }
   const int nb = (len + kBlock - 1) / kBlock;
   const int blk_begin = split * a.bps;
-  if (blk_begin >= nb) {  // uniform over the workgroup
+  if (!kAppend && blk_begin >= nb) {  // uniform over the workgroup
     // an empty row has no split to merge: in fused mode split 0 writes its zeros
     if (a.fused && nb == 0 && split == 0 && threadIdx.x < D)
       a.out[(static_cast<int64_t>(b) * a.heads + h) * D + threadIdx.x] = 0;
     return;
   }
-  const int blk_end = min(blk_begin + a.bps, nb);
+  // the blocks this split streams (in a decode step, all but the new token's block)
+  const int blk_end = min(blk_begin + a.bps, (sl.len_streamed + kBlock - 1) / kBlock);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -441,15 +517,38 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   };
 
   float p[TPL];
-  stream_wave_blocks<TPL>(
-      blk_begin, blk_end, wave, lane, row,
-      [&](int blk) { return ScaleZeroParams{ks[blk], kz[blk], vs[blk], vz[blk]}; }, load_codes,
-      [&](int blk, const ScaleZeroParams& pb, const uint4 (&kr)[TPL]) {
-        block_weights(blk, pb.ks, pb.kz, kr, p);
-      },
-      [&](int, const ScaleZeroParams& pb, const uint4 (&vr)[TPL]) {
-        block_accumulate(pb.vs, pb.vz, vr, p);
-      });
+  bool streaming = true;
+  if constexpr (kAppend) {
+    if (wave == kSplitWaves) {  // the append wave
+      streaming = false;
+      const BlockScales sc = step_append<SCHEME, D>(
+          a, sl, b, row, cap, lane, xs, [&](const AppendPlan (&plan)[2]) {
+            append_write_codes<SCHEME, D, kWave>(a.ap, row, sl.len0, lane, xs, plan);
+          });
+      if (sl.tail_blk >= 0) {
+        // the new codes were written a token row (a whole line) at a time; wait until
+        // they have completed (the workgroup's L1 keeps its waves coherent, so nothing is
+        // invalidated), and keep the loads below that point
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        uint4 kr[TPL], vr[TPL];
+        load_codes(false, sl.tail_blk, kr);
+        load_codes(true, sl.tail_blk, vr);
+        block_weights(sl.tail_blk, sc.ks, sc.kz, kr, p);
+        block_accumulate(sc.vs, sc.vz, vr, p);
+      }
+    }
+  }
+  if (streaming)
+    stream_wave_blocks<TPL>(
+        blk_begin, blk_end, wave, lane, row,
+        [&](int blk) { return ScaleZeroParams{ks[blk], kz[blk], vs[blk], vz[blk]}; },
+        load_codes,
+        [&](int blk, const ScaleZeroParams& pb, const uint4 (&kr)[TPL]) {
+          block_weights(blk, pb.ks, pb.kz, kr, p);
+        },
+        [&](int, const ScaleZeroParams& pb, const uint4 (&vr)[TPL]) {
+          block_accumulate(pb.vs, pb.vz, vr, p);
+        });
 
   // Per-lane result in true units: o_true[k] = o[k] * unit(k).
 #pragma unroll
@@ -464,16 +563,16 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
 
   float M = red_m[0];
 #pragma unroll
-  for (int w = 1; w < kSplitWaves; ++w) M = fmaxf(M, red_m[w]);
-  float alpha[kSplitWaves];
+  for (int w = 1; w < kStates; ++w) M = fmaxf(M, red_m[w]);
+  float alpha[kStates];
 #pragma unroll
-  for (int w = 0; w < kSplitWaves; ++w) alpha[w] = __builtin_amdgcn_exp2f(red_m[w] - M);
+  for (int w = 0; w < kStates; ++w) alpha[w] = __builtin_amdgcn_exp2f(red_m[w] - M);
 
   float od = 0.0f;
   if (threadIdx.x < D) {
     const int d = threadIdx.x, c = d / DPL, k = d % DPL;
 #pragma unroll
-    for (int w = 0; w < kSplitWaves; ++w) {
+    for (int w = 0; w < kStates; ++w) {
       float sw = 0.0f;
 #pragma unroll
       for (int g = 0; g < GROUPS; ++g) sw += red_o[w][g * LPT + c][k];
@@ -482,7 +581,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_kernel(AttnArg
   }
   float L = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kSplitWaves; ++w) {
+  for (int w = 0; w < kStates; ++w) {
     float sw = 0.0f;
     for (int g = 0; g < GROUPS; ++g) sw += red_l[w][g * LPT];
     L = __builtin_fmaf(alpha[w], sw, L);
@@ -558,32 +657,43 @@ __device__ __forceinline__ float row0_sum(float v) {
 }
 
 template <int D, bool kAppend>
-__global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(AttnArgs a) {
+__global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void
+attn_split_int4_kernel(AttnArgs a) {
   constexpr int KS = D / 32;               // 32-channel K steps of QK^T
   constexpr int NTV = D / 16;              // 16-channel N tiles of P.V
   constexpr int LOADS = D / 32;            // 16-byte loads per lane per region
   constexpr int kRegionBytes = 32 * D;     // one tensor's codes of one block
-  __shared__ __align__(16) _Float16 pimg[kSplitWaves][2][4][16][8];
-  __shared__ float red_o[kSplitWaves][D];
-  __shared__ float red_l[kSplitWaves];
-  __shared__ float red_m[kSplitWaves];
+  constexpr int kStates = kAppend ? kStepWaves : kSplitWaves;  // waves' partial states
+  __shared__ __align__(16) _Float16 pimg[kStates][2][4][16][8];
+  __shared__ float red_o[kStates][D];
+  __shared__ float red_l[kStates];
+  __shared__ float red_m[kStates];
+  __shared__ __align__(16) _Float16 xs[kAppend ? 2 * kBlock * D : 8];  // append staging
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int cap = a.max_blocks * kBlock;
-  int len = kAppend ? append_token<KVQ_INT4_SYM, D>(a.ap, b, static_cast<int64_t>(b) * a.heads + h)
-                    : a.seq_lens[b];
-  len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+  StepLens sl = {0, 0, -1, 0};
+  int len;
+  if constexpr (kAppend) {
+    sl = step_lengths(a, b, cap);
+    len = sl.len;
+  } else {
+    len = a.seq_lens[b];
+    len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+    sl.len_streamed = len;
+  }
   const int nb = (len + kBlock - 1) / kBlock;
   const int blk_begin = split * a.bps;
-  if (blk_begin >= nb) {  // uniform over the workgroup
+  if (!kAppend && blk_begin >= nb) {  // uniform over the workgroup
     // an empty row has no split to merge: in fused mode split 0 writes its zeros
     if (a.fused && nb == 0 && split == 0 && threadIdx.x < D)
       a.out[(static_cast<int64_t>(b) * a.heads + h) * D + threadIdx.x] = 0;
     return;
   }
-  const int blk_end = min(blk_begin + a.bps, nb);
+  // the blocks this split streams (in a decode step, all but the new token's block)
+  const int blk_end = min(blk_begin + a.bps, (sl.len_streamed + kBlock - 1) / kBlock);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -713,16 +823,38 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(At
   };
 
   float p[4];
-  stream_wave_blocks<LOADS>(
-      blk_begin, blk_end, wave, lane, row,
-      [&](int blk) { return ScaleParams{ks_ptr[blk], vs_ptr[blk]}; },
-      [&](bool is_v, int blk, uint4 (&r)[LOADS]) { load_codes(is_v ? vrsrc : krsrc, blk, r); },
-      [&](int blk, const ScaleParams& pb, const uint4 (&kr)[LOADS]) {
-        block_weights(blk, pb.ks, kr, p);
-      },
-      [&](int, const ScaleParams& pb, const uint4 (&vr)[LOADS]) {
-        block_accumulate(pb.vs, vr, p);
-      });
+  bool streaming = true;
+  if constexpr (kAppend) {
+    if (wave == kSplitWaves) {  // the append wave
+      streaming = false;
+      // the new token's block is coded in registers by the code writes
+      uint4 kr[LOADS], vr[LOADS];
+      const BlockScales sc = step_append<KVQ_INT4_SYM, D>(
+          a, sl, b, row, cap, lane, xs, [&](const AppendPlan (&plan)[2]) {
+            const int64_t blk = row * a.max_blocks + sl.len0 / kBlock;
+            const int slot = sl.len0 % kBlock;
+            int4_tail_fragments<D>(xs, slot, plan[0], false, lane, kr,
+                                   a.ap.k_codes + blk * kRegionBytes);
+            int4_tail_fragments<D>(xs + kBlock * D, slot, plan[1], true, lane, vr,
+                                   a.ap.v_codes + blk * kRegionBytes);
+          });
+      if (sl.tail_blk >= 0) {
+        block_weights(sl.tail_blk, sc.ks, kr, p);
+        block_accumulate(sc.vs, vr, p);
+      }
+    }
+  }
+  if (streaming)
+    stream_wave_blocks<LOADS>(
+        blk_begin, blk_end, wave, lane, row,
+        [&](int blk) { return ScaleParams{ks_ptr[blk], vs_ptr[blk]}; },
+        [&](bool is_v, int blk, uint4 (&r)[LOADS]) { load_codes(is_v ? vrsrc : krsrc, blk, r); },
+        [&](int blk, const ScaleParams& pb, const uint4 (&kr)[LOADS]) {
+          block_weights(blk, pb.ks, kr, p);
+        },
+        [&](int, const ScaleParams& pb, const uint4 (&vr)[LOADS]) {
+          block_accumulate(pb.vs, vr, p);
+        });
 
   const float lw = row0_sum(lane < 16 ? l : 0.0f);
   if (lane < 16) {
@@ -737,18 +869,18 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_kernel(At
 
   float M = red_m[0];
 #pragma unroll
-  for (int w = 1; w < kSplitWaves; ++w) M = fmaxf(M, red_m[w]);
-  float alpha[kSplitWaves];
+  for (int w = 1; w < kStates; ++w) M = fmaxf(M, red_m[w]);
+  float alpha[kStates];
 #pragma unroll
-  for (int w = 0; w < kSplitWaves; ++w) alpha[w] = __builtin_amdgcn_exp2f(red_m[w] - M);
+  for (int w = 0; w < kStates; ++w) alpha[w] = __builtin_amdgcn_exp2f(red_m[w] - M);
   float od = 0.0f;
   if (threadIdx.x < D) {
 #pragma unroll
-    for (int w = 0; w < kSplitWaves; ++w) od = __builtin_fmaf(alpha[w], red_o[w][threadIdx.x], od);
+    for (int w = 0; w < kStates; ++w) od = __builtin_fmaf(alpha[w], red_o[w][threadIdx.x], od);
   }
   float L = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kSplitWaves; ++w) L = __builtin_fmaf(alpha[w], red_l[w], L);
+  for (int w = 0; w < kStates; ++w) L = __builtin_fmaf(alpha[w], red_l[w], L);
   finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
 }
 
@@ -770,8 +902,8 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 template <int D, bool kAppend>
 hipError_t split_int4_t(int batch, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.heads, batch);
-  hipLaunchKernelGGL((attn_split_int4_kernel<D, kAppend>), grid, dim3(kSplitWaves * kWave), 0, s,
-                     a);
+  hipLaunchKernelGGL((attn_split_int4_kernel<D, kAppend>), grid,
+                     dim3((kAppend ? kStepWaves : kSplitWaves) * kWave), 0, s, a);
   return hipGetLastError();
 }
 
@@ -781,8 +913,8 @@ hipError_t split_t(int batch, const AttnArgs& a, hipStream_t s) {
     return split_int4_t<D, kAppend>(batch, a, s);
   } else {
     dim3 grid(a.n_split, a.heads, batch);
-    hipLaunchKernelGGL((attn_split_kernel<SCHEME, D, kAppend>), grid, dim3(kSplitWaves * kWave),
-                       0, s, a);
+    hipLaunchKernelGGL((attn_split_kernel<SCHEME, D, kAppend>), grid,
+                       dim3((kAppend ? kStepWaves : kSplitWaves) * kWave), 0, s, a);
     return hipGetLastError();
   }
 }

@@ -143,6 +143,13 @@ __device__ __forceinline__ uint32_t int4_dword_offset(int lane, int f) {
 // swizzle): loads past num_records return zeros and access no memory.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// 16-byte store of a value (component by component, so that a uint4 held in a register
+// array is never copied out of memory).
+__device__ __forceinline__ void store_b128(uint8_t* p, const uint4& v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
+}
+
 // 16-byte load through a buffer resource at voffset (per lane) + soffset (uniform);
 // AUX = cache policy bits (2: non-temporal).
 template <int AUX>

@@ -191,12 +191,16 @@ int decode_attn_combine(const kvq_cache* cache, void* out, void* workspace,
                         void* stream);
 
 /* One decode step of every row: kv_append of (k_new, v_new) followed by
- * decode_attn_qkv of q over the lengths after the append, with the results (cache,
- * seq_lens and out) bitwise those of the two calls made in that order on one stream.
- * When the plan for max_len_after gives one split per row (the automatic plan does
- * whenever B*H >= 256), it is one kernel launch: each row's workgroup appends the
- * row's token, then attends over the row including it, so the append's latency is
- * not a separate launch; otherwise it queues the two kernels. Arguments and limits are
+ * decode_attn_qkv of q over the lengths after the append. The cache and seq_lens end
+ * bitwise as after those two calls made in that order on one stream, and so does out
+ * when they are what runs: when the plan for max_len_after has several splits per
+ * row, the two kernels are queued. With one split per row (the automatic plan gives
+ * it whenever B*H >= 256) the step is one kernel launch: each row's workgroup has one
+ * wave more than the attention, which appends the row's token and then attends the
+ * block holding it while the other waves attend the rest of the row, so the append
+ * costs no launch and no time on the attention's path. out then equals the two calls'
+ * up to the order of the binary32 sums (the new token's block is merged last), i.e. to
+ * the last place of the fp16 result. Arguments and limits are
  * those of kv_append and decode_attn_qkv (max_len_after bounds the lengths after the
  * append and sizes the plan; the workspace is sized by
  * decode_attn_workspace_bytes(cache, max_len_after, blocks_per_split)); the same
