@@ -123,7 +123,9 @@ int kv_quantize_blocks(const kvq_cache* cache, const void* k, const void* v,
 /* Appends one decoded token per sequence: for every row, the token is written at
  * position n_b = seq_lens[b] (its fp16 value staged in the tail buffer), the row's
  * tail block is brought to exactly what kv_quantize_blocks would produce for the first
- * n_b + 1 tokens, and then seq_lens[b] is incremented. When the new token leaves the
+ * n_b + 1 tokens, and then seq_lens[b] is incremented. (Codes of positions past the
+ * length are zero as kv_quantize_blocks leaves them; a caller that shortens seq_lens
+ * and appends again may find stale codes there, which nothing reads.) When the new token leaves the
  * block's statistic (absmax, or min and max) unchanged only its own codes are written;
  * otherwise the whole tail block is re-quantized from the staged fp16 values.
  * Sequences with seq_lens[b] >= MB*64 are left unchanged. The tail staging (written
