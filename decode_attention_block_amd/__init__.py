@@ -41,7 +41,8 @@ class kvq_cache(ctypes.Structure):
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
                 ("k_zero", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
                 ("k_tail", ctypes.c_void_p), ("v_tail", ctypes.c_void_p),
-                ("seq_lens", ctypes.c_void_p)]
+                ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int32)]
 
 
 _lib = None
@@ -201,18 +202,29 @@ def decode_step_qkv(cache, k_new, v_new, q, softmax_scale, out, workspace, max_l
 
 class KVCache:
     """Device buffers of one quantized cache, allocated with torch, plus the C
-    descriptor pointing at them. Code buffers start zeroed."""
+    descriptor pointing at them. Code buffers start zeroed.
+
+    num_pages=None gives the dense layout ([B][H][max_blocks] blocks). With num_pages the
+    cache is paged: codes, scales and zero points are pools of num_pages pages (one
+    64-token block of one sequence for all heads each) and `block_table` (int32
+    [B][max_blocks], device) says which page holds block j of sequence b; it starts at
+    block_table[b][j] = b * max_blocks + j when the pool has room for that, else -1, and
+    the caller may set any mapping before the calls that use it."""
 
     def __init__(self, scheme, batch, heads, head_dim, max_blocks, device="cuda",
-                 with_tail=True, with_zero=None):
+                 with_tail=True, with_zero=None, num_pages=None):
         import torch
         self.scheme, self.batch, self.heads = scheme, batch, heads
         self.head_dim, self.max_blocks = head_dim, max_blocks
+        self.num_pages = num_pages
         rb = head_dim // 2 if scheme == INT4_SYM else head_dim
-        shape = (batch, heads, max_blocks, BLOCK_TOKENS, rb)
-        self.k_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
-        self.v_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
-        self.k_scale = torch.zeros((batch, heads, max_blocks), dtype=torch.float32, device=device)
+        if num_pages is None:
+            lead = (batch, heads, max_blocks)
+        else:
+            lead = (num_pages, heads)
+        self.k_codes = torch.zeros(lead + (BLOCK_TOKENS, rb), dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros_like(self.k_codes)
+        self.k_scale = torch.zeros(lead, dtype=torch.float32, device=device)
         self.v_scale = torch.zeros_like(self.k_scale)
         if with_zero is None:
             with_zero = True
@@ -222,32 +234,48 @@ class KVCache:
         self.k_tail = torch.zeros(tshape, dtype=torch.float16, device=device) if with_tail else None
         self.v_tail = torch.zeros(tshape, dtype=torch.float16, device=device) if with_tail else None
         self.seq_lens = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.block_table = None
+        if num_pages is not None:
+            ident = torch.arange(batch * max_blocks, dtype=torch.int32, device=device)
+            self.block_table = torch.where(ident < num_pages, ident,
+                                           torch.full_like(ident, -1)).view(batch, max_blocks)
         self.desc = kvq_cache(scheme, batch, heads, head_dim, max_blocks,
                               _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale),
                               _ptr(self.v_scale), _ptr(self.k_zero), _ptr(self.v_zero),
-                              _ptr(self.k_tail), _ptr(self.v_tail), _ptr(self.seq_lens))
+                              _ptr(self.k_tail), _ptr(self.v_tail), _ptr(self.seq_lens),
+                              _ptr(self.block_table), 0 if num_pages is None else num_pages)
 
     @property
     def capacity(self):
         return self.max_blocks * BLOCK_TOKENS
 
     def host_arrays(self, natural=True, seqs=None, blocks=None):
-        """The cache buffers copied to numpy, keyed like the oracle's cache dicts. With
-        natural=True int4 codes are returned in natural [token][channel] order (see
-        layout.py); otherwise as stored. `seqs` (a list of sequence indices) and `blocks`
-        (a slice of block indices) restrict the copy; "B" and "max_blocks" then give the
-        sizes of what was copied."""
+        """The cache buffers copied to numpy, keyed like the oracle's cache dicts
+        (dense [B][H][max_blocks] order; a paged cache is gathered through its block
+        table, entries clamped to the pool as the kernels do). With natural=True int4
+        codes are returned in natural [token][channel] order (see layout.py); otherwise
+        as stored. `seqs` (a list of sequence indices) and `blocks` (a slice of block
+        indices) restrict the copy; "B" and "max_blocks" then give the sizes of what was
+        copied."""
         from . import layout
         sel_b = slice(None) if seqs is None else list(seqs)
         sel_j = slice(None) if blocks is None else blocks
-        n_b = self.batch if seqs is None else len(sel_b)
-        n_j = len(range(self.max_blocks)[sel_j])
-        out = {"scheme": self.scheme, "B": n_b, "H": self.heads, "D": self.head_dim,
-               "max_blocks": n_j}
+        b_list = list(range(self.batch))[sel_b] if seqs is None else sel_b
+        j_list = list(range(self.max_blocks))[sel_j]
+        out = {"scheme": self.scheme, "B": len(b_list), "H": self.heads, "D": self.head_dim,
+               "max_blocks": len(j_list)}
+        if self.num_pages is not None:
+            table = self.block_table.cpu().numpy()[np.ix_(b_list, j_list)]
+            pages = np.clip(table, 0, self.num_pages - 1)
         for key in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
             t = getattr(self, key)
-            out[key] = None if t is None else np.ascontiguousarray(
-                t[sel_b][:, :, sel_j].cpu().numpy())
+            if t is None:
+                out[key] = None
+            elif self.num_pages is None:
+                out[key] = np.ascontiguousarray(t[sel_b][:, :, sel_j].cpu().numpy())
+            else:
+                pool = t.cpu().numpy()                      # [pages][H] + block shape
+                out[key] = np.ascontiguousarray(np.moveaxis(pool[pages], 2, 1))
         if natural and self.scheme == INT4_SYM:
             out["k_codes"] = layout.int4_to_natural(out["k_codes"], "k")
             out["v_codes"] = layout.int4_to_natural(out["v_codes"], "v")

@@ -26,6 +26,10 @@ int check_cache(const kvq_cache* c) {
   if (!aligned16(c->k_codes) || !aligned16(c->v_codes)) return KVQ_EALIGN;
   if ((c->k_tail && !aligned16(c->k_tail)) || (c->v_tail && !aligned16(c->v_tail)))
     return KVQ_EALIGN;
+  // paged layout: block indices (page * heads + head) are 32-bit in the kernels
+  if (c->block_table && (c->num_pages <= 0 ||
+                         static_cast<int64_t>(c->num_pages) * c->heads > INT32_MAX))
+    return KVQ_EINVAL;
   return KVQ_OK;
 }
 
@@ -79,10 +83,11 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
   int bps, n_split;
   int rc = plan(c, max_len, bps_req, &bps, &n_split);
   if (rc != KVQ_OK) return rc;
-  // the split kernels address a row's codes with 32-bit buffer offsets
+  // the split kernels address a row's codes with 32-bit buffer offsets (dense layout;
+  // the paged layout addresses each block separately)
   const int64_t row_code_bytes = static_cast<int64_t>(c->max_blocks) * kBlockTokens *
                                  (c->scheme == KVQ_INT4_SYM ? c->head_dim / 2 : c->head_dim);
-  if (row_code_bytes > INT32_MAX) return KVQ_ENOTSUP;
+  if (!c->block_table && row_code_bytes > INT32_MAX) return KVQ_ENOTSUP;
   if (n_split > 0) {
     if (!workspace || workspace_bytes_given < workspace_bytes(c, n_split))
       return KVQ_EWORKSPACE;
@@ -109,6 +114,8 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
   a->bps = bps;
   a->n_split = n_split;
   a->qk_scale = softmax_scale * 1.44269504088896340736f;  // log2(e)
+  a->block_table = c->block_table;
+  a->num_pages = c->num_pages;
   return KVQ_OK;
 }
 
@@ -139,6 +146,8 @@ int append_args(const kvq_cache* c, const void* k_new, const void* v_new, int32_
   a->batch = c->batch;
   a->heads = c->heads;
   a->max_blocks = c->max_blocks;
+  a->block_table = c->block_table;
+  a->num_pages = c->num_pages;
   return KVQ_OK;
 }
 
@@ -159,7 +168,7 @@ int kv_quantize_blocks(const kvq_cache* cache, const void* k, const void* v,
     return KVQ_EALIGN;
   const int nb = n_blocks_for(max_len);
   if (nb == 0) return KVQ_OK;
-  kvq::QuantArgs a;
+  kvq::QuantArgs a = {};
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.stride_b = stride_b;
@@ -177,6 +186,8 @@ int kv_quantize_blocks(const kvq_cache* cache, const void* k, const void* v,
   a.heads = cache->heads;
   a.max_blocks = cache->max_blocks;
   a.max_len = max_len;
+  a.block_table = cache->block_table;
+  a.num_pages = cache->num_pages;
   const hipError_t e = kvq::launch_quantize(cache->scheme, cache->head_dim, cache->batch, nb, a,
                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
@@ -184,7 +195,7 @@ int kv_quantize_blocks(const kvq_cache* cache, const void* k, const void* v,
 
 int kv_append(const kvq_cache* cache, const void* k_new, const void* v_new,
               int32_t max_len_after, void* stream) {
-  kvq::AppendArgs a;
+  kvq::AppendArgs a = {};
   const int rc = append_args(cache, k_new, v_new, max_len_after, &a);
   if (rc != KVQ_OK) return rc;
   const hipError_t e = kvq::launch_append(cache->scheme, cache->head_dim, a,

@@ -126,6 +126,14 @@ __device__ __forceinline__ void int4_write_block_from(const _Float16* xs, int nt
 template <int SCHEME>
 constexpr int kAppendStats = SCHEME == KVQ_INT4_SYM ? 4 : 8;  // old and new, K and V
 
+// Index of the block that receives the token of row `row` (= b * heads + h) at position
+// len (see block_slot).
+__device__ __forceinline__ int64_t append_slot(const AppendArgs& a, int64_t row, int len) {
+  return block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks,
+                    static_cast<int>(row / a.heads), static_cast<int>(row % a.heads),
+                    len / kBlock);
+}
+
 struct AppendPlan {  // one tensor's outcome: the block's scale, zero point, re-quantized?
   float s, zp;
   bool full;
@@ -220,7 +228,7 @@ __device__ __forceinline__ void append_write_codes(const AppendArgs& a, int64_t 
   const int tr = tid / TPT;
   const int chunk = tid % TPT;
   const int slot = len % kBlock;
-  const int64_t blk = row * a.max_blocks + len / kBlock;
+  const int64_t blk = append_slot(a, row, len);
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     const bool is_v = kv != 0;
@@ -281,7 +289,7 @@ __device__ __forceinline__ BlockScales append_finish(const AppendArgs& a, int64_
   constexpr int TPT = D / 8;
   constexpr int TPP = NT / TPT;
   const int slot = len % kBlock;
-  const int64_t blk = row * a.max_blocks + len / kBlock;
+  const int64_t blk = append_slot(a, row, len);
   if (tid / TPT == slot % TPP) {
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {

@@ -288,22 +288,22 @@ __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, i
   for (int i0 = 0; i0 < n_wave; i0 += kWave) {
     const int i1 = min(n_wave, i0 + kWave);
     const auto params = load_params(blk_of(min(i0 + lane, i1 - 1)));
-    load(false, blk_of(i0), kbuf);
+    load(false, blk_of(i0), params, 0, kbuf);
     for (int i = i0; i < i1 - 1; ++i) {
       const int blk = blk_of(i);
-      load(true, blk, vbuf);
+      load(true, blk, params, i - i0, vbuf);
       // keep each request where it is: the scheduler would otherwise sink it below the
       // work it is meant to overlap, to shorten its registers' lifetime
       __builtin_amdgcn_sched_barrier(0);
       const auto pb = params.at(i - i0);
       on_k(blk, pb, kbuf);
-      load(false, blk_of(i + 1), kbuf);
+      load(false, blk_of(i + 1), params, i + 1 - i0, kbuf);
       __builtin_amdgcn_sched_barrier(0);
       on_v(blk, pb, vbuf);
     }
     {  // the chunk's last block: nothing further to request
       const int blk = blk_of(i1 - 1);
-      load(true, blk, vbuf);
+      load(true, blk, params, i1 - 1 - i0, vbuf);
       __builtin_amdgcn_sched_barrier(0);
       const auto pb = params.at(i1 - 1 - i0);
       on_k(blk, pb, kbuf);
@@ -312,18 +312,33 @@ __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, i
   }
 }
 
-struct ScaleParams {  // block scales of K and V
+__device__ __forceinline__ int lane_int(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
+
+// Per-block values a lane preloads for the pipeline: block scales (and zero points) of K
+// and V, and, in the paged layout, the block's index in the pools (block_slot).
+struct ScaleParams {
   float ks, vs;
+  int slot;
   __device__ __forceinline__ ScaleParams at(int j) const {
-    return {lane_value(ks, j), lane_value(vs, j)};
+    return {lane_value(ks, j), lane_value(vs, j), lane_int(slot, j)};
   }
 };
-struct ScaleZeroParams {  // block scales and zero points of K and V
+struct ScaleZeroParams {
   float ks, kz, vs, vz;
+  int slot;
   __device__ __forceinline__ ScaleZeroParams at(int j) const {
-    return {lane_value(ks, j), lane_value(kz, j), lane_value(vs, j), lane_value(vz, j)};
+    return {lane_value(ks, j), lane_value(kz, j), lane_value(vs, j), lane_value(vz, j),
+            lane_int(slot, j)};
   }
 };
+
+// A buffer resource over one block region (the paged layout gives every block its own
+// base; offsets inside a region stay small).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const uint8_t* pool, int64_t slot,
+                                                              int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pool + slot * bytes), 0, bytes,
+                                           kBufferRsrcWord3);
+}
 
 // ---- fused decode step ----------------------------------------------------------------
 // In a decode step (kAppend) the workgroup of row (b, h) has one wave more than the
@@ -390,7 +405,7 @@ __device__ __forceinline__ BlockScales step_append(const AttnArgs& a, const Step
 }
 
 // ---- split kernel: grid (n_split, heads, batch), kSplitWaves waves ------------------
-template <int SCHEME, int D, bool kAppend>
+template <int SCHEME, int D, bool kAppend, bool kPaged>
 __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void attn_split_kernel(
     AttnArgs a) {
   using G = AGeo<SCHEME, D>;
@@ -436,20 +451,22 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   q.load(a.q + row * D + chunk * DPL);
   const float qsum_row = group_sum<LPT>(q.sum);
 
-  // The row's code regions as buffer resources (uniform base and block offset, the
-  // lane's 16-byte slot as the only per-lane address). The host keeps the row below 2^31
-  // bytes.
+  // Dense layout: the row's code regions as buffer resources (uniform base and block
+  // offset, the lane's 16-byte slot as the only per-lane address; the host keeps the row
+  // below 2^31 bytes). Paged layout: one resource per block at its page.
   constexpr int kRegionBytes = kBlock * G::kRowBytes;
-  const int row_bytes = a.max_blocks * kRegionBytes;
+  const int row_bytes = kPaged ? kRegionBytes : a.max_blocks * kRegionBytes;
+  const int64_t row_base = kPaged ? 0 : row * row_bytes;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.k_codes + row * row_bytes), 0, row_bytes, kBufferRsrcWord3);
+      const_cast<uint8_t*>(a.k_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.v_codes + row * row_bytes), 0, row_bytes, kBufferRsrcWord3);
+      const_cast<uint8_t*>(a.v_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
   const int lane_off = lane * 16;
-  const float* ks = a.k_scale + row * a.max_blocks;
-  const float* vs = a.v_scale + row * a.max_blocks;
-  const float* kz = a.k_zero + row * a.max_blocks;
-  const float* vz = a.v_zero + row * a.max_blocks;
+  const int64_t sbase = kPaged ? 0 : row * a.max_blocks;  // dense: the row's blocks
+  const float* ks = a.k_scale + sbase;
+  const float* vs = a.v_scale + sbase;
+  const float* kz = a.k_zero + sbase;
+  const float* vz = a.v_zero + sbase;
 
   float o[DPL];
 #pragma unroll
@@ -457,10 +474,24 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   float m = -__builtin_inff();  // running max of the base-2 scores (wave-uniform)
   float l = 0.0f;               // sum of weights over this lane's tokens
 
-  auto load_codes = [&](bool is_v, int blk, uint4 (&r)[TPL]) {
+  // Block blk's codes; in the paged layout `slot` locates the block.
+  auto load_codes = [&](bool is_v, int blk, int slot, uint4 (&r)[TPL]) {
+    if constexpr (kPaged) {
+      const __amdgpu_buffer_rsrc_t rs =
+          region_rsrc(is_v ? a.v_codes : a.k_codes, slot, kRegionBytes);
 #pragma unroll
-    for (int i = 0; i < TPL; ++i)
-      r[i] = load_stream(is_v ? vrsrc : krsrc, lane_off, blk * kRegionBytes + i * kWave * 16);
+      for (int i = 0; i < TPL; ++i) r[i] = load_stream(rs, lane_off, i * kWave * 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPL; ++i)
+        r[i] = load_stream(is_v ? vrsrc : krsrc, lane_off, blk * kRegionBytes + i * kWave * 16);
+    }
+  };
+  // the index of block blk in the per-block arrays (block_slot)
+  auto slot_of = [&](int blk) {
+    return kPaged ? static_cast<int>(block_slot(a.block_table, a.num_pages, a.heads,
+                                                a.max_blocks, b, h, blk))
+                  : blk;
   };
 
   // Scores of the lane's TPL tokens of block blk (base-2 logits), then the online
@@ -531,8 +562,9 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
         // invalidated), and keep the loads below that point
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
         uint4 kr[TPL], vr[TPL];
-        load_codes(false, sl.tail_blk, kr);
-        load_codes(true, sl.tail_blk, vr);
+        const int slot = slot_of(sl.tail_blk);
+        load_codes(false, sl.tail_blk, slot, kr);
+        load_codes(true, sl.tail_blk, slot, vr);
         block_weights(sl.tail_blk, sc.ks, sc.kz, kr, p);
         block_accumulate(sc.vs, sc.vz, vr, p);
       }
@@ -541,8 +573,13 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   if (streaming)
     stream_wave_blocks<TPL>(
         blk_begin, blk_end, wave, lane, row,
-        [&](int blk) { return ScaleZeroParams{ks[blk], kz[blk], vs[blk], vz[blk]}; },
-        load_codes,
+        [&](int blk) {
+          const int j = slot_of(blk);
+          return ScaleZeroParams{ks[j], kz[j], vs[j], vz[j], j};
+        },
+        [&](bool is_v, int blk, const ScaleZeroParams& ps, int j, uint4 (&r)[TPL]) {
+          load_codes(is_v, blk, kPaged ? lane_int(ps.slot, j) : 0, r);
+        },
         [&](int blk, const ScaleZeroParams& pb, const uint4 (&kr)[TPL]) {
           block_weights(blk, pb.ks, pb.kz, kr, p);
         },
@@ -656,7 +693,7 @@ __device__ __forceinline__ float row0_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
 }
 
-template <int D, bool kAppend>
+template <int D, bool kAppend, bool kPaged>
 __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void
 attn_split_int4_kernel(AttnArgs a) {
   constexpr int KS = D / 32;               // 32-channel K steps of QK^T
@@ -724,17 +761,20 @@ attn_split_int4_kernel(AttnArgs a) {
       }
   }
 
-  // The row's code regions as buffer resources: a load's address is then the uniform
-  // block offset (a scalar register) plus the lane's 16-byte slot, with no per-lane
-  // 64-bit address arithmetic. The host keeps max_blocks * 32 * D below 2^31.
-  const int row_bytes = a.max_blocks * kRegionBytes;
+  // Dense layout: the row's code regions as buffer resources, so a load's address is
+  // the uniform block offset (a scalar register) plus the lane's 16-byte slot, with no
+  // per-lane 64-bit address arithmetic (the host keeps max_blocks * 32 * D below 2^31).
+  // Paged layout: one resource per block at its page.
+  const int row_bytes = kPaged ? kRegionBytes : a.max_blocks * kRegionBytes;
+  const int64_t row_base = kPaged ? 0 : row * row_bytes;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.k_codes + row * row_bytes), 0, row_bytes, kBufferRsrcWord3);
+      const_cast<uint8_t*>(a.k_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.v_codes + row * row_bytes), 0, row_bytes, kBufferRsrcWord3);
+      const_cast<uint8_t*>(a.v_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
   const int lane_off = lane * 16;
-  const float* ks_ptr = a.k_scale + row * a.max_blocks;
-  const float* vs_ptr = a.v_scale + row * a.max_blocks;
+  const int64_t sbase = kPaged ? 0 : row * a.max_blocks;  // dense: the row's blocks
+  const float* ks_ptr = a.k_scale + sbase;
+  const float* vs_ptr = a.v_scale + sbase;
 
   float o[NTV];
 #pragma unroll
@@ -742,10 +782,24 @@ attn_split_int4_kernel(AttnArgs a) {
   float m = -__builtin_inff();  // running max of the base-2 scores (wave-uniform)
   float l = 0.0f;               // lanes 0..15: sum of their tokens' weights
 
-  auto load_codes = [&](__amdgpu_buffer_rsrc_t rsrc, int blk, uint4 (&r)[LOADS]) {
+  // Block blk's codes; in the paged layout `slot` locates the block.
+  auto load_codes = [&](bool is_v, int blk, int slot, uint4 (&r)[LOADS]) {
+    if constexpr (kPaged) {
+      const __amdgpu_buffer_rsrc_t rs =
+          region_rsrc(is_v ? a.v_codes : a.k_codes, slot, kRegionBytes);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      r[i] = load_stream(rsrc, lane_off, blk * kRegionBytes + i * kWave * 16);
+      for (int i = 0; i < LOADS; ++i) r[i] = load_stream(rs, lane_off, i * kWave * 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        r[i] = load_stream(is_v ? vrsrc : krsrc, lane_off, blk * kRegionBytes + i * kWave * 16);
+    }
+  };
+  // the index of block blk in the per-block arrays (block_slot)
+  auto slot_of = [&](int blk) {
+    return kPaged ? static_cast<int>(block_slot(a.block_table, a.num_pages, a.heads,
+                                                a.max_blocks, b, h, blk))
+                  : blk;
   };
 
 
@@ -831,7 +885,8 @@ attn_split_int4_kernel(AttnArgs a) {
       uint4 kr[LOADS], vr[LOADS];
       const BlockScales sc = step_append<KVQ_INT4_SYM, D>(
           a, sl, b, row, cap, lane, xs, [&](const AppendPlan (&plan)[2]) {
-            const int64_t blk = row * a.max_blocks + sl.len0 / kBlock;
+            const int64_t blk = block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks,
+                                           b, h, sl.len0 / kBlock);
             const int slot = sl.len0 % kBlock;
             int4_tail_fragments<D>(xs, slot, plan[0], false, lane, kr,
                                    a.ap.k_codes + blk * kRegionBytes);
@@ -847,8 +902,13 @@ attn_split_int4_kernel(AttnArgs a) {
   if (streaming)
     stream_wave_blocks<LOADS>(
         blk_begin, blk_end, wave, lane, row,
-        [&](int blk) { return ScaleParams{ks_ptr[blk], vs_ptr[blk]}; },
-        [&](bool is_v, int blk, uint4 (&r)[LOADS]) { load_codes(is_v ? vrsrc : krsrc, blk, r); },
+        [&](int blk) {
+          const int j = slot_of(blk);
+          return ScaleParams{ks_ptr[j], vs_ptr[j], j};
+        },
+        [&](bool is_v, int blk, const ScaleParams& ps, int j, uint4 (&r)[LOADS]) {
+          load_codes(is_v, blk, kPaged ? lane_int(ps.slot, j) : 0, r);
+        },
         [&](int blk, const ScaleParams& pb, const uint4 (&kr)[LOADS]) {
           block_weights(blk, pb.ks, kr, p);
         },
@@ -899,33 +959,30 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   merge_row<D, false>(a, row, n, d);
 }
 
-template <int D, bool kAppend>
-hipError_t split_int4_t(int batch, const AttnArgs& a, hipStream_t s) {
+template <int SCHEME, int D, bool kAppend, bool kPaged>
+hipError_t split_t(int batch, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.heads, batch);
-  hipLaunchKernelGGL((attn_split_int4_kernel<D, kAppend>), grid,
-                     dim3((kAppend ? kStepWaves : kSplitWaves) * kWave), 0, s, a);
+  dim3 block((kAppend ? kStepWaves : kSplitWaves) * kWave);
+  if constexpr (SCHEME == KVQ_INT4_SYM)
+    hipLaunchKernelGGL((attn_split_int4_kernel<D, kAppend, kPaged>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<SCHEME, D, kAppend, kPaged>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 template <int SCHEME, int D, bool kAppend>
-hipError_t split_t(int batch, const AttnArgs& a, hipStream_t s) {
-  if constexpr (SCHEME == KVQ_INT4_SYM) {
-    return split_int4_t<D, kAppend>(batch, a, s);
-  } else {
-    dim3 grid(a.n_split, a.heads, batch);
-    hipLaunchKernelGGL((attn_split_kernel<SCHEME, D, kAppend>), grid,
-                       dim3((kAppend ? kStepWaves : kSplitWaves) * kWave), 0, s, a);
-    return hipGetLastError();
-  }
+hipError_t layout_t(int batch, const AttnArgs& a, hipStream_t s) {
+  return a.block_table ? split_t<SCHEME, D, kAppend, true>(batch, a, s)
+                       : split_t<SCHEME, D, kAppend, false>(batch, a, s);
 }
 
 template <bool kAppend>
 hipError_t launch(int scheme, int head_dim, int batch, const AttnArgs& a, hipStream_t s) {
   if (scheme == KVQ_INT4_SYM)
-    return head_dim == 128 ? split_t<KVQ_INT4_SYM, 128, kAppend>(batch, a, s)
-                           : split_t<KVQ_INT4_SYM, 64, kAppend>(batch, a, s);
-  return head_dim == 128 ? split_t<KVQ_UINT8_ASYM, 128, kAppend>(batch, a, s)
-                         : split_t<KVQ_UINT8_ASYM, 64, kAppend>(batch, a, s);
+    return head_dim == 128 ? layout_t<KVQ_INT4_SYM, 128, kAppend>(batch, a, s)
+                           : layout_t<KVQ_INT4_SYM, 64, kAppend>(batch, a, s);
+  return head_dim == 128 ? layout_t<KVQ_UINT8_ASYM, 128, kAppend>(batch, a, s)
+                         : layout_t<KVQ_UINT8_ASYM, 64, kAppend>(batch, a, s);
 }
 
 }  // namespace

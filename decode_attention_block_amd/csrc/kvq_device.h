@@ -139,6 +139,17 @@ __device__ __forceinline__ uint32_t int4_dword_offset(int lane, int f) {
   return static_cast<uint32_t>(((f >> 2) * 64 + lane) * 16 + (f & 3) * 4);
 }
 
+// Index of block j of row (b, h) in the code, scale and zero-point arrays: dense
+// [B][H][max_blocks], or, with a block table, [num_pages][H] at the page the table
+// gives for (b, j), clamped to the pool.
+__device__ __forceinline__ int64_t block_slot(const int32_t* table, int num_pages, int heads,
+                                              int max_blocks, int b, int h, int j) {
+  if (table == nullptr) return (static_cast<int64_t>(b) * heads + h) * max_blocks + j;
+  int p = table[static_cast<int64_t>(b) * max_blocks + j];
+  p = p < 0 ? 0 : (p >= num_pages ? num_pages - 1 : p);
+  return static_cast<int64_t>(p) * heads + h;
+}
+
 // Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no
 // swizzle): loads past num_records return zeros and access no memory.
 constexpr int kBufferRsrcWord3 = 0x00020000;

@@ -22,6 +22,8 @@ struct QuantArgs {
   uint16_t* v_tail;
   const int32_t* seq_lens;
   int heads, max_blocks, max_len;
+  const int32_t* block_table;  // paged layout, else nullptr
+  int num_pages;
 };
 
 struct AppendArgs {
@@ -37,6 +39,8 @@ struct AppendArgs {
   uint16_t* v_tail;
   int32_t* seq_lens;
   int batch, heads, max_blocks;
+  const int32_t* block_table;  // paged layout, else nullptr
+  int num_pages;
 };
 
 struct AttnArgs {
@@ -55,6 +59,8 @@ struct AttnArgs {
   int heads, max_blocks, max_len, bps, n_split;
   int fused;           // 1: the last workgroup of each row merges the splits and writes out
   float qk_scale;      // softmax_scale * log2(e)
+  const int32_t* block_table;  // paged layout, else nullptr
+  int num_pages;
   AppendArgs ap;       // fused decode step: the token each row's workgroup appends first
 };
 

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(QuantArgs a) 
   const int zpi = static_cast<int>(zp);
 
   const int64_t row = static_cast<int64_t>(b) * a.heads + h;
-  const int64_t blk = row * a.max_blocks + j;
+  const int64_t blk = block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks, b, h, j);
   uint8_t* codes = (kv ? a.v_codes : a.k_codes) + blk * kBlock * G::kRowBytes;
   if constexpr (SCHEME == KVQ_INT4_SYM) {
     int4_write_block_from<D>(xs, ntok, s, kv != 0, codes, tid);  // block_max synced xs

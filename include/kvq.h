@@ -40,7 +40,7 @@ extern "C" {
 #endif
 
 #define KVQ_BLOCK_TOKENS 64
-#define KVQ_VERSION 1
+#define KVQ_VERSION 2
 
 /* Cache formats. */
 enum kvq_scheme {
@@ -87,7 +87,23 @@ enum kvq_status {
  *                      needs to re-quantize that block. May be NULL if kv_append is
  *                      never called.
  *   seq_lens         : int32 [B], the number of valid tokens of each sequence (device
- *                      memory). Entries are clamped to [0, MB*64] by every kernel. */
+ *                      memory). Entries are clamped to [0, MB*64] by every kernel.
+ *   block_table      : NULL for the dense layout above. Otherwise the cache is paged
+ *                      ([Pg3] §四: PagedAttention against KV-cache fragmentation; [Pg1]
+ *                      §3.1: a cache sized to the current length from a memory pool):
+ *                      int32 [B][MB] device memory, entry (b, j) = the page that holds
+ *                      block j of sequence b, and the per-block arrays become pools of
+ *                      num_pages pages, a page being one 64-token block of one sequence
+ *                      for all H heads:
+ *                        k_codes, v_codes : [num_pages][H][64][D/2 | D] (same block
+ *                                           regions and order as above),
+ *                        k_scale .. v_zero: [num_pages][H].
+ *                      Tail staging and seq_lens stay per sequence. Entries for blocks
+ *                      a call reads or writes must be set before the call (an append
+ *                      that opens block j writes page (b, j)); entries outside
+ *                      [0, num_pages) are clamped into it. Every call gives bitwise the
+ *                      results of the dense layout with the same contents.
+ *   num_pages        : pages in the pools (>= 1 when block_table is set, else ignored). */
 typedef struct kvq_cache {
   int32_t scheme;
   int32_t batch;
@@ -103,6 +119,8 @@ typedef struct kvq_cache {
   void* k_tail;
   void* v_tail;
   int32_t* seq_lens;
+  const int32_t* block_table;
+  int32_t num_pages;
 } kvq_cache;
 
 /* Quantizes the prefill: for every row (b, h), blocks [0, ceil(n_b / 64)) of K and V,

@@ -32,16 +32,17 @@ def test_library_exports_every_declared_symbol():
     L = kvq.load_library()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert kvq.kvq_version() == 1
+    assert kvq.kvq_version() == 2
 
 
 def cache(scheme=0, B=2, H=4, D=128, MB=3, **kw):
     fields = dict(k_codes=FAKE, v_codes=FAKE, k_scale=FAKE, v_scale=FAKE, k_zero=FAKE,
-                  v_zero=FAKE, k_tail=FAKE, v_tail=FAKE, seq_lens=FAKE)
+                  v_zero=FAKE, k_tail=FAKE, v_tail=FAKE, seq_lens=FAKE, block_table=None,
+                  num_pages=0)
     fields.update(kw)
     return kvq.kvq_cache(scheme, B, H, D, MB, *[fields[f] for f in (
         "k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero", "k_tail", "v_tail",
-        "seq_lens")])
+        "seq_lens", "block_table", "num_pages")])
 
 
 def rc_quant(c, k=FAKE, v=FAKE, strides=(3 * 64 * 4 * 128, 4 * 128, 128), max_len=100):
@@ -107,6 +108,18 @@ def test_capacity_and_lengths():
     assert rc_attn(cache(MB=(1 << 19) - 1, D=128), ws=0) == EWS           # just fits
     assert rc_attn(cache(scheme=1, MB=(1 << 18) + 1, D=128)) == ENOTSUP  # uint8: 8 KiB
     assert rc_attn(cache(scheme=1, MB=1 << 18, D=64), ws=0) == EWS
+
+
+@no_gpu_only
+def test_paged_layout_rules():
+    # a block table needs a pool, and page * heads must stay a 32-bit index
+    assert rc_quant(cache(block_table=FAKE, num_pages=0)) == EINVAL
+    assert rc_quant(cache(block_table=FAKE, num_pages=-3)) == EINVAL
+    assert rc_quant(cache(H=64, block_table=FAKE, num_pages=(1 << 25) + 1)) == EINVAL
+    assert rc_attn(cache(H=64, block_table=FAKE, num_pages=(1 << 25) - 1), ws=0) == EWS
+    # pages are addressed one by one: rows of 2^31 bytes or more are fine
+    assert rc_attn(cache(MB=(1 << 19) + 1, D=128, block_table=FAKE, num_pages=8), ws=0) == EWS
+    assert rc_step(cache(B=1, H=1, MB=4, block_table=FAKE, num_pages=0)) == EINVAL
 
 
 @no_gpu_only
