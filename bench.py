@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--blocks-per-split", type=int, default=0)
     p.add_argument("--separate", action="store_true",
                    help="time the step as kv_append + decode_attn_qkv (two calls)")
+    p.add_argument("--paged", action="store_true",
+                   help="time --workload on a paged cache (shuffled page pool)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate host time spent timing the oracle")
     p.add_argument("--no-cpu", action="store_true")
@@ -206,10 +208,13 @@ class Timer:
         return sum(a.elapsed_time(b) for a, b in self.segments)
 
 
-def quantized_copies(kvq, torch, w, layer, lens, max_blocks, n_copies, device_inputs):
+def quantized_copies(kvq, torch, w, layer, lens, max_blocks, n_copies, device_inputs,
+                     paged=False):
     """n_copies caches holding the quantized prefill of one layer; returns them and the
     prefill kernel times (ms). device_inputs: draw K and V with the device-side recipe
-    (same distributions, other values) instead of the host recipe."""
+    (same distributions, other values) instead of the host recipe. paged: each copy is a
+    paged cache whose block table scatters the blocks over its pool in a seeded random
+    order."""
     n = int(np.max(lens))
     wl = wl_mod()
     if device_inputs:
@@ -219,8 +224,15 @@ def quantized_copies(kvq, torch, w, layer, lens, max_blocks, n_copies, device_in
         k = torch.from_numpy(wl.prefill_batch(w, layer, 0, n_tokens=n)).cuda()
         v = torch.from_numpy(wl.prefill_batch(w, layer, 1, n_tokens=n)).cuda()
     caches, ms = [], []
-    for _ in range(n_copies):
-        c = kvq.KVCache(w.scheme, w.batch, w.heads, w.head_dim, max_blocks)
+    for i in range(n_copies):
+        if paged:
+            n_pages = w.batch * max_blocks
+            c = kvq.KVCache(w.scheme, w.batch, w.heads, w.head_dim, max_blocks,
+                            num_pages=n_pages)
+            perm = np.random.default_rng([w.index, i]).permutation(n_pages).astype(np.int32)
+            c.block_table.copy_(torch.from_numpy(perm.reshape(w.batch, max_blocks)))
+        else:
+            c = kvq.KVCache(w.scheme, w.batch, w.heads, w.head_dim, max_blocks)
         c.seq_lens.copy_(torch.from_numpy(np.asarray(lens, np.int32)))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -244,7 +256,7 @@ def workspace(kvq, torch, cache, lengths, bps):
 
 
 def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs,
-                         separate=False):
+                         separate=False, paged=False):
     """Single-layer fixed-length workloads; step = decode_step_qkv (or, with separate,
     kv_append + decode_attn_qkv; the sampled kernel is then the attention alone).
 
@@ -264,7 +276,7 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
     max_blocks = (w.context + growth + 63) // 64
     t_setup = time.perf_counter()
     caches, prefill_ms = quantized_copies(kvq, torch, w, 0, wl.lengths(w), max_blocks, copies,
-                                          device_inputs)
+                                          device_inputs, paged)
     kn = np.stack([wl.appended_kv(w, 0, s, 0, growth) for s in range(B)], axis=1)
     vn = np.stack([wl.appended_kv(w, 0, s, 1, growth) for s in range(B)], axis=1)
     k_new = torch.from_numpy(kn).cuda()          # [growth][B][H][D]
@@ -334,7 +346,8 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
         "step": ("kv_append + decode_attn_qkv" if separate else
                  "decode_step_qkv (%s)" % ("append and attention in one launch" if one_launch
                                            else "append, then attention")),
-        "kernel": kernel_name(w, fused=one_launch),
+        "kernel": kernel_name(w, fused=one_launch, paged=paged),
+        "layout": "paged (block table over a shuffled page pool)" if paged else "dense",
         "steps": steps, "warmup": warmup,
         "ms_per_step": total_ms / steps,
         "gbs": sum(step_bytes) / (total_ms / 1e3) / 1e9,
@@ -417,22 +430,22 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
     return res
 
 
-def kernel_name(w, fused):
-    """The timed kernel as rocprofv3 lists it (template arguments: head_dim, and whether
-    the workgroup appends the row's token first)."""
-    b = "true" if fused else "false"
+def kernel_name(w, fused, paged=False):
+    """The timed kernel as rocprofv3 lists it (template arguments: head_dim, whether the
+    workgroup also appends the row's token, whether the cache is paged)."""
+    f, p = ("true" if fused else "false"), ("true" if paged else "false")
     if w.scheme == 0:
-        return f"attn_split_int4_kernel<{w.head_dim}, {b}>"
-    return f"attn_split_kernel<1, {w.head_dim}, {b}>"
+        return f"attn_split_int4_kernel<{w.head_dim}, {f}, {p}>"
+    return f"attn_split_kernel<1, {w.head_dim}, {f}, {p}>"
 
 
 def measure(kvq, torch, w, steps, warmup, bps, keep_host=False, device_inputs=False,
-            separate=False):
+            separate=False, paged=False):
     if w.layers > 1:
         res = run_layers(kvq, torch, w, steps, warmup, bps, device_inputs), None
     else:
         res = run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs,
-                                   separate)
+                                   separate, paged)
     res[0]["inputs"] = ("K/V drawn on the device (torch generator, same distributions)"
                         if device_inputs else "K/V from the seeded host recipe")
     return res
@@ -464,13 +477,13 @@ def main():
     big = w.decode_steps > 0 or w.layers > 1
     res, host_cache = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
                               keep_host=with_cpu and not big, device_inputs=big,
-                              separate=args.separate)
+                              separate=args.separate, paged=args.paged)
     if args.profile_loop:
         print(json.dumps(res), flush=True)
         return
 
     B, H, D = w.batch, w.heads, w.head_dim
-    fused = res["kernel"].endswith("true>")
+    fused = ", true," in res["kernel"]
     result = {
         "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s, int4 KV, B=8 ctx 8K",
         "value": res["gbs"],
@@ -490,7 +503,7 @@ def main():
                    "context": w.context, "context_range_timed": res["context"],
                    "kv_format": "int4 block-64 symmetric" if w.scheme == 0
                    else "uint8 block-64 asymmetric",
-                   "step": res["step"],
+                   "step": res["step"], "layout": res.get("layout", "dense"),
                    "cache_copies_rotated": res.get("cache_copies_rotated"),
                    "blocks_per_split": res["blocks_per_split"],
                    "splits_per_row": res["splits_per_row"], "parallelism": "single GPU"},
@@ -526,6 +539,12 @@ def main():
             r, _ = measure(kvq, torch, ow, steps, warm, args.blocks_per_split,
                            device_inputs=ow.decode_steps > 0 or ow.layers > 1,
                            separate=args.separate)
+            others.append(r)
+            torch.cuda.empty_cache()
+        if not args.paged and w.layers == 1:
+            print(f"[bench] {w.name} paged", file=sys.stderr, flush=True)
+            r, _ = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
+                           device_inputs=big, separate=args.separate, paged=True)
             others.append(r)
             torch.cuda.empty_cache()
         result["workloads"] = others
