@@ -23,7 +23,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_ENOTSUP", -3: "KVQ_ECAPACITY",
 
 EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan",
            "decode_attn_workspace_bytes", "decode_attn_qkv", "decode_attn_split",
-           "decode_attn_combine", "decode_step_qkv", "kvq_strerror", "kvq_version"]
+           "decode_attn_combine", "decode_step_qkv", "decode_attn_gqa",
+           "decode_attn_gqa_workspace_bytes", "kvq_strerror", "kvq_version"]
 
 
 class KvqError(RuntimeError):
@@ -72,6 +73,8 @@ def load_library():
         "decode_attn_split": ([C, P, ctypes.c_float, P, sz, i32, i32, P], ctypes.c_int),
         "decode_attn_combine": ([C, P, P, sz, i32, i32, P], ctypes.c_int),
         "decode_step_qkv": ([C, P, P, P, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
+        "decode_attn_gqa": ([C, P, i32, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
+        "decode_attn_gqa_workspace_bytes": ([C, i32, i32, i32], sz),
         "kvq_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "kvq_version": ([], ctypes.c_int),
     }
@@ -145,11 +148,18 @@ def decode_attn_workspace_bytes(cache, max_len, blocks_per_split=0):
                                                       int(blocks_per_split))
 
 
-def make_workspace(cache, max_len, blocks_per_split=0, device="cuda"):
-    """A zero-filled device workspace of decode_attn_workspace_bytes(...) bytes (its
-    arrival counters must start at zero; the library leaves them zero)."""
+def decode_attn_gqa_workspace_bytes(cache, group, max_len, blocks_per_split=0):
+    return load_library().decode_attn_gqa_workspace_bytes(_desc(cache), int(group), int(max_len),
+                                                          int(blocks_per_split))
+
+
+def make_workspace(cache, max_len, blocks_per_split=0, device="cuda", group=1):
+    """A zero-filled device workspace of decode_attn_workspace_bytes(...) bytes (or
+    decode_attn_gqa_workspace_bytes(...) for group > 1; its arrival counters must start
+    at zero, and the library leaves them zero)."""
     import torch
-    n = decode_attn_workspace_bytes(cache, max_len, blocks_per_split)
+    n = (decode_attn_workspace_bytes(cache, max_len, blocks_per_split) if group == 1 else
+         decode_attn_gqa_workspace_bytes(cache, group, max_len, blocks_per_split))
     return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
 
 
@@ -164,6 +174,19 @@ def decode_attn_qkv(cache, q, softmax_scale, out, workspace, max_len, blocks_per
                                         _ptr(workspace), ws_bytes, int(max_len),
                                         int(blocks_per_split), _stream(stream))
     _check(rc, "decode_attn_qkv")
+
+
+def decode_attn_gqa(cache, q, group, softmax_scale, out, workspace, max_len, blocks_per_split=0,
+                    stream=None):
+    """Grouped-query attention: q, out fp16 CUDA tensors [B][H * group][D] contiguous,
+    query head h * group + g reading cache head h."""
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B][H * group][D]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().decode_attn_gqa(_desc(cache), _ptr(q), int(group), float(softmax_scale),
+                                        _ptr(out), _ptr(workspace), ws_bytes, int(max_len),
+                                        int(blocks_per_split), _stream(stream))
+    _check(rc, "decode_attn_gqa")
 
 
 def decode_attn_split(cache, q, softmax_scale, workspace, max_len, blocks_per_split=0,

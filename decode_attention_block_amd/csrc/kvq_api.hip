@@ -71,15 +71,15 @@ size_t counter_bytes(const kvq_cache* c) {
   return (rows * sizeof(uint32_t) + 255) / 256 * 256;
 }
 
-size_t workspace_bytes(const kvq_cache* c, int n_split) {
-  const size_t parts = static_cast<size_t>(c->batch) * c->heads * n_split;
+size_t workspace_bytes(const kvq_cache* c, int n_split, int group = 1) {
+  const size_t parts = static_cast<size_t>(c->batch) * c->heads * group * n_split;
   return counter_bytes(c) + parts * (static_cast<size_t>(c->head_dim) + 2) * sizeof(float);
 }
 
 // Fills the attention launch descriptor after validating the workspace.
 int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
               void* workspace, size_t workspace_bytes_given, int32_t max_len, int32_t bps_req,
-              int fused, kvq::AttnArgs* a) {
+              int fused, kvq::AttnArgs* a, int group = 1) {
   int bps, n_split;
   int rc = plan(c, max_len, bps_req, &bps, &n_split);
   if (rc != KVQ_OK) return rc;
@@ -89,11 +89,11 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
                                  (c->scheme == KVQ_INT4_SYM ? c->head_dim / 2 : c->head_dim);
   if (!c->block_table && row_code_bytes > INT32_MAX) return KVQ_ENOTSUP;
   if (n_split > 0) {
-    if (!workspace || workspace_bytes_given < workspace_bytes(c, n_split))
+    if (!workspace || workspace_bytes_given < workspace_bytes(c, n_split, group))
       return KVQ_EWORKSPACE;
     if (!aligned16(workspace)) return KVQ_EALIGN;
   }
-  const size_t parts = static_cast<size_t>(c->batch) * c->heads * n_split;
+  const size_t parts = static_cast<size_t>(c->batch) * c->heads * group * n_split;
   a->k_codes = static_cast<const uint8_t*>(c->k_codes);
   a->v_codes = static_cast<const uint8_t*>(c->v_codes);
   a->k_scale = c->k_scale;
@@ -287,6 +287,35 @@ int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new
   return kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a, s) == hipSuccess
              ? KVQ_OK
              : KVQ_EHIP;
+}
+
+size_t decode_attn_gqa_workspace_bytes(const kvq_cache* cache, int32_t group, int32_t max_len,
+                                       int32_t blocks_per_split) {
+  int bps, n_split;
+  if (group < 1 || plan(cache, max_len, blocks_per_split, &bps, &n_split) != KVQ_OK) return 0;
+  return workspace_bytes(cache, n_split, group);
+}
+
+int decode_attn_gqa(const kvq_cache* cache, const void* q, int32_t group, float softmax_scale,
+                    void* out, void* workspace, size_t workspace_bytes_given, int32_t max_len,
+                    int32_t blocks_per_split, void* stream) {
+  if (group == 1)
+    return decode_attn_qkv(cache, q, softmax_scale, out, workspace, workspace_bytes_given,
+                           max_len, blocks_per_split, stream);
+  if (group != 2 && group != 4 && group != 8) return KVQ_EINVAL;
+  if (!q || !out) return KVQ_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_EALIGN;
+  int rc = check_cache(cache);
+  if (rc != KVQ_OK) return rc;
+  if (cache->scheme != KVQ_INT4_SYM) return KVQ_ENOTSUP;
+  kvq::AttnArgs a = {};
+  rc = attn_args(cache, q, softmax_scale, out, workspace, workspace_bytes_given, max_len,
+                 blocks_per_split, 1, &a, group);
+  if (rc != KVQ_OK) return rc;
+  if (a.n_split == 0) a.n_split = 1;  // every row's zeros are still written
+  return kvq::launch_attn_gqa(cache->head_dim, group, cache->batch, a,
+                              static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK
+                                                                              : KVQ_EHIP;
 }
 
 const char* kvq_strerror(int status) {

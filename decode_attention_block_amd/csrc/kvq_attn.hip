@@ -944,6 +944,317 @@ attn_split_int4_kernel(AttnArgs a) {
   finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
 }
 
+// ---- grouped-query attention: G query heads per cached head ---------------------------
+// Query head h * G + g reads cache row (b, h), so the codes of a block are converted to
+// matrix-core operands once for all G queries: rows 0..G-1 of the QK^T A tile hold the
+// G queries (the one-query kernel above leaves rows 1..15 zero). Output element i of
+// lane l is row 4 * (l / 16) + i, column l % 16, so each 16-lane group holds four query
+// rows and each row keeps its own running max (the accumulators are rescaled when any
+// row's max rises). P.V: the G rows of weights reach the A layout through a per-wave LDS
+// image, split as above into fp16 high and low parts (of p * 2^14), which are two A
+// operands accumulated into the same output rows by separate MFMAs.
+
+// Maximum / sum over the 16 lanes of each DPP row; every lane of the row gets it.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  return fmaxf(v, dpp<kDppRowMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v + dpp<kDppRowMirror>(v);
+}
+
+template <int D, int G, bool kPaged>
+__global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;            // 32-channel K steps of QK^T
+  constexpr int NTV = D / 16;           // 16-channel N tiles of P.V
+  constexpr int LOADS = D / 32;         // 16-byte loads per lane per region
+  constexpr int kRegionBytes = 32 * D;  // one tensor's codes of one block
+  // per wave: [high, low][k step][8-token group][row][slot]
+  __shared__ __align__(16) _Float16 pimg[kSplitWaves][2][2][4][16][8];
+  __shared__ float red_o[kSplitWaves][G][D];
+  __shared__ float red_l[kSplitWaves][G];
+  __shared__ float red_m[kSplitWaves][G];
+
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int cap = a.max_blocks * kBlock;
+  const int64_t row = static_cast<int64_t>(b) * a.heads + h;  // the cache row
+  int len = a.seq_lens[b];
+  len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+  const int nb = (len + kBlock - 1) / kBlock;
+  const int blk_begin = split * a.bps;
+  if (blk_begin >= nb) {  // uniform over the workgroup
+    // an empty row has no split to merge: in fused mode split 0 writes its zeros
+    if (a.fused && nb == 0 && split == 0)
+      for (int t = threadIdx.x; t < G * D; t += kSplitWaves * kWave) a.out[row * G * D + t] = 0;
+    return;
+  }
+  const int blk_end = min(blk_begin + a.bps, nb);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r16 = lane % 16;  // A row / output column of this lane
+  const int grp = lane / 16;  // 8-element K group of this lane's fragments; its output rows / 4
+
+  {  // this wave's P images: rows G..15 stay zero
+    uint4* img = reinterpret_cast<uint4*>(&pimg[wave][0][0][0][0][0]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) img[lane + k * kWave] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // Query operand: row g < G holds query g in slot order, x16 slots pre-divided by 16.
+  half8_t aq[KS];
+  {
+    const uint16_t* qrow = a.q + (row * G + min(r16, G - 1)) * D;
+    const float keep = r16 < G ? 1.0f : 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint16_t bits = qrow[32 * ks + 8 * grp + slot_nibble(j)];
+        float x = static_cast<float>(__builtin_bit_cast(_Float16, bits)) * keep;
+        if (j & 2) x *= 0.0625f;
+        aq[ks][j] = static_cast<_Float16>(x);
+      }
+  }
+
+  const int row_bytes = kPaged ? kRegionBytes : a.max_blocks * kRegionBytes;
+  const int64_t row_base = kPaged ? 0 : row * row_bytes;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.k_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.v_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
+  const int lane_off = lane * 16;
+  const int64_t sbase = kPaged ? 0 : row * a.max_blocks;
+  const float* ks_ptr = a.k_scale + sbase;
+  const float* vs_ptr = a.v_scale + sbase;
+
+  float o[NTV][4];
+#pragma unroll
+  for (int n = 0; n < NTV; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[n][i] = 0.0f;
+  float m[4], l[4];  // per output row 4 * grp + i: running max (base 2), lane's weight sum
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -__builtin_inff();
+    l[i] = 0.0f;
+  }
+
+  auto load_codes = [&](bool is_v, int blk, int slot, uint4 (&r)[LOADS]) {
+    if constexpr (kPaged) {
+      const __amdgpu_buffer_rsrc_t rs =
+          region_rsrc(is_v ? a.v_codes : a.k_codes, slot, kRegionBytes);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) r[i] = load_stream(rs, lane_off, i * kWave * 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        r[i] = load_stream(is_v ? vrsrc : krsrc, lane_off, blk * kRegionBytes + i * kWave * 16);
+    }
+  };
+  auto slot_of = [&](int blk) {
+    return kPaged ? static_cast<int>(block_slot(a.block_table, a.num_pages, a.heads,
+                                                a.max_blocks, b, h, blk))
+                  : blk;
+  };
+
+  // Scores of the block's 64 tokens for the lane's rows, the per-row online-softmax
+  // update, and the weights p[nt][i] (token 16 nt + r16, row 4 grp + i).
+  auto block_weights = [&](int blk, float kscale, const uint4 (&kr)[LOADS], float (&p)[4][4]) {
+    const float sk = kscale * a.qk_scale * 1024.0f;  // operands carry 2^-10
+    float4_t acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            aq[ks], int4_operand(dword_of(kr, nt * KS + ks)), acc[nt], 0, 0, 0);
+    float s[4][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[nt][i] = acc[nt][i] * sk;
+    if (blk == nb - 1) {  // tokens past the length in the last block weigh nothing
+      const int valid = len - blk * kBlock;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        if (16 * nt + r16 >= valid) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[nt][i] = -__builtin_inff();
+        }
+    }
+    float mb[4];
+    bool raise = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mb[i] = row16_max(fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i])));
+      raise |= mb[i] > m[i];
+    }
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // some row's max rose
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mn = fmaxf(m[i], mb[i]);
+        const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);
+        l[i] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NTV; ++n) o[n][i] *= alpha;
+        m[i] = mn;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[nt][i] = __builtin_amdgcn_exp2f(s[nt][i] - m[i]);
+        l[i] += p[nt][i];
+      }
+  };
+
+  // o[n][i] += sv * sum_t p_t * c(t, 16 n + r16) for row 4 grp + i.
+  const int p_slot = nibble_slot(r16 & 7);                 // this lane's tokens' slot
+  const float p_unit = (p_slot & 2) ? 1024.0f : 16384.0f;  // x16 slots: 2^14 / 16
+  auto block_accumulate = [&](float vscale, const uint4 (&vr)[LOADS], const float (&p)[4][4]) {
+    const float sv = vscale * (1024.0f / 16384.0f);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int kstep = nt >> 1, kgrp = (nt & 1) * 2 + (r16 >> 3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+        if (r < G) {
+          const float x = p[nt][i] * p_unit;
+          const _Float16 hi = static_cast<_Float16>(x);
+          pimg[wave][0][kstep][kgrp][r][p_slot] = hi;
+          pimg[wave][1][kstep][kgrp][r][p_slot] = static_cast<_Float16>(x - static_cast<float>(hi));
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const half8_t ah0 = *reinterpret_cast<const half8_t*>(&pimg[wave][0][0][grp][r16][0]);
+    const half8_t ah1 = *reinterpret_cast<const half8_t*>(&pimg[wave][0][1][grp][r16][0]);
+    const half8_t al0 = *reinterpret_cast<const half8_t*>(&pimg[wave][1][0][grp][r16][0]);
+    const half8_t al1 = *reinterpret_cast<const half8_t*>(&pimg[wave][1][1][grp][r16][0]);
+#pragma unroll
+    for (int n = 0; n < NTV; ++n) {
+      const half8_t v0 = int4_operand(dword_of(vr, 2 * n));
+      const half8_t v1 = int4_operand(dword_of(vr, 2 * n + 1));
+      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah0, v0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah1, v1, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al0, v0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al1, v1, acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[n][i] = __builtin_fmaf(sv, acc[i], o[n][i]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  float p[4][4];
+  stream_wave_blocks<LOADS>(
+      blk_begin, blk_end, wave, lane, row,
+      [&](int blk) {
+        const int j = slot_of(blk);
+        return ScaleParams{ks_ptr[j], vs_ptr[j], j};
+      },
+      [&](bool is_v, int blk, const ScaleParams& ps, int j, uint4 (&r)[LOADS]) {
+        load_codes(is_v, blk, kPaged ? lane_int(ps.slot, j) : 0, r);
+      },
+      [&](int blk, const ScaleParams& pb, const uint4 (&kr)[LOADS]) {
+        block_weights(blk, pb.ks, kr, p);
+      },
+      [&](int, const ScaleParams& pb, const uint4 (&vr)[LOADS]) {
+        block_accumulate(pb.vs, vr, p);
+      });
+
+  // The waves' states per row through LDS (a wave with no block has m = -inf, l = o = 0).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * grp + i;
+    const float lr = row16_sum(l[i]);
+    if (r < G) {
+      if (r16 == 0) {
+        red_l[wave][r] = lr;
+        red_m[wave][r] = m[i];
+      }
+#pragma unroll
+      for (int n = 0; n < NTV; ++n) red_o[wave][r][16 * n + r16] = o[n][i];
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves per (row, channel), then finish as the one-query kernel does, for all
+  // G output rows of the cache row (one arrival ticket per cache row).
+  const int n_row = (nb + a.bps - 1) / a.bps;
+  const int64_t qrow0 = row * G;  // first output row
+  constexpr int kThreadsWg = kSplitWaves * kWave;
+  auto merged = [&](int g, int d, float& M, float& L) {
+    M = red_m[0][g];
+#pragma unroll
+    for (int w = 1; w < kSplitWaves; ++w) M = fmaxf(M, red_m[w][g]);
+    float od = 0.0f;
+    L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+      const float alpha = __builtin_amdgcn_exp2f(red_m[w][g] - M);
+      od = __builtin_fmaf(alpha, red_o[w][g][d], od);
+      L = __builtin_fmaf(alpha, red_l[w][g], L);
+    }
+    return od;
+  };
+  if (a.fused && n_row == 1) {
+    for (int t = threadIdx.x; t < G * D; t += kThreadsWg) {
+      float M, L;
+      const float od = merged(t / D, t % D, M, L);
+      a.out[qrow0 * D + t] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(od / L));
+    }
+    return;
+  }
+  for (int t = threadIdx.x; t < G * D; t += kThreadsWg) {
+    const int g = t / D, d = t % D;
+    float M, L;
+    const float od = merged(g, d, M, L);
+    float* po = a.ws_o + ((qrow0 + g) * a.n_split + split) * D;
+    float* ml = a.ws_ml + ((qrow0 + g) * a.n_split + split) * 2;
+    if (a.fused) {
+      store_shared(po + d, od);
+      if (d == 0) {
+        store_shared(ml, M);
+        store_shared(ml + 1, L);
+      }
+    } else {
+      po[d] = od;
+      if (d == 0) {
+        ml[0] = M;
+        ml[1] = L;
+      }
+    }
+  }
+  if (!a.fused) return;
+  __shared__ uint32_t ticket;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores completed
+  __syncthreads();
+  // system scope: the read-modify-write is performed at memory, past the per-XCD L2s
+  if (threadIdx.x == 0)
+    ticket = __hip_atomic_fetch_add(a.counters + row, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  if (ticket == static_cast<uint32_t>(n_row - 1)) {
+    for (int t = threadIdx.x; t < G * D; t += kThreadsWg)
+      merge_row<D, true>(a, qrow0 + t / D, n_row, t % D);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(a.counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 // ---- combine kernel: grid (heads, batch), D threads ---------------------------------
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
@@ -995,6 +1306,32 @@ hipError_t launch_attn_split(int scheme, int head_dim, int batch, const AttnArgs
 hipError_t launch_decode_step(int scheme, int head_dim, int batch, const AttnArgs& a,
                               hipStream_t s) {
   return launch<true>(scheme, head_dim, batch, a, s);
+}
+
+namespace {
+template <int D, int G>
+hipError_t gqa_t(int batch, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.n_split, a.heads, batch);
+  dim3 block(kSplitWaves * kWave);
+  if (a.block_table)
+    hipLaunchKernelGGL((attn_split_int4_gqa_kernel<D, G, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_split_int4_gqa_kernel<D, G, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+template <int D>
+hipError_t gqa_d(int group, int batch, const AttnArgs& a, hipStream_t s) {
+  switch (group) {
+    case 2: return gqa_t<D, 2>(batch, a, s);
+    case 4: return gqa_t<D, 4>(batch, a, s);
+    default: return gqa_t<D, 8>(batch, a, s);
+  }
+}
+}  // namespace
+
+hipError_t launch_attn_gqa(int head_dim, int group, int batch, const AttnArgs& a,
+                           hipStream_t s) {
+  return head_dim == 128 ? gqa_d<128>(group, batch, a, s) : gqa_d<64>(group, batch, a, s);
 }
 
 hipError_t launch_attn_combine(int head_dim, int batch, const AttnArgs& a, hipStream_t s) {

@@ -7,7 +7,9 @@ from it without sharing any of the method.
 Shapes follow the workloads on the pages: Llama-2-7B-shaped heads (32 heads of 128
 channels, 32 layers) as in page "DeepSeek-R1推理延迟骤降41.8%？…" §2.1; batch 8 at
 context 8192 as in page "第一章：DeepSeek R1推理模型性能跃迁全景概览" chapter 1's deployment
-table; batch 16 at 32K context as in that page's §2.3 table.
+table; batch 16 at 32K context as in that page's §2.3 table. The grouped-query workload
+(64 query heads over 8 cached heads) stands for decoding with shared cached heads
+(page "DeepSeek R1性能优化有哪些技巧" §二: MLA decodes as multi-query attention).
 
 Recipe (every draw from numpy PCG64 seeded by SeedSequence([SEED, workload index,
 layer, stream id, sequence])):
@@ -51,6 +53,7 @@ class Workload:
     layers: int = 1
     decode_steps: int = 0   # tokens appended per sequence, one per decode step
     ragged: tuple = None    # (lo, hi) inclusive range of per-sequence lengths
+    group: int = 1          # query heads per cached head (grouped-query attention)
 
     @property
     def max_len(self):
@@ -73,6 +76,10 @@ WORKLOADS = [
     Workload(4, "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4", 8, 32, 128, 8192,
              INT4_SYM, "student_t3_half", "student_t3_half", layers=32,
              ragged=(1024, 8192)),
+    # grouped-query decode: 64 query heads over 8 cached heads (a Llama-2-70B-shaped
+    # layer), the cache of the 8K workloads' shape otherwise
+    Workload(5, "llama70b_gqa8_b8_h8_d128_ctx8k_int4", 8, 8, 128, 8192, INT4_SYM,
+             "normal_outliers", "normal_outliers", group=8),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -122,9 +129,9 @@ def appended_kv(w, layer, seq, which, n_steps=None):
 
 
 def query(w, layer, step=0):
-    """float16 [B][H][D] query for one decode step of one layer."""
+    """float16 [B][H * group][D] query for one decode step of one layer."""
     g = rng(w, layer, STREAM_Q, step)
-    return draw(g, "normal0", (w.batch, w.heads, w.head_dim))
+    return draw(g, "normal0", (w.batch, w.heads * w.group, w.head_dim))
 
 
 def lengths(w):

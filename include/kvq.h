@@ -231,6 +231,28 @@ int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new
                     float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                     int32_t max_len_after, int32_t blocks_per_split, void* stream);
 
+/* Grouped-query decode attention (several query heads share each cached head, as in
+ * multi-query and grouped-query attention): query head hq = h * group + g of sequence b
+ * attends over cache row (b, h), for g < group. The result is decode_attn_qkv's for
+ * each query head against its cache row (same definition, splits and merge); the
+ * codes of a block are turned into matrix-core operands once for all `group` queries.
+ * (Decode attention as in decode_attn_qkv with cached heads shared between query
+ * heads: MLA with its projections absorbed decodes as multi-query attention, [Pg3] §二.)
+ *   q, out    : fp16 [B][H * group][D] contiguous, 16-byte aligned.
+ *   group     : 1 (exactly decode_attn_qkv), 2, 4 or 8 (KVQ_EINVAL otherwise); values
+ *               above 1 need KVQ_INT4_SYM (KVQ_ENOTSUP otherwise).
+ *   workspace : >= decode_attn_gqa_workspace_bytes(cache, group, max_len,
+ *               blocks_per_split) bytes (one arrival counter per cache row, partial
+ *               states per query row); zero counters before first use, left zero.
+ * Other arguments as decode_attn_qkv. Returns KVQ_OK or a negative kvq_status. */
+int decode_attn_gqa(const kvq_cache* cache, const void* q, int32_t group, float softmax_scale,
+                    void* out, void* workspace, size_t workspace_bytes, int32_t max_len,
+                    int32_t blocks_per_split, void* stream);
+
+/* Bytes of device workspace decode_attn_gqa needs (0 on invalid arguments). */
+size_t decode_attn_gqa_workspace_bytes(const kvq_cache* cache, int32_t group, int32_t max_len,
+                                       int32_t blocks_per_split);
+
 /* Human-readable text of a kvq_status (static storage). */
 const char* kvq_strerror(int status);
 

@@ -122,6 +122,28 @@ def test_paged_layout_rules():
     assert rc_step(cache(B=1, H=1, MB=4, block_table=FAKE, num_pages=0)) == EINVAL
 
 
+def rc_gqa(c, q=FAKE, group=2, out=FAKE, ws=FAKE, ws_bytes=1 << 30, max_len=100, bps=0):
+    return kvq.load_library().decode_attn_gqa(ctypes.byref(c), q, group, 0.1, out, ws, ws_bytes,
+                                              max_len, bps, None)
+
+
+@no_gpu_only
+def test_grouped_query_rules():
+    assert rc_gqa(cache(), group=3) == EINVAL
+    assert rc_gqa(cache(), group=16) == EINVAL
+    assert rc_gqa(cache(), group=0) == EINVAL
+    assert rc_gqa(cache(scheme=1), group=2) == ENOTSUP      # int4 only
+    assert rc_gqa(cache(), q=FAKE + 2) == EALIGN
+    assert rc_gqa(cache(), out=0) == EINVAL
+    c = cache(B=2, H=4, D=128, MB=3)
+    need = kvq.decode_attn_gqa_workspace_bytes(c, 4, 192, 1)
+    assert need == 256 + 2 * 4 * 4 * 3 * (128 + 2) * 4     # partial states per query row
+    assert kvq.decode_attn_gqa_workspace_bytes(c, 1, 192, 1) == \
+        kvq.decode_attn_workspace_bytes(c, 192, 1)
+    assert rc_gqa(c, group=4, ws_bytes=need - 1, max_len=192, bps=1) == EWS
+    assert rc_gqa(c, group=4, max_len=193) == ECAP
+
+
 @no_gpu_only
 def test_workspace_rules():
     c = cache(B=2, H=4, D=128, MB=3)
