@@ -25,6 +25,9 @@ them under "workloads":
     outside the timed region);
   * the 32-layer ragged workload: one step is decode_attn_qkv over each of the 32
     layers' caches (per-sequence lengths 1024..8192, no append in this workload).
+  * the grouped-query workload (64 query heads over 8 cached heads, batch 8, context
+    8192): one step is decode_attn_gqa over one of the rotated cache copies;
+  * the headline decode step again on paged caches (shuffled page pools).
 
 Prints one JSON line. --profile-loop runs only the timed loop of --workload (for
 rocprofv3), --copy-probe times a plain device copy of known size (the calibration
@@ -50,7 +53,7 @@ EVENT_STRIDE = 8               # HIP events around every 8th attention launch wh
                                # adds ~5 us to its step
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 OTHERS = ("llama7b_b8_h32_d128_ctx8k_uint8", "long_b16_h32_d128_ctx32k_append64_int4",
-          "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4")
+          "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4", "llama70b_gqa8_b8_h8_d128_ctx8k_int4")
 
 
 def parse():
@@ -82,14 +85,15 @@ def code_bytes_per_token(w):
 
 
 def attention_bytes(w, lens):
-    """Algorithmic bytes of one decode_attn_qkv call: K and V codes of the valid
-    tokens, their block scales (and zero points for uint8), q and out."""
+    """Algorithmic bytes of one decode_attn_qkv (decode_attn_gqa) call: K and V codes of
+    the valid tokens, their block scales (and zero points for uint8), q and out (one
+    row per query head)."""
     per_block_scalars = 2 * (2 if w.scheme == 1 else 1) * 4
     total = 0
     for n in lens:
         nb = (int(n) + 63) // 64
         total += w.heads * (2 * int(n) * code_bytes_per_token(w) + nb * per_block_scalars)
-    total += 2 * w.batch * w.heads * w.head_dim * 2  # q in, out
+    total += 2 * w.batch * w.heads * w.group * w.head_dim * 2  # q in, out
     return total
 
 
@@ -368,6 +372,65 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_in
     return res, host_cache
 
 
+def run_gqa(kvq, torch, w, steps, warmup, bps, paged=False):
+    """Grouped-query workload: one step is decode_attn_gqa (w.group query heads per
+    cached head) over one of enough cache copies (>= CACHE_BYTES_TARGET in all) that the
+    Infinity Cache cannot hold them; lengths fixed at the context (no append)."""
+    wl = wl_mod()
+    B, H, D, G = w.batch, w.heads, w.head_dim, w.group
+    lens = wl.lengths(w)
+    L = int(lens.max())
+    per_cache = 2 * B * H * L * code_bytes_per_token(w)
+    copies = max(1, math.ceil(CACHE_BYTES_TARGET / per_cache))
+    t_setup = time.perf_counter()
+    caches, prefill_ms = quantized_copies(kvq, torch, w, 0, lens, w.max_blocks, copies, False,
+                                          paged)
+    q = torch.from_numpy(wl.query(w, 0)).cuda()
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(kvq.decode_attn_gqa_workspace_bytes(caches[0], G, L, bps), 16),
+                     dtype=torch.uint8, device="cuda")
+    sm = wl.softmax_scale(w)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    timer = Timer(torch)
+
+    def run(n):
+        for j in range(n):
+            kvq.decode_attn_gqa(caches[j % copies], q, G, sm, out, ws, L, bps)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0 = timer.event()
+    run(steps)
+    timer.segments.append((t0, timer.event()))
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - wall0
+    total_ms = timer.total_ms()
+    per_launch = attention_bytes(w, lens)
+    bps_eff, n_split = kvq.decode_attn_plan(caches[0], L, bps)
+    res = {
+        "workload": w.name,
+        "step": f"decode_attn_gqa ({G} query heads per cached head)",
+        "kernel": f"attn_split_int4_gqa_kernel<{D}, {G}, {'true' if paged else 'false'}>",
+        "layout": "paged (block table over a shuffled page pool)" if paged else "dense",
+        "steps": steps, "warmup": warmup,
+        "ms_per_step": total_ms / steps,
+        "gbs": per_launch * steps / (total_ms / 1e3) / 1e9,
+        "tokens_per_s": B * steps / (total_ms / 1e3),
+        "kernel_avg_us": total_ms / steps * 1e3,
+        "kernel_gbs": per_launch / (total_ms / steps / 1e3) / 1e9,
+        "kernel_bytes_per_launch": float(per_launch),
+        "kernel_timing": "timed segment / launches (one launch per step)",
+        "context": [L, L], "cache_copies_rotated": copies,
+        "blocks_per_split": bps_eff, "splits_per_row": n_split,
+        "prefill_quantize_ms": float(np.median(prefill_ms)),
+        "host_wall_s": wall_s, "setup_s": setup_s,
+    }
+    res["kernel_frac"] = res["kernel_gbs"] / HBM_PEAK_GBS
+    return res
+
+
 def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
     """The 32-layer ragged workload: one step is decode_attn_qkv over every layer's
     cache, each layer with its own K, V and query."""
@@ -443,6 +506,8 @@ def measure(kvq, torch, w, steps, warmup, bps, keep_host=False, device_inputs=Fa
             separate=False, paged=False):
     if w.layers > 1:
         res = run_layers(kvq, torch, w, steps, warmup, bps, device_inputs), None
+    elif w.group > 1:
+        res = run_gqa(kvq, torch, w, steps, warmup, bps, paged), None
     else:
         res = run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs,
                                    separate, paged)
