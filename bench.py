@@ -574,7 +574,7 @@ def main():
                    "splits_per_row": res["splits_per_row"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm",
                      "kernel": res["kernel"] + (" (decode_step_qkv: append + attention)"
-                                                if fused else " (decode_attn_qkv)"),
+                                                if fused else f" ({res['step']})"),
                      "achieved": res["kernel_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": res["kernel_gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic() if w.name == HEADLINE and fused else None,
