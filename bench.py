@@ -490,6 +490,36 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
         "host_wall_s": wall_s, "setup_s": setup_s,
     }
     res["kernel_frac"] = res["kernel_gbs"] / HBM_PEAK_GBS
+    res.update(graph_step(torch, w, caches, queries, sm, steps, warmup, bps, step))
+    return res
+
+
+def graph_step(torch, w, caches, queries, sm, steps, warmup, bps, eager_step):
+    """The same 32-layer step captured once as a HIP graph (one replay per step) against
+    the eager calls: GPU time per step (HIP events around the timed segment) and host
+    time to queue one step."""
+    from decode_attention_block_amd.graph import DecodeGraph
+    dg = DecodeGraph(caches, sm, append=False, blocks_per_split=bps)
+    for i, q in enumerate(queries):
+        dg.q[i].copy_(q)
+    for _ in range(warmup):
+        dg.replay()
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in (("graph", dg.replay), ("eager", lambda: eager_step(True))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        host = 0.0
+        e0.record()
+        for _ in range(steps):
+            h0 = time.perf_counter()
+            fn()
+            host += time.perf_counter() - h0
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{name}_ms_per_step"] = e0.elapsed_time(e1) / steps
+        res[f"{name}_host_us_per_step"] = host / steps * 1e6
+    res["graph"] = (f"{w.layers} decode_attn_qkv calls captured as one HIP graph "
+                    f"(host bound fixed at the capacity, {caches[0].capacity} tokens)")
     return res
 
 
@@ -580,6 +610,7 @@ def main():
                      "traffic": measured_traffic() if w.name == HEADLINE and fused else None,
                      "avg_kernel_us": res["kernel_avg_us"], "timing": res["kernel_timing"],
                      "algorithmic_bytes_per_launch": res["kernel_bytes_per_launch"]},
+        "graph_step": {k: res[k] for k in res if k.startswith(("graph", "eager"))} or None,
         "prefill_quantize": {"ms": res.get("prefill_quantize_ms"),
                              "gbs": res.get("prefill_quantize_gbs")},
         "host_wall_s": res["host_wall_s"],
