@@ -438,6 +438,12 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
     B, H, D = w.batch, w.heads, w.head_dim
     lens = wl.lengths(w)
     L = int(lens.max())
+    plan_note = "automatic"
+    if bps == 0 and w.ragged is not None:
+        # a ragged batch: the caller, who knows it, splits rows at about half the
+        # longest one, so the longest rows share their blocks between workgroups
+        bps = ((L + 63) // 64 + 1) // 2
+        plan_note = "half the longest row (chosen by the caller for a ragged batch)"
     t_setup = time.perf_counter()
     caches, prefill_ms, queries = [], [], []
     for layer in range(w.layers):
@@ -485,7 +491,7 @@ def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
         "kernel_bytes_per_launch": float(per_launch),
         "kernel_timing": "timed segment / launches (one launch per layer)",
         "context": [int(lens.min()), L], "mean_context": float(lens.mean()),
-        "blocks_per_split": bps_eff, "splits_per_row": n_split,
+        "blocks_per_split": bps_eff, "splits_per_row": n_split, "plan": plan_note,
         "prefill_quantize_ms_per_layer": float(np.median(prefill_ms)),
         "host_wall_s": wall_s, "setup_s": setup_s,
     }
