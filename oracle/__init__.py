@@ -17,6 +17,7 @@ from . import build as _build
 BLOCK = 64
 INT4_SYM = 0
 UINT8_ASYM = 1
+FP8_E4M3 = 2
 
 _lib = None
 
@@ -40,6 +41,10 @@ def lib():
         L.oracle_attention.argtypes = [i32] * 5 + [P] * 6 + [P, P, ctypes.c_double, i64,
                                                              i64, P]
         L.oracle_attention.restype = ctypes.c_int
+        L.oracle_e4m3_code.argtypes = [P, P, i64]
+        L.oracle_e4m3_code.restype = None
+        L.oracle_e4m3_value.argtypes = [P, P, i64]
+        L.oracle_e4m3_value.restype = None
         _lib = L
     return _lib
 
@@ -57,6 +62,22 @@ def half_to_float(bits):
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     out = np.empty(bits.shape, dtype=np.float32)
     lib().oracle_half_to_float(_ptr(bits), _ptr(out), bits.size)
+    return out
+
+
+def e4m3_code(x):
+    """float32 array -> uint8 FP8 E4M3 codes (nearest, ties to even, saturating)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().oracle_e4m3_code(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def e4m3_value(codes):
+    """uint8 FP8 E4M3 codes -> float64 values."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    lib().oracle_e4m3_value(_ptr(codes), _ptr(out), codes.size)
     return out
 
 
@@ -143,7 +164,7 @@ def attention(cache, q, lens, sm_scale, rows=None):
 def dequantize(cache, b, h, length):
     """Dequantized K^ and V^ (float64 [length][D]) of row (b, h), straight from the
     cache layout: int4 (nibble - 8)*s with offset-binary nibbles (low nibble = even
-    channel), uint8 (c - zp)*s."""
+    channel), uint8 (c - zp)*s, FP8 E4M3 value(c)*s."""
     c = cache
     D = c["D"]
     nb = (length + BLOCK - 1) // BLOCK
@@ -156,6 +177,8 @@ def dequantize(cache, b, h, length):
             vals[:, 0::2] = (codes & 0x0F).astype(np.int64) - 8
             vals[:, 1::2] = (codes >> 4).astype(np.int64) - 8
             out.append(vals.astype(np.float64) * s[:, None])
+        elif c["scheme"] == FP8_E4M3:
+            out.append(e4m3_value(codes) * s[:, None])
         else:
             z = np.repeat(c[which + "_zero"][b, h, :nb].astype(np.float64), BLOCK)[:length]
             out.append((codes.astype(np.float64) - z[:, None]) * s[:, None])

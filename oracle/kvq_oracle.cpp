@@ -14,6 +14,7 @@
 //         and its quantize_block generator: 4-bit codes, one scale per 64-token block
 //         equal to the block's absolute maximum divided by 7.5, codes rounded and
 //         clamped to [-8, 7].
+//   [Pg3] "DeepSeek R1性能优化有哪些技巧" (ddd.cn), §一 "精度与量化": an FP8 KV cache.
 //   Attention itself is not written out on the pages; the plain definition used here is
 //   textbook scaled dot-product attention (Vaswani et al., 2017) over the dequantized
 //   cache, for one query token.
@@ -33,7 +34,12 @@
 //   * bytes of tokens at or past the length inside the last block are 0;
 //   * cache layout: codes [B][H][max_blocks][64][D/2 or D] bytes, scales and zero
 //     points [B][H][max_blocks] binary32;
-//   * a row of length 0 attends to nothing; its output is defined as all zeros.
+//   * a row of length 0 attends to nothing; its output is defined as all zeros;
+//   * the FP8 scheme (the pages name FP8 KV without its scaling) mirrors the 4-bit
+//     one: per 64-token block s = absmax / 448 (448 = the largest finite E4M3
+//     magnitude), code = the E4M3 value nearest to x / s (ties to even mantissa, the
+//     sign kept, so -0 and negative values that round to zero give 0x80), 0 when s = 0;
+//     one byte per channel, [token][channel].
 //
 // Build: g++ -std=c++17 -O2 -fPIC -shared -ffp-contract=off (no fast-math), x86-64 SSE
 // arithmetic (binary32 operations round once, to nearest-even).
@@ -148,11 +154,70 @@ void quantize_block_uint8(RowIn x, int first, int ntok, int D, uint8_t* codes,
   *zero = zp;
 }
 
+// ---- 8-bit floating-point block: FP8 E4M3 ([Pg3] §一) ------------------------------
+// E4M3 ("fn" variant of the OCP 8-bit floating-point formats): 1 sign bit, 4 exponent
+// bits with bias 7, 3 fraction bits. Exponent field 0 encodes (m/8) * 2^-6; otherwise
+// (1 + m/8) * 2^(e-7). S.1111.111 is NaN, there are no infinities, so the largest
+// finite magnitude is 1.75 * 2^8 = 448 (code 0x7E).
+double e4m3_value(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  const double v = (e == 0) ? std::ldexp(m / 8.0, -6) : std::ldexp(1.0 + m / 8.0, e - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+// The code of the finite E4M3 value nearest to q (|q| finite): the 127 non-negative
+// finite codes are searched in order, a tie goes to the even code (whose fraction is
+// even), and the sign bit is q's. Beyond 448 the nearest finite value is 448.
+uint8_t e4m3_code(float q) {
+  const double a = std::fabs(static_cast<double>(q));
+  int best = 0;
+  double best_d = a;  // distance to code 0 (value 0)
+  for (int c = 1; c <= 0x7E; ++c) {
+    const double d = std::fabs(e4m3_value(static_cast<uint8_t>(c)) - a);
+    if (d < best_d || (d == best_d && c % 2 == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return static_cast<uint8_t>(best | (std::signbit(q) ? 0x80 : 0));
+}
+
+void quantize_block_fp8(RowIn x, int first, int ntok, int D, uint8_t* codes, float* scale,
+                        float* zero) {
+  // step 1: the block's absolute maximum over its valid tokens and all channels
+  float a = 0.0f;
+  for (int t = 0; t < ntok; ++t)
+    for (int d = 0; d < D; ++d) {
+      const float v = std::fabs(half_to_f32(x.p[(first + t) * x.st + d]));
+      if (v > a) a = v;
+    }
+  // step 2: scale = absmax / 448 (one binary32 division)
+  const float s = (a == 0.0f) ? 0.0f : a / 448.0f;
+  // step 3: code = nearest E4M3 value of x / s (0 when s = 0), one byte per channel
+  std::memset(codes, 0, static_cast<size_t>(kBlock) * D);
+  for (int t = 0; t < ntok; ++t)
+    for (int d = 0; d < D; ++d)
+      codes[t * D + d] =
+          (s == 0.0f) ? 0 : e4m3_code(half_to_f32(x.p[(first + t) * x.st + d]) / s);
+  *scale = s;
+  *zero = 0.0f;
+}
+
+void quantize_block(int scheme, RowIn x, int first, int ntok, int D, uint8_t* codes,
+                    float* scale, float* zero) {
+  if (scheme == 0)
+    quantize_block_int4(x, first, ntok, D, codes, scale, zero);
+  else if (scheme == 1)
+    quantize_block_uint8(x, first, ntok, D, codes, scale, zero);
+  else
+    quantize_block_fp8(x, first, ntok, D, codes, scale, zero);
+}
+
 int row_bytes(int scheme, int D) { return scheme == 0 ? D / 2 : D; }
 
 bool shape_ok(int scheme, int B, int H, int D, int max_blocks) {
-  return (scheme == 0 || scheme == 1) && B > 0 && H > 0 && D > 0 && D % 2 == 0 &&
-         max_blocks > 0;
+  return (scheme == 0 || scheme == 1 || scheme == 2) && B > 0 && H > 0 && D > 0 &&
+         D % 2 == 0 && max_blocks > 0;
 }
 
 // Dequantized value of channel d of token t in block j of row r (binary64, exact).
@@ -166,6 +231,7 @@ double dequant(int scheme, int D, int max_blocks, const uint8_t* codes, const fl
     const int nib = (d % 2 == 0) ? (row[d / 2] & 0x0F) : (row[d / 2] >> 4);
     return static_cast<double>(nib - 8) * s;  // offset-binary nibble
   }
+  if (scheme == 2) return e4m3_value(row[d]) * s;
   return (static_cast<double>(row[d]) - static_cast<double>(zero[blk])) * s;
 }
 
@@ -173,7 +239,16 @@ double dequant(int scheme, int D, int max_blocks, const uint8_t* codes, const fl
 
 extern "C" {
 
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }
+
+// FP8 E4M3 codes of binary32 values (nearest, ties to even, saturating) and the values
+// of codes (binary64, exact).
+void oracle_e4m3_code(const float* in, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_code(in[i]);
+}
+void oracle_e4m3_value(const uint8_t* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_value(in[i]);
+}
 
 // binary16 bit patterns -> binary32 values (exact).
 void oracle_half_to_float(const uint16_t* in, float* out, int64_t n) {
@@ -212,10 +287,7 @@ int oracle_quantize_cache(int scheme, int B, int H, int D, int max_blocks,
           uint8_t* out = codes + blk * kBlock * rb;
           float zdummy;
           float* zp = zero ? zero + blk : &zdummy;
-          if (scheme == 0)
-            quantize_block_int4(x, first, ntok, D, out, scale + blk, zp);
-          else
-            quantize_block_uint8(x, first, ntok, D, out, scale + blk, zp);
+          quantize_block(scheme, x, first, ntok, D, out, scale + blk, zp);
         }
       }
     }
@@ -250,10 +322,7 @@ int oracle_append(int scheme, int B, int H, int D, int max_blocks, const uint16_
         float* zero = tensor == 0 ? k_zero : v_zero;
         float zdummy;
         float* zp = zero ? zero + blk : &zdummy;
-        if (scheme == 0)
-          quantize_block_int4(x, first, ntok, D, out, scale, zp);
-        else
-          quantize_block_uint8(x, first, ntok, D, out, scale, zp);
+        quantize_block(scheme, x, first, ntok, D, out, scale, zp);
       }
     }
   }

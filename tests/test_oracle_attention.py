@@ -37,7 +37,7 @@ def test_two_token_closed_form():
     assert np.all(o[2:] == 0)
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, oracle.FP8_E4M3])
 def test_length_one_returns_first_value_row(scheme):
     rs = np.random.default_rng(2)
     x = rs.standard_normal((1, 64, 2, 128)).astype(np.float16)
@@ -78,7 +78,8 @@ def test_empty_row_is_zero():
 
 
 @pytest.mark.parametrize("scheme,dist", [(INT4, "normal_outliers"), (UINT8, "normal0.5"),
-                                         (INT4, "student_t3_half")])
+                                         (INT4, "student_t3_half"),
+                                         (oracle.FP8_E4M3, "normal_outliers")])
 def test_matches_torch_sdpa_fp64(scheme, dist):
     torch = pytest.importorskip("torch")
     F = torch.nn.functional
@@ -133,3 +134,21 @@ def test_rows_subset_matches_full():
     full = oracle.attention(c, q, lens, wl.softmax_scale(w))
     part = oracle.attention(c, q, lens, wl.softmax_scale(w), rows=(1, 2))
     assert np.array_equal(part[0, 1], full[0, 1]) and np.isnan(part[0, 0]).all()
+
+
+def test_fp8_dequantization_matches_torch_float8():
+    """FP8 K^ = value(code) * s with value() as torch's float8_e4m3fn decodes the same
+    byte (an independent decoder), for every element of a quantized cache."""
+    torch = pytest.importorskip("torch")
+    w = wl.WORKLOADS[0]
+    g = wl.rng(w, 12, 0, 0)
+    x = wl.draw(g, "normal_outliers", (1, 130, 2, 64))
+    lens = np.array([130], np.int32)
+    c = oracle.quantize_cache(oracle.FP8_E4M3, x, x, lens, 3)
+    for h in range(2):
+        kh, _ = oracle.dequantize(c, 0, h, 130)
+        codes = c["k_codes"][0, h].reshape(-1, 64)[:130]
+        vals = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn)
+        s = np.repeat(c["k_scale"][0, h].astype(np.float64), 64)[:130]
+        ref = vals.to(torch.float64).numpy() * s[:, None]
+        assert np.array_equal(kh, ref)

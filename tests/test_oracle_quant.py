@@ -140,7 +140,7 @@ def test_roundtrip_bound_and_invariants(scheme, dist):
             assert set(codes[blk == mx].tolist()) <= {254, 255}
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, oracle.FP8_E4M3])
 def test_token_permutation_within_block(scheme):
     rs = np.random.default_rng(5)
     x = rs.standard_normal((1, 64, 1, 64)).astype(np.float16)
@@ -173,7 +173,7 @@ def test_int4_matches_listing_expression_in_torch():
             assert f32bits(c["k_scale"][0, h, j]) == f32bits(scale.numpy())
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, oracle.FP8_E4M3])
 def test_append_is_requantized_tail(scheme):
     """Appending token by token (oracle_append) ends in the same cache as quantizing the
     whole history at once, at every length crossed (0->1, 63->64, 64->65, ...)."""
@@ -193,3 +193,83 @@ def test_append_is_requantized_tail(scheme):
         ref = oracle.quantize_cache(scheme, k, v, lens, MB)
         for key in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
             assert np.array_equal(c[key], ref[key]), (key, lens)
+
+
+# ---- FP8 E4M3 (pinned against torch's own float8_e4m3fn conversions) -------------------
+FP8 = oracle.FP8_E4M3
+
+
+def test_e4m3_values_match_torch_float8_on_every_code():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    finite = (codes & 0x7F) != 0x7F
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_value(codes)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.signbit(got[finite]), np.signbit(ref[finite]))
+    # the format's landmarks: 2^-9 (smallest subnormal), 2^-6 (smallest normal), 1, 448
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+
+
+def test_e4m3_code_matches_torch_rounding():
+    """Nearest value, ties to even, sign kept: torch's float32 -> float8_e4m3fn cast on
+    random values over the whole range, every exact value, and every exact midpoint."""
+    torch = pytest.importorskip("torch")
+    rs = np.random.default_rng(11)
+    vals = np.concatenate([
+        rs.standard_normal(20000).astype(np.float32) * np.float32(30),
+        (rs.uniform(-1, 1, 20000) * 2.0 ** rs.integers(-14, 9, 20000)).astype(np.float32),
+        np.float32([0.0, -0.0, 463.9, -463.0, 447.99, 1e-30, -1e-30]),
+    ])
+    finite = oracle.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+    mids = ((finite[1:] + finite[:-1]) / 2).astype(np.float32)
+    vals = np.concatenate([vals, finite.astype(np.float32), mids, -mids])
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_code(vals), ref)
+
+
+def test_e4m3_code_saturates_to_the_largest_finite_value():
+    # the nearest finite value beyond 448 is 448 (torch's cast gives NaN from 480 on)
+    big = np.float32([448.0, 464.0, 480.0, 1000.0, 3.0e38, -500.0])
+    assert oracle.e4m3_code(big).tolist() == [0x7E] * 5 + [0xFE]
+
+
+def test_fp8_block_scale_and_exact_grid():
+    """A block whose values are exactly s times E4M3 values (s = absmax / 448 a power of
+    two) is coded to those values; the scale is absmax / 448 in binary32."""
+    rs = np.random.default_rng(2)
+    codes = rs.integers(0, 0x7F, size=(64, 64)).astype(np.uint8)
+    codes[0, 0] = 0x7E                                   # the block's absmax: 448 * s
+    signs = rs.integers(0, 2, size=codes.shape).astype(np.uint8) << 7
+    codes = codes | signs
+    s = 2.0 ** -6
+    vals = (oracle.e4m3_value(codes) * s).astype(np.float16)
+    assert np.array_equal(vals.astype(np.float64), oracle.e4m3_value(codes) * s)  # exact
+    x = vals.reshape(1, 64, 1, 64)
+    c = oracle.quantize_cache(FP8, x, x, np.array([64], np.int32), 1)
+    assert c["k_scale"][0, 0, 0] == np.float32(s)
+    got = c["k_codes"][0, 0, 0]
+    # -0 values (a zero code with the sign bit) keep their sign
+    assert np.array_equal(got, codes)
+
+
+@pytest.mark.parametrize("dist", DISTS)
+def test_fp8_roundtrip_bound(dist):
+    """Every element is within half a step of its E4M3 grid after scaling: |x/s - v| <=
+    half the gap to the neighbouring values (relative 2^-4, absolute 2^-10 below 2^-6)."""
+    w = wl.WORKLOADS[1]
+    g = wl.rng(w, 98, 0, 0)
+    B, S, H, D = 1, 200, 2, 64
+    x = wl.draw(g, dist, (B, S, H, D))
+    lens = np.array([200], np.int32)
+    c = oracle.quantize_cache(FP8, x, x, lens, 4)
+    for b, h, j, blk in _blocks(x, lens):
+        s = np.float64(c["k_scale"][b, h, j])
+        a = np.abs(blk).max()
+        assert f32bits(c["k_scale"][b, h, j]) == f32bits(np.float32(a) / np.float32(448))
+        kh, _ = oracle.dequantize(c, b, h, lens[b])
+        q = blk.astype(np.float64) / s
+        v = kh[64 * j:64 * j + blk.shape[0]] / s
+        bound = np.maximum(np.abs(q) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6)
+        assert (np.abs(q - v) <= bound).all()
