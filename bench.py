@@ -19,7 +19,7 @@ clocks) run first, from the same prefill lengths, which are restored before timi
 
 The same run also measures the other workloads (unless --headline-only) and reports
 them under "workloads":
-  * the 8K uint8 workload, with the same step and rotation;
+  * the 8K uint8 and FP8 E4M3 workloads, with the same step and rotation;
   * the 32K workload (batch 16, context 32768): its 64-step decode loop of
     decode_step_qkv, repeated from the same prefill (lengths reset between loops,
     outside the timed region);
@@ -52,7 +52,10 @@ EVENT_STRIDE = 8               # HIP events around every 8th attention launch wh
                                # has several launches: a pair of events around a launch
                                # adds ~5 us to its step
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
-OTHERS = ("llama7b_b8_h32_d128_ctx8k_uint8", "long_b16_h32_d128_ctx32k_append64_int4",
+KV_FORMATS = {0: "int4 block-64 symmetric", 1: "uint8 block-64 asymmetric",
+              2: "fp8 e4m3 block-64 scaled"}
+OTHERS = ("llama7b_b8_h32_d128_ctx8k_uint8", "llama7b_b8_h32_d128_ctx8k_fp8",
+          "long_b16_h32_d128_ctx32k_append64_int4",
           "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4", "llama70b_gqa8_b8_h8_d128_ctx8k_int4")
 
 
@@ -535,7 +538,7 @@ def kernel_name(w, fused, paged=False):
     f, p = ("true" if fused else "false"), ("true" if paged else "false")
     if w.scheme == 0:
         return f"attn_split_int4_kernel<{w.head_dim}, {f}, {p}>"
-    return f"attn_split_kernel<1, {w.head_dim}, {f}, {p}>"
+    return f"attn_split_kernel<{w.scheme}, {w.head_dim}, {f}, {p}>"
 
 
 def measure(kvq, torch, w, steps, warmup, bps, keep_host=False, device_inputs=False,
@@ -602,8 +605,7 @@ def main():
         "tokens_per_s": res["tokens_per_s"],
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D,
                    "context": w.context, "context_range_timed": res["context"],
-                   "kv_format": "int4 block-64 symmetric" if w.scheme == 0
-                   else "uint8 block-64 asymmetric",
+                   "kv_format": KV_FORMATS[w.scheme],
                    "step": res["step"], "layout": res.get("layout", "dense"),
                    "cache_copies_rotated": res.get("cache_copies_rotated"),
                    "blocks_per_split": res["blocks_per_split"],

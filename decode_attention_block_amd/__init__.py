@@ -16,6 +16,7 @@ from . import build as _build
 
 INT4_SYM = 0
 UINT8_ASYM = 1
+FP8_E4M3 = 2
 BLOCK_TOKENS = 64
 
 STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_ENOTSUP", -3: "KVQ_ECAPACITY",

@@ -15,7 +15,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int check_cache(const kvq_cache* c) {
   if (!c) return KVQ_EINVAL;
-  if (c->scheme != KVQ_INT4_SYM && c->scheme != KVQ_UINT8_ASYM) return KVQ_EINVAL;
+  if (c->scheme != KVQ_INT4_SYM && c->scheme != KVQ_UINT8_ASYM && c->scheme != KVQ_FP8_E4M3)
+    return KVQ_EINVAL;
   if (c->batch <= 0 || c->heads <= 0 || c->max_blocks <= 0) return KVQ_EINVAL;
   if (c->batch > 32767 || c->heads > 65535) return KVQ_EINVAL;  // launch-grid limits
   if (static_cast<int64_t>(c->max_blocks) * kBlockTokens > INT32_MAX) return KVQ_EINVAL;
@@ -322,7 +323,9 @@ const char* kvq_strerror(int status) {
   switch (status) {
     case KVQ_OK: return "ok";
     case KVQ_EINVAL: return "invalid argument (null pointer, bad scheme, shape, count or length)";
-    case KVQ_ENOTSUP: return "unsupported head_dim (64 and 128 are supported)";
+    case KVQ_ENOTSUP:
+      return "unsupported configuration (head_dim other than 64 or 128, or a size or scheme "
+             "limit of the call)";
     case KVQ_ECAPACITY: return "length bound exceeds the cache capacity (max_blocks * 64)";
     case KVQ_EALIGN: return "pointer or stride breaks the 16-byte alignment rule";
     case KVQ_EWORKSPACE: return "workspace missing or too small";

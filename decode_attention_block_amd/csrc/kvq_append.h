@@ -64,6 +64,9 @@ __device__ __forceinline__ void store_codes(uint8_t* token_row, int chunk, const
   if constexpr (SCHEME == KVQ_INT4_SYM) {
     const uint32_t w = valid ? pack_int4x8(x, s) : 0u;
     *reinterpret_cast<uint32_t*>(token_row + chunk * 4) = w;
+  } else if constexpr (SCHEME == KVQ_FP8_E4M3) {
+    const uint2 w = valid ? pack_fp8x8(x, s) : make_uint2(0u, 0u);
+    *reinterpret_cast<uint2*>(token_row + chunk * 8) = w;
   } else {
     const uint2 w = valid ? pack_uint8x8(x, s, zpi) : make_uint2(0u, 0u);
     *reinterpret_cast<uint2*>(token_row + chunk * 8) = w;
@@ -124,7 +127,7 @@ __device__ __forceinline__ void int4_write_block_from(const _Float16* xs, int nt
 // channels (tid % (D/8)) * 8 .. +7. xs: 2 * kBlock * D fp16 of LDS, 16-byte aligned;
 // red: kAppendStats<SCHEME> * NT / kWave floats of LDS (unused for one wave).
 template <int SCHEME>
-constexpr int kAppendStats = SCHEME == KVQ_INT4_SYM ? 4 : 8;  // old and new, K and V
+constexpr int kAppendStats = SCHEME != KVQ_UINT8_ASYM ? 4 : 8;  // old and new, K and V
 
 // Index of the block that receives the token of row `row` (= b * heads + h) at position
 // len (see block_slot).
@@ -187,7 +190,7 @@ __device__ __forceinline__ void append_stage(const AppendArgs& a, int64_t row, i
         }
       }
     }
-    if constexpr (SCHEME == KVQ_INT4_SYM) {
+    if constexpr (SCHEME != KVQ_UINT8_ASYM) {  // absmax schemes
       st[kv * NS + 0] = amax_o;
       st[kv * NS + 1] = amax_n;
     } else {
@@ -206,9 +209,9 @@ __device__ __forceinline__ void append_stage(const AppendArgs& a, int64_t row, i
   for (int kv = 0; kv < 2; ++kv) {
     const float* sv = st + kv * NS;
     plan[kv].zp = 0.0f;
-    if constexpr (SCHEME == KVQ_INT4_SYM) {
+    if constexpr (SCHEME != KVQ_UINT8_ASYM) {  // absmax schemes
       plan[kv].full = slot == 0 || sv[0] != sv[1];
-      plan[kv].s = int4_scale(sv[1]);
+      plan[kv].s = SCHEME == KVQ_INT4_SYM ? int4_scale(sv[1]) : fp8_scale(sv[1]);
     } else {
       plan[kv].full = slot == 0 || sv[0] != sv[2] || sv[1] != sv[3];
       uint8_scale_zero(-sv[2], sv[3], plan[kv].s, plan[kv].zp);

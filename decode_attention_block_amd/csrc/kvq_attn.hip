@@ -169,9 +169,10 @@ __device__ __forceinline__ float fma_h(_Float16 a, _Float16 b, float c) {
 }
 
 // Partial dot product of one 16-byte code chunk (channels c0 .. c0+31 for int4,
-// c0 .. c0+15 for uint8) with the lane's query, in units of the stored unsigned code u
-// (int4: u = c + 8; uint8: u = c). Code and query are both fp16 operands of
-// v_fma_mix_f32; the products are exact in binary32.
+// c0 .. c0+15 for uint8 and FP8) with the lane's query, in units of the stored unsigned
+// code u (int4: u = c + 8; uint8: u = c; FP8: the code's value itself). Code and query
+// are both fp16 operands of v_fma_mix_f32 (FP8: binary32 values); the products are
+// exact in binary32.
 template <int SCHEME, int D>
 __device__ __forceinline__ float chunk_dot(const uint4& raw, const Query<SCHEME, D>& q) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -196,6 +197,20 @@ __device__ __forceinline__ float chunk_dot(const uint4& raw, const Query<SCHEME,
       hi = fma_h(p3.y, q.at(c + 7), hi);
     }
     return __builtin_fmaf(hi, 1048576.0f, lo * 16777216.0f);
+  } else if constexpr (SCHEME == KVQ_FP8_E4M3) {
+    // the hardware decodes E4M3 codes to binary32 exactly, two per instruction
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[j]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[j]), true);
+      const int c = 4 * j;
+      a0 = __builtin_fmaf(lo[0], static_cast<float>(q.at(c + 0)), a0);
+      a1 = __builtin_fmaf(lo[1], static_cast<float>(q.at(c + 1)), a1);
+      a0 = __builtin_fmaf(hi[0], static_cast<float>(q.at(c + 2)), a0);
+      a1 = __builtin_fmaf(hi[1], static_cast<float>(q.at(c + 3)), a1);
+    }
+    return a0 + a1;
   } else {
     float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
@@ -240,6 +255,18 @@ __device__ __forceinline__ void chunk_axpy(const uint4& raw, float p, half2_t of
       oj[6] = __builtin_fmaf(static_cast<float>(p2.y), p, oj[6]);
       oj[3] = __builtin_fmaf(static_cast<float>(p3.x), p, oj[3]);
       oj[7] = __builtin_fmaf(static_cast<float>(p3.y), p, oj[7]);
+    }
+  } else if constexpr (SCHEME == KVQ_FP8_E4M3) {
+    // FP8 codes carry no offset and decode exactly to binary32
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[j]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[j]), true);
+      float* oj = o + 4 * j;
+      oj[0] = __builtin_fmaf(lo[0], p, oj[0]);
+      oj[1] = __builtin_fmaf(lo[1], p, oj[1]);
+      oj[2] = __builtin_fmaf(hi[0], p, oj[2]);
+      oj[3] = __builtin_fmaf(hi[1], p, oj[3]);
     }
   } else {
 #pragma unroll
@@ -465,8 +492,10 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   const int64_t sbase = kPaged ? 0 : row * a.max_blocks;  // dense: the row's blocks
   const float* ks = a.k_scale + sbase;
   const float* vs = a.v_scale + sbase;
-  const float* kz = a.k_zero + sbase;
-  const float* vz = a.v_zero + sbase;
+  // zero points exist for uint8 only (FP8 caches may have none)
+  constexpr bool kZero = SCHEME == KVQ_UINT8_ASYM;
+  const float* kz = kZero ? a.k_zero + sbase : nullptr;
+  const float* vz = kZero ? a.v_zero + sbase : nullptr;
 
   float o[DPL];
 #pragma unroll
@@ -499,7 +528,8 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   auto block_weights = [&](int blk, float kscale, float kzero, const uint4 (&kr)[TPL],
                            float (&p)[TPL]) {
     const float sk = kscale * a.qk_scale;
-    const float bias_k = (SCHEME == KVQ_INT4_SYM ? 8.0f : kzero) * qsum_row;
+    const float offset = SCHEME == KVQ_INT4_SYM ? 8.0f : SCHEME == KVQ_UINT8_ASYM ? kzero : 0.0f;
+    const float bias_k = offset * qsum_row;
     float s[TPL];
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
@@ -531,8 +561,21 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   };
 
   // o += sum_i p_i * sv * (V code - offset) over the lane's TPL tokens of block blk.
-  auto block_accumulate = [&](float vscale, float vzero, const uint4 (&vr)[TPL],
+  // Tokens past the length weigh 0; their (padding) codes only matter for FP8, where a
+  // byte may decode to NaN and 0 * NaN is NaN: there they are replaced by code 0.
+  auto block_accumulate = [&](int blk, float vscale, float vzero, const uint4 (&vr_in)[TPL],
                               const float (&p)[TPL]) {
+    uint4 vr[TPL];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) vr[i] = vr_in[i];
+    if constexpr (SCHEME == KVQ_FP8_E4M3) {
+      if (blk == nb - 1) {  // wave-uniform
+        const int valid = len - blk * kBlock;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+          if (i * GROUPS + group >= valid) vr[i] = uint4{0u, 0u, 0u, 0u};
+      }
+    }
     const float sv = vscale;
     half2_t off_lo, off_hi;
     if constexpr (SCHEME == KVQ_INT4_SYM) {
@@ -566,7 +609,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
         load_codes(false, sl.tail_blk, slot, kr);
         load_codes(true, sl.tail_blk, slot, vr);
         block_weights(sl.tail_blk, sc.ks, sc.kz, kr, p);
-        block_accumulate(sc.vs, sc.vz, vr, p);
+        block_accumulate(sl.tail_blk, sc.vs, sc.vz, vr, p);
       }
     }
   }
@@ -575,7 +618,8 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
         blk_begin, blk_end, wave, lane, row,
         [&](int blk) {
           const int j = slot_of(blk);
-          return ScaleZeroParams{ks[j], kz[j], vs[j], vz[j], j};
+          if constexpr (kZero) return ScaleZeroParams{ks[j], kz[j], vs[j], vz[j], j};
+          else return ScaleZeroParams{ks[j], 0.0f, vs[j], 0.0f, j};
         },
         [&](bool is_v, int blk, const ScaleZeroParams& ps, int j, uint4 (&r)[TPL]) {
           load_codes(is_v, blk, kPaged ? lane_int(ps.slot, j) : 0, r);
@@ -583,14 +627,14 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
         [&](int blk, const ScaleZeroParams& pb, const uint4 (&kr)[TPL]) {
           block_weights(blk, pb.ks, pb.kz, kr, p);
         },
-        [&](int, const ScaleZeroParams& pb, const uint4 (&vr)[TPL]) {
-          block_accumulate(pb.vs, pb.vz, vr, p);
+        [&](int blk, const ScaleZeroParams& pb, const uint4 (&vr)[TPL]) {
+          block_accumulate(blk, pb.vs, pb.vz, vr, p);
         });
 
   // Per-lane result in true units: o_true[k] = o[k] * unit(k).
 #pragma unroll
   for (int k = 0; k < DPL; ++k) {
-    float unit = 16777216.0f;
+    float unit = SCHEME == KVQ_FP8_E4M3 ? 1.0f : 16777216.0f;
     if constexpr (SCHEME == KVQ_INT4_SYM) unit = (k & 1) ? 1048576.0f : 16777216.0f;
     red_o[wave][lane][k] = o[k] * unit;
   }
@@ -1289,11 +1333,18 @@ hipError_t layout_t(int batch, const AttnArgs& a, hipStream_t s) {
 
 template <bool kAppend>
 hipError_t launch(int scheme, int head_dim, int batch, const AttnArgs& a, hipStream_t s) {
-  if (scheme == KVQ_INT4_SYM)
-    return head_dim == 128 ? layout_t<KVQ_INT4_SYM, 128, kAppend>(batch, a, s)
-                           : layout_t<KVQ_INT4_SYM, 64, kAppend>(batch, a, s);
-  return head_dim == 128 ? layout_t<KVQ_UINT8_ASYM, 128, kAppend>(batch, a, s)
-                         : layout_t<KVQ_UINT8_ASYM, 64, kAppend>(batch, a, s);
+  const bool d128 = head_dim == 128;
+  switch (scheme) {
+    case KVQ_INT4_SYM:
+      return d128 ? layout_t<KVQ_INT4_SYM, 128, kAppend>(batch, a, s)
+                  : layout_t<KVQ_INT4_SYM, 64, kAppend>(batch, a, s);
+    case KVQ_FP8_E4M3:
+      return d128 ? layout_t<KVQ_FP8_E4M3, 128, kAppend>(batch, a, s)
+                  : layout_t<KVQ_FP8_E4M3, 64, kAppend>(batch, a, s);
+    default:
+      return d128 ? layout_t<KVQ_UINT8_ASYM, 128, kAppend>(batch, a, s)
+                  : layout_t<KVQ_UINT8_ASYM, 64, kAppend>(batch, a, s);
+  }
 }
 
 }  // namespace

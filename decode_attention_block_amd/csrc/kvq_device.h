@@ -107,6 +107,43 @@ __device__ __forceinline__ uint32_t uint8_code(float x, float s, int zpi) {
   return static_cast<uint32_t>(c);
 }
 
+// FP8 E4M3 (OCP "fn": bias 7, subnormals (m/8)*2^-6, largest finite 448 = code 0x7E):
+// s = absmax / 448 (0 for an all-zero block); the code of x is the E4M3 value nearest
+// to x / s with ties to the even code, the sign kept, saturating at 448. Every step
+// below is exact but the final rint: scaling by powers of two and subtracting the
+// binade's leading 8.
+__device__ __forceinline__ float fp8_scale(float absmax) {
+  return absmax == 0.0f ? 0.0f : absmax / 448.0f;
+}
+
+__device__ __forceinline__ uint32_t fp8_code(float x, float s) {
+  if (s == 0.0f) return 0u;
+  const float q = x / s;
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  uint32_t c;
+  if (a >= 448.0f) {
+    c = 0x7Eu;
+  } else if (a < 0.015625f) {  // below 2^-6: the subnormal grid, steps of 2^-9
+    c = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));  // 8 is code 0x08 = 2^-6
+  } else {
+    const int e = static_cast<int>((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;
+    const float m = __builtin_rintf(__builtin_ldexpf(a, 3 - e) - 8.0f);  // 0..8
+    c = static_cast<uint32_t>((e + 7) * 8) + static_cast<uint32_t>(m);   // 8 carries
+  }
+  return sign | c;
+}
+
+// 8 consecutive channels -> 8 bytes of FP8 codes.
+__device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], float s) {
+  uint2 r;
+  r.x = fp8_code(x[0], s) | (fp8_code(x[1], s) << 8) | (fp8_code(x[2], s) << 16) |
+        (fp8_code(x[3], s) << 24);
+  r.y = fp8_code(x[4], s) | (fp8_code(x[5], s) << 8) | (fp8_code(x[6], s) << 16) |
+        (fp8_code(x[7], s) << 24);
+  return r;
+}
+
 // 8 consecutive channels -> 4 bytes of int4 nibbles (channel 2k low, 2k+1 high).
 __device__ __forceinline__ uint32_t pack_int4x8(const float (&x)[8], float s) {
   uint32_t w = 0;

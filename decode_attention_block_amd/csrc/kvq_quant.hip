@@ -2,8 +2,10 @@
 //
 // Formats follow page "DeepSeek-R1推理延迟骤降41.8%？独家披露3类硬件感知调度策略" §2.1
 // ("分块量化压缩设计": 4-bit codes, one scale per 64-token block = absmax / 7.5, codes
-// rounded and clamped to [-8, 7]) and page "第一章：DeepSeek R1推理模型性能跃迁全景概览"
-// §2.2 (INT8 codes with scales from each chunk's extremes; asymmetric min/max reading).
+// rounded and clamped to [-8, 7]), page "第一章：DeepSeek R1推理模型性能跃迁全景概览"
+// §2.2 (INT8 codes with scales from each chunk's extremes; asymmetric min/max reading)
+// and page "DeepSeek R1性能优化有哪些技巧" §一 (an FP8 KV cache; here E4M3 codes with a
+// 4-bit-style per-block scale, absmax / 448).
 //
 // One 256-thread workgroup owns one 64-token block of one (sequence, head, K|V) row.
 // Each thread holds 8 channels of one token per 16-byte load, so every wave-wide load
@@ -66,10 +68,10 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(QuantArgs a) 
   }
 
   float s, zp = 0.0f;
-  if constexpr (SCHEME == KVQ_INT4_SYM) {
+  if constexpr (SCHEME != KVQ_UINT8_ASYM) {  // absmax schemes
     float st[1] = {amax};
     block_max<1>(st, red);
-    s = int4_scale(st[0]);
+    s = SCHEME == KVQ_INT4_SYM ? int4_scale(st[0]) : fp8_scale(st[0]);
   } else {
     float st[2] = {-mn, mx};
     block_max<2>(st, red);
@@ -135,18 +137,30 @@ hipError_t append_t(const AppendArgs& a, hipStream_t s) {
 
 hipError_t launch_quantize(int scheme, int head_dim, int batch, int n_blocks,
                            const QuantArgs& a, hipStream_t s) {
-  if (scheme == KVQ_INT4_SYM)
-    return head_dim == 128 ? quantize_t<KVQ_INT4_SYM, 128>(batch, n_blocks, a, s)
-                           : quantize_t<KVQ_INT4_SYM, 64>(batch, n_blocks, a, s);
-  return head_dim == 128 ? quantize_t<KVQ_UINT8_ASYM, 128>(batch, n_blocks, a, s)
-                         : quantize_t<KVQ_UINT8_ASYM, 64>(batch, n_blocks, a, s);
+  const bool d128 = head_dim == 128;
+  switch (scheme) {
+    case KVQ_INT4_SYM:
+      return d128 ? quantize_t<KVQ_INT4_SYM, 128>(batch, n_blocks, a, s)
+                  : quantize_t<KVQ_INT4_SYM, 64>(batch, n_blocks, a, s);
+    case KVQ_FP8_E4M3:
+      return d128 ? quantize_t<KVQ_FP8_E4M3, 128>(batch, n_blocks, a, s)
+                  : quantize_t<KVQ_FP8_E4M3, 64>(batch, n_blocks, a, s);
+    default:
+      return d128 ? quantize_t<KVQ_UINT8_ASYM, 128>(batch, n_blocks, a, s)
+                  : quantize_t<KVQ_UINT8_ASYM, 64>(batch, n_blocks, a, s);
+  }
 }
 
 hipError_t launch_append(int scheme, int head_dim, const AppendArgs& a, hipStream_t s) {
-  if (scheme == KVQ_INT4_SYM)
-    return head_dim == 128 ? append_t<KVQ_INT4_SYM, 128>(a, s) : append_t<KVQ_INT4_SYM, 64>(a, s);
-  return head_dim == 128 ? append_t<KVQ_UINT8_ASYM, 128>(a, s)
-                         : append_t<KVQ_UINT8_ASYM, 64>(a, s);
+  const bool d128 = head_dim == 128;
+  switch (scheme) {
+    case KVQ_INT4_SYM:
+      return d128 ? append_t<KVQ_INT4_SYM, 128>(a, s) : append_t<KVQ_INT4_SYM, 64>(a, s);
+    case KVQ_FP8_E4M3:
+      return d128 ? append_t<KVQ_FP8_E4M3, 128>(a, s) : append_t<KVQ_FP8_E4M3, 64>(a, s);
+    default:
+      return d128 ? append_t<KVQ_UINT8_ASYM, 128>(a, s) : append_t<KVQ_UINT8_ASYM, 64>(a, s);
+  }
 }
 
 }  // namespace kvq

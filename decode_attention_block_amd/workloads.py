@@ -1,4 +1,4 @@
-"""The five synthetic decode workloads and their seeded input generators.
+"""The synthetic decode workloads and their seeded input generators.
 
 This module draws random numbers and nothing else: it holds no quantization or
 attention arithmetic, so both the HIP path and the CPU oracle can take their inputs
@@ -35,6 +35,7 @@ SEED = 20261202
 BLOCK = 64
 INT4_SYM = 0
 UINT8_ASYM = 1
+FP8_E4M3 = 2
 
 STREAM_K, STREAM_V, STREAM_Q, STREAM_LENS, STREAM_K_APPEND, STREAM_V_APPEND = range(6)
 
@@ -80,6 +81,9 @@ WORKLOADS = [
     # layer), the cache of the 8K workloads' shape otherwise
     Workload(5, "llama70b_gqa8_b8_h8_d128_ctx8k_int4", 8, 8, 128, 8192, INT4_SYM,
              "normal_outliers", "normal_outliers", group=8),
+    # the 8K shape with the FP8 E4M3 cache (page "DeepSeek R1性能优化有哪些技巧" §一)
+    Workload(6, "llama7b_b8_h32_d128_ctx8k_fp8", 8, 32, 128, 8192, FP8_E4M3,
+             "normal_outliers", "normal_outliers"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 

@@ -40,7 +40,7 @@ extern "C" {
 #endif
 
 #define KVQ_BLOCK_TOKENS 64
-#define KVQ_VERSION 2
+#define KVQ_VERSION 3
 
 /* Cache formats. */
 enum kvq_scheme {
@@ -53,14 +53,21 @@ enum kvq_scheme {
    * zp = rint(RN(-min / s)) + 0.0f, code = clamp(rint(RN(x / s)) + (int)zp, 0, 255).
    * A chunk whose elements all equal c: c == 0 gives s = 0, zp = 0, codes 0;
    * otherwise the range is widened to [min(c,0), max(c,0)]. */
-  KVQ_UINT8_ASYM = 1
+  KVQ_UINT8_ASYM = 1,
+  /* [Pg3] §一 (FP8 KV cache; its scaling is not given there, this mirrors the 4-bit
+   * scheme): s = RN(absmax / 448f) (448 = the largest finite E4M3 magnitude; s = 0 for
+   * an all-zero block); code = the FP8 E4M3 (OCP "fn" variant: bias 7, no
+   * infinities) value nearest to RN(x / s), ties to even, sign kept, saturating at
+   * +-448; 0 when s = 0. One byte per channel, stored like KVQ_UINT8_ASYM codes. Zero
+   * points (if the buffers are given) are written +0.0f. */
+  KVQ_FP8_E4M3 = 2
 };
 
 /* Status codes. */
 enum kvq_status {
   KVQ_OK = 0,
   KVQ_EINVAL = -1,     /* null pointer, bad scheme/shape/count, negative length */
-  KVQ_ENOTSUP = -2,    /* head_dim other than 64 or 128; kv_append limits (see there) */
+  KVQ_ENOTSUP = -2,    /* head_dim other than 64 or 128; size or scheme limits of a call */
   KVQ_ECAPACITY = -3,  /* a length bound exceeds max_blocks * 64 */
   KVQ_EALIGN = -4,     /* a pointer or stride breaks the 16-byte alignment rule */
   KVQ_EWORKSPACE = -5, /* workspace missing or smaller than decode_attn_workspace_bytes */
@@ -69,9 +76,9 @@ enum kvq_status {
 
 /* Cache descriptor. Plain data; every pointer is device memory owned by the caller.
  * B = batch, H = heads, D = head_dim, MB = max_blocks (capacity MB * 64 tokens/row).
- *   k_codes, v_codes : uint8 [B][H][MB][64][D/2 (int4) | D (uint8)], 16-byte aligned;
+ *   k_codes, v_codes : uint8 [B][H][MB][64][D/2 (int4) | D (uint8, fp8)], 16-byte aligned;
  *                      each block of a row is one contiguous 32*D (int4) or 64*D
- *                      (uint8) byte region. uint8 codes are stored [token][channel].
+ *                      (uint8, fp8) byte region, uint8 and fp8 codes [token][channel].
  *                      int4 codes are stored in matrix-core operand order: the region
  *                      is 64 lanes x F = D/8 dwords, dword f of lane l at byte
  *                      ((f/4)*64 + l)*16 + (f%4)*4, nibble q (bits 4q..4q+3) =
@@ -81,7 +88,7 @@ enum kvq_status {
  *                      are written as zero nibbles / bytes by the quantizing calls.
  *   k_scale, v_scale : float [B][H][MB].
  *   k_zero,  v_zero  : float [B][H][MB]; required for KVQ_UINT8_ASYM, may be NULL for
- *                      KVQ_INT4_SYM.
+ *                      KVQ_INT4_SYM and KVQ_FP8_E4M3.
  *   k_tail,  v_tail  : fp16 [B][H][64][D], 16-byte aligned: the original fp16 values
  *                      of each row's open (partially filled) block, which kv_append
  *                      needs to re-quantize that block. May be NULL if kv_append is

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = kvq.load_library()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert kvq.kvq_version() == 2
+    assert kvq.kvq_version() == 3
 
 
 def cache(scheme=0, B=2, H=4, D=128, MB=3, **kw):
@@ -72,7 +72,8 @@ EINVAL, ENOTSUP, ECAP, EALIGN, EWS = -1, -2, -3, -4, -5
 def test_null_and_bad_descriptor():
     L = kvq.load_library()
     assert L.kv_quantize_blocks(None, FAKE, FAKE, 0, 0, 0, 10, None) == EINVAL
-    assert rc_quant(cache(scheme=2)) == EINVAL
+    assert rc_quant(cache(scheme=3)) == EINVAL
+    assert rc_quant(cache(scheme=-1)) == EINVAL
     assert rc_quant(cache(B=0)) == EINVAL
     assert rc_quant(cache(H=-1)) == EINVAL
     assert rc_quant(cache(MB=0)) == EINVAL
@@ -107,6 +108,7 @@ def test_capacity_and_lengths():
     assert rc_attn(cache(MB=(1 << 19) + 1, D=128)) == ENOTSUP            # int4: 4 KiB blocks
     assert rc_attn(cache(MB=(1 << 19) - 1, D=128), ws=0) == EWS           # just fits
     assert rc_attn(cache(scheme=1, MB=(1 << 18) + 1, D=128)) == ENOTSUP  # uint8: 8 KiB
+    assert rc_attn(cache(scheme=2, MB=(1 << 18) + 1, D=128)) == ENOTSUP  # FP8: 8 KiB
     assert rc_attn(cache(scheme=1, MB=1 << 18, D=64), ws=0) == EWS
 
 
@@ -133,6 +135,7 @@ def test_grouped_query_rules():
     assert rc_gqa(cache(), group=16) == EINVAL
     assert rc_gqa(cache(), group=0) == EINVAL
     assert rc_gqa(cache(scheme=1), group=2) == ENOTSUP      # int4 only
+    assert rc_gqa(cache(scheme=2), group=2) == ENOTSUP
     assert rc_gqa(cache(), q=FAKE + 2) == EALIGN
     assert rc_gqa(cache(), out=0) == EINVAL
     c = cache(B=2, H=4, D=128, MB=3)
@@ -165,7 +168,7 @@ def test_decode_step_validates_like_append_and_attention():
     assert rc_step(cache(), v=FAKE + 2) == EALIGN
     assert rc_step(cache(), q=FAKE + 4) == EALIGN
     assert rc_step(cache(), out=FAKE + 4) == EALIGN
-    assert rc_step(cache(scheme=2)) == EINVAL
+    assert rc_step(cache(scheme=3)) == EINVAL
     assert rc_step(cache(D=96)) == ENOTSUP
     assert rc_step(cache(v_tail=0)) == EINVAL
     assert rc_step(cache(H=256)) == ENOTSUP

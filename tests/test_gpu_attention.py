@@ -12,7 +12,7 @@ from helpers import (ATTN_TOL, attn_errors, gpu_attention, gpu_quantize, oracle_
 
 pytestmark = pytest.mark.gpu
 
-INT4, UINT8 = oracle.INT4_SYM, oracle.UINT8_ASYM
+INT4, UINT8, FP8 = oracle.INT4_SYM, oracle.UINT8_ASYM, oracle.FP8_E4M3
 
 
 def _workload_case(index, layer=0, seqs=None):
@@ -25,7 +25,7 @@ def _workload_case(index, layer=0, seqs=None):
     return w, k, v, q, lens
 
 
-@pytest.mark.parametrize("index", [0, 1, 2])
+@pytest.mark.parametrize("index", [0, 1, 2, 6])
 def test_workload_attention_all_rows(index):
     w, k, v, q, lens = _workload_case(index)
     say("attention", w.name)
@@ -61,7 +61,7 @@ def _small_case(scheme, D, seed=7, B=4, H=3, S=700, lens=(700, 1, 333, 64)):
     return k, v, q, np.array(lens, np.int32)
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("D", [64, 128])
 def test_split_counts_all_agree_with_oracle(scheme, D):
     """Every split size (1 block .. one split for the whole row, and the automatic
@@ -82,7 +82,7 @@ def test_split_counts_all_agree_with_oracle(scheme, D):
     assert spread <= 1e-5 * max(1.0, np.abs(outs[0]).max()) + 2 ** -10 * np.abs(outs[0]).max()
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 def test_padding_poison_and_determinism(scheme):
     """Garbage in the padding bytes of each last block changes nothing (bitwise), and
     repeated calls are bitwise identical."""
@@ -123,7 +123,7 @@ def test_empty_and_single_token_rows():
     assert norm_err <= ATTN_TOL
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("bps", [2, 0])
 def test_split_and_combine_phases_equal_fused_call(scheme, bps):
     """decode_attn_split + decode_attn_combine give bitwise the fused result (several
@@ -149,7 +149,7 @@ def test_split_and_combine_phases_equal_fused_call(scheme, bps):
     assert np.array_equal(out.cpu().numpy(), fused.cpu().numpy())
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("bps", [0, 3])
 def test_ragged_rows(scheme, D, bps):

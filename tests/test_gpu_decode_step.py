@@ -13,7 +13,7 @@ from helpers import ATTN_TOL, attn_errors, gpu_quantize, oracle_cache, say, to_g
 
 pytestmark = pytest.mark.gpu
 
-INT4, UINT8 = oracle.INT4_SYM, oracle.UINT8_ASYM
+INT4, UINT8, FP8 = oracle.INT4_SYM, oracle.UINT8_ASYM, oracle.FP8_E4M3
 
 
 def _history(scheme, B, H, D, S, seed):
@@ -59,7 +59,7 @@ def _assert_same_output(out, out_ref, bitwise):
 
 # (B, H): 8 x 32 = 256 rows -> one split per row (single launch); 3 x 5 -> several
 # splits per row (append and attention as two launches).
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("BH", [(8, 32), (3, 5)])
 def test_step_equals_append_then_attention(scheme, D, BH):
@@ -131,7 +131,7 @@ def test_step_on_full_rows_attends_without_appending():
         assert np.array_equal(after["v_scale"][b], before["v_scale"][b])
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 def test_step_with_lengths_beyond_the_bound(scheme):
     """Rows longer than max_len_after still append, and are attended over their first
     max_len_after tokens (as decode_attn_qkv clamps): the new token's block is then cut

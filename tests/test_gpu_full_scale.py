@@ -1,6 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the benchmark
-times: prefill with kv_quantize_blocks, then decode steps of kv_append (one token per
-sequence) followed by the fused decode_attn_qkv with the automatic split plan.
+times: prefill with kv_quantize_blocks, then decode steps of decode_step_qkv (append
+one token per sequence and head, then attend, with the automatic split plan: one
+launch when a split per row fills the GPU).
 
 The oracle checks sampled outputs it can compute one by one:
   * the prefill blocks of the sampled sequences, bitwise;
@@ -59,9 +60,9 @@ def _decode_steps(w, n_steps, attn_steps, seqs, prefill_seqs):
     worst = 0.0
     for s in range(1, n_steps + 1):
         L = L0 + s
-        kvq.kv_append(c, k_new[s - 1], v_new[s - 1], L)
         q = wl.query(w, 0, s - 1)
-        kvq.decode_attn_qkv(c, torch.from_numpy(q).cuda(), sm, out, ws, L, 0)
+        kvq.decode_step_qkv(c, k_new[s - 1], v_new[s - 1], torch.from_numpy(q).cuda(), sm,
+                            out, ws, L, 0)
         torch.cuda.synchronize()
         assert (c.seq_lens.cpu().numpy() == L).all(), s
         tail = c.host_arrays(blocks=slice(j_new, j_new + 1))
@@ -86,7 +87,7 @@ def _decode_steps(w, n_steps, attn_steps, seqs, prefill_seqs):
     assert worst <= ATTN_TOL
 
 
-@pytest.mark.parametrize("index,n_steps", [(1, 28), (2, 55)])
+@pytest.mark.parametrize("index,n_steps", [(1, 28), (2, 55), (6, 28)])
 def test_ctx8k_decode_steps_as_benchmarked(index, n_steps):
     """The 8K workloads over the context growth the benchmark's rotation reaches;
     attention of all 256 rows checked at the first and last step, the prefill of

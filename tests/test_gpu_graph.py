@@ -10,7 +10,7 @@ from helpers import gpu_quantize, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
-INT4, UINT8 = oracle.INT4_SYM, oracle.UINT8_ASYM
+INT4, UINT8, FP8 = oracle.INT4_SYM, oracle.UINT8_ASYM, oracle.FP8_E4M3
 
 
 def _layers(scheme, n_layers, B, H, D, S, lens, MB, seed):
@@ -32,7 +32,7 @@ def _same(a, b):
     return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("append", [True, False])
 def test_graph_replays_equal_eager_steps(scheme, append):
     import decode_attention_block_amd as kvq

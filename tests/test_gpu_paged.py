@@ -11,7 +11,7 @@ from helpers import assert_cache_equal, oracle_cache, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
-INT4, UINT8 = oracle.INT4_SYM, oracle.UINT8_ASYM
+INT4, UINT8, FP8 = oracle.INT4_SYM, oracle.UINT8_ASYM, oracle.FP8_E4M3
 SENTINEL = 0xA5
 
 
@@ -60,7 +60,7 @@ def _assert_same_cache(dense, paged, lens):
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), (key, b)
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("D", [64, 128])
 def test_paged_prefill_and_attention_equal_dense(scheme, D):
     import decode_attention_block_amd as kvq
@@ -85,7 +85,7 @@ def test_paged_prefill_and_attention_equal_dense(scheme, D):
         assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), bps
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("BH", [(8, 32), (3, 5)])
 def test_paged_appends_and_decode_steps_equal_dense(scheme, BH):
     """kv_append and decode_step_qkv (one launch for 8 x 32 rows, two launches for

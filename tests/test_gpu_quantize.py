@@ -9,10 +9,10 @@ from helpers import assert_cache_equal, gpu_quantize, oracle_cache, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
-INT4, UINT8 = oracle.INT4_SYM, oracle.UINT8_ASYM
+INT4, UINT8, FP8 = oracle.INT4_SYM, oracle.UINT8_ASYM, oracle.FP8_E4M3
 
 
-@pytest.mark.parametrize("index", [0, 1, 2])
+@pytest.mark.parametrize("index", [0, 1, 2, 6])
 def test_workload_prefill_bitexact(index):
     """Whole-workload prefill of the tiny and both 8K workloads; the oracle checks
     sequences 0 and B-1 of the 8K ones (all heads, all blocks)."""
@@ -48,7 +48,7 @@ def test_ragged_long_student_t_prefill_bitexact():
         assert_cache_equal(sub, ref, lens[seqs])
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("D", [64, 128])
 def test_edge_cases_bitexact(scheme, D):
     """Ragged lengths 0, 1, 63, 64, 65, 200; a transposed [B][H][S][D] input layout;
@@ -83,7 +83,7 @@ def test_edge_cases_bitexact(scheme, D):
     assert not g["k_codes"][3, :, 1:].any() and not g["k_scale"][3, :, 1:].any()
 
 
-@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("D", [64, 128])
 def test_append_matches_bulk_every_step(scheme, D):
     """Token-by-token kv_append from prefill lengths 0, 1, 61, 64 and 127 through 0->1,
@@ -130,3 +130,56 @@ def test_append_at_capacity_leaves_row_unchanged():
     after = c.host_arrays()
     assert np.array_equal(after["k_codes"][0], before["k_codes"][0])
     assert np.array_equal(after["k_scale"][0], before["k_scale"][0])
+
+
+def _fp8_rounding_history(D, rs):
+    """[2][S=160][H=4][D] fp16 values whose blocks have power-of-two FP8 scales
+    (absmax 448 * 2^k, so x / s is exact): every halfway point between neighbouring
+    E4M3 magnitudes (normal and subnormal, both signs), the magnitudes themselves,
+    values that round to (signed) zero, and 448 * 2^k; head 3 is random (scales not
+    powers of two, absmax / s lands just above or below 448)."""
+    mags = [(1 + m / 8) * 2.0 ** e for e in range(-6, 9) for m in range(8)]
+    mags = [x for x in mags if x <= 448] + [m / 8 * 2.0 ** -6 for m in range(1, 8)]
+    mags = np.array(sorted(mags))
+    halves = (mags[1:] + mags[:-1]) / 2
+    tiny = np.array([2.0 ** -10, 2.0 ** -11, 2.0 ** -12])   # half a step and below
+    pool = np.concatenate([mags, halves, tiny])
+    S, H = 160, 4
+    x = np.empty((2, S, H, D), np.float64)
+    for b in range(2):
+        for h in range(3):
+            k = [0, -2, 3][h] - b                  # scale 2^k
+            vals = rs.choice(pool, (S, D)) * rs.choice([-1.0, 1.0], (S, D))
+            for j in range(0, S, 64):              # every block holds 448 * 2^k once
+                vals[j + rs.integers(0, min(64, S - j)), rs.integers(0, D)] = 448.0
+            x[b, :, h] = vals * 2.0 ** k
+        x[b, :, 3] = rs.standard_normal((S, D)) * 3
+    out = x.astype(np.float16)
+    assert np.array_equal(out[:, :, :3].astype(np.float64), x[:, :, :3])  # exact in fp16
+    return out
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_rounding_ties_subnormals_saturation_bitexact(D):
+    """FP8 E4M3 codes on values that sit exactly on the rounding decisions (ties to the
+    even code, the subnormal range, signed zeros, the largest magnitude): prefill, then
+    kv_append token by token across a block boundary, bit-exact against the oracle
+    after every step."""
+    import decode_attention_block_amd as kvq
+    import torch
+    say("fp8 rounding", D)
+    rs = np.random.default_rng(300 + D)
+    k = _fp8_rounding_history(D, rs)
+    v = np.ascontiguousarray(k[:, ::-1])
+    lens = np.array([120, 60], np.int32)
+    MB = 3
+    c = gpu_quantize(FP8, k, v, lens, MB)
+    assert_cache_equal(c.host_arrays(), oracle_cache(FP8, k, v, lens, MB), lens)
+    codes = c.host_arrays()["k_codes"]
+    assert (codes == 0x80).any() and (codes == 0x7E).any() and (codes == 0xFE).any()
+    for step in range(10):
+        kvq.kv_append(c, to_gpu(k[np.arange(2), lens]), to_gpu(v[np.arange(2), lens]),
+                      int(lens.max()) + 1)
+        lens = lens + 1
+        torch.cuda.synchronize()
+        assert_cache_equal(c.host_arrays(), oracle_cache(FP8, k, v, lens, MB), lens)
