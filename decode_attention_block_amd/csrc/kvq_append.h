@@ -60,7 +60,7 @@ struct QGeo {
 
 template <int SCHEME, int D>
 __device__ __forceinline__ void store_codes(uint8_t* token_row, int chunk, const float (&x)[8],
-                                            float s, int zpi, bool valid) {
+                                            const Divisor& s, int zpi, bool valid) {
   if constexpr (SCHEME == KVQ_INT4_SYM) {
     const uint32_t w = valid ? pack_int4x8(x, s) : 0u;
     *reinterpret_cast<uint32_t*>(token_row + chunk * 4) = w;
@@ -73,39 +73,46 @@ __device__ __forceinline__ void store_codes(uint8_t* token_row, int chunk, const
   }
 }
 
+// int4: dword f of lane `lane` of a block region in fragment order, coded from the
+// block's fp16 values staged in LDS (xs[t * D + d], natural order); nibbles of tokens
+// t >= ntok are zero. K: the 8 channels 32 (f % (D/32)) + 8 (lane / 16) .. of token
+// 16 (f / (D/32)) + lane % 16 (one 16-byte read); V: tokens 32 (f % 2) + 8 (lane / 16) ..
+// of channel 16 (f / 2) + lane % 16.
+template <int D>
+__device__ __forceinline__ uint32_t int4_fragment_word(const _Float16* xs, int ntok,
+                                                       const Divisor& s, bool is_v, int lane,
+                                                       int f) {
+  constexpr int KS = D / 32;  // 32-channel K steps
+  float x[8];
+  uint32_t mask = 0xFFFFFFFFu;
+  if (!is_v) {
+    const int t = 16 * (f / KS) + lane % 16;
+    if (t >= ntok) return 0u;
+    unpack8(*reinterpret_cast<const uint4*>(xs + t * D + 32 * (f % KS) + 8 * (lane / 16)), x);
+  } else {
+    const int d = 16 * (f / 2) + lane % 16;
+    const int t0 = 32 * (f % 2) + 8 * (lane / 16);
+    const int n = ntok - t0;  // tokens of the 8 that exist
+    if (n <= 0) return 0u;
+    if (n < 8) mask = (1u << (4 * n)) - 1u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = static_cast<float>(xs[(t0 + q) * D + d]);
+  }
+  return pack_int4x8(x, s) & mask;
+}
+
 // int4: writes one block region (K or V) in fragment order from the block's fp16 values
 // staged in LDS (xs[t * D + d], natural order); tokens t >= ntok give zero nibbles.
 // Called by NT threads (tid = 0 .. NT-1).
 template <int D, int NT = kThreads>
-__device__ __forceinline__ void int4_write_block_from(const _Float16* xs, int ntok, float s,
+__device__ __forceinline__ void int4_write_block_from(const _Float16* xs, int ntok, const Divisor& s,
                                                       bool is_v, uint8_t* out, int tid) {
-  constexpr int KS = D / 32;      // 32-channel K steps
   constexpr int kChunks = 2 * D;  // 16-byte chunks per region (32 * D bytes)
   for (int c = tid; c < kChunks; c += NT) {
     const int lane = c % kWave, i = c / kWave;
     uint32_t w[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int f = 4 * i + r;
-      uint32_t word = 0;
-      if (!is_v) {
-        const int t = 16 * (f / KS) + lane % 16;
-        const int d0 = 32 * (f % KS) + 8 * (lane / 16);
-        if (t < ntok) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            word |= int4_code(static_cast<float>(xs[t * D + d0 + q]), s) << (4 * q);
-        }
-      } else {
-        const int d = 16 * (f / 2) + lane % 16;
-        const int t0 = 32 * (f % 2) + 8 * (lane / 16);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (t0 + q < ntok)
-            word |= int4_code(static_cast<float>(xs[(t0 + q) * D + d]), s) << (4 * q);
-      }
-      w[r] = word;
-    }
+    for (int r = 0; r < 4; ++r) w[r] = int4_fragment_word<D>(xs, ntok, s, is_v, lane, 4 * i + r);
     *reinterpret_cast<uint4*>(out + c * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
@@ -146,34 +153,86 @@ struct BlockScales {
   float ks, kz, vs, vz;
 };
 
-template <int SCHEME, int D, int NT>
-__device__ __forceinline__ void append_stage(const AppendArgs& a, int64_t row, int len, int tid,
-                                             const uint4 (&fresh)[2], _Float16* xs, float* red,
-                                             AppendPlan (&plan)[2]) {
+// The staged tokens of the open block as loaded by append_stage_load: pass p of tensor kv
+// holds this thread's 16 bytes of token p * (NT / (D/8)) + tid / (D/8).
+template <int D, int NT>
+struct StagedTokens {
+  static constexpr int kPasses = (kBlock + NT / (D / 8) - 1) / (NT / (D / 8));
+  uint4 v[2][kPasses];
+};
+
+// Requests the staged tokens 0 .. slot-1 of the open block (slot = len % 64). They are
+// read through buffer resources that end at token `slot`: every lane loads
+// unconditionally and the loads past the end return zeros without touching memory.
+template <int D, int NT>
+__device__ __forceinline__ void append_stage_load(const AppendArgs& a, int64_t row, int len,
+                                                  int tid, StagedTokens<D, NT>& g) {
+  constexpr int TPT = D / 8;
+  constexpr int TPP = NT / TPT;
+  const int tr = tid / TPT;
+  const int chunk = tid % TPT;
+  const int slot = len % kBlock;
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (kv ? a.v_tail : a.k_tail) + row * kBlock * D, 0, slot * D * 2, kBufferRsrcWord3);
+#pragma unroll
+    for (int p = 0; p < StagedTokens<D, NT>::kPasses; ++p)
+      g.v[kv][p] = load_b128<0>(rs, ((p * TPP + tr) * D + chunk * 8) * 2, 0);
+  }
+}
+
+// One wave requests the staged tokens 0 .. slot-1 of the open block straight into LDS,
+// in xs's layout (tensor kv at xs + kv * 64 * D, token t at t * D): each request moves
+// 1 KiB, lane l's 16 bytes to byte 16 l of it, and the lanes past the end of the buffer
+// resource (tokens >= slot) write zeros.
+template <int D>
+__device__ __forceinline__ void append_stage_load_lds(const AppendArgs& a, int64_t row, int len,
+                                                      int lane, _Float16* xs) {
+  typedef __attribute__((address_space(3))) void* lds_t;
+  const int slot = len % kBlock;
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (kv ? a.v_tail : a.k_tail) + row * kBlock * D, 0, slot * D * 2, kBufferRsrcWord3);
+#pragma unroll
+    for (int p = 0; p < kBlock * D * 2 / 1024; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t)(xs + kv * kBlock * D + p * 512), 16,
+                                               lane * 16, p * 1024, 0, 0);
+  }
+}
+
+// The staged tokens and the new one into xs, the statistics, the plan. staged(kv, p, t,
+// chunk) gives this thread's 16 bytes of token t of tensor kv (pass p). kInLds: the
+// tokens, the new one included, are in xs already (staged reads them there).
+template <int SCHEME, int D, int NT, bool kInLds = false, class Staged>
+__device__ __forceinline__ void append_stage_reduce(int len, int tid, Staged staged,
+                                                    const uint4 (&fresh)[2], _Float16* xs,
+                                                    float* red, AppendPlan (&plan)[2]) {
   constexpr int TPT = D / 8;             // threads per token row (16 bytes each)
   constexpr int TPP = NT / TPT;          // tokens per pass
-  constexpr int PASSES = kBlock / TPP;
+  constexpr int PASSES = (kBlock + TPP - 1) / TPP;  // the last may run past the block
   constexpr int NS = kAppendStats<SCHEME> / 2;  // statistics per tensor
   const int tr = tid / TPT;
   const int chunk = tid % TPT;
   const int slot = len % kBlock;
 
-  // The staged tokens are read through buffer resources that end at token `slot`:
-  // every lane loads unconditionally and the loads past the end return zeros without
-  // touching memory.
   float st[2 * NS];
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (kv ? a.v_tail : a.k_tail) + row * kBlock * D, 0, slot * D * 2, kBufferRsrcWord3);
     float amax_o = 0.0f, mn_o = __builtin_inff(), mx_o = -__builtin_inff();
     float amax_n = 0.0f, mn_n = __builtin_inff(), mx_n = -__builtin_inff();
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int t = p * TPP + tr;
-      const uint4 staged = load_b128<0>(rs, (t * D + chunk * 8) * 2, 0);
-      const uint4 raw = t == slot ? fresh[kv] : staged;
-      *reinterpret_cast<uint4*>(xs + kv * kBlock * D + t * D + chunk * 8) = raw;
+      uint4 raw;  // zeros past the slot
+      if constexpr (kInLds) {
+        raw = staged(kv, p, t, chunk);
+      } else {
+        raw = t == slot ? fresh[kv] : staged(kv, p, t, chunk);
+        if (PASSES * TPP == kBlock || t < kBlock)
+          *reinterpret_cast<uint4*>(xs + kv * kBlock * D + t * D + chunk * 8) = raw;
+      }
       float x[8];
       unpack8(raw, x);
 #pragma unroll
@@ -219,6 +278,16 @@ __device__ __forceinline__ void append_stage(const AppendArgs& a, int64_t row, i
   }
 }
 
+template <int SCHEME, int D, int NT>
+__device__ __forceinline__ void append_stage(const AppendArgs& a, int64_t row, int len, int tid,
+                                             const uint4 (&fresh)[2], _Float16* xs, float* red,
+                                             AppendPlan (&plan)[2]) {
+  StagedTokens<D, NT> g;
+  append_stage_load<D, NT>(a, row, len, tid, g);
+  append_stage_reduce<SCHEME, D, NT>(
+      len, tid, [&](int kv, int p, int, int) { return g.v[kv][p]; }, fresh, xs, red, plan);
+}
+
 // Code writes through memory (see above): the whole block, or the new token's codes.
 template <int SCHEME, int D, int NT>
 __device__ __forceinline__ void append_write_codes(const AppendArgs& a, int64_t row, int len,
@@ -235,7 +304,7 @@ __device__ __forceinline__ void append_write_codes(const AppendArgs& a, int64_t 
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     const bool is_v = kv != 0;
-    const float s = plan[kv].s;
+    const Divisor s(plan[kv].s);
     uint8_t* codes = (is_v ? a.v_codes : a.k_codes) + blk * kBlock * RB;
     const _Float16* xt = xs + kv * kBlock * D;  // tokens 0..slot, zeros after
     if constexpr (SCHEME == KVQ_INT4_SYM) {
@@ -246,12 +315,9 @@ __device__ __forceinline__ void append_write_codes(const AppendArgs& a, int64_t 
         constexpr int KS = D / 32;
         for (int idx = tid; idx < D / 8; idx += NT) {
           const int ks = idx / 4, g = idx % 4;
-          uint32_t word = 0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            word |= int4_code(static_cast<float>(xt[slot * D + 32 * ks + 8 * g + q]), s) << (4 * q);
-          const int f = (slot / 16) * KS + ks;
-          *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(16 * g + slot % 16, f)) = word;
+          const int lane = 16 * g + slot % 16, f = (slot / 16) * KS + ks;
+          *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(lane, f)) =
+              int4_fragment_word<D>(xt, slot + 1, s, false, lane, f);
         }
       } else {
         // V: each channel's new nibble shares a dword with 7 other tokens; with the
@@ -259,13 +325,9 @@ __device__ __forceinline__ void append_write_codes(const AppendArgs& a, int64_t 
         // stored nibbles (and zeros past the token), so the cache is never read back
         const int ks = slot / 32, g = (slot % 32) / 8, t0 = 32 * ks + 8 * g;
         for (int d = tid; d < D; d += NT) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (t0 + q <= slot)
-              word |= int4_code(static_cast<float>(xt[(t0 + q) * D + d]), s) << (4 * q);
-          const int f = 2 * (d / 16) + ks;
-          *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(16 * g + d % 16, f)) = word;
+          const int lane = 16 * g + d % 16, f = 2 * (d / 16) + ks;
+          *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(lane, f)) =
+              int4_fragment_word<D>(xt, slot + 1, s, true, lane, f);
         }
       }
     } else {
@@ -342,69 +404,55 @@ __device__ __forceinline__ uint32_t get_dword(const uint4 (&r)[N], int f) {
 // Code writes of one int4 tensor by one wave that also leaves the block's new codes in
 // registers, so the wave can attend the block without reading it back: r receives
 // chunk i (i < D/32) of the lane, i.e. bytes ((i * 64) + lane) * 16 .. +15 of the
-// region, computed from the staged values (tokens 0..slot, zeros after). The cache gets
-// the same bytes as from append_write_codes, except that a V append writes only the
-// byte holding the token's nibble: stores into the code buffer cost the concurrent
-// code stream far more than their size, so they are kept to what changes (the whole
-// block, or the token's D/2 bytes of K and D bytes of V).
+// region. `old` holds the same chunks as stored before the append. A re-quantized block
+// is coded whole from the staged values (tokens 0..slot, zeros after) and written
+// whole; otherwise the other tokens keep their codes, so the token's codes are coded
+// and patched into `old`, and only they are written (the token's D/2 bytes of K, and
+// of V the byte holding each channel's nibble): stores into the code buffer cost the
+// concurrent code stream far more than their size.
 template <int D>
 __device__ __forceinline__ void int4_tail_fragments(const _Float16* xt, int slot,
                                                     const AppendPlan& pl, bool is_v, int lane,
+                                                    const uint4 (&old)[D / 32],
                                                     uint4 (&r)[D / 32], uint8_t* codes) {
   constexpr int LOADS = D / 32;  // chunks per lane
   constexpr int KS = D / 32;     // K: dwords per token per lane group
-  const float s = pl.s;
+  const Divisor s(pl.s);
+  if (pl.full) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      uint32_t w[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = int4_fragment_word<D>(xt, slot + 1, s, is_v, lane, 4 * i + c);
+      r[i] = make_uint4(w[0], w[1], w[2], w[3]);
+      store_b128(codes + (i * kWave + lane) * 16, r[i]);
+    }
+    return;
+  }
+  // K: lane 16g + slot % 16 holds the token's channels 32 ks + 8 g .. in dwords
+  // (slot / 16) * KS + ks. V: lanes 16g .. 16g + 15, g = (slot % 32) / 8, hold the token
+  // in nibble slot % 8 of dword 2 nt + slot / 32 for channel 16 nt + lane % 16.
+  const bool owner = is_v ? lane / 16 == (slot % 32) / 8 : lane % 16 == slot % 16;
+  const int q = slot % 8;
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    uint32_t w[4];
+    uint32_t w[4] = {old[i].x, old[i].y, old[i].z, old[i].w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int f = 4 * i + c;
-      uint32_t word = 0;
       if (!is_v) {
-        const int t = 16 * (f / KS) + lane % 16;
-        const int d0 = 32 * (f % KS) + 8 * (lane / 16);
-        if (t <= slot) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            word |= int4_code(static_cast<float>(xt[t * D + d0 + q]), s) << (4 * q);
+        if (f / KS == slot / 16 && owner) {  // the token's dword f
+          w[c] = int4_fragment_word<D>(xt, slot + 1, s, false, lane, f);
+          *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(lane, f)) = w[c];
         }
-      } else {
-        const int d = 16 * (f / 2) + lane % 16;
-        const int t0 = 32 * (f % 2) + 8 * (lane / 16);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (t0 + q <= slot)
-            word |= int4_code(static_cast<float>(xt[(t0 + q) * D + d]), s) << (4 * q);
+      } else if (f % 2 == slot / 32 && owner) {  // channel 16 (f / 2) + lane % 16
+        const uint32_t code =
+            int4_code(static_cast<float>(xt[slot * D + 16 * (f / 2) + lane % 16]), s);
+        w[c] = (w[c] & ~(0xFu << (4 * q))) | (code << (4 * q));
+        codes[int4_dword_offset(lane, f) + q / 2] = static_cast<uint8_t>(w[c] >> (8 * (q / 2)));
       }
-      w[c] = word;
     }
     r[i] = make_uint4(w[0], w[1], w[2], w[3]);
-    if (pl.full) store_b128(codes + (i * kWave + lane) * 16, make_uint4(w[0], w[1], w[2], w[3]));
-  }
-  if (pl.full) return;
-  if (!is_v) {
-    // lane 16g + slot % 16 holds the token's 8-channel group g of each 32-channel step
-    // ks: dwords (slot / 16) * KS + ks
-    if (lane % 16 == slot % 16) {
-      const int f0 = (slot / 16) * KS;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(lane, f0 + ks)) =
-            get_dword(r, f0 + ks);
-    }
-  } else {
-    // lanes 16g .. 16g + 15 (g = (slot % 32) / 8) hold the token in nibble slot % 8 of
-    // dword 2 * nt + slot / 32 for channel 16 * nt + lane % 16
-    if (lane / 16 == (slot % 32) / 8) {
-      const int ks = slot / 32, q = slot % 8;
-#pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) {
-        const int f = 2 * nt + ks;
-        codes[int4_dword_offset(lane, f) + q / 2] =
-            static_cast<uint8_t>(get_dword(r, f) >> (8 * (q / 2)));
-      }
-    }
   }
 }
 

@@ -369,14 +369,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const uint8_t* poo
 
 // ---- fused decode step ----------------------------------------------------------------
 // In a decode step (kAppend) the workgroup of row (b, h) has one wave more than the
-// attention: waves 0 .. kSplitWaves-1 attend the blocks the append leaves untouched
-// while the last wave appends the row's new token (append_stage .. append_finish) and
-// then attends the block that holds it. The row's length is read once, before anything else; the append
-// wave then takes the sequence's arrival ticket (1 << 24 added to seq_lens[b], as in
-// kv_append) and the last of the sequence's `heads` workgroups stores the new length.
-// Since every workgroup of the sequence reads the length before it takes its ticket,
-// none can see the new length, and the ticket's latency hides behind the append instead
-// of delaying the attention.
+// attention. The row's length is read once, before anything else. Then the whole
+// workgroup stages the open block (append_stage over all its threads: the row's staged
+// tokens and the new one into LDS, the block statistics before and after the token, the
+// plan), and the waves part: waves 0 .. kSplitWaves-1 attend the blocks the append
+// leaves untouched while the last wave writes the new codes, the token's staging and the
+// scales, and attends the block that holds the token. Staging together at the start,
+// while the memory pipeline is still empty, matters: afterwards the streaming waves keep
+// the compute unit's queue of memory requests full, and a wave that has to issue dozens
+// of requests behind them (32 loads per lane for the staged block) waits tens of
+// microseconds, longer than the streaming itself.
+// The append wave takes the sequence's arrival ticket (1 << 24 added to seq_lens[b], as
+// in kv_append) right after the length is read, and the last of the sequence's `heads`
+// workgroups stores the new length when its work is done. Since every workgroup of the
+// sequence reads the length before it takes its ticket, none can see the new length.
 constexpr int kStepWaves = kSplitWaves + 1;
 
 struct StepLens {
@@ -402,33 +408,92 @@ __device__ __forceinline__ StepLens step_lengths(const AttnArgs& a, int b, int c
   return r;
 }
 
-// The append wave's part of the step before it attends: ticket, append, and (by the
-// last arrival of the sequence) the new length. write_codes(plan) does the code writes
-// (after append_stage, before append_finish). Returns the scales (and zero points) of
-// the block holding the new token.
-template <int SCHEME, int D, class WriteCodes>
-__device__ __forceinline__ BlockScales step_append(const AttnArgs& a, const StepLens& sl, int b,
-                                                   int64_t row, int cap, int lane, _Float16* xs,
-                                                   WriteCodes write_codes) {
-  uint32_t* lens = reinterpret_cast<uint32_t*>(a.ap.seq_lens);
-  uint32_t ticket = 0;
-  if (lane == 0)
-    ticket = __hip_atomic_fetch_add(lens + b, 1u << 24, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_SYSTEM);
-  BlockScales sc = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (sl.len0 < cap) {
-    const int off = (lane % (D / 8)) * 8;
-    const uint4 fresh[2] = {*reinterpret_cast<const uint4*>(a.ap.k_new + row * D + off),
-                            *reinterpret_cast<const uint4*>(a.ap.v_new + row * D + off)};
-    AppendPlan plan[2];
-    append_stage<SCHEME, D, kWave>(a.ap, row, sl.len0, lane, fresh, xs, nullptr, plan);
-    write_codes(plan);
-    sc = append_finish<D, kWave>(a.ap, row, sl.len0, lane, fresh, plan);
+// The append wave's view of the open block: `fresh` is the lane's 16 bytes of the new K
+// and V token (channels (lane % (D/8)) * 8 ..), `plan` the outcome per tensor. The new
+// token is held across the release as plain vector values (u32x4).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Requests the row's staged tokens (into xs) and the new token (append wave, row below
+// capacity).
+template <int D>
+__device__ __forceinline__ void step_stage_load(const AttnArgs& a, const StepLens& sl,
+                                                int64_t row, int lane, _Float16* xs,
+                                                u32x4& fresh_k, u32x4& fresh_v) {
+  append_stage_load_lds<D>(a.ap, row, sl.len0, lane, xs);
+  const int off = (lane % (D / 8)) * 8;
+  fresh_k = *reinterpret_cast<const u32x4*>(a.ap.k_new + row * D + off);
+  fresh_v = *reinterpret_cast<const u32x4*>(a.ap.v_new + row * D + off);
+}
+
+// After step_release: waits for the staged tokens, puts the new token in its row of xs
+// and reduces the block (append wave).
+template <int SCHEME, int D>
+__device__ __forceinline__ void step_stage_reduce(const StepLens& sl, int lane, _Float16* xs,
+                                                  const uint4 (&fresh)[2],
+                                                  AppendPlan (&plan)[2]) {
+  constexpr int TPT = D / 8;  // lanes per token row
+  const int slot = sl.len0 % kBlock;
+  __builtin_amdgcn_s_waitcnt(0);  // the loads into LDS have landed
+  if (lane / TPT == slot % (kWave / TPT)) {
+    _Float16* row_k = xs + slot * D + (lane % TPT) * 8;
+    *reinterpret_cast<u32x4*>(row_k) = u32x4{fresh[0].x, fresh[0].y, fresh[0].z, fresh[0].w};
+    *reinterpret_cast<u32x4*>(row_k + kBlock * D) =
+        u32x4{fresh[1].x, fresh[1].y, fresh[1].z, fresh[1].w};
   }
+  __builtin_amdgcn_wave_barrier();
+  append_stage_reduce<SCHEME, D, kWave, true>(
+      sl.len0, lane,
+      [&](int kv, int, int t, int chunk) {
+        return *reinterpret_cast<const uint4*>(xs + kv * kBlock * D + t * D + chunk * 8);
+      },
+      fresh, xs, nullptr, plan);
+}
+
+// Releases the streaming waves once the append wave has issued its requests, so that
+// those go first in the compute unit's memory pipeline (a barrier without a memory
+// fence: nothing waits for the requests themselves).
+__device__ __forceinline__ void step_release() { __builtin_amdgcn_s_barrier(); }
+
+// The sequence's arrival ticket, taken by the append wave after the length was read;
+// step_ticket_done (after the wave's work) stores the new length if this was the
+// sequence's last arrival. The atomic's latency (the sequence's `heads` tickets are
+// serialized at memory) must overlap the wave's work, so nothing may wait for it before
+// the end: it is issued after the wave's loads have been waited for (vector memory
+// requests complete in order, so a later wait would include it), and as one request of
+// the whole wave whose lanes past the first fall outside a 4-byte buffer resource
+// (seq_lens[b]) and so do not touch memory; a branch around a one-lane atomic would
+// merge its result with the other lanes' value and make the compiler wait for it at
+// once. System scope (cache policy sc1): the add is performed at memory, past the per-XCD
+// L2s. The result is meaningful in lane 0.
+constexpr int kCachePolicySystem = 16;  // sc1
+
+__device__ __forceinline__ uint32_t step_ticket(const AttnArgs& a, int b, int lane) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(a.ap.seq_lens + b, 0, 4, kBufferRsrcWord3);
+  return static_cast<uint32_t>(__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(
+      1 << 24, rs, lane == 0 ? 0 : 4, 0, kCachePolicySystem));
+}
+
+__device__ __forceinline__ void step_ticket_done(const AttnArgs& a, const StepLens& sl, int b,
+                                                 int cap, uint32_t ticket, int lane) {
   if (lane == 0 && (ticket >> 24) == static_cast<uint32_t>(a.heads - 1))
-    __hip_atomic_exchange(lens + b, static_cast<uint32_t>(sl.len0 < cap ? sl.len0 + 1 : sl.len0),
+    __hip_atomic_exchange(reinterpret_cast<uint32_t*>(a.ap.seq_lens) + b,
+                          static_cast<uint32_t>(sl.len0 < cap ? sl.len0 + 1 : sl.len0),
                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  return sc;
+}
+
+// The append wave's writes after the stage: write_codes(plan) writes the codes, then the
+// token's fp16 staging and the changed scales. Returns the scales (and zero points) of
+// the block holding the new token.
+template <int D, class WriteCodes>
+__device__ __forceinline__ BlockScales step_append(const AttnArgs& a, const StepLens& sl,
+                                                   int64_t row, int cap, int lane,
+                                                   const uint4 (&fresh)[2],
+                                                   const AppendPlan (&plan)[2],
+                                                   WriteCodes write_codes) {
+  if (sl.len0 >= cap) return {0.0f, 0.0f, 0.0f, 0.0f};
+  write_codes(plan);
+  return append_finish<D, kWave>(a.ap, row, sl.len0, lane, fresh, plan);
 }
 
 // ---- split kernel: grid (n_split, heads, batch), kSplitWaves waves ------------------
@@ -592,11 +657,20 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
 
   float p[TPL];
   bool streaming = true;
+  uint32_t ticket = 0;  // the append wave's arrival ticket (lane 0)
   if constexpr (kAppend) {
+    u32x4 fresh_k = {0u, 0u, 0u, 0u}, fresh_v = {0u, 0u, 0u, 0u};
+    if (wave == kSplitWaves && sl.len0 < cap)
+      step_stage_load<D>(a, sl, row, lane, xs, fresh_k, fresh_v);
+    step_release();
     if (wave == kSplitWaves) {  // the append wave
       streaming = false;
-      const BlockScales sc = step_append<SCHEME, D>(
-          a, sl, b, row, cap, lane, xs, [&](const AppendPlan (&plan)[2]) {
+      const uint4 fresh[2] = {make_uint4(fresh_k.x, fresh_k.y, fresh_k.z, fresh_k.w),
+                              make_uint4(fresh_v.x, fresh_v.y, fresh_v.z, fresh_v.w)};
+      AppendPlan plan[2];
+      if (sl.len0 < cap) step_stage_reduce<SCHEME, D>(sl, lane, xs, fresh, plan);
+      const BlockScales sc = step_append<D>(
+          a, sl, row, cap, lane, fresh, plan, [&](const AppendPlan (&plan)[2]) {
             append_write_codes<SCHEME, D, kWave>(a.ap, row, sl.len0, lane, xs, plan);
           });
       if (sl.tail_blk >= 0) {
@@ -611,6 +685,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
         block_weights(sl.tail_blk, sc.ks, sc.kz, kr, p);
         block_accumulate(sl.tail_blk, sc.vs, sc.vz, vr, p);
       }
+      ticket = step_ticket(a, b, lane);
     }
   }
   if (streaming)
@@ -668,6 +743,9 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
     L = __builtin_fmaf(alpha[w], sw, L);
   }
   finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
+  if constexpr (kAppend) {
+    if (wave == kSplitWaves) step_ticket_done(a, sl, b, cap, ticket, lane);
+  }
 }
 
 // ---- int4 split kernel on the matrix cores --------------------------------------------
@@ -845,6 +923,12 @@ attn_split_int4_kernel(AttnArgs a) {
                                                 a.max_blocks, b, h, blk))
                   : blk;
   };
+  // block `slot` (block_slot order) of a code pool, any layout, through the caches
+  auto load_codes_at = [&](bool is_v, int64_t slot, uint4 (&r)[LOADS]) {
+    const __amdgpu_buffer_rsrc_t rs = region_rsrc(is_v ? a.v_codes : a.k_codes, slot, kRegionBytes);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) r[i] = load_b128<0>(rs, lane_off, i * kWave * 16);
+  };
 
 
   // Scores of the block's 64 tokens (lanes 0..15 hold tokens 16*nt + lane), the
@@ -922,20 +1006,36 @@ attn_split_int4_kernel(AttnArgs a) {
 
   float p[4];
   bool streaming = true;
+  uint32_t ticket = 0;  // the append wave's arrival ticket (lane 0)
   if constexpr (kAppend) {
+    // the append wave requests the staged tokens, the new token and the new token's
+    // block as it is before the append, then releases the others
+    const int64_t tblk = block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks, b, h,
+                                    min(sl.len0, cap - 1) / kBlock);
+    uint4 kold[LOADS], vold[LOADS];
+    u32x4 fresh_k = {0u, 0u, 0u, 0u}, fresh_v = {0u, 0u, 0u, 0u};
+    if (wave == kSplitWaves) {
+      if (sl.len0 < cap) step_stage_load<D>(a, sl, row, lane, xs, fresh_k, fresh_v);
+      load_codes_at(false, tblk, kold);
+      load_codes_at(true, tblk, vold);
+    }
+    step_release();
     if (wave == kSplitWaves) {  // the append wave
       streaming = false;
-      // the new token's block is coded in registers by the code writes
+      const uint4 fresh[2] = {make_uint4(fresh_k.x, fresh_k.y, fresh_k.z, fresh_k.w),
+                              make_uint4(fresh_v.x, fresh_v.y, fresh_v.z, fresh_v.w)};
+      AppendPlan plan[2];
+      if (sl.len0 < cap) step_stage_reduce<KVQ_INT4_SYM, D>(sl, lane, xs, fresh, plan);
+      ticket = step_ticket(a, b, lane);
+      // the code writes leave the block's new codes in registers
       uint4 kr[LOADS], vr[LOADS];
-      const BlockScales sc = step_append<KVQ_INT4_SYM, D>(
-          a, sl, b, row, cap, lane, xs, [&](const AppendPlan (&plan)[2]) {
-            const int64_t blk = block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks,
-                                           b, h, sl.len0 / kBlock);
+      const BlockScales sc = step_append<D>(
+          a, sl, row, cap, lane, fresh, plan, [&](const AppendPlan (&plan)[2]) {
             const int slot = sl.len0 % kBlock;
-            int4_tail_fragments<D>(xs, slot, plan[0], false, lane, kr,
-                                   a.ap.k_codes + blk * kRegionBytes);
-            int4_tail_fragments<D>(xs + kBlock * D, slot, plan[1], true, lane, vr,
-                                   a.ap.v_codes + blk * kRegionBytes);
+            int4_tail_fragments<D>(xs, slot, plan[0], false, lane, kold, kr,
+                                   a.ap.k_codes + tblk * kRegionBytes);
+            int4_tail_fragments<D>(xs + kBlock * D, slot, plan[1], true, lane, vold, vr,
+                                   a.ap.v_codes + tblk * kRegionBytes);
           });
       if (sl.tail_blk >= 0) {
         block_weights(sl.tail_blk, sc.ks, kr, p);
@@ -986,6 +1086,9 @@ attn_split_int4_kernel(AttnArgs a) {
 #pragma unroll
   for (int w = 0; w < kStates; ++w) L = __builtin_fmaf(alpha[w], red_l[w], L);
   finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
+  if constexpr (kAppend) {
+    if (wave == kSplitWaves) step_ticket_done(a, sl, b, cap, ticket, lane);
+  }
 }
 
 // ---- grouped-query attention: G query heads per cached head ---------------------------

@@ -91,75 +91,159 @@ __device__ __forceinline__ void uint8_scale_zero(float mn, float mx, float& s, f
   zp = __builtin_rintf(-mn / s) + 0.0f;
 }
 
+// ---- codes: rounding decisions on the quotient x / s --------------------------------
+// Every code is a rounding decision on the correctly rounded quotient RN(x / s). It is
+// taken on q = RN(x * r), r = RN(1 / s), one multiply instead of a division:
+// q = (x / s)(1 + e1)(1 + e2) and RN(x / s) = (x / s)(1 + e3), |ei| <= 2^-24, so
+// |q - RN(x / s)| < 2^-22 |q|. When q lies farther than 2^-20 |q| from every decision
+// boundary, both round to the same code; otherwise the division is done. (q - rint(q) and
+// the distance to the boundary are exact by Sterbenz's lemma, and 2^-20 |q| is a
+// power-of-two scaling, so the test itself does not round.) The slow path is taken for
+// about one value in 10^5 and for a block's extreme element, whose quotient sits on a
+// boundary (7.5 for int4).
+struct Divisor {
+  float s, r;
+  __device__ explicit Divisor(float s_) : s(s_), r(s_ == 0.0f ? 0.0f : 1.0f / s_) {}
+};
+
+// rint(q), q = RN(x * r); `near` is or-ed with whether rint(RN(x / s)) may differ.
+__device__ __forceinline__ float rint_quotient_fast(float x, const Divisor& d, bool& near) {
+  const float q = x * d.r;
+  const float c = __builtin_rintf(q);
+  near |= !(0.5f - fabsf(q - c) > fabsf(q) * 0x1p-20f);
+  return c;
+}
+
+// rint(RN(x / s)) (round half to even), s != 0.
+__device__ __forceinline__ float rint_quotient(float x, const Divisor& d) {
+  bool near = false;
+  const float c = rint_quotient_fast(x, d, near);
+  return near ? __builtin_rintf(x / d.s) : c;
+}
+
 // int4 code c = clamp(rint(x / s), -8, 7) (0 when s = 0), returned as the stored
 // offset-binary nibble c + 8.
-__device__ __forceinline__ uint32_t int4_code(float x, float s) {
-  if (s == 0.0f) return 8u;
-  int c = static_cast<int>(__builtin_rintf(x / s));
+__device__ __forceinline__ uint32_t int4_code(float x, const Divisor& d) {
+  if (d.s == 0.0f) return 8u;
+  int c = static_cast<int>(rint_quotient(x, d));
   c = c < -8 ? -8 : (c > 7 ? 7 : c);
   return static_cast<uint32_t>(c + 8);
 }
 
-__device__ __forceinline__ uint32_t uint8_code(float x, float s, int zpi) {
-  if (s == 0.0f) return 0u;
-  int c = static_cast<int>(__builtin_rintf(x / s)) + zpi;
+__device__ __forceinline__ uint32_t uint8_code(float x, const Divisor& d, int zpi) {
+  if (d.s == 0.0f) return 0u;
+  int c = static_cast<int>(rint_quotient(x, d)) + zpi;
   c = c < 0 ? 0 : (c > 255 ? 255 : c);
   return static_cast<uint32_t>(c);
 }
 
 // FP8 E4M3 (OCP "fn": bias 7, subnormals (m/8)*2^-6, largest finite 448 = code 0x7E):
 // s = absmax / 448 (0 for an all-zero block); the code of x is the E4M3 value nearest
-// to x / s with ties to the even code, the sign kept, saturating at 448. Every step
-// below is exact but the final rint: scaling by powers of two and subtracting the
-// binade's leading 8.
+// to x / s with ties to the even code, the sign kept, saturating at 448.
 __device__ __forceinline__ float fp8_scale(float absmax) {
   return absmax == 0.0f ? 0.0f : absmax / 448.0f;
 }
 
-__device__ __forceinline__ uint32_t fp8_code(float x, float s) {
-  if (s == 0.0f) return 0u;
-  const float q = x / s;
+// The E4M3 code of q. Every step is exact but the rint: scaling by powers of two to the
+// position t on the binade's grid of 8 steps (the subnormal grid below 2^-6), whose
+// rounding carries into the next binade at 8. `near` is set when t lies within 2^-16
+// of a half step, i.e. within 2^-20 |q| of a decision boundary (t < 16): a value that
+// close to q may round the other way. There is no boundary at 448 (432 .. 448 -> 0x7E).
+__device__ __forceinline__ uint32_t fp8_round(float q, bool& near) {
   const uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 24) & 0x80u;
   const float a = fabsf(q);
-  uint32_t c;
   if (a >= 448.0f) {
-    c = 0x7Eu;
-  } else if (a < 0.015625f) {  // below 2^-6: the subnormal grid, steps of 2^-9
-    c = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));  // 8 is code 0x08 = 2^-6
+    near = false;
+    return sign | 0x7Eu;
+  }
+  float t;
+  uint32_t base;
+  if (a < 0.015625f) {  // below 2^-6: the subnormal grid, steps of 2^-9
+    t = a * 512.0f;
+    base = 0u;
   } else {
     const int e = static_cast<int>((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;
-    const float m = __builtin_rintf(__builtin_ldexpf(a, 3 - e) - 8.0f);  // 0..8
-    c = static_cast<uint32_t>((e + 7) * 8) + static_cast<uint32_t>(m);   // 8 carries
+    t = __builtin_ldexpf(a, 3 - e) - 8.0f;  // 0 <= t < 8
+    base = static_cast<uint32_t>((e + 7) * 8);
   }
-  return sign | c;
+  const float m = __builtin_rintf(t);  // 8 carries into the next binade
+  near = 0.5f - fabsf(t - m) <= 0x1p-16f;
+  return sign | (base + static_cast<uint32_t>(m));
 }
 
-// 8 consecutive channels -> 8 bytes of FP8 codes.
-__device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], float s) {
-  uint2 r;
-  r.x = fp8_code(x[0], s) | (fp8_code(x[1], s) << 8) | (fp8_code(x[2], s) << 16) |
-        (fp8_code(x[3], s) << 24);
-  r.y = fp8_code(x[4], s) | (fp8_code(x[5], s) << 8) | (fp8_code(x[6], s) << 16) |
-        (fp8_code(x[7], s) << 24);
-  return r;
+__device__ __forceinline__ uint32_t fp8_code(float x, const Divisor& d) {
+  if (d.s == 0.0f) return 0u;
+  bool near;
+  const uint32_t c = fp8_round(x * d.r, near);
+  if (!near) return c;
+  return fp8_round(x / d.s, near);
 }
 
-// 8 consecutive channels -> 4 bytes of int4 nibbles (channel 2k low, 2k+1 high).
-__device__ __forceinline__ uint32_t pack_int4x8(const float (&x)[8], float s) {
+// The packers below code 8 values with the multiply and take one branch, for all 8, in
+// the rare case that one of them needs the division.
+
+// 8 values -> 8 bytes of FP8 codes (x[i] in byte i).
+__device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], const Divisor& d) {
+  if (d.s == 0.0f) return make_uint2(0u, 0u);
+  uint32_t c[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bool n;
+    c[i] = fp8_round(x[i] * d.r, n);
+    near |= n;
+  }
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bool n;
+      c[i] = fp8_round(x[i] / d.s, n);
+    }
+  }
+  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                    c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+// 8 values -> 4 bytes of int4 nibbles c + 8 (x[i] in bits 4i .. 4i+3; for 8 consecutive
+// channels: channel 2k in the low nibble of byte k).
+__device__ __forceinline__ uint32_t pack_int4x8(const float (&x)[8], const Divisor& d) {
+  if (d.s == 0.0f) return 0x88888888u;
+  float c[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = rint_quotient_fast(x[i], d, near);
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_rintf(x[i] / d.s);
+  }
   uint32_t w = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w |= int4_code(x[i], s) << (4 * i);
+  for (int i = 0; i < 8; ++i) {
+    const float v = __builtin_fminf(__builtin_fmaxf(c[i], -8.0f), 7.0f) + 8.0f;  // exact
+    w |= static_cast<uint32_t>(v) << (4 * i);
+  }
   return w;
 }
 
-// 8 consecutive channels -> 8 bytes of uint8 codes.
-__device__ __forceinline__ uint2 pack_uint8x8(const float (&x)[8], float s, int zpi) {
-  uint2 r;
-  r.x = uint8_code(x[0], s, zpi) | (uint8_code(x[1], s, zpi) << 8) |
-        (uint8_code(x[2], s, zpi) << 16) | (uint8_code(x[3], s, zpi) << 24);
-  r.y = uint8_code(x[4], s, zpi) | (uint8_code(x[5], s, zpi) << 8) |
-        (uint8_code(x[6], s, zpi) << 16) | (uint8_code(x[7], s, zpi) << 24);
-  return r;
+// 8 values -> 8 bytes of uint8 codes (x[i] in byte i).
+__device__ __forceinline__ uint2 pack_uint8x8(const float (&x)[8], const Divisor& d, int zpi) {
+  if (d.s == 0.0f) return make_uint2(0u, 0u);
+  float c[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = rint_quotient_fast(x[i], d, near);
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_rintf(x[i] / d.s);
+  }
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int v = static_cast<int>(c[i]) + zpi;
+    b[i] = static_cast<uint32_t>(v < 0 ? 0 : (v > 255 ? 255 : v));
+  }
+  return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                    b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
 }
 
 // ---- int4 cache block layout ---------------------------------------------------------

@@ -78,17 +78,18 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(QuantArgs a) 
     uint8_scale_zero(-st[0], st[1], s, zp);
   }
   const int zpi = static_cast<int>(zp);
+  const Divisor dv(s);
 
   const int64_t row = static_cast<int64_t>(b) * a.heads + h;
   const int64_t blk = block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks, b, h, j);
   uint8_t* codes = (kv ? a.v_codes : a.k_codes) + blk * kBlock * G::kRowBytes;
   if constexpr (SCHEME == KVQ_INT4_SYM) {
-    int4_write_block_from<D>(xs, ntok, s, kv != 0, codes, tid);  // block_max synced xs
+    int4_write_block_from<D>(xs, ntok, dv, kv != 0, codes, tid);  // block_max synced xs
   } else {
 #pragma unroll
     for (int p = 0; p < G::kPasses; ++p) {
       const int t = p * G::kTokensPerPass + tr;
-      store_codes<SCHEME, D>(codes + t * G::kRowBytes, chunk, x[p], s, zpi, t < ntok);
+      store_codes<SCHEME, D>(codes + t * G::kRowBytes, chunk, x[p], dv, zpi, t < ntok);
     }
   }
   if (tid == 0) {
