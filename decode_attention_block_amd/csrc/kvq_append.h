@@ -323,7 +323,7 @@ __device__ __forceinline__ void append_write_codes(const AppendArgs& a, int64_t 
         // V: each channel's new nibble shares a dword with 7 other tokens; with the
         // scale unchanged, rebuilding the dword from the staged values reproduces the
         // stored nibbles (and zeros past the token), so the cache is never read back
-        const int ks = slot / 32, g = (slot % 32) / 8, t0 = 32 * ks + 8 * g;
+        const int ks = slot / 32, g = (slot % 32) / 8;
         for (int d = tid; d < D; d += NT) {
           const int lane = 16 * g + d % 16, f = 2 * (d / 16) + ks;
           *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(lane, f)) =

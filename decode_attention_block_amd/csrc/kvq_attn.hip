@@ -369,20 +369,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const uint8_t* poo
 
 // ---- fused decode step ----------------------------------------------------------------
 // In a decode step (kAppend) the workgroup of row (b, h) has one wave more than the
-// attention. The row's length is read once, before anything else. Then the whole
-// workgroup stages the open block (append_stage over all its threads: the row's staged
-// tokens and the new one into LDS, the block statistics before and after the token, the
-// plan), and the waves part: waves 0 .. kSplitWaves-1 attend the blocks the append
-// leaves untouched while the last wave writes the new codes, the token's staging and the
-// scales, and attends the block that holds the token. Staging together at the start,
-// while the memory pipeline is still empty, matters: afterwards the streaming waves keep
-// the compute unit's queue of memory requests full, and a wave that has to issue dozens
-// of requests behind them (32 loads per lane for the staged block) waits tens of
-// microseconds, longer than the streaming itself.
+// attention. The row's length is read once, before anything else. The last wave (the
+// append wave) then requests the row's staged tokens (straight into LDS), the new token
+// and, for int4, the open block's codes, and only then releases the other waves with a
+// barrier, so that its requests enter the compute unit's memory pipeline first: once the
+// streaming waves keep that pipeline full, a wave with dozens of requests queued behind
+// them waits tens of microseconds, longer than the streaming itself. Waves
+// 0 .. kSplitWaves-1 then attend the blocks the append leaves untouched while the append
+// wave reduces the block statistics before and after the token, writes the new codes
+// (the whole block if its statistic changed, else the token's codes), the token's staging
+// and the scales, and attends the block that holds the token.
 // The append wave takes the sequence's arrival ticket (1 << 24 added to seq_lens[b], as
-// in kv_append) right after the length is read, and the last of the sequence's `heads`
-// workgroups stores the new length when its work is done. Since every workgroup of the
-// sequence reads the length before it takes its ticket, none can see the new length.
+// in kv_append) once its own loads have completed, and the last of the sequence's `heads`
+// workgroups stores the new length when its work is done. Every workgroup of the
+// sequence reads the length before it takes its ticket, and the length changes only at
+// the last ticket, so none can see the new length.
 constexpr int kStepWaves = kSplitWaves + 1;
 
 struct StepLens {
