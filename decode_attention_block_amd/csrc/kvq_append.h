@@ -401,20 +401,18 @@ __device__ __forceinline__ uint32_t get_dword(const uint4 (&r)[N], int f) {
   return v;
 }
 
-// Code writes of one int4 tensor by one wave that also leaves the block's new codes in
-// registers, so the wave can attend the block without reading it back: r receives
-// chunk i (i < D/32) of the lane, i.e. bytes ((i * 64) + lane) * 16 .. +15 of the
-// region. `old` holds the same chunks as stored before the append. A re-quantized block
-// is coded whole from the staged values (tokens 0..slot, zeros after) and written
-// whole; otherwise the other tokens keep their codes, so the token's codes are coded
-// and patched into `old`, and only they are written (the token's D/2 bytes of K, and
-// of V the byte holding each channel's nibble): stores into the code buffer cost the
-// concurrent code stream far more than their size.
+// The new codes of one int4 tensor's open block, built in registers by one wave: r
+// receives chunk i (i < D/32) of the lane, i.e. bytes ((i * 64) + lane) * 16 .. +15 of
+// the block's region. `old` holds the same chunks as stored before the append. A
+// re-quantized block is coded whole from the staged values (tokens 0..slot, zeros after);
+// otherwise the other tokens keep their codes, so only the token's codes are coded and
+// patched into `old`. Nothing is written here: the wave writes r whole at the end of the
+// decode step, after the stream of the row's other blocks (see the step kernel).
 template <int D>
 __device__ __forceinline__ void int4_tail_fragments(const _Float16* xt, int slot,
                                                     const AppendPlan& pl, bool is_v, int lane,
                                                     const uint4 (&old)[D / 32],
-                                                    uint4 (&r)[D / 32], uint8_t* codes) {
+                                                    uint4 (&r)[D / 32]) {
   constexpr int LOADS = D / 32;  // chunks per lane
   constexpr int KS = D / 32;     // K: dwords per token per lane group
   const Divisor s(pl.s);
@@ -425,7 +423,6 @@ __device__ __forceinline__ void int4_tail_fragments(const _Float16* xt, int slot
 #pragma unroll
       for (int c = 0; c < 4; ++c) w[c] = int4_fragment_word<D>(xt, slot + 1, s, is_v, lane, 4 * i + c);
       r[i] = make_uint4(w[0], w[1], w[2], w[3]);
-      store_b128(codes + (i * kWave + lane) * 16, r[i]);
     }
     return;
   }
@@ -441,15 +438,12 @@ __device__ __forceinline__ void int4_tail_fragments(const _Float16* xt, int slot
     for (int c = 0; c < 4; ++c) {
       const int f = 4 * i + c;
       if (!is_v) {
-        if (f / KS == slot / 16 && owner) {  // the token's dword f
+        if (f / KS == slot / 16 && owner)  // the token's dword f
           w[c] = int4_fragment_word<D>(xt, slot + 1, s, false, lane, f);
-          *reinterpret_cast<uint32_t*>(codes + int4_dword_offset(lane, f)) = w[c];
-        }
       } else if (f % 2 == slot / 32 && owner) {  // channel 16 (f / 2) + lane % 16
         const uint32_t code =
             int4_code(static_cast<float>(xt[slot * D + 16 * (f / 2) + lane % 16]), s);
         w[c] = (w[c] & ~(0xFu << (4 * q))) | (code << (4 * q));
-        codes[int4_dword_offset(lane, f) + q / 2] = static_cast<uint8_t>(w[c] >> (8 * (q / 2)));
       }
     }
     r[i] = make_uint4(w[0], w[1], w[2], w[3]);

@@ -376,9 +376,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const uint8_t* poo
 // streaming waves keep that pipeline full, a wave with dozens of requests queued behind
 // them waits tens of microseconds, longer than the streaming itself. Waves
 // 0 .. kSplitWaves-1 then attend the blocks the append leaves untouched while the append
-// wave reduces the block statistics before and after the token, writes the new codes
-// (the whole block if its statistic changed, else the token's codes), the token's staging
-// and the scales, and attends the block that holds the token.
+// wave reduces the block statistics before and after the token, codes the block (the
+// whole block if its statistic changed, else the token), writes the token's staging and
+// the scales, and attends the block that holds the token. The uint8 and FP8 waves write
+// the token's codes at once and read the block back; the int4 wave holds the new block
+// in registers and writes it whole at the end of the kernel.
 // The append wave takes the sequence's arrival ticket (1 << 24 added to seq_lens[b], as
 // in kv_append) once its own loads have completed, and the last of the sequence's `heads`
 // workgroups stores the new length when its work is done. Every workgroup of the
@@ -483,8 +485,9 @@ __device__ __forceinline__ void step_ticket_done(const AttnArgs& a, const StepLe
                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// The append wave's writes after the stage: write_codes(plan) writes the codes, then the
-// token's fp16 staging and the changed scales. Returns the scales (and zero points) of
+// The append wave's work after the stage: write_codes(plan) writes the codes (uint8,
+// FP8) or builds them in registers (int4, written at the end of the kernel), then the
+// token's fp16 staging and the changed scales are written. Returns the scales (and zero points) of
 // the block holding the new token.
 template <int D, class WriteCodes>
 __device__ __forceinline__ BlockScales step_append(const AttnArgs& a, const StepLens& sl,
@@ -1008,10 +1011,12 @@ attn_split_int4_kernel(AttnArgs a) {
   float p[4];
   bool streaming = true;
   uint32_t ticket = 0;  // the append wave's arrival ticket (lane 0)
+  uint4 kr[LOADS], vr[LOADS];  // the append wave: the open block's new codes
+  int64_t tblk = 0;            // the append wave: the open block's index (block_slot)
   if constexpr (kAppend) {
     // the append wave requests the staged tokens, the new token and the new token's
     // block as it is before the append, then releases the others
-    const int64_t tblk = block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks, b, h,
+    tblk = block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks, b, h,
                                     min(sl.len0, cap - 1) / kBlock);
     uint4 kold[LOADS], vold[LOADS];
     u32x4 fresh_k = {0u, 0u, 0u, 0u}, fresh_v = {0u, 0u, 0u, 0u};
@@ -1028,15 +1033,12 @@ attn_split_int4_kernel(AttnArgs a) {
       AppendPlan plan[2];
       if (sl.len0 < cap) step_stage_reduce<KVQ_INT4_SYM, D>(sl, lane, xs, fresh, plan);
       ticket = step_ticket(a, b, lane);
-      // the code writes leave the block's new codes in registers
-      uint4 kr[LOADS], vr[LOADS];
+      // the block's new codes, in registers until the end of the kernel
       const BlockScales sc = step_append<D>(
           a, sl, row, cap, lane, fresh, plan, [&](const AppendPlan (&plan)[2]) {
             const int slot = sl.len0 % kBlock;
-            int4_tail_fragments<D>(xs, slot, plan[0], false, lane, kold, kr,
-                                   a.ap.k_codes + tblk * kRegionBytes);
-            int4_tail_fragments<D>(xs + kBlock * D, slot, plan[1], true, lane, vold, vr,
-                                   a.ap.v_codes + tblk * kRegionBytes);
+            int4_tail_fragments<D>(xs, slot, plan[0], false, lane, kold, kr);
+            int4_tail_fragments<D>(xs + kBlock * D, slot, plan[1], true, lane, vold, vr);
           });
       if (sl.tail_blk >= 0) {
         block_weights(sl.tail_blk, sc.ks, kr, p);
@@ -1088,7 +1090,23 @@ attn_split_int4_kernel(AttnArgs a) {
   for (int w = 0; w < kStates; ++w) L = __builtin_fmaf(alpha[w], red_l[w], L);
   finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
   if constexpr (kAppend) {
-    if (wave == kSplitWaves) step_ticket_done(a, sl, b, cap, ticket, lane);
+    if (wave == kSplitWaves) {
+      // The open block's new codes, written whole (whole 64-byte lines) once the row's
+      // other blocks have been streamed: stores into the code buffer during the stream
+      // slow it by more than their size (measured on the 8K int4 step: token-sized
+      // stores at once 47.8 us, whole block at once 49.0 us, whole block at the end
+      // 46.5 us, no stores 45.6 us).
+      if (sl.len0 < cap) {
+        uint8_t* kc = a.ap.k_codes + tblk * kRegionBytes;
+        uint8_t* vc = a.ap.v_codes + tblk * kRegionBytes;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          store_b128(kc + (i * kWave + lane) * 16, kr[i]);
+          store_b128(vc + (i * kWave + lane) * 16, vr[i]);
+        }
+      }
+      step_ticket_done(a, sl, b, cap, ticket, lane);
+    }
   }
 }
 
