@@ -411,7 +411,7 @@ def run_gqa(kvq, torch, w, steps, warmup, bps, paged=False):
     wall_s = time.perf_counter() - wall0
     total_ms = timer.total_ms()
     per_launch = attention_bytes(w, lens)
-    bps_eff, n_split = kvq.decode_attn_plan(caches[0], L, bps)
+    bps_eff, n_split = kvq.decode_attn_gqa_plan(caches[0], G, L, bps)
     res = {
         "workload": w.name,
         "step": f"decode_attn_gqa ({G} query heads per cached head)",

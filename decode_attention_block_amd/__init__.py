@@ -25,7 +25,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_ENOTSUP", -3: "KVQ_ECAPACITY",
 EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan",
            "decode_attn_workspace_bytes", "decode_attn_qkv", "decode_attn_split",
            "decode_attn_combine", "decode_step_qkv", "decode_attn_gqa",
-           "decode_attn_gqa_workspace_bytes", "kvq_strerror", "kvq_version"]
+           "decode_attn_gqa_workspace_bytes", "decode_attn_gqa_plan", "kvq_strerror",
+           "kvq_version"]
 
 
 class KvqError(RuntimeError):
@@ -76,6 +77,8 @@ def load_library():
         "decode_step_qkv": ([C, P, P, P, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
         "decode_attn_gqa": ([C, P, i32, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
         "decode_attn_gqa_workspace_bytes": ([C, i32, i32, i32], sz),
+        "decode_attn_gqa_plan": ([C, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
+                                 ctypes.c_int),
         "kvq_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "kvq_version": ([], ctypes.c_int),
     }
@@ -141,6 +144,15 @@ def decode_attn_plan(cache, max_len, blocks_per_split=0):
     rc = load_library().decode_attn_plan(_desc(cache), int(max_len), int(blocks_per_split),
                                          ctypes.byref(bps), ctypes.byref(ns))
     _check(rc, "decode_attn_plan")
+    return bps.value, ns.value
+
+
+def decode_attn_gqa_plan(cache, group, max_len, blocks_per_split=0):
+    bps, ns = ctypes.c_int32(), ctypes.c_int32()
+    rc = load_library().decode_attn_gqa_plan(_desc(cache), int(group), int(max_len),
+                                             int(blocks_per_split), ctypes.byref(bps),
+                                             ctypes.byref(ns))
+    _check(rc, "decode_attn_gqa_plan")
     return bps.value, ns.value
 
 

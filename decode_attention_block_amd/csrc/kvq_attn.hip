@@ -57,32 +57,65 @@ __device__ __forceinline__ uint4 load_stream(__amdgpu_buffer_rsrc_t rsrc, int vo
 }
 
 // Partial states cross workgroups (and L2 slices: the eight XCDs do not share an L2)
-// through agent-scope atomic stores and loads, which go to memory instead of a
-// possibly stale L2 line; a full device-scope fence would write back and invalidate
-// the whole L2 in every workgroup.
+// through agent-scope atomic stores and agent-coherent loads (merge_row), which go to
+// memory instead of a possibly stale L2 line; a full device-scope fence would write
+// back and invalidate the whole L2 in every workgroup.
 __device__ __forceinline__ void store_shared(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_shared(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Log-sum-exp merge of the n partial states of one row into its fp16 output channel d:
 // M = max_j m_j, o = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M); zeros when n = 0.
+// The partials are read kMergeChunk splits at a time, all of a chunk's loads issued
+// before any is used, so a merge costs about 2 n / kMergeChunk memory round trips
+// instead of 2 n (the sums still run over j in order, so the result does not depend on
+// the chunking). They are buffer loads over exactly the row's partials (loads past the
+// n-th return 0 and are masked out); in the fused merge (kCoherent) they carry the
+// agent-scope coherence bit sc1, so that they read what other workgroups stored with
+// agent-scope atomic stores rather than a possibly stale L2 line, as an agent-scope
+// atomic load would, but without an atomic's ordering, which made every load wait for
+// the previous one.
+constexpr int kMergeChunk = 8;
+constexpr int kCachePolicyAgent = 16;  // sc1
+
 template <int D, bool kCoherent>
 __device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t row, int n, int d) {
-  auto ld = [](const float* p) { return kCoherent ? load_shared(p) : *p; };
   _Float16 r = 0;
   if (n > 0) {
-    const float* ml = a.ws_ml + row * a.n_split * 2;
-    const float* po = a.ws_o + row * a.n_split * D + d;
-    float M = ld(ml);
-    for (int j = 1; j < n; ++j) M = fmaxf(M, ld(ml + 2 * j));
+    constexpr int aux = kCoherent ? kCachePolicyAgent : 0;
+    const __amdgpu_buffer_rsrc_t mlr = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_ml + row * a.n_split * 2, 0, n * 2 * 4, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t por = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_o + row * a.n_split * D, 0, n * D * 4, kBufferRsrcWord3);
+    auto ld = [](__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, aux));
+    };
+    float M = -__builtin_inff();
+    for (int j0 = 0; j0 < n; j0 += kMergeChunk) {
+      float m[kMergeChunk];
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k) m[k] = ld(mlr, 0, (j0 + k) * 8);
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k)
+        if (j0 + k < n) M = fmaxf(M, m[k]);
+    }
     float L = 0.0f, acc = 0.0f;
-    for (int j = 0; j < n; ++j) {
-      const float w = __builtin_amdgcn_exp2f(ld(ml + 2 * j) - M);
-      L = __builtin_fmaf(w, ld(ml + 2 * j + 1), L);
-      acc = __builtin_fmaf(w, ld(po + j * D), acc);
+    for (int j0 = 0; j0 < n; j0 += kMergeChunk) {
+      float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k) {
+        m[k] = ld(mlr, 0, (j0 + k) * 8);
+        l[k] = ld(mlr, 0, (j0 + k) * 8 + 4);
+        o[k] = ld(por, d * 4, (j0 + k) * D * 4);
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k) {
+        if (j0 + k < n) {
+          const float w = __builtin_amdgcn_exp2f(m[k] - M);
+          L = __builtin_fmaf(w, l[k], L);
+          acc = __builtin_fmaf(w, o[k], acc);
+        }
+      }
     }
     r = static_cast<_Float16>(acc / L);
   }
@@ -1414,8 +1447,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
                                     __HIP_MEMORY_SCOPE_SYSTEM);
   __syncthreads();
   if (ticket == static_cast<uint32_t>(n_row - 1)) {
+    // a wave's 64 threads share t / D (D is a multiple of the wave size): a uniform row
     for (int t = threadIdx.x; t < G * D; t += kThreadsWg)
-      merge_row<D, true>(a, qrow0 + t / D, n_row, t % D);
+      merge_row<D, true>(a, qrow0 + __builtin_amdgcn_readfirstlane(t / D), n_row, t % D);
     if (threadIdx.x == 0)
       __hip_atomic_store(a.counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }

@@ -241,8 +241,10 @@ int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new
 /* Grouped-query decode attention (several query heads share each cached head, as in
  * multi-query and grouped-query attention): query head hq = h * group + g of sequence b
  * attends over cache row (b, h), for g < group. The result is decode_attn_qkv's for
- * each query head against its cache row (same definition, splits and merge); the
- * codes of a block are turned into matrix-core operands once for all `group` queries.
+ * each query head against its cache row (same definition, splits and merge for the
+ * same blocks_per_split); the codes of a block are turned into matrix-core operands
+ * once for all `group` queries. The automatic plan (blocks_per_split = 0) aims at about
+ * two workgroups per compute unit for group > 1 (decode_attn_gqa_plan).
  * (Decode attention as in decode_attn_qkv with cached heads shared between query
  * heads: MLA with its projections absorbed decodes as multi-query attention, [Pg3] §二.)
  *   q, out    : fp16 [B][H * group][D] contiguous, 16-byte aligned.
@@ -259,6 +261,14 @@ int decode_attn_gqa(const kvq_cache* cache, const void* q, int32_t group, float 
 /* Bytes of device workspace decode_attn_gqa needs (0 on invalid arguments). */
 size_t decode_attn_gqa_workspace_bytes(const kvq_cache* cache, int32_t group, int32_t max_len,
                                        int32_t blocks_per_split);
+
+/* Work split of decode_attn_gqa, as decode_attn_plan: writes the effective blocks per
+ * split and splits per cache row for this group and max_len (group 1 gives
+ * decode_attn_plan's). Host only. Returns KVQ_OK, KVQ_EINVAL for group < 1, or
+ * decode_attn_plan's errors. */
+int decode_attn_gqa_plan(const kvq_cache* cache, int32_t group, int32_t max_len,
+                         int32_t blocks_per_split, int32_t* blocks_per_split_out,
+                         int32_t* splits_per_row_out);
 
 /* Human-readable text of a kvq_status (static storage). */
 const char* kvq_strerror(int status);

@@ -203,6 +203,19 @@ def test_automatic_plan_fills_the_gpu_with_fewest_splits():
     assert kvq.decode_attn_plan(cache(B=1, H=2, MB=4), 256) == (1, 4)
 
 
+def test_grouped_query_plan_aims_at_two_workgroups_per_cu():
+    # 8 sequences x 8 cached heads, 8K: 64 rows -> 8 splits of 16 blocks (512 workgroups)
+    c = cache(B=8, H=8, MB=128)
+    assert kvq.decode_attn_gqa_plan(c, 8, 8192) == (16, 8)
+    assert kvq.decode_attn_gqa_plan(c, 1, 8192) == kvq.decode_attn_plan(c, 8192) == (32, 4)
+    assert kvq.decode_attn_gqa_plan(c, 4, 8192, 5) == (5, (128 + 4) // 5)
+    # the workspace follows the grouped plan
+    assert kvq.decode_attn_gqa_workspace_bytes(c, 8, 8192, 0) == \
+        kvq.decode_attn_gqa_workspace_bytes(c, 8, 8192, 16)
+    with pytest.raises(kvq.KvqError):
+        kvq.decode_attn_gqa_plan(c, 0, 8192)
+
+
 def test_strerror_names_every_status():
     for code in range(-6, 1):
         assert kvq.kvq_strerror(code) != "unknown status"
