@@ -403,49 +403,24 @@ __device__ __forceinline__ uint32_t get_dword(const uint4 (&r)[N], int f) {
 
 // The new codes of one int4 tensor's open block, built in registers by one wave: r
 // receives chunk i (i < D/32) of the lane, i.e. bytes ((i * 64) + lane) * 16 .. +15 of
-// the block's region. `old` holds the same chunks as stored before the append. A
-// re-quantized block is coded whole from the staged values (tokens 0..slot, zeros after);
-// otherwise the other tokens keep their codes, so only the token's codes are coded and
-// patched into `old`. Nothing is written here: the wave writes r whole at the end of the
-// decode step, after the stream of the row's other blocks (see the step kernel).
+// the block's region, coded from the staged values (tokens 0..slot, zeros after) with
+// the block's scale after the append. Whether or not the token changed the scale this
+// is the block's content: every stored code of the open block is the code of its staged
+// value under the block's current scale (prefill, re-quantization and appends all code
+// that way), so the block need not be read back. Nothing is written here: the wave
+// writes r whole at the end of the decode step, after the stream of the row's other
+// blocks (see the step kernel).
 template <int D>
 __device__ __forceinline__ void int4_tail_fragments(const _Float16* xt, int slot,
                                                     const AppendPlan& pl, bool is_v, int lane,
-                                                    const uint4 (&old)[D / 32],
                                                     uint4 (&r)[D / 32]) {
   constexpr int LOADS = D / 32;  // chunks per lane
-  constexpr int KS = D / 32;     // K: dwords per token per lane group
   const Divisor s(pl.s);
-  if (pl.full) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      uint32_t w[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) w[c] = int4_fragment_word<D>(xt, slot + 1, s, is_v, lane, 4 * i + c);
-      r[i] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    return;
-  }
-  // K: lane 16g + slot % 16 holds the token's channels 32 ks + 8 g .. in dwords
-  // (slot / 16) * KS + ks. V: lanes 16g .. 16g + 15, g = (slot % 32) / 8, hold the token
-  // in nibble slot % 8 of dword 2 nt + slot / 32 for channel 16 nt + lane % 16.
-  const bool owner = is_v ? lane / 16 == (slot % 32) / 8 : lane % 16 == slot % 16;
-  const int q = slot % 8;
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    uint32_t w[4] = {old[i].x, old[i].y, old[i].z, old[i].w};
+    uint32_t w[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int f = 4 * i + c;
-      if (!is_v) {
-        if (f / KS == slot / 16 && owner)  // the token's dword f
-          w[c] = int4_fragment_word<D>(xt, slot + 1, s, false, lane, f);
-      } else if (f % 2 == slot / 32 && owner) {  // channel 16 (f / 2) + lane % 16
-        const uint32_t code =
-            int4_code(static_cast<float>(xt[slot * D + 16 * (f / 2) + lane % 16]), s);
-        w[c] = (w[c] & ~(0xFu << (4 * q))) | (code << (4 * q));
-      }
-    }
+    for (int c = 0; c < 4; ++c) w[c] = int4_fragment_word<D>(xt, slot + 1, s, is_v, lane, 4 * i + c);
     r[i] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }

@@ -960,12 +960,6 @@ attn_split_int4_kernel(AttnArgs a) {
                                                 a.max_blocks, b, h, blk))
                   : blk;
   };
-  // block `slot` (block_slot order) of a code pool, any layout, through the caches
-  auto load_codes_at = [&](bool is_v, int64_t slot, uint4 (&r)[LOADS]) {
-    const __amdgpu_buffer_rsrc_t rs = region_rsrc(is_v ? a.v_codes : a.k_codes, slot, kRegionBytes);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) r[i] = load_b128<0>(rs, lane_off, i * kWave * 16);
-  };
 
 
   // Scores of the block's 64 tokens (lanes 0..15 hold tokens 16*nt + lane), the
@@ -1047,17 +1041,13 @@ attn_split_int4_kernel(AttnArgs a) {
   uint4 kr[LOADS], vr[LOADS];  // the append wave: the open block's new codes
   int64_t tblk = 0;            // the append wave: the open block's index (block_slot)
   if constexpr (kAppend) {
-    // the append wave requests the staged tokens, the new token and the new token's
-    // block as it is before the append, then releases the others
+    // the append wave requests the staged tokens and the new token, then releases the
+    // others
     tblk = block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks, b, h,
-                                    min(sl.len0, cap - 1) / kBlock);
-    uint4 kold[LOADS], vold[LOADS];
+                      min(sl.len0, cap - 1) / kBlock);
     u32x4 fresh_k = {0u, 0u, 0u, 0u}, fresh_v = {0u, 0u, 0u, 0u};
-    if (wave == kSplitWaves) {
-      if (sl.len0 < cap) step_stage_load<D>(a, sl, row, lane, xs, fresh_k, fresh_v);
-      load_codes_at(false, tblk, kold);
-      load_codes_at(true, tblk, vold);
-    }
+    if (wave == kSplitWaves && sl.len0 < cap)
+      step_stage_load<D>(a, sl, row, lane, xs, fresh_k, fresh_v);
     step_release();
     if (wave == kSplitWaves) {  // the append wave
       streaming = false;
@@ -1070,8 +1060,8 @@ attn_split_int4_kernel(AttnArgs a) {
       const BlockScales sc = step_append<D>(
           a, sl, row, cap, lane, fresh, plan, [&](const AppendPlan (&plan)[2]) {
             const int slot = sl.len0 % kBlock;
-            int4_tail_fragments<D>(xs, slot, plan[0], false, lane, kold, kr);
-            int4_tail_fragments<D>(xs + kBlock * D, slot, plan[1], true, lane, vold, vr);
+            int4_tail_fragments<D>(xs, slot, plan[0], false, lane, kr);
+            int4_tail_fragments<D>(xs + kBlock * D, slot, plan[1], true, lane, vr);
           });
       if (sl.tail_blk >= 0) {
         block_weights(sl.tail_blk, sc.ks, kr, p);
