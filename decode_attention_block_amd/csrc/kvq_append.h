@@ -101,6 +101,30 @@ __device__ __forceinline__ uint32_t int4_fragment_word(const _Float16* xs, int n
   return pack_int4x8(x, s) & mask;
 }
 
+// uint8 / FP8: 16-byte chunk i of lane `lane` of a block region (bytes
+// (i * 64 + lane) * 16 .. +15, i.e. 16 channels of one token), coded from the block's
+// fp16 values staged in LDS (xs[t * D + d]) with scale s (and zero point zpi); tokens
+// t >= ntok give zero bytes.
+template <int SCHEME, int D>
+__device__ __forceinline__ uint4 byte_codes_chunk(const _Float16* xs, int ntok, const Divisor& s,
+                                                  int zpi, int lane, int i) {
+  const int byte = (i * kWave + lane) * 16;
+  const int t = byte / D, d0 = byte % D;
+  if (t >= ntok) return make_uint4(0u, 0u, 0u, 0u);
+  float x0[8], x1[8];
+  unpack8(*reinterpret_cast<const uint4*>(xs + t * D + d0), x0);
+  unpack8(*reinterpret_cast<const uint4*>(xs + t * D + d0 + 8), x1);
+  uint2 c0, c1;
+  if constexpr (SCHEME == KVQ_FP8_E4M3) {
+    c0 = pack_fp8x8(x0, s);
+    c1 = pack_fp8x8(x1, s);
+  } else {
+    c0 = pack_uint8x8(x0, s, zpi);
+    c1 = pack_uint8x8(x1, s, zpi);
+  }
+  return make_uint4(c0.x, c0.y, c1.x, c1.y);
+}
+
 // int4: writes one block region (K or V) in fragment order from the block's fp16 values
 // staged in LDS (xs[t * D + d], natural order); tokens t >= ntok give zero nibbles.
 // Called by NT threads (tid = 0 .. NT-1).

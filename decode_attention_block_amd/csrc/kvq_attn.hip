@@ -411,9 +411,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const uint8_t* poo
 // 0 .. kSplitWaves-1 then attend the blocks the append leaves untouched while the append
 // wave reduces the block statistics before and after the token, codes the block (the
 // whole block if its statistic changed, else the token), writes the token's staging and
-// the scales, and attends the block that holds the token. The uint8 and FP8 waves write
-// the token's codes at once and read the block back; the int4 wave holds the new block
-// in registers and writes it whole at the end of the kernel.
+// the scales, and attends the block that holds the token. The block's new codes stay in
+// the append wave's registers (coded from the staged values) and are written at the end
+// of the kernel: int4 the whole block, uint8 and FP8 the token's row (the whole block if
+// it was re-quantized).
 // The append wave takes the sequence's arrival ticket (1 << 24 added to seq_lens[b], as
 // in kv_append) once its own loads have completed, and the last of the sequence's `heads`
 // workgroups stores the new length when its work is done. Every workgroup of the
@@ -518,9 +519,9 @@ __device__ __forceinline__ void step_ticket_done(const AttnArgs& a, const StepLe
                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// The append wave's work after the stage: write_codes(plan) writes the codes (uint8,
-// FP8) or builds them in registers (int4, written at the end of the kernel), then the
-// token's fp16 staging and the changed scales are written. Returns the scales (and zero points) of
+// The append wave's work after the stage: write_codes(plan) builds the block's new codes
+// in registers (written at the end of the kernel), then the token's fp16 staging and the
+// changed scales are written. Returns the scales (and zero points) of
 // the block holding the new token.
 template <int D, class WriteCodes>
 __device__ __forceinline__ BlockScales step_append(const AttnArgs& a, const StepLens& sl,
@@ -694,8 +695,13 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
 
   float p[TPL];
   bool streaming = true;
-  uint32_t ticket = 0;  // the append wave's arrival ticket (lane 0)
+  uint32_t ticket = 0;          // the append wave's arrival ticket (lane 0)
+  uint4 kr[TPL], vr[TPL];       // the append wave: the open block's new codes
+  AppendPlan plan[2];           // the append wave: the open block's outcome
+  int64_t tblk = 0;             // the append wave: the open block's index (block_slot)
   if constexpr (kAppend) {
+    tblk = block_slot(a.block_table, a.num_pages, a.heads, a.max_blocks, b, h,
+                      min(sl.len0, cap - 1) / kBlock);
     u32x4 fresh_k = {0u, 0u, 0u, 0u}, fresh_v = {0u, 0u, 0u, 0u};
     if (wave == kSplitWaves && sl.len0 < cap)
       step_stage_load<D>(a, sl, row, lane, xs, fresh_k, fresh_v);
@@ -704,25 +710,29 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
       streaming = false;
       const uint4 fresh[2] = {make_uint4(fresh_k.x, fresh_k.y, fresh_k.z, fresh_k.w),
                               make_uint4(fresh_v.x, fresh_v.y, fresh_v.z, fresh_v.w)};
-      AppendPlan plan[2];
       if (sl.len0 < cap) step_stage_reduce<SCHEME, D>(sl, lane, xs, fresh, plan);
+      ticket = step_ticket(a, b, lane);
+      // The block's new codes, in registers until the end of the kernel, coded from the
+      // staged values with the block's scale after the append: every stored code of an
+      // open block is the code of its staged value under the block's current scale, so
+      // this is the block's content whether or not the scale changed.
       const BlockScales sc = step_append<D>(
           a, sl, row, cap, lane, fresh, plan, [&](const AppendPlan (&plan)[2]) {
-            append_write_codes<SCHEME, D, kWave>(a.ap, row, sl.len0, lane, xs, plan);
+            const int ntok = sl.len0 % kBlock + 1;
+#pragma unroll
+            for (int kv = 0; kv < 2; ++kv) {
+              const Divisor d(plan[kv].s);
+              const int zpi = static_cast<int>(plan[kv].zp);
+              const _Float16* xt = xs + kv * kBlock * D;
+#pragma unroll
+              for (int i = 0; i < TPL; ++i)
+                (kv ? vr : kr)[i] = byte_codes_chunk<SCHEME, D>(xt, ntok, d, zpi, lane, i);
+            }
           });
       if (sl.tail_blk >= 0) {
-        // the new codes were written a token row (a whole line) at a time; wait until
-        // they have completed (the workgroup's L1 keeps its waves coherent, so nothing is
-        // invalidated), and keep the loads below that point
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-        uint4 kr[TPL], vr[TPL];
-        const int slot = slot_of(sl.tail_blk);
-        load_codes(false, sl.tail_blk, slot, kr);
-        load_codes(true, sl.tail_blk, slot, vr);
         block_weights(sl.tail_blk, sc.ks, sc.kz, kr, p);
         block_accumulate(sl.tail_blk, sc.vs, sc.vz, vr, p);
       }
-      ticket = step_ticket(a, b, lane);
     }
   }
   if (streaming)
@@ -781,7 +791,25 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   }
   finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
   if constexpr (kAppend) {
-    if (wave == kSplitWaves) step_ticket_done(a, sl, b, cap, ticket, lane);
+    if (wave == kSplitWaves) {
+      // The new codes, written once the row's other blocks have been streamed (stores
+      // into the code buffer during the stream slow it by more than their size): the
+      // whole block if it was re-quantized, else the token's row (whole 64-byte lines).
+      if (sl.len0 < cap) {
+        const int slot = sl.len0 % kBlock;
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv) {
+          uint8_t* codes = (kv ? a.ap.v_codes : a.ap.k_codes) + tblk * kRegionBytes;
+#pragma unroll
+          for (int i = 0; i < TPL; ++i) {
+            const int t = (i * kWave + lane) * 16 / D;
+            if (plan[kv].full || t == slot)
+              store_b128(codes + (i * kWave + lane) * 16, (kv ? vr : kr)[i]);
+          }
+        }
+      }
+      step_ticket_done(a, sl, b, cap, ticket, lane);
+    }
   }
 }
 
