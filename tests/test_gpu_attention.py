@@ -229,3 +229,41 @@ def test_zero_context_call_writes_zeros():
     kvq.decode_attn_qkv(c, qt, 0.1, out, None, 0)
     torch.cuda.synchronize()
     assert not out.cpu().numpy().any()
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+@pytest.mark.parametrize("bps", [1, 2, 5])
+def test_many_splits_per_row(scheme, bps):
+    """Rows cut into many splits (up to 41, several chunks of partial states in the
+    merge, and a last chunk partly past the row's splits): fused call within tolerance
+    of the oracle, bitwise equal to split + combine and to itself on a repeat; counters
+    back at zero."""
+    import decode_attention_block_amd as kvq
+    import torch
+    B, H, S = 3, 2, 2600
+    lens = np.array([2600, 577, 1], np.int32)
+    k, v, q, _ = _small_case(scheme, 64, seed=31, B=B, H=H, S=S, lens=lens)
+    c = gpu_quantize(scheme, k, v, lens, 41)
+    L = int(lens.max())
+    say("many splits", scheme, "plan", kvq.decode_attn_plan(c, L, bps))
+    assert kvq.decode_attn_plan(c, L, bps)[1] == (41 + bps - 1) // bps
+    sm = 0.125
+    qt = to_gpu(q)
+    ws = kvq.make_workspace(c, L, bps)
+    fused = torch.empty_like(qt)
+    kvq.decode_attn_qkv(c, qt, sm, fused, ws, L, bps)
+    torch.cuda.synchronize()
+    o = fused.cpu().numpy()
+    ref = oracle.attention(c.host_arrays(), q, lens, sm)
+    norm_err, _ = attn_errors(o, ref)
+    print(f"many splits scheme {scheme} bps {bps}: normwise {norm_err:.3e}")
+    assert norm_err <= ATTN_TOL
+    assert not ws[:4 * B * H].any()
+    again = torch.empty_like(qt)
+    kvq.decode_attn_qkv(c, qt, sm, again, ws, L, bps)
+    out = torch.full_like(qt, 7.0)
+    kvq.decode_attn_split(c, qt, sm, ws, L, bps)
+    kvq.decode_attn_combine(c, out, ws, L, bps)
+    torch.cuda.synchronize()
+    assert np.array_equal(again.cpu().numpy(), o)
+    assert np.array_equal(out.cpu().numpy(), o)
