@@ -332,12 +332,18 @@ __device__ __forceinline__ float lane_value(float v, int i) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
 }
 
-template <int LOADS, class LoadParams, class Load, class OnK, class OnV>
+// `start()` runs once, after the wave's first code load has been issued and before
+// anything waits for it: work that waits for the query's own load goes there, so the
+// stream's first requests are not held behind it.
+template <int LOADS, class LoadParams, class Load, class OnK, class OnV, class Start>
 __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, int wave, int lane,
                                                    int64_t row, LoadParams load_params, Load load,
-                                                   OnK on_k, OnV on_v) {
+                                                   OnK on_k, OnV on_v, Start start) {
   const int n = blk_end - blk_begin;
-  if (n <= 0) return;  // uniform (a decode step's streaming waves may have no block)
+  if (n <= 0) {  // uniform (a decode step's streaming waves may have no block)
+    start();
+    return;
+  }
   const int rot = static_cast<int>((static_cast<uint32_t>(row) * 2654435761u) >> 8) % n;
   const int n_wave = wave < n ? (n - wave + kSplitWaves - 1) / kSplitWaves : 0;
   auto blk_of = [&](int i) {
@@ -349,6 +355,10 @@ __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, i
     const int i1 = min(n_wave, i0 + kWave);
     const auto params = load_params(blk_of(min(i0 + lane, i1 - 1)));
     load(false, blk_of(i0), params, 0, kbuf);
+    if (i0 == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      start();
+    }
     for (int i = i0; i < i1 - 1; ++i) {
       const int blk = blk_of(i);
       load(true, blk, params, i - i0, vbuf);
@@ -751,7 +761,8 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
         },
         [&](int blk, const ScaleZeroParams& pb, const uint4 (&vr)[TPL]) {
           block_accumulate(blk, pb.vs, pb.vz, vr, p);
-        });
+        },
+        [] {});
 
   // Per-lane result in true units: o_true[k] = o[k] * unit(k).
 #pragma unroll
@@ -834,6 +845,22 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // the slot of nibble q (the inverse). Arithmetic rather than a table: a table indexed by
 // lane would be read from memory.
 __device__ __forceinline__ constexpr int slot_nibble(int j) { return (j >> 1) | ((j & 1) << 2); }
+
+// Marks the query's raw bits as produced at this point (an empty asm statement that the
+// compiler must keep after the memory requests issued before it): the operand built
+// from them is then not hoisted above the stream's first requests, and the wait for the
+// query's load lands here.
+__device__ __forceinline__ uint4 query_ready(uint4 r) {
+  asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w) : : "memory");
+  return r;
+}
+
+// Element k (0..7) of 8 fp16 values held in a uint4 (k a compile-time constant after
+// unrolling, so this stays in registers).
+__device__ __forceinline__ _Float16 half_of(const uint4& r, int k) {
+  const uint32_t w = k < 2 ? r.x : (k < 4 ? r.y : (k < 6 ? r.z : r.w));
+  return __builtin_bit_cast(_Float16, static_cast<uint16_t>((k & 1) ? w >> 16 : w & 0xFFFFu));
+}
 __device__ __forceinline__ constexpr int nibble_slot(int q) { return ((q & 3) << 1) | (q >> 2); }
 
 // 8 stored nibbles -> fp16 operands in slot order: slots 2, 3, 6, 7 hold 16*c * 2^-10,
@@ -932,21 +959,28 @@ attn_split_int4_kernel(AttnArgs a) {
     img[lane + kWave] = make_uint4(0u, 0u, 0u, 0u);
   }
 
-  // Query operand: row 0 holds q in slot order, x16 slots pre-divided by 16.
+  // Query operand: row 0 holds q in slot order, x16 slots pre-divided by 16. The query's
+  // bits are requested here; make_query builds the operand once the wave's first code
+  // requests are out (stream_wave_blocks' start), so they do not wait behind this load.
+  uint4 qraw[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qraw[ks] = *reinterpret_cast<const uint4*>(a.q + row * D + 32 * ks + 8 * grp);
   half8_t aq[KS];
-  {
-    const uint16_t* qrow = a.q + row * D;
+  auto make_query = [&]() {
     const float keep = r16 == 0 ? 1.0f : 0.0f;
+    uint4 qr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qr[ks] = query_ready(qraw[ks]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint16_t bits = qrow[32 * ks + 8 * grp + slot_nibble(j)];
-        float x = static_cast<float>(__builtin_bit_cast(_Float16, bits)) * keep;
+        float x = static_cast<float>(half_of(qr[ks], slot_nibble(j))) * keep;
         if (j & 2) x *= 0.0625f;
         aq[ks][j] = static_cast<_Float16>(x);
       }
-  }
+  };
 
   // Dense layout: the row's code regions as buffer resources, so a load's address is
   // the uniform block offset (a scalar register) plus the lane's 16-byte slot, with no
@@ -1092,6 +1126,7 @@ attn_split_int4_kernel(AttnArgs a) {
             int4_tail_fragments<D>(xs + kBlock * D, slot, plan[1], true, lane, vr);
           });
       if (sl.tail_blk >= 0) {
+        make_query();
         block_weights(sl.tail_blk, sc.ks, kr, p);
         block_accumulate(sc.vs, vr, p);
       }
@@ -1112,7 +1147,8 @@ attn_split_int4_kernel(AttnArgs a) {
         },
         [&](int, const ScaleParams& pb, const uint4 (&vr)[LOADS]) {
           block_accumulate(pb.vs, vr, p);
-        });
+        },
+        make_query);
 
   const float lw = row0_sum(lane < 16 ? l : 0.0f);
   if (lane < 16) {
@@ -1225,21 +1261,29 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
     for (int k = 0; k < 4; ++k) img[lane + k * kWave] = make_uint4(0u, 0u, 0u, 0u);
   }
 
-  // Query operand: row g < G holds query g in slot order, x16 slots pre-divided by 16.
-  half8_t aq[KS];
+  // Query operand: row g < G holds query g in slot order, x16 slots pre-divided by 16,
+  // built by make_query once the wave's first code requests are out (as above).
+  uint4 qraw[KS];
   {
-    const uint16_t* qrow = a.q + (row * G + min(r16, G - 1)) * D;
+    const uint16_t* qrow = a.q + (row * G + min(r16, G - 1)) * D + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
+  }
+  half8_t aq[KS];
+  auto make_query = [&]() {
     const float keep = r16 < G ? 1.0f : 0.0f;
+    uint4 qr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qr[ks] = query_ready(qraw[ks]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint16_t bits = qrow[32 * ks + 8 * grp + slot_nibble(j)];
-        float x = static_cast<float>(__builtin_bit_cast(_Float16, bits)) * keep;
+        float x = static_cast<float>(half_of(qr[ks], slot_nibble(j))) * keep;
         if (j & 2) x *= 0.0625f;
         aq[ks][j] = static_cast<_Float16>(x);
       }
-  }
+  };
 
   const int row_bytes = kPaged ? kRegionBytes : a.max_blocks * kRegionBytes;
   const int64_t row_base = kPaged ? 0 : row * row_bytes;
@@ -1390,7 +1434,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
       },
       [&](int, const ScaleParams& pb, const uint4 (&vr)[LOADS]) {
         block_accumulate(pb.vs, vr, p);
-      });
+      },
+      make_query);
 
   // The waves' states per row through LDS (a wave with no block has m = -inf, l = o = 0).
 #pragma unroll
