@@ -166,6 +166,15 @@ __device__ __forceinline__ void finish_split(const AttnArgs& a, int64_t row, int
   }
 }
 
+// Marks the query's raw bits as produced at this point (an empty asm statement that the
+// compiler must keep after the memory requests issued before it): the operand built
+// from them is then not hoisted above the stream's first requests, and the wait for the
+// query's load lands here.
+__device__ __forceinline__ uint4 query_ready(uint4 r) {
+  asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w) : : "memory");
+  return r;
+}
+
 template <int SCHEME, int D>
 struct Query {
   using G = AGeo<SCHEME, D>;
@@ -174,12 +183,19 @@ struct Query {
   uint32_t qh[G::kDPL / 2];
   float sum;  // sum of the lane's query channels
 
-  __device__ __forceinline__ void load(const uint16_t* q) {
-    constexpr int kLoads = G::kDPL / 8;
+  static constexpr int kLoads = G::kDPL / 8;
+  uint4 raw[kLoads];  // the lane's channels as requested
+
+  // Requests the lane's channels; ready() waits for them and fills qh and sum.
+  __device__ __forceinline__ void request(const uint16_t* q) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) raw[i] = *reinterpret_cast<const uint4*>(q + 8 * i);
+  }
+  __device__ __forceinline__ void ready() {
     sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const uint4 r = *reinterpret_cast<const uint4*>(q + 8 * i);
+      const uint4 r = query_ready(raw[i]);
       qh[4 * i + 0] = r.x;
       qh[4 * i + 1] = r.y;
       qh[4 * i + 2] = r.z;
@@ -587,9 +603,15 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   const int group = lane / LPT;
   const int64_t row = static_cast<int64_t>(b) * a.heads + h;
 
+  // The query is requested here and made ready (make_query) once the wave's first code
+  // requests are out (stream_wave_blocks' start), so they do not wait behind its load.
   Query<SCHEME, D> q;
-  q.load(a.q + row * D + chunk * DPL);
-  const float qsum_row = group_sum<LPT>(q.sum);
+  q.request(a.q + row * D + chunk * DPL);
+  float qsum_row = 0.0f;
+  auto make_query = [&]() {
+    q.ready();
+    qsum_row = group_sum<LPT>(q.sum);
+  };
 
   // Dense layout: the row's code regions as buffer resources (uniform base and block
   // offset, the lane's 16-byte slot as the only per-lane address; the host keeps the row
@@ -740,6 +762,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
             }
           });
       if (sl.tail_blk >= 0) {
+        make_query();
         block_weights(sl.tail_blk, sc.ks, sc.kz, kr, p);
         block_accumulate(sl.tail_blk, sc.vs, sc.vz, vr, p);
       }
@@ -762,7 +785,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
         [&](int blk, const ScaleZeroParams& pb, const uint4 (&vr)[TPL]) {
           block_accumulate(blk, pb.vs, pb.vz, vr, p);
         },
-        [] {});
+        make_query);
 
   // Per-lane result in true units: o_true[k] = o[k] * unit(k).
 #pragma unroll
@@ -845,15 +868,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // the slot of nibble q (the inverse). Arithmetic rather than a table: a table indexed by
 // lane would be read from memory.
 __device__ __forceinline__ constexpr int slot_nibble(int j) { return (j >> 1) | ((j & 1) << 2); }
-
-// Marks the query's raw bits as produced at this point (an empty asm statement that the
-// compiler must keep after the memory requests issued before it): the operand built
-// from them is then not hoisted above the stream's first requests, and the wait for the
-// query's load lands here.
-__device__ __forceinline__ uint4 query_ready(uint4 r) {
-  asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w) : : "memory");
-  return r;
-}
 
 // Element k (0..7) of 8 fp16 values held in a uint4 (k a compile-time constant after
 // unrolling, so this stays in registers).
