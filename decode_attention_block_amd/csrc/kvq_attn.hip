@@ -69,8 +69,10 @@ __device__ __forceinline__ void store_shared(float* p, float v) {
 // The partials are read kMergeChunk splits at a time, all of a chunk's loads issued
 // before any is used, so a merge costs about 2 n / kMergeChunk memory round trips
 // instead of 2 n (the sums still run over j in order, so the result does not depend on
-// the chunking). They are buffer loads over exactly the row's partials (loads past the
-// n-th return 0 and are masked out); in the fused merge (kCoherent) they carry the
+// the chunking). They are buffer loads over exactly the row's partials, every offset in
+// the per-lane (VGPR) operand, which the range check covers, so loads past the n-th
+// return 0 without touching memory and are masked out; in the fused merge (kCoherent)
+// they carry the
 // agent-scope coherence bit sc1, so that they read what other workgroups stored with
 // agent-scope atomic stores rather than a possibly stale L2 line, as an agent-scope
 // atomic load would, but without an atomic's ordering, which made every load wait for
@@ -87,14 +89,14 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t row, int n,
         a.ws_ml + row * a.n_split * 2, 0, n * 2 * 4, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t por = __builtin_amdgcn_make_buffer_rsrc(
         a.ws_o + row * a.n_split * D, 0, n * D * 4, kBufferRsrcWord3);
-    auto ld = [](__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
-      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, aux));
+    auto ld = [](__amdgpu_buffer_rsrc_t rs, int voff) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, aux));
     };
     float M = -__builtin_inff();
     for (int j0 = 0; j0 < n; j0 += kMergeChunk) {
       float m[kMergeChunk];
 #pragma unroll
-      for (int k = 0; k < kMergeChunk; ++k) m[k] = ld(mlr, 0, (j0 + k) * 8);
+      for (int k = 0; k < kMergeChunk; ++k) m[k] = ld(mlr, (j0 + k) * 8);
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k)
         if (j0 + k < n) M = fmaxf(M, m[k]);
@@ -104,9 +106,9 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t row, int n,
       float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k) {
-        m[k] = ld(mlr, 0, (j0 + k) * 8);
-        l[k] = ld(mlr, 0, (j0 + k) * 8 + 4);
-        o[k] = ld(por, d * 4, (j0 + k) * D * 4);
+        m[k] = ld(mlr, (j0 + k) * 8);
+        l[k] = ld(mlr, (j0 + k) * 8 + 4);
+        o[k] = ld(por, ((j0 + k) * D + d) * 4);
       }
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k) {
