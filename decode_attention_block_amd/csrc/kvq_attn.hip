@@ -66,10 +66,11 @@ __device__ __forceinline__ void store_shared(float* p, float v) {
 
 // Log-sum-exp merge of the n partial states of one row into its fp16 output channel d:
 // M = max_j m_j, o = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M); zeros when n = 0.
-// The partials are read kMergeChunk splits at a time, all of a chunk's loads issued
-// before any is used, so a merge costs about 2 n / kMergeChunk memory round trips
-// instead of 2 n (the sums still run over j in order, so the result does not depend on
-// the chunking). They are buffer loads over exactly the row's partials, every offset in
+// A row of at most kMergeChunk splits is read in one batch (one memory round trip);
+// longer rows kMergeChunk splits at a time, all of a chunk's loads issued before any is
+// used, in two passes (the max, then the sums): about 2 n / kMergeChunk round trips
+// instead of 2 n. The sums run over j in order either way, so the result does not
+// depend on the batching. They are buffer loads over exactly the row's partials, every offset in
 // the per-lane (VGPR) operand, which the range check covers, so loads past the n-th
 // return 0 without touching memory and are masked out; in the fused merge (kCoherent)
 // they carry the
@@ -93,6 +94,30 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t row, int n,
       return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, aux));
     };
     float M = -__builtin_inff();
+    float L = 0.0f, acc = 0.0f;
+    if (n <= kMergeChunk) {  // one batch: every partial state of the row at once
+      float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k) {
+        m[k] = ld(mlr, k * 8);
+        l[k] = ld(mlr, k * 8 + 4);
+        o[k] = ld(por, (k * D + d) * 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every request out before the first use
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k)
+        if (k < n) M = fmaxf(M, m[k]);
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k) {
+        if (k < n) {
+          const float w = __builtin_amdgcn_exp2f(m[k] - M);
+          L = __builtin_fmaf(w, l[k], L);
+          acc = __builtin_fmaf(w, o[k], acc);
+        }
+      }
+      a.out[row * D + d] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc / L));
+      return;
+    }
     for (int j0 = 0; j0 < n; j0 += kMergeChunk) {
       float m[kMergeChunk];
 #pragma unroll
@@ -101,7 +126,6 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t row, int n,
       for (int k = 0; k < kMergeChunk; ++k)
         if (j0 + k < n) M = fmaxf(M, m[k]);
     }
-    float L = 0.0f, acc = 0.0f;
     for (int j0 = 0; j0 < n; j0 += kMergeChunk) {
       float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
 #pragma unroll
