@@ -70,11 +70,11 @@ __device__ __forceinline__ void store_shared(float* p, float v) {
 // longer rows kMergeChunk splits at a time, all of a chunk's loads issued before any is
 // used, in two passes (the max, then the sums): about 2 n / kMergeChunk round trips
 // instead of 2 n. The sums run over j in order either way, so the result does not
-// depend on the batching. They are buffer loads over exactly the row's partials, every offset in
-// the per-lane (VGPR) operand, which the range check covers, so loads past the n-th
-// return 0 without touching memory and are masked out; in the fused merge (kCoherent)
-// they carry the
-// agent-scope coherence bit sc1, so that they read what other workgroups stored with
+// depend on the batching. They are buffer loads over exactly the row's partials, every
+// offset in the per-lane (VGPR) operand, which the range check covers dword by dword
+// (also where the compiler merges neighbouring loads), so loads past the n-th return 0
+// without touching memory and are masked out. In the fused merge (kCoherent) they carry
+// the agent-scope coherence bit sc1, so that they read what other workgroups stored with
 // agent-scope atomic stores rather than a possibly stale L2 line, as an agent-scope
 // atomic load would, but without an atomic's ordering, which made every load wait for
 // the previous one.
@@ -455,9 +455,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const uint8_t* poo
 // ---- fused decode step ----------------------------------------------------------------
 // In a decode step (kAppend) the workgroup of row (b, h) has one wave more than the
 // attention. The row's length is read once, before anything else. The last wave (the
-// append wave) then requests the row's staged tokens (straight into LDS), the new token
-// and, for int4, the open block's codes, and only then releases the other waves with a
-// barrier, so that its requests enter the compute unit's memory pipeline first: once the
+// append wave) then requests the row's staged tokens (straight into LDS) and the new
+// token, and only then releases the other waves with a barrier, so that its requests enter the compute unit's memory pipeline first: once the
 // streaming waves keep that pipeline full, a wave with dozens of requests queued behind
 // them waits tens of microseconds, longer than the streaming itself. Waves
 // 0 .. kSplitWaves-1 then attend the blocks the append leaves untouched while the append
