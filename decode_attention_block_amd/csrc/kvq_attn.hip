@@ -1140,6 +1140,7 @@ attn_split_int4_kernel(AttnArgs a) {
   bool streaming = true;
   uint32_t ticket = 0;  // the append wave's arrival ticket (lane 0)
   uint4 kr[LOADS], vr[LOADS];  // the append wave: the open block's new codes
+  AppendPlan plan[2];          // the append wave: the open block's outcome
   int64_t tblk = 0;            // the append wave: the open block's index (block_slot)
   if constexpr (kAppend) {
     // the append wave requests the staged tokens and the new token, then releases the
@@ -1154,7 +1155,6 @@ attn_split_int4_kernel(AttnArgs a) {
       streaming = false;
       const uint4 fresh[2] = {make_uint4(fresh_k.x, fresh_k.y, fresh_k.z, fresh_k.w),
                               make_uint4(fresh_v.x, fresh_v.y, fresh_v.z, fresh_v.w)};
-      AppendPlan plan[2];
       if (sl.len0 < cap) step_stage_reduce<KVQ_INT4_SYM, D>(sl, lane, xs, fresh, plan);
       ticket = step_ticket(a, b, lane);
       // the block's new codes, in registers until the end of the kernel
@@ -1217,18 +1217,27 @@ attn_split_int4_kernel(AttnArgs a) {
   finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
   if constexpr (kAppend) {
     if (wave == kSplitWaves) {
-      // The open block's new codes, written whole (whole 64-byte lines) once the row's
-      // other blocks have been streamed: stores into the code buffer during the stream
-      // slow it by more than their size (measured on the 8K int4 step: token-sized
-      // stores at once 47.8 us, whole block at once 49.0 us, whole block at the end
-      // 46.5 us, no stores 45.6 us).
+      // The open block's new codes, written once the row's other blocks have been
+      // streamed: stores into the code buffer during the stream slow it by more than
+      // their size (measured on the 8K int4 step: token-sized stores at once 47.8 us,
+      // whole block at once 49.0 us, whole block at the end 46.5 us, no stores 45.6
+      // us). Whole 64-byte lines: the block if it was re-quantized, else the lines that
+      // hold the token's nibbles.
       if (sl.len0 < cap) {
         uint8_t* kc = a.ap.k_codes + tblk * kRegionBytes;
         uint8_t* vc = a.ap.v_codes + tblk * kRegionBytes;
+        const int slot = sl.len0 % kBlock;
+        // the 64-byte lines (4 lanes' chunks) that hold the token's nibbles: K dwords
+        // (slot / 16) * KS .. + KS - 1 (chunk (slot / 16) * KS / 4) of lanes 16 g + slot %
+        // 16; V every chunk of lanes 16 g', g' = (slot % 32) / 8
+        const bool k_line = (lane % 16) / 4 == (slot % 16) / 4;
+        const bool v_line = lane / 16 == (slot % 32) / 8;
+        const int k_chunk = (slot / 16) * KS / 4;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-          store_b128(kc + (i * kWave + lane) * 16, kr[i]);
-          store_b128(vc + (i * kWave + lane) * 16, vr[i]);
+          if (plan[0].full || (k_line && i == k_chunk))
+            store_b128(kc + (i * kWave + lane) * 16, kr[i]);
+          if (plan[1].full || v_line) store_b128(vc + (i * kWave + lane) * 16, vr[i]);
         }
       }
       step_ticket_done(a, sl, b, cap, ticket, lane);
