@@ -52,8 +52,14 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(QuantArgs a) 
   for (int p = 0; p < G::kPasses; ++p) {
     const int t = p * G::kTokensPerPass + tr;
     const bool valid = t < ntok;
-    raw[p] = valid ? *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(t) * a.stride_t)
-                   : make_uint4(0u, 0u, 0u, 0u);
+    // the fp16 inputs are read once: non-temporal loads (8K workload, all blocks: uint8
+    // 384 -> 326 us, FP8 464 -> 456 us, int4 unchanged at about 340 us)
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    v4u r4 = {0u, 0u, 0u, 0u};
+    if (valid)
+      r4 = __builtin_nontemporal_load(
+          reinterpret_cast<const v4u*>(src + static_cast<int64_t>(t) * a.stride_t));
+    raw[p] = make_uint4(r4.x, r4.y, r4.z, r4.w);
     unpack8(raw[p], x[p]);
     if constexpr (SCHEME == KVQ_INT4_SYM)
       *reinterpret_cast<uint4*>(xs + t * D + chunk * 8) = raw[p];
