@@ -64,6 +64,22 @@ __device__ __forceinline__ void store_shared(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Publication of a workgroup's partial state before its arrival ticket. Every wave
+// waits until its own vector memory requests have completed (s_waitcnt vmcnt(0);
+// expcnt and lgkmcnt left at their maxima, i.e. not waited for): the agent-scope
+// stores above are acknowledged only once they have been written through to memory, so
+// after the wait they are visible to every workgroup on any XCD. The workgroup
+// barrier that follows then orders all waves' completed stores before thread 0's
+// ticket, which is performed at memory. A workgroup-scope release fence would not do
+// this: outside thread-group-split mode it compiles to nothing, and the barrier alone
+// lets a wave arrive with its stores still in flight. The reader (the last arriver)
+// issues its loads only after the ticket's result has returned and a barrier, and every
+// one of them carries the agent-coherence bit (merge_row), so none can be served by a
+// stale cache line.
+__device__ __forceinline__ void wait_own_stores() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15) on gfx9-family chips
+}
+
 // Log-sum-exp merge of the n partial states of one row into its fp16 output channel d:
 // M = max_j m_j, o = sum_j o_j 2^(m_j - M) / sum_j l_j 2^(m_j - M); zeros when n = 0.
 // A row of at most kMergeChunk splits is read in one batch (one memory round trip);
@@ -178,7 +194,7 @@ __device__ __forceinline__ void finish_split(const AttnArgs& a, int64_t row, int
     store_shared(ml + 1, L);
   }
   __shared__ uint32_t ticket;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores completed
+  wait_own_stores();  // every wave's partial stores have reached memory
   __syncthreads();
   // system scope: the read-modify-write is performed at memory, past the per-XCD L2s
   if (tid == 0)
@@ -1550,7 +1566,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
   }
   if (!a.fused) return;
   __shared__ uint32_t ticket;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this thread's stores completed
+  wait_own_stores();  // every wave's partial stores have reached memory
   __syncthreads();
   // system scope: the read-modify-write is performed at memory, past the per-XCD L2s
   if (threadIdx.x == 0)
