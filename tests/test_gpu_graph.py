@@ -1,12 +1,15 @@
 """A multi-layer decode step captured as a HIP graph (decode_attention_block_amd.graph)
 must give, replay after replay, bitwise what the same calls give eagerly: caches,
-lengths and outputs of every layer, with eager work between the replays."""
+lengths and outputs of every layer, with eager work between the replays. After the last
+replay every layer's cache must also equal the oracle's quantization of the whole
+history bit for bit, and every layer's output must be within the attention tolerance
+of the oracle's fp64 attention over that cache."""
 import numpy as np
 import pytest
 
 import oracle
 from decode_attention_block_amd import workloads as wl
-from helpers import gpu_quantize, say, to_gpu
+from helpers import ATTN_TOL, assert_cache_equal, attn_errors, gpu_quantize, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -34,33 +37,36 @@ def _same(a, b):
 
 @pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("append", [True, False])
-def test_graph_replays_equal_eager_steps(scheme, append):
+@pytest.mark.parametrize("bps", [0, 1])  # one split per row (one launch), or four per row
+def test_graph_replays_equal_eager_steps(scheme, append, bps):
     import decode_attention_block_amd as kvq
     from decode_attention_block_amd.graph import DecodeGraph
     import torch
-    say("graph", scheme, append)
+    say("graph", scheme, append, bps)
     L, B, H, D, MB, S = 3, 8, 32, 64, 4, 256
     lens = np.array([0, 1, 63, 64, 100, 127, 5, 200], np.int32)
     k_all, v_all, eager, graphed = _layers(scheme, L, B, H, D, S, lens, MB, seed=scheme)
     sm = 1.0 / np.sqrt(D)
-    dg = DecodeGraph(graphed, sm, append=append)
+    dg = DecodeGraph(graphed, sm, append=append, blocks_per_split=bps)
     cap = MB * 64
-    ws = [kvq.make_workspace(c, cap) for c in eager]
+    ws = [kvq.make_workspace(c, cap, bps) for c in eager]
     out = [torch.empty((B, H, D), dtype=torch.float16, device="cuda") for _ in range(L)]
     cur = lens.copy()
     rs = np.random.default_rng(5)
+    q_host = [None] * L
     for step in range(4):
         for i in range(L):
-            q = to_gpu(rs.standard_normal((B, H, D)).astype(np.float16))
+            q_host[i] = rs.standard_normal((B, H, D)).astype(np.float16)
+            q = to_gpu(q_host[i])
             dg.q[i].copy_(q)
             if append:
                 kn = to_gpu(k_all[i][np.arange(B), cur])
                 vn = to_gpu(v_all[i][np.arange(B), cur])
                 dg.k_new[i].copy_(kn)
                 dg.v_new[i].copy_(vn)
-                kvq.decode_step_qkv(eager[i], kn, vn, q, sm, out[i], ws[i], cap)
+                kvq.decode_step_qkv(eager[i], kn, vn, q, sm, out[i], ws[i], cap, bps)
             else:
-                kvq.decode_attn_qkv(eager[i], q, sm, out[i], ws[i], cap)
+                kvq.decode_attn_qkv(eager[i], q, sm, out[i], ws[i], cap, bps)
         dg.replay()
         torch.cuda.synchronize()
         if append:
@@ -71,3 +77,10 @@ def test_graph_replays_equal_eager_steps(scheme, append):
             assert _same(out[i], dg.out[i]), (step, i)
             for key in ("k_codes", "v_codes", "k_scale", "v_scale", "k_tail", "v_tail"):
                 assert _same(getattr(eager[i], key), getattr(graphed[i], key)), (step, i, key)
+    # the replayed state against the oracle: caches bit for bit, outputs within tolerance
+    for i in range(L):
+        ref = oracle.quantize_cache(scheme, k_all[i], v_all[i], cur, MB)
+        assert_cache_equal(graphed[i].host_arrays(), ref, cur)
+        o_ref = oracle.attention(ref, q_host[i], cur, sm)
+        norm_err, _ = attn_errors(dg.out[i].cpu().numpy(), o_ref)
+        assert norm_err <= ATTN_TOL, (i, norm_err)
