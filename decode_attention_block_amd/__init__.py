@@ -8,7 +8,6 @@ library's HIP kernels; there is no CPU fallback, and a missing or unloadable lib
 raises. PyTorch provides device memory and streams.
 """
 import ctypes
-import os
 
 import numpy as np
 
@@ -25,8 +24,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_ENOTSUP", -3: "KVQ_ECAPACITY",
 EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan",
            "decode_attn_workspace_bytes", "decode_attn_qkv", "decode_attn_split",
            "decode_attn_combine", "decode_step_qkv", "decode_attn_gqa",
-           "decode_attn_gqa_workspace_bytes", "decode_attn_gqa_plan", "kvq_strerror",
-           "kvq_version"]
+           "decode_attn_gqa_workspace_bytes", "decode_attn_gqa_plan", "kvq_probe_stream_read",
+           "kvq_strerror", "kvq_version"]
 
 
 class KvqError(RuntimeError):
@@ -56,11 +55,12 @@ def lib_path():
 
 
 def load_library():
-    """Loads libkvq.so, building it first only if no built library exists."""
+    """Loads libkvq.so, building it first if there is none or its sources have changed
+    since it was built (build.stale())."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
+    if _build.stale():
         _build.build()
     L = ctypes.CDLL(_build.LIB)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -79,6 +79,7 @@ def load_library():
         "decode_attn_gqa_workspace_bytes": ([C, i32, i32, i32], sz),
         "decode_attn_gqa_plan": ([C, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
                                  ctypes.c_int),
+        "kvq_probe_stream_read": ([P, sz, i32, P, P], ctypes.c_int),
         "kvq_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "kvq_version": ([], ctypes.c_int),
     }
@@ -234,6 +235,18 @@ def decode_step_qkv(cache, k_new, v_new, q, softmax_scale, out, workspace, max_l
                                         ws_bytes, int(max_len_after), int(blocks_per_split),
                                         _stream(stream))
     _check(rc, "decode_step_qkv")
+
+
+def kvq_probe_stream_read(buf, workgroups, sink, stream=None):
+    """Measurement aid: one streaming read of the device tensor `buf` (its whole storage)
+    by at most `workgroups` workgroups; sink: int32/uint32 device tensor of at least
+    workgroups * 256 elements."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() * sink.element_size() < 4 * 256 * int(workgroups):
+        raise ValueError("sink too small")
+    rc = load_library().kvq_probe_stream_read(_ptr(buf), nbytes, int(workgroups), _ptr(sink),
+                                              _stream(stream))
+    _check(rc, "kvq_probe_stream_read")
 
 
 class KVCache:

@@ -7,13 +7,14 @@ Flags that matter for the results:
     attention kernel feeds codes to the dot units as fp16 subnormals);
   * -Xclang -target-feature -Xclang -packed-fp32-ops: no packed binary32 VALU ops.
 """
+import hashlib
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["kvq_quant.hip", "kvq_attn.hip", "kvq_api.hip"]
+SOURCES = ["kvq_quant.hip", "kvq_attn.hip", "kvq_api.hip", "kvq_probe.hip"]
 HEADERS = ["kvq_device.h", "kvq_internal.h", "kvq_append.h"]
 LIB = os.path.join(HERE, "libkvq.so")
 ARCH = "gfx950"
@@ -33,6 +34,18 @@ def inputs():
         os.path.join(ROOT, "include", "kvq.h")]
 
 
+STAMP = LIB + ".inputs.sha256"  # hash of the sources and flags the library was built from
+
+
+def inputs_hash(extra=()):
+    """sha256 over the build flags and the contents of every source and header."""
+    h = hashlib.sha256(" ".join([*FLAGS, *extra]).encode())
+    for p in inputs():
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
 def build(verbose=False, extra=()):
     cmd = ["hipcc", *FLAGS, *extra, "-o", LIB + ".tmp", *sources()]
     if verbose:
@@ -46,14 +59,19 @@ def build(verbose=False, extra=()):
     if msg.strip() and verbose:
         print(msg)
     os.replace(LIB + ".tmp", LIB)
+    with open(STAMP, "w") as f:
+        f.write(inputs_hash(extra) + "\n")
     return LIB
 
 
 def stale():
-    if not os.path.exists(LIB):
+    """True when there is no built library or its sources (or flags) have changed since
+    it was built: the recorded hash is compared with the current contents, so copying
+    the tree (which may reset file times) does not make a library stale."""
+    if not os.path.exists(LIB) or not os.path.exists(STAMP):
         return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in inputs())
+    with open(STAMP) as f:
+        return f.read().strip() != inputs_hash()
 
 
 if __name__ == "__main__":

@@ -25,6 +25,19 @@ def test_outlier_mixture_statistics():
     assert abs(x[~big].std() - 1.0) < 0.01 and abs(x.mean()) < 0.01
 
 
+def test_outlier_positions_are_distinct():
+    """Each outlier is scaled once (x20, never x400): the positions are distinct, and
+    their number has the Binomial(n, 0.001) mean."""
+    counts = []
+    for seed in range(20):
+        g = np.random.Generator(np.random.PCG64(seed))
+        pos = wl.outlier_positions(g, 200_000)
+        assert len(np.unique(pos)) == len(pos)
+        assert pos.min() >= 0 and pos.max() < 200_000
+        counts.append(len(pos))
+    assert abs(np.mean(counts) - 200.0) < 3 * np.sqrt(200.0 / 20)
+
+
 def test_uint8_workload_value_mean():
     w = wl.WORKLOADS[2]
     v = wl.prefill_kv(w, 0, 0, 1, n_tokens=256).astype(np.float64)
