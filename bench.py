@@ -14,20 +14,28 @@ resident in HBM when timing starts. Steps rotate over enough copies of the cache
 (>= 1 GiB in all) that the 256 MB Infinity Cache cannot hold them, so every step
 reads its cache from HBM. Each copy gains one token per use, so the context grows
 from 8192 by at most ceil(steps / copies) tokens; bytes are counted from the actual
-lengths. Warm-up steps (the GPU takes a few milliseconds of load to reach steady
-clocks) run first, from the same prefill lengths, which are restored before timing.
+lengths.
 
-The same run also measures the other workloads (unless --headline-only) and reports
-them under "workloads":
-  * the 8K uint8 and FP8 E4M3 workloads, with the same step and rotation;
-  * the 32K workload (batch 16, context 32768): its 64-step decode loop of
-    decode_step_qkv, repeated from the same prefill (lengths reset between loops,
-    outside the timed region);
-  * the 32-layer ragged workload: one step is decode_attn_qkv over each of the 32
-    layers' caches (per-sequence lengths 1024..8192, no append in this workload).
-  * the grouped-query workload (64 query heads over 8 cached heads, batch 8, context
-    8192): one step is decode_attn_gqa over one of the rotated cache copies;
-  * the headline decode step again on paged caches (shuffled page pools).
+Timing. The steps run in segments that start from the prefill lengths (restored
+between segments, outside the timed region). Each segment's launches are captured once
+as a HIP graph and the timed region replays them, bracketed by HIP events on the launch
+stream: the GPU then runs the steps back to back, and the time is the kernels' own,
+not the host's pace of queueing them (queued one by one from Python, a step of the
+headline takes the host about as long as the GPU, so eager timing measures the host).
+The eager time of the same steps is reported beside it. Per-step times (p10, p50, p90)
+come from a separate sampling pass: HIP event pairs around each eagerly queued step,
+all queued behind a few large device copies so that the host is ahead of the GPU.
+Warm-up steps (the given number) run first through the same graphs.
+
+The same run measures the other workloads (unless --headline-only) and reports them
+under "workloads": the tiny workload (call latency), the 8K uint8 and FP8 E4M3
+workloads, the 32K workload (its 64-step decode loop from the same prefill), the
+32-layer ragged workload (one step = decode_attn_qkv over the 32 layers' caches), the
+grouped-query workload (64 query heads over 8 cached heads), and the headline step on
+paged caches. Beside every workload the CPU oracle (the plain C++ implementation the
+tests check against) is timed on the host's cores on a sample of the same inputs: the
+prefill quantization and one decode step (append + attention), on one thread and with
+the sample's heads split over every host thread.
 
 Prints one JSON line. --profile-loop runs only the timed loop of --workload (for
 rocprofv3), --copy-probe times a plain device copy of known size (the calibration
@@ -39,6 +47,7 @@ import math
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -48,14 +57,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_int4_b8h32d128_ctx8k_traffic.json")
 CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
-EVENT_STRIDE = 8               # HIP events around every 8th attention launch when a step
-                               # has several launches: a pair of events around a launch
-                               # adds ~5 us to its step
+SAMPLED_STEPS = 32             # steps timed one by one for the percentiles
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 KV_FORMATS = {0: "int4 block-64 symmetric", 1: "uint8 block-64 asymmetric",
               2: "fp8 e4m3 block-64 scaled"}
-OTHERS = ("llama7b_b8_h32_d128_ctx8k_uint8", "llama7b_b8_h32_d128_ctx8k_fp8",
-          "long_b16_h32_d128_ctx32k_append64_int4",
+DTYPES = {0: "int4 codes x fp16 query -> fp32 accumulate (matrix cores)",
+          1: "uint8 codes x fp16 query -> fp32 accumulate",
+          2: "fp8 e4m3 codes x fp16 query -> fp32 accumulate"}
+OTHERS = ("tiny_b1_h2_d64_ctx256_int4", "llama7b_b8_h32_d128_ctx8k_uint8",
+          "llama7b_b8_h32_d128_ctx8k_fp8", "long_b16_h32_d128_ctx32k_append64_int4",
           "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4", "llama70b_gqa8_b8_h8_d128_ctx8k_int4")
 
 
@@ -70,8 +80,10 @@ def parse():
                    help="time the step as kv_append + decode_attn_qkv (two calls)")
     p.add_argument("--paged", action="store_true",
                    help="time --workload on a paged cache (shuffled page pool)")
+    p.add_argument("--eager", action="store_true",
+                   help="time the steps as queued one by one from the host (no graph)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="approximate host time spent timing the oracle")
+                   help="approximate host time spent timing the oracle's headline decode step")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--headline-only", action="store_true",
                    help="measure only --workload, not the other workloads")
@@ -83,34 +95,54 @@ def parse():
     return p.parse_args()
 
 
+def wl_mod():
+    from decode_attention_block_amd import workloads
+    return workloads
+
+
+# ---- algorithmic bytes ----------------------------------------------------------------
 def code_bytes_per_token(w):
     return w.head_dim // 2 if w.scheme == 0 else w.head_dim
 
 
-def attention_bytes(w, lens):
-    """Algorithmic bytes of one decode_attn_qkv (decode_attn_gqa) call: K and V codes of
-    the valid tokens, their block scales (and zero points for uint8), q and out (one
-    row per query head)."""
+def attention_bytes(w, lens, heads=None):
+    """Algorithmic bytes of one decode_attn_qkv (decode_attn_gqa) call over the given
+    per-sequence lengths: K and V codes of the valid tokens, their block scales (and zero
+    points for uint8), q and out (one row per query head)."""
+    H = w.heads if heads is None else heads
     per_block_scalars = 2 * (2 if w.scheme == 1 else 1) * 4
     total = 0
     for n in lens:
         nb = (int(n) + 63) // 64
-        total += w.heads * (2 * int(n) * code_bytes_per_token(w) + nb * per_block_scalars)
-    total += 2 * w.batch * w.heads * w.group * w.head_dim * 2  # q in, out
+        total += H * (2 * int(n) * code_bytes_per_token(w) + nb * per_block_scalars)
+    total += 2 * len(lens) * H * w.group * w.head_dim * 2  # q in, out
     return total
 
 
-def append_bytes(w):
-    """Algorithmic bytes of one kv_append: the new K and V tokens in (fp16), their
-    staged fp16 copy and their codes out."""
-    rows = w.batch * w.heads
+def append_bytes(w, seqs=None, heads=None):
+    """Algorithmic bytes of one kv_append: the new K and V tokens in (fp16), their staged
+    fp16 copy and their codes out."""
+    rows = (w.batch if seqs is None else seqs) * (w.heads if heads is None else heads)
     return rows * 2 * (w.head_dim * 2 * 2 + code_bytes_per_token(w))
 
 
+def prefill_bytes(w, lens, heads=None):
+    """Algorithmic bytes of kv_quantize_blocks over the given lengths: fp16 K and V in,
+    codes and block scales (zero points) out."""
+    H = w.heads if heads is None else heads
+    per_block_scalars = 2 * (2 if w.scheme == 1 else 1) * 4
+    total = 0
+    for n in lens:
+        nb = (int(n) + 63) // 64
+        total += H * (2 * int(n) * (2 * w.head_dim + code_bytes_per_token(w)) +
+                      nb * per_block_scalars)
+    return total
+
+
 def measured_traffic():
-    """HBM bytes per launch of the headline step kernel from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs (scaled by the counters' reading for a 1 GiB copy), or None once the kernel's
-    sources differ from the ones the counters were taken on."""
+    """HBM bytes per launch of the headline step kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (scaled by the counters' reading for a 1 GiB copy), or
+    None once the kernel's sources differ from the ones the counters were taken on."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
@@ -126,6 +158,13 @@ def measured_traffic():
         return None
 
 
+def pct(xs):
+    xs = np.asarray(xs, np.float64)
+    return {"p10": float(np.percentile(xs, 10)), "p50": float(np.percentile(xs, 50)),
+            "p90": float(np.percentile(xs, 90))}
+
+
+# ---- probes ---------------------------------------------------------------------------
 def copy_probe():
     import torch
     n = 1 << 30
@@ -146,90 +185,236 @@ def copy_probe():
     return {"copy_bytes": n, "copy_ms": ms, "copy_gbs_read_plus_write": 2 * n / ms / 1e6}
 
 
-def cpu_baseline(w, host_cache, q, lens, budget_s):
-    """The oracle (single-threaded C++, fp64 attention over the dequantized cache) timed
-    on the host: whole passes over all (sequence, head) rows of the workload's attention,
-    repeated until about budget_s seconds have passed."""
-    import oracle
-    sm = float(np.float32(1) / np.sqrt(np.float32(w.head_dim)))
-    passes = 0
-    t0 = time.perf_counter()
+def read_ceiling(kvq, torch):
+    """The GPU's practical streaming-read rate: kvq_probe_stream_read over 2 GiB (8x the
+    Infinity Cache), at several workgroup counts; the best is the ceiling."""
+    n = 2 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(7)
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    by = {}
+    for wg in (256, 512, 1024, 2048, 4096):
+        for _ in range(2):
+            kvq.kvq_probe_stream_read(buf, wg, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            kvq.kvq_probe_stream_read(buf, wg, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        by[str(wg)] = n / (e0.elapsed_time(e1) / reps / 1e3) / 1e9
+    best = max(by.values())
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"gbs": best, "frac_of_peak": best / HBM_PEAK_GBS, "bytes": n,
+            "kernel": "kvq_probe_stream_read (contiguous slab per 256-thread workgroup, "
+                      "16-byte non-temporal loads)", "gbs_by_workgroups": by}
+
+
+# ---- timing machinery -----------------------------------------------------------------
+class Stepper:
+    """Times steps of a workload. queue(j) queues step j of a segment (0 <= j < seg_cap;
+    the caller's inputs for step j are fixed); reset() restores the state a segment
+    starts from (queued on the stream, outside any timed region). Segments of n steps
+    are captured once as HIP graphs (torch's graph capture of the library's launches)
+    and replayed."""
+
+    def __init__(self, torch, queue, seg_cap, reset=None):
+        self.torch, self.queue, self.seg_cap, self.reset = torch, queue, seg_cap, reset
+        self.graphs = {}
+
+    def _graph(self, n):
+        if n not in self.graphs:
+            torch = self.torch
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for j in range(n):
+                    self.queue(j)
+            torch.cuda.synchronize()
+            self.graphs[n] = g
+        return self.graphs[n]
+
+    def _segments(self, n_steps):
+        done = 0
+        while done < n_steps:
+            n = min(self.seg_cap, n_steps - done)
+            yield n
+            done += n
+
+    def run(self, n_steps, timed, graph=True):
+        """n_steps steps; returns their total GPU time in ms (HIP events around every
+        segment) when timed."""
+        torch = self.torch
+        total = 0.0
+        for n in self._segments(n_steps):
+            if graph:
+                g = self._graph(n)
+            if self.reset:
+                self.reset()
+            torch.cuda.synchronize()
+            if timed:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            if graph:
+                g.replay()
+            else:
+                for j in range(n):
+                    self.queue(j)
+            if timed:
+                e1.record()
+            torch.cuda.synchronize()
+            if timed:
+                total += e0.elapsed_time(e1)
+        return total
+
+    def sample(self, n):
+        """Per-step GPU times (ms) of the first n steps of a segment: HIP event pairs
+        around each step, all queued behind about 4 ms of device copies."""
+        torch = self.torch
+        n = min(n, self.seg_cap)
+        if self.reset:
+            self.reset()
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(32):
+            b.copy_(a)
+        pairs = []
+        for j in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            self.queue(j)
+            e1.record()
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        del a, b
+        return [e0.elapsed_time(e1) for e0, e1 in pairs]
+
+
+# ---- the oracle beside the GPU --------------------------------------------------------
+def _repeat(fn, budget_s, min_reps=1):
+    reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.attention(host_cache, q, lens, sm)
-        passes += 1
-        elapsed = time.perf_counter() - t0
-        if elapsed >= budget_s:
-            break
-    gbs = passes * attention_bytes(w, lens) / elapsed / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} full passes of the decode attention (all {w.batch * w.heads} "
-                      f"sequence-head rows, context {int(lens[0])}) of {w.name} by the fp64 "
-                      f"oracle on one host thread, {elapsed:.1f} s; kv_append not included",
-            "tokens_per_s": w.batch * passes / elapsed}
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if reps >= min_reps and el >= budget_s:
+            return el / reps, reps
 
 
-def cpu_baseline_all_cores(w, host_cache, q, lens, budget_s):
-    """The same unchanged oracle routine with the rows of each pass partitioned over all
-    host cores this process may use (threads; the C++ routine runs outside the GIL)."""
+def oracle_legs(w, k_s, v_s, q_s, length, budget_s, label, new_kv=None):
+    """The CPU oracle on a sample of the workload: k_s, v_s float16 [1][>=length][Hs][D]
+    (one sequence, Hs heads of the same inputs the GPU quantized) and q_s
+    [1][Hs * group][D]. Times, on one host thread and with the heads split over all host
+    threads: the prefill quantization of the sample (oracle.quantize_cache over `length`
+    tokens) and one decode step: with new_kv = (k, v) [1][Hs][D], oracle.append of that
+    token then oracle.attention over length + 1 tokens, as the GPU's decode step does;
+    without, oracle.attention over `length` tokens (workloads whose step is attention
+    only), once per query head of a group."""
     import oracle
-    from concurrent.futures import ThreadPoolExecutor
-    sm = float(np.float32(1) / np.sqrt(np.float32(w.head_dim)))
-    n_rows = w.batch * w.heads
-    cores = max(1, min(len(os.sched_getaffinity(0)), n_rows))
-    bounds = [(n_rows * i // cores, n_rows * (i + 1) // cores) for i in range(cores)]
-    passes = 0
+    Hs, D, G = k_s.shape[2], w.head_dim, w.group
+    if new_kv is not None:
+        hk = np.concatenate([k_s[:, :length], new_kv[0][:, None]], axis=1)
+        hv = np.concatenate([v_s[:, :length], new_kv[1][:, None]], axis=1)
+        n_attn = length + 1
+    else:
+        hk, hv, n_attn = k_s[:, :length], v_s[:, :length], length
+    mb = (length + 1 + 63) // 64
+    l0, l1 = np.array([length], np.int32), np.array([n_attn], np.int32)
+    sm = float(np.float32(1) / np.sqrt(np.float32(D)))
+    qg = [np.ascontiguousarray(q_s.reshape(1, Hs, G, D)[:, :, g]) for g in range(G)]
+
+    def quant(h0, h1):
+        return oracle.quantize_cache(w.scheme, hk[:, :, h0:h1], hv[:, :, h0:h1], l0, mb)
+
+    def step_fn(h0, h1):
+        c = quant(h0, h1)
+        qs = [np.ascontiguousarray(q[:, h0:h1]) for q in qg]
+
+        def step():
+            if new_kv is not None:
+                oracle.append(c, hk[:, :, h0:h1], hv[:, :, h0:h1], l1)
+            for q in qs:
+                oracle.attention(c, q, l1, sm)
+        return step
+
+    q_bytes = prefill_bytes(w, [length], heads=Hs)
+    s_bytes = attention_bytes(w, [n_attn], heads=Hs)
+    if new_kv is not None:
+        s_bytes += append_bytes(w, seqs=1, heads=Hs)
+    cores = max(1, min(len(os.sched_getaffinity(0)), Hs))
+    parts = [(Hs * i // cores, Hs * (i + 1) // cores) for i in range(cores)]
+    res = {"sample": f"{label}: sequence 0, heads 0..{Hs - 1} of the workload's inputs, "
+                     f"context {length}" + (" + 1 appended token" if new_kv is not None
+                                             else ""),
+           "step": ("oracle.append + oracle.attention" if new_kv is not None else
+                    "oracle.attention" + (f" x {G} (query heads per cached head)"
+                                          if G > 1 else "")),
+           "host_threads_available": len(os.sched_getaffinity(0))}
+    t, n = _repeat(lambda: quant(0, Hs), budget_s * 0.25)
+    res["prefill_quantize_1core"] = {"ms": t * 1e3, "gbs": q_bytes / t / 1e9, "reps": n,
+                                     "cores": 1}
+    step1 = step_fn(0, Hs)
+    t, n = _repeat(step1, budget_s * 0.35)
+    res["decode_step_1core"] = {"ms": t * 1e3, "gbs": s_bytes / t / 1e9, "reps": n, "cores": 1,
+                                "tokens_per_s": 1.0 / t}
     with ThreadPoolExecutor(cores) as ex:
-        t0 = time.perf_counter()
-        while True:
-            list(ex.map(lambda r: oracle.attention(host_cache, q, lens, sm, rows=r), bounds))
-            passes += 1
-            elapsed = time.perf_counter() - t0
-            if elapsed >= budget_s:
-                break
-    gbs = passes * attention_bytes(w, lens) / elapsed / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{passes} full passes of the same decode attention, rows split over "
-                      f"{cores} host threads, {elapsed:.1f} s",
-            "tokens_per_s": w.batch * passes / elapsed}
+        t, n = _repeat(lambda: list(ex.map(lambda p: quant(*p), parts)), budget_s * 0.15)
+        res["prefill_quantize_all_cores"] = {"ms": t * 1e3, "gbs": q_bytes / t / 1e9,
+                                             "reps": n, "cores": cores}
+        steps = list(ex.map(lambda p: step_fn(*p), parts))
+        t, n = _repeat(lambda: list(ex.map(lambda s: s(), steps)), budget_s * 0.25)
+        res["decode_step_all_cores"] = {"ms": t * 1e3, "gbs": s_bytes / t / 1e9, "reps": n,
+                                        "cores": cores, "tokens_per_s": 1.0 / t}
+    return res
 
 
-class Timer:
-    """HIP events around sampled kernel launches (every EVENT_STRIDE-th) and around
-    each timed segment, all on the current stream (the one the library's kernels are
-    queued on). An event pair measures the launch including its dispatch."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.kernel = []     # (start, end) event pairs
-        self.segments = []
-
-    def event(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def kernel_ms(self):
-        return [a.elapsed_time(b) for a, b in self.kernel]
-
-    def total_ms(self):
-        return sum(a.elapsed_time(b) for a, b in self.segments)
+def ratios(gpu_step_gbs, gpu_prefill_gbs, legs):
+    if not legs:
+        return None
+    return {"decode_step_gpu_over_1core": gpu_step_gbs / legs["decode_step_1core"]["gbs"],
+            "decode_step_gpu_over_all_cores": gpu_step_gbs / legs["decode_step_all_cores"]["gbs"],
+            "prefill_gpu_over_1core": (gpu_prefill_gbs / legs["prefill_quantize_1core"]["gbs"]
+                                       if gpu_prefill_gbs else None),
+            "prefill_gpu_over_all_cores": (gpu_prefill_gbs /
+                                           legs["prefill_quantize_all_cores"]["gbs"]
+                                           if gpu_prefill_gbs else None)}
 
 
-def quantized_copies(kvq, torch, w, layer, lens, max_blocks, n_copies, device_inputs,
-                     paged=False):
-    """n_copies caches holding the quantized prefill of one layer; returns them and the
-    prefill kernel times (ms). device_inputs: draw K and V with the device-side recipe
-    (same distributions, other values) instead of the host recipe. paged: each copy is a
-    paged cache whose block table scatters the blocks over its pool in a seeded random
-    order."""
-    n = int(np.max(lens))
+def host_sample(t, heads):
+    """Sequence 0, the first `heads` heads of a [B][S][H][D] fp16 tensor (torch or
+    numpy), on the host."""
+    x = t[0:1, :, :heads]
+    if hasattr(x, "cpu"):
+        x = x.contiguous().cpu().numpy()
+    return np.ascontiguousarray(x)
+
+
+def sample_heads(w):
+    """Heads of sequence 0 the oracle leg takes: all of them, except at 32K context
+    (a quarter, so that one single-threaded prefill quantization stays near 2 s)."""
+    return max(1, min(w.heads, w.heads * 8192 // max(w.context, 1)))
+
+
+# ---- workloads ------------------------------------------------------------------------
+def prefill_inputs(torch, w, layer, n, device_inputs):
     wl = wl_mod()
     if device_inputs:
-        k = wl.prefill_batch_device(w, layer, 0, n_tokens=n)
-        v = wl.prefill_batch_device(w, layer, 1, n_tokens=n)
-    else:
-        k = torch.from_numpy(wl.prefill_batch(w, layer, 0, n_tokens=n)).cuda()
-        v = torch.from_numpy(wl.prefill_batch(w, layer, 1, n_tokens=n)).cuda()
+        return (wl.prefill_batch_device(w, layer, 0, n_tokens=n),
+                wl.prefill_batch_device(w, layer, 1, n_tokens=n))
+    return (torch.from_numpy(wl.prefill_batch(w, layer, 0, n_tokens=n)).cuda(),
+            torch.from_numpy(wl.prefill_batch(w, layer, 1, n_tokens=n)).cuda())
+
+
+def quantized_copies(kvq, torch, w, k, v, lens, max_blocks, n_copies, paged=False):
+    """n_copies caches holding the quantized prefill k, v (device tensors); returns them
+    and the prefill kernel times (ms). paged: each copy is a paged cache whose block table
+    scatters the blocks over its pool in a seeded random order."""
+    n = int(np.max(lens))
     caches, ms = [], []
     for i in range(n_copies):
         if paged:
@@ -248,288 +433,7 @@ def quantized_copies(kvq, torch, w, layer, lens, max_blocks, n_copies, device_in
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
         caches.append(c)
-    del k, v
     return caches, ms
-
-
-def wl_mod():
-    from decode_attention_block_amd import workloads
-    return workloads
-
-
-def workspace(kvq, torch, cache, lengths, bps):
-    n = max(kvq.decode_attn_workspace_bytes(cache, int(L), bps) for L in lengths)
-    return torch.zeros(n, dtype=torch.uint8, device="cuda")   # counters start at zero
-
-
-def run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs,
-                         separate=False, paged=False):
-    """Single-layer fixed-length workloads; step = decode_step_qkv (or, with separate,
-    kv_append + decode_attn_qkv; the sampled kernel is then the attention alone).
-
-    Steps run in segments that start from the prefill lengths (reset between segments,
-    untimed): the 32K workload's segments are its 64-step decode loop on one cache; the
-    8K workloads rotate over cache copies, each gaining one token per use. Warm-up steps
-    are whole steps too, in segments of their own."""
-    wl = wl_mod()
-    B, H, D = w.batch, w.heads, w.head_dim
-    per_cache = 2 * B * H * w.context * code_bytes_per_token(w)
-    if w.decode_steps:
-        copies, growth = 1, w.decode_steps
-    else:
-        copies = max(1, math.ceil(CACHE_BYTES_TARGET / per_cache))
-        growth = math.ceil(steps / copies)
-    seg_cap = copies * growth                # steps before lengths must be reset
-    max_blocks = (w.context + growth + 63) // 64
-    t_setup = time.perf_counter()
-    caches, prefill_ms = quantized_copies(kvq, torch, w, 0, wl.lengths(w), max_blocks, copies,
-                                          device_inputs, paged)
-    kn = np.stack([wl.appended_kv(w, 0, s, 0, growth) for s in range(B)], axis=1)
-    vn = np.stack([wl.appended_kv(w, 0, s, 1, growth) for s in range(B)], axis=1)
-    k_new = torch.from_numpy(kn).cuda()          # [growth][B][H][D]
-    v_new = torch.from_numpy(vn).cuda()
-    queries = torch.from_numpy(np.stack([wl.query(w, 0, s) for s in range(seg_cap)])).cuda()
-    host_cache = caches[0].host_arrays() if keep_host else None
-    ws = workspace(kvq, torch, caches[0], range(w.context, w.context + growth + 1), bps)
-    out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
-    sm = wl.softmax_scale(w)
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t_setup
-
-    timer = Timer(torch)
-    kernel_bytes, step_bytes = [], []
-    # One launch per step: the kernel's average duration is the timed segments' total
-    # over the steps (HIP events bracket the segments); several launches per step: HIP
-    # events around every EVENT_STRIDE-th launch of the attention kernel.
-    bps_eff, n_split = kvq.decode_attn_plan(caches[0], w.context + growth, bps)
-    one_launch = not separate and n_split == 1
-
-    def step(j, timed):
-        """Step j of a segment: copy j % copies gains its (j // copies)-th token."""
-        c = caches[j % copies]
-        used = j // copies
-        L = w.context + used + 1
-        if separate:
-            kvq.kv_append(c, k_new[used], v_new[used], L)
-        sample = timed and not one_launch and j % EVENT_STRIDE == 0
-        if sample:
-            e0 = timer.event()
-        if separate:
-            kvq.decode_attn_qkv(c, queries[j], sm, out, ws, L, bps)
-        else:
-            kvq.decode_step_qkv(c, k_new[used], v_new[used], queries[j], sm, out, ws, L, bps)
-        if sample:
-            timer.kernel.append((e0, timer.event()))
-            kernel_bytes.append(attention_bytes(w, [L] * B) +
-                                (0 if separate else append_bytes(w)))
-        if timed:
-            step_bytes.append(attention_bytes(w, [L] * B) + append_bytes(w))
-            if one_launch:
-                kernel_bytes.append(step_bytes[-1])
-
-    def run(n_steps, timed):
-        done = 0
-        while done < n_steps:
-            for c in caches:
-                c.seq_lens.fill_(w.context)
-            torch.cuda.synchronize()
-            n = min(seg_cap, n_steps - done)
-            t0 = timer.event() if timed else None
-            for j in range(n):
-                step(j, timed)
-            if timed:
-                timer.segments.append((t0, timer.event()))
-            done += n
-        torch.cuda.synchronize()
-
-    run(warmup, False)
-    wall0 = time.perf_counter()
-    run(steps, True)
-    wall_s = time.perf_counter() - wall0
-    total_ms = timer.total_ms()
-    kernel_ms = [total_ms / steps] if one_launch else timer.kernel_ms()
-    res = {
-        "workload": w.name,
-        "step": ("kv_append + decode_attn_qkv" if separate else
-                 "decode_step_qkv (%s)" % ("append and attention in one launch" if one_launch
-                                           else "append, then attention")),
-        "kernel": kernel_name(w, fused=one_launch, paged=paged),
-        "layout": "paged (block table over a shuffled page pool)" if paged else "dense",
-        "steps": steps, "warmup": warmup,
-        "ms_per_step": total_ms / steps,
-        "gbs": sum(step_bytes) / (total_ms / 1e3) / 1e9,
-        "tokens_per_s": B * steps / (total_ms / 1e3),
-        "kernel_avg_us": float(np.mean(kernel_ms)) * 1e3,
-        "kernel_gbs": float(np.mean(kernel_bytes)) / (float(np.mean(kernel_ms)) / 1e3) / 1e9,
-        "kernel_bytes_per_launch": float(np.mean(kernel_bytes)),
-        "kernel_timing": ("timed segments / steps (one launch per step)" if one_launch else
-                          f"HIP event pairs around every {EVENT_STRIDE}th attention launch"),
-        "context": [w.context + 1, w.context + growth],
-        "cache_copies_rotated": copies, "blocks_per_split": bps_eff, "splits_per_row": n_split,
-        "prefill_quantize_ms": float(np.median(prefill_ms)),
-        "prefill_quantize_gbs": (2 * B * w.context * H * D * 2 + per_cache)
-        / (float(np.median(prefill_ms)) / 1e3) / 1e9,
-        "host_wall_s": wall_s, "setup_s": setup_s,
-    }
-    res["kernel_frac"] = res["kernel_gbs"] / HBM_PEAK_GBS
-    return res, host_cache
-
-
-def run_gqa(kvq, torch, w, steps, warmup, bps, paged=False):
-    """Grouped-query workload: one step is decode_attn_gqa (w.group query heads per
-    cached head) over one of enough cache copies (>= CACHE_BYTES_TARGET in all) that the
-    Infinity Cache cannot hold them; lengths fixed at the context (no append)."""
-    wl = wl_mod()
-    B, H, D, G = w.batch, w.heads, w.head_dim, w.group
-    lens = wl.lengths(w)
-    L = int(lens.max())
-    per_cache = 2 * B * H * L * code_bytes_per_token(w)
-    copies = max(1, math.ceil(CACHE_BYTES_TARGET / per_cache))
-    t_setup = time.perf_counter()
-    caches, prefill_ms = quantized_copies(kvq, torch, w, 0, lens, w.max_blocks, copies, False,
-                                          paged)
-    q = torch.from_numpy(wl.query(w, 0)).cuda()
-    out = torch.empty_like(q)
-    ws = torch.zeros(max(kvq.decode_attn_gqa_workspace_bytes(caches[0], G, L, bps), 16),
-                     dtype=torch.uint8, device="cuda")
-    sm = wl.softmax_scale(w)
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t_setup
-    timer = Timer(torch)
-
-    def run(n):
-        for j in range(n):
-            kvq.decode_attn_gqa(caches[j % copies], q, G, sm, out, ws, L, bps)
-
-    run(warmup)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0 = timer.event()
-    run(steps)
-    timer.segments.append((t0, timer.event()))
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - wall0
-    total_ms = timer.total_ms()
-    per_launch = attention_bytes(w, lens)
-    bps_eff, n_split = kvq.decode_attn_gqa_plan(caches[0], G, L, bps)
-    res = {
-        "workload": w.name,
-        "step": f"decode_attn_gqa ({G} query heads per cached head)",
-        "kernel": f"attn_split_int4_gqa_kernel<{D}, {G}, {'true' if paged else 'false'}>",
-        "layout": "paged (block table over a shuffled page pool)" if paged else "dense",
-        "steps": steps, "warmup": warmup,
-        "ms_per_step": total_ms / steps,
-        "gbs": per_launch * steps / (total_ms / 1e3) / 1e9,
-        "tokens_per_s": B * steps / (total_ms / 1e3),
-        "kernel_avg_us": total_ms / steps * 1e3,
-        "kernel_gbs": per_launch / (total_ms / steps / 1e3) / 1e9,
-        "kernel_bytes_per_launch": float(per_launch),
-        "kernel_timing": "timed segment / launches (one launch per step)",
-        "context": [L, L], "cache_copies_rotated": copies,
-        "blocks_per_split": bps_eff, "splits_per_row": n_split,
-        "prefill_quantize_ms": float(np.median(prefill_ms)),
-        "host_wall_s": wall_s, "setup_s": setup_s,
-    }
-    res["kernel_frac"] = res["kernel_gbs"] / HBM_PEAK_GBS
-    return res
-
-
-def run_layers(kvq, torch, w, steps, warmup, bps, device_inputs):
-    """The 32-layer ragged workload: one step is decode_attn_qkv over every layer's
-    cache, each layer with its own K, V and query."""
-    wl = wl_mod()
-    B, H, D = w.batch, w.heads, w.head_dim
-    lens = wl.lengths(w)
-    L = int(lens.max())
-    plan_note = "automatic"
-    if bps == 0 and w.ragged is not None:
-        # a ragged batch: the caller, who knows it, splits rows at about half the
-        # longest one, so the longest rows share their blocks between workgroups
-        bps = ((L + 63) // 64 + 1) // 2
-        plan_note = "half the longest row (chosen by the caller for a ragged batch)"
-    t_setup = time.perf_counter()
-    caches, prefill_ms, queries = [], [], []
-    for layer in range(w.layers):
-        c, ms = quantized_copies(kvq, torch, w, layer, lens, w.max_blocks, 1, device_inputs)
-        caches += c
-        prefill_ms += ms
-        queries.append(torch.from_numpy(wl.query(w, layer)).cuda())
-    ws = workspace(kvq, torch, caches[0], [L], bps)
-    out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
-    sm = wl.softmax_scale(w)
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t_setup
-    timer = Timer(torch)
-
-    def step(timed):
-        # one launch per layer and nothing else: the kernel's average duration is the
-        # timed segment over the launches
-        for layer in range(w.layers):
-            kvq.decode_attn_qkv(caches[layer], queries[layer], sm, out, ws, L, bps)
-
-    wall0 = time.perf_counter()
-    for _ in range(warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = timer.event()
-    for _ in range(steps):
-        step(True)
-    timer.segments.append((t0, timer.event()))
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - wall0
-    total_ms = timer.total_ms()
-    per_launch = attention_bytes(w, lens)
-    kernel_ms = [total_ms / (steps * w.layers)]
-    bps_eff, n_split = kvq.decode_attn_plan(caches[0], L, bps)
-    res = {
-        "workload": w.name,
-        "step": f"decode_attn_qkv over {w.layers} layers",
-        "kernel": kernel_name(w, fused=False),
-        "steps": steps, "warmup": warmup,
-        "ms_per_step": total_ms / steps,
-        "gbs": per_launch * w.layers * steps / (total_ms / 1e3) / 1e9,
-        "tokens_per_s": B * steps / (total_ms / 1e3),
-        "kernel_avg_us": float(np.mean(kernel_ms)) * 1e3,
-        "kernel_gbs": per_launch / (float(np.mean(kernel_ms)) / 1e3) / 1e9,
-        "kernel_bytes_per_launch": float(per_launch),
-        "kernel_timing": "timed segment / launches (one launch per layer)",
-        "context": [int(lens.min()), L], "mean_context": float(lens.mean()),
-        "blocks_per_split": bps_eff, "splits_per_row": n_split, "plan": plan_note,
-        "prefill_quantize_ms_per_layer": float(np.median(prefill_ms)),
-        "host_wall_s": wall_s, "setup_s": setup_s,
-    }
-    res["kernel_frac"] = res["kernel_gbs"] / HBM_PEAK_GBS
-    res.update(graph_step(torch, w, caches, queries, sm, steps, warmup, bps, step))
-    return res
-
-
-def graph_step(torch, w, caches, queries, sm, steps, warmup, bps, eager_step):
-    """The same 32-layer step captured once as a HIP graph (one replay per step) against
-    the eager calls: GPU time per step (HIP events around the timed segment) and host
-    time to queue one step."""
-    from decode_attention_block_amd.graph import DecodeGraph
-    dg = DecodeGraph(caches, sm, append=False, blocks_per_split=bps)
-    for i, q in enumerate(queries):
-        dg.q[i].copy_(q)
-    for _ in range(warmup):
-        dg.replay()
-    torch.cuda.synchronize()
-    res = {}
-    for name, fn in (("graph", dg.replay), ("eager", lambda: eager_step(True))):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        host = 0.0
-        e0.record()
-        for _ in range(steps):
-            h0 = time.perf_counter()
-            fn()
-            host += time.perf_counter() - h0
-        e1.record()
-        torch.cuda.synchronize()
-        res[f"{name}_ms_per_step"] = e0.elapsed_time(e1) / steps
-        res[f"{name}_host_us_per_step"] = host / steps * 1e6
-    res["graph"] = (f"{w.layers} decode_attn_qkv calls captured as one HIP graph "
-                    f"(host bound fixed at the capacity, {caches[0].capacity} tokens)")
-    return res
 
 
 def kernel_name(w, fused, paged=False):
@@ -541,17 +445,277 @@ def kernel_name(w, fused, paged=False):
     return f"attn_split_kernel<{w.scheme}, {w.head_dim}, {f}, {p}>"
 
 
-def measure(kvq, torch, w, steps, warmup, bps, keep_host=False, device_inputs=False,
-            separate=False, paged=False):
-    if w.layers > 1:
-        res = run_layers(kvq, torch, w, steps, warmup, bps, device_inputs), None
-    elif w.group > 1:
-        res = run_gqa(kvq, torch, w, steps, warmup, bps, paged), None
+def timing_fields(stepper, steps, warmup, eager, launches_per_step, step_bytes_fn,
+                  per_launch_bytes):
+    """Warm-up, the timed steps (graph replays, or eager), the eager comparison and the
+    per-step percentiles; step_bytes_fn(total steps) = algorithmic bytes of the timed
+    steps."""
+    stepper.run(warmup, timed=False, graph=not eager)
+    wall0 = time.perf_counter()
+    total_ms = stepper.run(steps, timed=True, graph=not eager)
+    wall_s = time.perf_counter() - wall0
+    eager_ms = total_ms if eager else stepper.run(steps, timed=True, graph=False)
+    samples = stepper.sample(SAMPLED_STEPS)
+    bytes_ = step_bytes_fn(steps)
+    launch_us = total_ms / (steps * launches_per_step) * 1e3
+    return {
+        "steps": steps, "warmup": warmup,
+        "timing": ("eager calls, HIP events around each segment" if eager else
+                   "HIP graph replay of each segment's steps, HIP events around each segment"),
+        "ms_per_step": total_ms / steps,
+        "gbs": bytes_ / (total_ms / 1e3) / 1e9,
+        "eager_ms_per_step": eager_ms / steps,
+        "eager_gbs": bytes_ / (eager_ms / 1e3) / 1e9,
+        "step_us": {k: v * 1e3 for k, v in pct(samples).items()},
+        "step_us_sampling": (f"HIP event pairs around each of {len(samples)} steps queued "
+                             "behind device copies (includes the events' own time)"),
+        "kernel_avg_us": launch_us,
+        "kernel_gbs": per_launch_bytes / (launch_us / 1e6) / 1e9,
+        "kernel_bytes_per_launch": float(per_launch_bytes),
+        "host_wall_s": wall_s,
+    }
+
+
+def run_append_attention(kvq, torch, w, steps, warmup, bps, device_inputs, separate=False,
+                         paged=False, eager=False, with_cpu=False, cpu_budget=4.0):
+    """Single-layer fixed-length workloads; step = decode_step_qkv (or, with separate,
+    kv_append + decode_attn_qkv). The 32K workload's segments are its 64-step decode
+    loop on one cache; the 8K workloads rotate over cache copies, each gaining one
+    token per use; the tiny workload runs on one cache (it is far smaller than the
+    caches, and its line is the call latency)."""
+    wl = wl_mod()
+    B, H, D = w.batch, w.heads, w.head_dim
+    per_cache = 2 * B * H * w.context * code_bytes_per_token(w)
+    tiny = per_cache < (1 << 20)
+    if w.decode_steps:
+        copies, growth = 1, w.decode_steps
+    elif tiny:
+        copies, growth = 1, min(steps, 64)
     else:
-        res = run_append_attention(kvq, torch, w, steps, warmup, bps, keep_host, device_inputs,
-                                   separate, paged)
-    res[0]["inputs"] = ("K/V drawn on the device (torch generator, same distributions)"
-                        if device_inputs else "K/V from the seeded host recipe")
+        copies = max(1, math.ceil(CACHE_BYTES_TARGET / per_cache))
+        growth = math.ceil(steps / copies)
+    seg_cap = copies * growth                # steps before lengths must be reset
+    max_blocks = (w.context + growth + 63) // 64
+    t_setup = time.perf_counter()
+    lens0 = wl.lengths(w)
+    k, v = prefill_inputs(torch, w, 0, w.context, device_inputs)
+    caches, prefill_ms = quantized_copies(kvq, torch, w, k, v, lens0, max_blocks, copies, paged)
+    Hs = sample_heads(w)
+    ks = host_sample(k, Hs) if with_cpu else None
+    vs = host_sample(v, Hs) if with_cpu else None
+    del k, v
+    torch.cuda.empty_cache()
+    kn = np.stack([wl.appended_kv(w, 0, s, 0, growth) for s in range(B)], axis=1)
+    vn = np.stack([wl.appended_kv(w, 0, s, 1, growth) for s in range(B)], axis=1)
+    k_new = torch.from_numpy(kn).cuda()          # [growth][B][H][D]
+    v_new = torch.from_numpy(vn).cuda()
+    q_host = [wl.query(w, 0, s) for s in range(seg_cap)]
+    queries = torch.from_numpy(np.stack(q_host)).cuda()
+    ws = torch.zeros(max(kvq.decode_attn_workspace_bytes(caches[0], L, bps)
+                         for L in range(w.context, w.context + growth + 1)),
+                     dtype=torch.uint8, device="cuda")          # counters start at zero
+    out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
+    sm = wl.softmax_scale(w)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    bps_eff, n_split = kvq.decode_attn_plan(caches[0], w.context + growth, bps)
+    one_launch = not separate and n_split == 1
+
+    def queue(j):
+        """Step j of a segment: copy j % copies gains its (j // copies)-th token."""
+        c = caches[j % copies]
+        used = j // copies
+        L = w.context + used + 1
+        if separate:
+            kvq.kv_append(c, k_new[used], v_new[used], L)
+            kvq.decode_attn_qkv(c, queries[j], sm, out, ws, L, bps)
+        else:
+            kvq.decode_step_qkv(c, k_new[used], v_new[used], queries[j], sm, out, ws, L, bps)
+
+    def reset():
+        for c in caches:
+            c.seq_lens.fill_(w.context)
+
+    def step_bytes(n):
+        tot = 0
+        for j in range(n):
+            L = w.context + (j % seg_cap) // copies + 1
+            tot += attention_bytes(w, [L] * B) + append_bytes(w)
+        return tot
+
+    stepper = Stepper(torch, queue, seg_cap, reset)
+    launches = 1 if one_launch else 2
+    per_launch = step_bytes(steps) / steps
+    res = timing_fields(stepper, steps, warmup, eager, launches, step_bytes,
+                        per_launch if one_launch else 0.0)
+    res.update({
+        "workload": w.name,
+        "step": ("kv_append + decode_attn_qkv" if separate else
+                 "decode_step_qkv (%s)" % ("append and attention in one launch" if one_launch
+                                           else "append, then attention")),
+        "kernel": kernel_name(w, fused=one_launch, paged=paged),
+        "layout": "paged (block table over a shuffled page pool)" if paged else "dense",
+        "tokens_per_s": B * steps / (res["ms_per_step"] * steps / 1e3),
+        "context": [w.context + 1, w.context + growth],
+        "cache_copies_rotated": copies, "blocks_per_split": bps_eff, "splits_per_row": n_split,
+        "prefill_quantize_ms": float(np.median(prefill_ms)),
+        "prefill_quantize_gbs": prefill_bytes(w, lens0) / (float(np.median(prefill_ms)) / 1e3)
+        / 1e9,
+        "setup_s": setup_s,
+    })
+    if not one_launch:
+        res.pop("kernel_gbs")
+        res.pop("kernel_bytes_per_launch")
+        res["kernel_avg_us"] = None
+    res["kernel_frac"] = res.get("kernel_gbs", 0.0) / HBM_PEAK_GBS
+    if tiny:
+        # the call latency a host sees: one eager decode_step_qkv, then a synchronize
+        lat = []
+        reset()
+        torch.cuda.synchronize()
+        for j in range(min(seg_cap, 64)):
+            t0 = time.perf_counter()
+            queue(j)
+            torch.cuda.synchronize()
+            lat.append((time.perf_counter() - t0) * 1e6)
+        res["host_call_latency_us"] = pct(lat)
+    if with_cpu:
+        kn_s = np.ascontiguousarray(kn[0, 0:1, :Hs])
+        vn_s = np.ascontiguousarray(vn[0, 0:1, :Hs])
+        qs = np.ascontiguousarray(q_host[0][0:1, :Hs * w.group])
+        res["oracle"] = oracle_legs(w, ks, vs, qs, int(lens0[0]), cpu_budget, w.name,
+                                    new_kv=(kn_s, vn_s))
+        res["gpu_over_oracle"] = ratios(res["gbs"], res["prefill_quantize_gbs"], res["oracle"])
+    return res
+
+
+def run_gqa(kvq, torch, w, steps, warmup, bps, paged=False, eager=False, with_cpu=False,
+            cpu_budget=4.0):
+    """Grouped-query workload: one step is decode_attn_gqa (w.group query heads per
+    cached head) over one of enough cache copies (>= CACHE_BYTES_TARGET in all) that the
+    Infinity Cache cannot hold them; lengths fixed at the context (no append)."""
+    wl = wl_mod()
+    B, H, D, G = w.batch, w.heads, w.head_dim, w.group
+    lens = wl.lengths(w)
+    L = int(lens.max())
+    per_cache = 2 * B * H * L * code_bytes_per_token(w)
+    copies = max(1, math.ceil(CACHE_BYTES_TARGET / per_cache))
+    t_setup = time.perf_counter()
+    k, v = prefill_inputs(torch, w, 0, L, False)
+    caches, prefill_ms = quantized_copies(kvq, torch, w, k, v, lens, w.max_blocks, copies, paged)
+    Hs = sample_heads(w)
+    ks = host_sample(k, Hs) if with_cpu else None
+    vs = host_sample(v, Hs) if with_cpu else None
+    del k, v
+    q_host = wl.query(w, 0)
+    q = torch.from_numpy(q_host).cuda()
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(kvq.decode_attn_gqa_workspace_bytes(caches[0], G, L, bps), 16),
+                     dtype=torch.uint8, device="cuda")
+    sm = wl.softmax_scale(w)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    per_launch = attention_bytes(w, lens)
+
+    def queue(j):
+        kvq.decode_attn_gqa(caches[j % copies], q, G, sm, out, ws, L, bps)
+
+    stepper = Stepper(torch, queue, max(steps, warmup, SAMPLED_STEPS))
+    res = timing_fields(stepper, steps, warmup, eager, 1, lambda n: n * per_launch, per_launch)
+    bps_eff, n_split = kvq.decode_attn_gqa_plan(caches[0], G, L, bps)
+    res.update({
+        "workload": w.name,
+        "step": f"decode_attn_gqa ({G} query heads per cached head)",
+        "kernel": f"attn_split_int4_gqa_kernel<{D}, {G}, {'true' if paged else 'false'}>",
+        "layout": "paged (block table over a shuffled page pool)" if paged else "dense",
+        "tokens_per_s": B * steps / (res["ms_per_step"] * steps / 1e3),
+        "context": [L, L], "cache_copies_rotated": copies,
+        "blocks_per_split": bps_eff, "splits_per_row": n_split,
+        "prefill_quantize_ms": float(np.median(prefill_ms)),
+        "prefill_quantize_gbs": prefill_bytes(w, lens) / (float(np.median(prefill_ms)) / 1e3)
+        / 1e9,
+        "setup_s": setup_s,
+    })
+    res["kernel_frac"] = res["kernel_gbs"] / HBM_PEAK_GBS
+    if with_cpu:
+        res["oracle"] = oracle_legs(w, ks, vs, np.ascontiguousarray(q_host[0:1, :Hs * G]), L,
+                                    cpu_budget, w.name)
+        # the step is attention alone on both sides
+        res["gpu_over_oracle"] = ratios(res["gbs"], res["prefill_quantize_gbs"], res["oracle"])
+    return res
+
+
+def run_layers(kvq, torch, w, steps, warmup, bps, eager=False, with_cpu=False, cpu_budget=4.0):
+    """The 32-layer ragged workload: one step is decode_attn_qkv over every layer's
+    cache, each layer with its own K, V and query (no append in this workload)."""
+    wl = wl_mod()
+    B, H, D = w.batch, w.heads, w.head_dim
+    lens = wl.lengths(w)
+    L = int(lens.max())
+    t_setup = time.perf_counter()
+    caches, prefill_ms, queries = [], [], []
+    ks = vs = None
+    Hs = sample_heads(w)
+    for layer in range(w.layers):
+        k, v = prefill_inputs(torch, w, layer, L, True)
+        c, ms = quantized_copies(kvq, torch, w, k, v, lens, w.max_blocks, 1)
+        if with_cpu and layer == 0:
+            ks, vs = host_sample(k, Hs), host_sample(v, Hs)
+        del k, v
+        caches += c
+        prefill_ms += ms
+        queries.append(torch.from_numpy(wl.query(w, layer)).cuda())
+    torch.cuda.empty_cache()
+    ws = torch.zeros(max(kvq.decode_attn_workspace_bytes(caches[0], L, bps), 16),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
+    sm = wl.softmax_scale(w)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    per_launch = attention_bytes(w, lens)
+
+    def queue(j):
+        for layer in range(w.layers):
+            kvq.decode_attn_qkv(caches[layer], queries[layer], sm, out, ws, L, bps)
+
+    stepper = Stepper(torch, queue, max(steps, warmup, SAMPLED_STEPS))
+    res = timing_fields(stepper, steps, warmup, eager, w.layers,
+                        lambda n: n * w.layers * per_launch, per_launch)
+    bps_eff, n_split = kvq.decode_attn_plan(caches[0], L, bps)
+    res.update({
+        "workload": w.name,
+        "step": f"decode_attn_qkv over {w.layers} layers",
+        "kernel": kernel_name(w, fused=False),
+        "tokens_per_s": B * steps / (res["ms_per_step"] * steps / 1e3),
+        "context": [int(lens.min()), L], "mean_context": float(lens.mean()),
+        "blocks_per_split": bps_eff, "splits_per_row": n_split,
+        "plan": "automatic" if bps == 0 else f"{bps} blocks per split (caller's choice)",
+        "prefill_quantize_ms_per_layer": float(np.median(prefill_ms)),
+        "prefill_quantize_gbs": prefill_bytes(w, lens) / (float(np.median(prefill_ms)) / 1e3)
+        / 1e9,
+        "setup_s": setup_s,
+    })
+    res["kernel_frac"] = res["kernel_gbs"] / HBM_PEAK_GBS
+    if with_cpu:
+        res["oracle"] = oracle_legs(w, ks, vs, np.ascontiguousarray(wl.query(w, 0)[0:1, :Hs]),
+                                    int(lens[0]), cpu_budget, w.name + " layer 0")
+        res["gpu_over_oracle"] = ratios(res["gbs"], res["prefill_quantize_gbs"], res["oracle"])
+    return res
+
+
+def measure(kvq, torch, w, steps, warmup, bps, separate=False, paged=False, eager=False,
+            with_cpu=False, cpu_budget=4.0):
+    big = w.decode_steps > 0 or w.layers > 1
+    if w.layers > 1:
+        res = run_layers(kvq, torch, w, steps, warmup, bps, eager, with_cpu, cpu_budget)
+    elif w.group > 1:
+        res = run_gqa(kvq, torch, w, steps, warmup, bps, paged, eager, with_cpu, cpu_budget)
+    else:
+        res = run_append_attention(kvq, torch, w, steps, warmup, bps, big, separate, paged,
+                                   eager, with_cpu, cpu_budget)
+    res["inputs"] = ("K/V drawn on the device (torch generator, same distributions)"
+                     if big else "K/V from the seeded host recipe")
     return res
 
 
@@ -578,16 +742,18 @@ def main():
     with_cpu = not (args.no_cpu or args.profile_loop)
     print(f"[bench] {w.name}: {args.steps} steps after {args.warmup} warm-up",
           file=sys.stderr, flush=True)
-    big = w.decode_steps > 0 or w.layers > 1
-    res, host_cache = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
-                              keep_host=with_cpu and not big, device_inputs=big,
-                              separate=args.separate, paged=args.paged)
+    res = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
+                  separate=args.separate, paged=args.paged, eager=args.eager,
+                  with_cpu=with_cpu, cpu_budget=args.cpu_seconds)
     if args.profile_loop:
         print(json.dumps(res), flush=True)
         return
+    print("[bench] stream-read ceiling", file=sys.stderr, flush=True)
+    ceiling = read_ceiling(kvq, torch)
 
     B, H, D = w.batch, w.heads, w.head_dim
     fused = ", true," in res["kernel"]
+    achieved = res.get("kernel_gbs")
     result = {
         "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s, int4 KV, B=8 ctx 8K",
         "value": res["gbs"],
@@ -599,7 +765,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPES[w.scheme],
         "data": "synthetic (seeded; see decode_attention_block_amd/workloads.py)",
         "pct_of_hbm_peak": 100.0 * res["gbs"] / HBM_PEAK_GBS,
         "tokens_per_s": res["tokens_per_s"],
@@ -613,24 +779,38 @@ def main():
         "roofline": {"bound": "hbm",
                      "kernel": res["kernel"] + (" (decode_step_qkv: append + attention)"
                                                 if fused else f" ({res['step']})"),
-                     "achieved": res["kernel_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": res["kernel_gbs"] / HBM_PEAK_GBS,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS if achieved else None,
                      "traffic": measured_traffic() if w.name == HEADLINE and fused else None,
-                     "avg_kernel_us": res["kernel_avg_us"], "timing": res["kernel_timing"],
-                     "algorithmic_bytes_per_launch": res["kernel_bytes_per_launch"]},
-        "graph_step": {k: res[k] for k in res if k.startswith(("graph", "eager"))} or None,
+                     "avg_kernel_us": res["kernel_avg_us"],
+                     "timing": res["timing"] + " / launches",
+                     "algorithmic_bytes_per_launch": res.get("kernel_bytes_per_launch"),
+                     "frac_of_read_ceiling": achieved / ceiling["gbs"] if achieved else None},
+        "read_ceiling": ceiling,
+        "step_us": res["step_us"],
+        "step_us_sampling": res["step_us_sampling"],
+        "eager": {"ms_per_step": res["eager_ms_per_step"], "gbs": res["eager_gbs"],
+                  "note": "the same steps queued one by one from the host"},
         "prefill_quantize": {"ms": res.get("prefill_quantize_ms"),
                              "gbs": res.get("prefill_quantize_gbs")},
         "host_wall_s": res["host_wall_s"],
         "setup_s": res["setup_s"],
     }
-    if with_cpu and host_cache is not None:
-        lens0 = np.full(B, w.context, np.int32)
-        result["cpu_baseline"] = cpu_baseline(w, host_cache, wl.query(w, 0), lens0,
-                                              args.cpu_seconds)
-        result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(
-            w, host_cache, wl.query(w, 0), lens0, args.cpu_seconds / 2)
-        del host_cache
+    if with_cpu and "oracle" in res:
+        legs = res["oracle"]
+        one, allc = legs["decode_step_1core"], legs["decode_step_all_cores"]
+        result["cpu_baseline"] = {
+            "value": one["gbs"], "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": legs["sample"] + f"; one decode step (oracle.append + oracle.attention) "
+                      f"repeated {one['reps']} times on one host thread, "
+                      f"{one['ms'] * one['reps'] / 1e3:.1f} s",
+            "tokens_per_s": one["tokens_per_s"]}
+        result["cpu_baseline_all_cores"] = {
+            "value": allc["gbs"], "unit": "GB/s", "cores": allc["cores"], "kind": "oracle",
+            "sample": legs["sample"] + f"; heads split over {allc['cores']} host threads",
+            "tokens_per_s": allc["tokens_per_s"]}
+        result["oracle"] = legs
+        result["gpu_over_oracle"] = res["gpu_over_oracle"]
     if not args.headline_only:
         others = []
         for name in OTHERS:
@@ -638,17 +818,21 @@ def main():
                 continue
             ow = wl.BY_NAME[name]
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            steps = 64 * 3 if ow.decode_steps else (20 if ow.layers > 1 else args.steps)
-            warm = 10 if ow.layers > 1 else args.warmup
-            r, _ = measure(kvq, torch, ow, steps, warm, args.blocks_per_split,
-                           device_inputs=ow.decode_steps > 0 or ow.layers > 1,
-                           separate=args.separate)
+            if ow.decode_steps:
+                st, warm = 64 * 3, 64
+            elif ow.layers > 1:
+                st, warm = max(5, min(args.steps, 20)), max(2, min(args.warmup, 10))
+            else:
+                st, warm = args.steps, args.warmup
+            r = measure(kvq, torch, ow, st, warm, args.blocks_per_split,
+                        separate=args.separate, eager=args.eager, with_cpu=with_cpu,
+                        cpu_budget=4.0)
             others.append(r)
             torch.cuda.empty_cache()
-        if not args.paged and w.layers == 1:
+        if not args.paged and w.layers == 1 and w.group == 1:
             print(f"[bench] {w.name} paged", file=sys.stderr, flush=True)
-            r, _ = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
-                           device_inputs=big, separate=args.separate, paged=True)
+            r = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
+                        separate=args.separate, paged=True, eager=args.eager)
             others.append(r)
             torch.cuda.empty_cache()
         result["workloads"] = others

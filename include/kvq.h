@@ -270,6 +270,19 @@ int decode_attn_gqa_plan(const kvq_cache* cache, int32_t group, int32_t max_len,
                          int32_t blocks_per_split, int32_t* blocks_per_split_out,
                          int32_t* splits_per_row_out);
 
+/* Measurement aid (not part of the method): reads `bytes` bytes of device memory at
+ * `buf` once, the way the attention kernels read a row's codes (each of at most
+ * `workgroups` 256-thread workgroups streams one contiguous slab, 16-byte non-temporal
+ * loads), and stores one folded word per thread to `sink` (device memory, at least
+ * workgroups * 256 uint32). Its rate is the practical streaming-read ceiling of the
+ * GPU that the decode kernels' HBM rates are set against. Asynchronous on `stream`.
+ *   buf        : device memory, 16-byte aligned, bytes > 0.
+ *   workgroups : > 0; slabs are whole 4 KiB units below 2^31 bytes (KVQ_ENOTSUP when
+ *                bytes / workgroups does not fit).
+ * Returns KVQ_OK, KVQ_EINVAL, KVQ_EALIGN, KVQ_ENOTSUP or KVQ_EHIP. */
+int kvq_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
+                          void* stream);
+
 /* Human-readable text of a kvq_status (static storage). */
 const char* kvq_strerror(int status);
 

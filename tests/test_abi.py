@@ -220,3 +220,16 @@ def test_strerror_names_every_status():
     for code in range(-6, 1):
         assert kvq.kvq_strerror(code) != "unknown status"
     assert kvq.kvq_strerror(-99) == "unknown status"
+
+
+@no_gpu_only
+def test_stream_read_probe_validation():
+    L = kvq.load_library()
+    probe = L.kvq_probe_stream_read
+    assert probe(None, 4096, 256, FAKE, None) == EINVAL
+    assert probe(FAKE, 0, 256, FAKE, None) == EINVAL
+    assert probe(FAKE, 4096, 0, FAKE, None) == EINVAL
+    assert probe(FAKE, 4096, 256, None, None) == EINVAL
+    assert probe(FAKE + 8, 4096, 256, FAKE, None) == EALIGN
+    # one workgroup cannot stream 3 GiB in a slab below 2^31 bytes
+    assert probe(FAKE, 3 << 30, 1, FAKE, None) == ENOTSUP
