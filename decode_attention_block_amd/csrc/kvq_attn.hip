@@ -1263,13 +1263,18 @@ attn_split_int4_kernel(AttnArgs a) {
 
 // ---- grouped-query attention: G query heads per cached head ---------------------------
 // Query head h * G + g reads cache row (b, h), so the codes of a block are converted to
-// matrix-core operands once for all G queries: rows 0..G-1 of the QK^T A tile hold the
-// G queries (the one-query kernel above leaves rows 1..15 zero). Output element i of
-// lane l is row 4 * (l / 16) + i, column l % 16, so each 16-lane group holds four query
-// rows and each row keeps its own running max (the accumulators are rescaled when any
-// row's max rises). P.V: the G rows of weights reach the A layout through a per-wave LDS
-// image, split as above into fp16 high and low parts (of p * 2^14), which are two A
-// operands accumulated into the same output rows by separate MFMAs.
+// matrix-core operands once for all G queries. Rows 0..G-1 of the QK^T A tile hold the
+// G queries and rows G..2G-1 hold them again (the one-query kernel above leaves rows
+// 1..15 zero; the tile costs the same either way). Output element i of lane l is row
+// 4 * (l / 16) + i, column l % 16, so each 16-lane group holds four rows and each row
+// keeps its own running max (the accumulators are rescaled when any row's max rises);
+// a repeated row computes exactly what its original does. P.V: the weights reach the A
+// layout through a per-wave LDS image, split as above into fp16 high and low parts (of
+// p * 2^14): row g < G of the image takes the high part of query g's weights, row G + g
+// (the repeat) the low part, so one A operand carries both and a 16-channel tile takes
+// two MFMAs (one per 32-token K step) instead of four. Output row g then holds the
+// high parts' sum and row G + g the low parts'; the two are added once per split, in
+// the merge of the waves through LDS.
 
 // Maximum / sum over the 16 lanes of each DPP row; every lane of the row gets it.
 __device__ __forceinline__ float row16_max(float v) {
@@ -1291,9 +1296,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
   constexpr int NTV = D / 16;           // 16-channel N tiles of P.V
   constexpr int LOADS = D / 32;         // 16-byte loads per lane per region
   constexpr int kRegionBytes = 32 * D;  // one tensor's codes of one block
-  // per wave: [high, low][k step][8-token group][row][slot]
-  __shared__ __align__(16) _Float16 pimg[kSplitWaves][2][2][4][16][8];
-  __shared__ float red_o[kSplitWaves][G][D];
+  // per wave: [k step][8-token group][row][slot]; rows < G high parts, G..2G-1 low parts
+  __shared__ __align__(16) _Float16 pimg[kSplitWaves][2][4][16][8];
+  __shared__ float red_o[kSplitWaves][2 * G][D];  // rows G..2G-1: the low parts' sums
   __shared__ float red_l[kSplitWaves][G];
   __shared__ float red_m[kSplitWaves][G];
 
@@ -1319,23 +1324,24 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
   const int r16 = lane % 16;  // A row / output column of this lane
   const int grp = lane / 16;  // 8-element K group of this lane's fragments; its output rows / 4
 
-  {  // this wave's P images: rows G..15 stay zero
-    uint4* img = reinterpret_cast<uint4*>(&pimg[wave][0][0][0][0][0]);
+  {  // this wave's P image: rows 2G..15 stay zero
+    uint4* img = reinterpret_cast<uint4*>(&pimg[wave][0][0][0][0]);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) img[lane + k * kWave] = make_uint4(0u, 0u, 0u, 0u);
+    for (int k = 0; k < 2; ++k) img[lane + k * kWave] = make_uint4(0u, 0u, 0u, 0u);
   }
 
-  // Query operand: row g < G holds query g in slot order, x16 slots pre-divided by 16,
-  // built by make_query once the wave's first code requests are out (as above).
+  // Query operand: rows g and G + g (g < G) hold query g in slot order, x16 slots
+  // pre-divided by 16, built by make_query once the wave's first code requests are out
+  // (as above).
   uint4 qraw[KS];
   {
-    const uint16_t* qrow = a.q + (row * G + min(r16, G - 1)) * D + 8 * grp;
+    const uint16_t* qrow = a.q + (row * G + (r16 < 2 * G ? r16 % G : 0)) * D + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
   }
   half8_t aq[KS];
   auto make_query = [&]() {
-    const float keep = r16 < G ? 1.0f : 0.0f;
+    const float keep = r16 < 2 * G ? 1.0f : 0.0f;
     uint4 qr[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qr[ks] = query_ready(qraw[ks]);
@@ -1444,7 +1450,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
       }
   };
 
-  // o[n][i] += sv * sum_t p_t * c(t, 16 n + r16) for row 4 grp + i.
+  // o[n][i] += sv * sum_t w_t * c(t, 16 n + r16) for row r = 4 grp + i, where w is the
+  // high part of the weights of query r (r < G) or the low part of those of query r - G
+  // (G <= r < 2G).
   const int p_slot = nibble_slot(r16 & 7);                 // this lane's tokens' slot
   const float p_unit = (p_slot & 2) ? 1024.0f : 16384.0f;  // x16 slots: 2^14 / 16
   auto block_accumulate = [&](float vscale, const uint4 (&vr)[LOADS], const float (&p)[4][4]) {
@@ -1455,28 +1463,24 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * grp + i;
-        if (r < G) {
+        if (r < 2 * G) {
           const float x = p[nt][i] * p_unit;
           const _Float16 hi = static_cast<_Float16>(x);
-          pimg[wave][0][kstep][kgrp][r][p_slot] = hi;
-          pimg[wave][1][kstep][kgrp][r][p_slot] = static_cast<_Float16>(x - static_cast<float>(hi));
+          pimg[wave][kstep][kgrp][r][p_slot] =
+              r < G ? hi : static_cast<_Float16>(x - static_cast<float>(hi));
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    const half8_t ah0 = *reinterpret_cast<const half8_t*>(&pimg[wave][0][0][grp][r16][0]);
-    const half8_t ah1 = *reinterpret_cast<const half8_t*>(&pimg[wave][0][1][grp][r16][0]);
-    const half8_t al0 = *reinterpret_cast<const half8_t*>(&pimg[wave][1][0][grp][r16][0]);
-    const half8_t al1 = *reinterpret_cast<const half8_t*>(&pimg[wave][1][1][grp][r16][0]);
+    const half8_t ap0 = *reinterpret_cast<const half8_t*>(&pimg[wave][0][grp][r16][0]);
+    const half8_t ap1 = *reinterpret_cast<const half8_t*>(&pimg[wave][1][grp][r16][0]);
 #pragma unroll
     for (int n = 0; n < NTV; ++n) {
-      const half8_t v0 = int4_operand(dword_of(vr, 2 * n));
-      const half8_t v1 = int4_operand(dword_of(vr, 2 * n + 1));
       float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah0, v0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah1, v1, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al0, v0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al1, v1, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap0, int4_operand(dword_of(vr, 2 * n)), acc,
+                                                   0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap1, int4_operand(dword_of(vr, 2 * n + 1)),
+                                                   acc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[n][i] = __builtin_fmaf(sv, acc[i], o[n][i]);
     }
@@ -1501,16 +1505,18 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
       },
       make_query);
 
-  // The waves' states per row through LDS (a wave with no block has m = -inf, l = o = 0).
+  // The waves' states per row through LDS (a wave with no block has m = -inf, l = o = 0):
+  // o of rows 0..2G-1 (high and low parts), max and weight sum of rows 0..G-1 (a
+  // repeated row's are the same).
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * grp + i;
     const float lr = row16_sum(l[i]);
-    if (r < G) {
-      if (r16 == 0) {
-        red_l[wave][r] = lr;
-        red_m[wave][r] = m[i];
-      }
+    if (r < G && r16 == 0) {
+      red_l[wave][r] = lr;
+      red_m[wave][r] = m[i];
+    }
+    if (r < 2 * G) {
 #pragma unroll
       for (int n = 0; n < NTV; ++n) red_o[wave][r][16 * n + r16] = o[n][i];
     }
@@ -1531,7 +1537,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
 #pragma unroll
     for (int w = 0; w < kSplitWaves; ++w) {
       const float alpha = __builtin_amdgcn_exp2f(red_m[w][g] - M);
-      od = __builtin_fmaf(alpha, red_o[w][g][d], od);
+      od = __builtin_fmaf(alpha, red_o[w][g][d] + red_o[w][G + g][d], od);
       L = __builtin_fmaf(alpha, red_l[w][g], L);
     }
     return od;
