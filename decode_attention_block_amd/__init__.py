@@ -22,7 +22,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_ENOTSUP", -3: "KVQ_ECAPACITY",
           -4: "KVQ_EALIGN", -5: "KVQ_EWORKSPACE", -6: "KVQ_EHIP"}
 
 EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan",
-           "decode_attn_workspace_bytes", "decode_attn_qkv", "decode_attn_split",
+           "decode_attn_workspace_bytes", "decode_attn_qkv", "decode_attn_qkv_noalloc",
+           "decode_attn_split",
            "decode_attn_combine", "decode_step_qkv", "decode_attn_gqa",
            "decode_attn_gqa_workspace_bytes", "decode_attn_gqa_plan", "kvq_probe_stream_read",
            "kvq_strerror", "kvq_version"]
@@ -72,6 +73,7 @@ def load_library():
                              ctypes.c_int),
         "decode_attn_workspace_bytes": ([C, i32, i32], sz),
         "decode_attn_qkv": ([C, P, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
+        "decode_attn_qkv_noalloc": ([C, P, ctypes.c_float, P, i32, i32, P], ctypes.c_int),
         "decode_attn_split": ([C, P, ctypes.c_float, P, sz, i32, i32, P], ctypes.c_int),
         "decode_attn_combine": ([C, P, P, sz, i32, i32, P], ctypes.c_int),
         "decode_step_qkv": ([C, P, P, P, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
@@ -188,6 +190,19 @@ def decode_attn_qkv(cache, q, softmax_scale, out, workspace, max_len, blocks_per
                                         _ptr(workspace), ws_bytes, int(max_len),
                                         int(blocks_per_split), _stream(stream))
     _check(rc, "decode_attn_qkv")
+
+
+def decode_attn_qkv_noalloc(cache, q, softmax_scale, out, max_len, blocks_per_split=0,
+                            stream=None):
+    """decode_attn_qkv with no workspace argument: the library works in a static device
+    array of its own (KVQ_NOALLOC_SCRATCH_BYTES per GPU); calls on one GPU must not
+    overlap."""
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous [B][H][D]")
+    rc = load_library().decode_attn_qkv_noalloc(_desc(cache), _ptr(q), float(softmax_scale),
+                                                _ptr(out), int(max_len), int(blocks_per_split),
+                                                _stream(stream))
+    _check(rc, "decode_attn_qkv_noalloc")
 
 
 def decode_attn_gqa(cache, q, group, softmax_scale, out, workspace, max_len, blocks_per_split=0,

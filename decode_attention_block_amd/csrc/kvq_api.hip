@@ -1,7 +1,10 @@
 // kvq_api.hip — the C ABI of libkvq (declared in include/kvq.h): argument validation,
-// the split plan and kernel launches. No allocation; nothing kept between calls except
-// what lives in caller-owned buffers (the workspace's arrival counters).
+// the split plan and kernel launches. No allocation. Nothing is kept between calls except
+// what lives in caller-owned buffers (the workspace's arrival counters), and, for
+// decode_attn_qkv_noalloc only, a static device array per GPU with its address.
 #include <stdint.h>
+
+#include <mutex>
 
 #include "kvq.h"
 #include "kvq_internal.h"
@@ -158,6 +161,49 @@ int append_args(const kvq_cache* c, const void* k_new, const void* v_new, int32_
   return KVQ_OK;
 }
 
+// ---- the no-allocation variant of decode_attn_qkv -----------------------------------
+// Its arrival counters and partial states live in `scratch`, a device array of static
+// storage (one copy per GPU, zero when the code object is loaded). Layout: the first
+// kScratchRows uint32 are the rows' arrival counters, always at the same place, so that
+// calls of any shape find them zero (every call leaves the counters it used at zero);
+// the partial states of one call follow them. Host code never passes `scratch` itself
+// to a kernel: its name is a host-side stand-in, and the device address of each GPU's
+// copy comes from hipGetSymbolAddress.
+constexpr int64_t kScratchRows = 65536;
+constexpr size_t kScratchCounterBytes = kScratchRows * sizeof(uint32_t);
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+__global__ void clear_counters_kernel(uint32_t* c, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) c[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// This GPU's copy of `scratch` (device address), looked up once per device with that
+// device current; the first lookup also clears the counter region on `stream` (unless
+// the stream is being captured, where the kernel would only be recorded: the array is
+// zero from the code object's load). Returns nullptr on a HIP error.
+uint8_t* scratch_for_current_device(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return nullptr;
+  if (cs == hipStreamCaptureStatusNone) {
+    hipLaunchKernelGGL(clear_counters_kernel, dim3((kScratchRows + 255) / 256), dim3(256), 0,
+                       stream, static_cast<uint32_t*>(p), kScratchRows);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+  }
+  g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -271,6 +317,37 @@ int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, 
   return kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a,
                                 static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK
                                                                                 : KVQ_EHIP;
+}
+
+int decode_attn_qkv_noalloc(const kvq_cache* cache, const void* q, float softmax_scale,
+                            void* out, int32_t max_len, int32_t blocks_per_split, void* stream) {
+  if (!q || !out) return KVQ_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_EALIGN;
+  int rc = check_cache(cache);
+  if (rc != KVQ_OK) return rc;
+  int bps, n_split;
+  rc = plan(cache, max_len, blocks_per_split, &bps, &n_split);
+  if (rc != KVQ_OK) return rc;
+  // the partial states must fit behind the fixed counter region, the rows into it
+  const int64_t rows = static_cast<int64_t>(cache->batch) * cache->heads;
+  const size_t parts = static_cast<size_t>(rows) * static_cast<size_t>(n_split);
+  const size_t need = parts * (static_cast<size_t>(cache->head_dim) + 2) * sizeof(float);
+  if (rows > kScratchRows || need > KVQ_NOALLOC_SCRATCH_BYTES - kScratchCounterBytes)
+    return KVQ_EWORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* base = scratch_for_current_device(s);
+  if (!base) return KVQ_EHIP;
+  kvq::AttnArgs a = {};
+  // the descriptor's workspace fields are set below, from the scratch layout
+  rc = attn_args(cache, q, softmax_scale, out, base, workspace_bytes(cache, n_split), max_len,
+                 blocks_per_split, 1, &a);
+  if (rc != KVQ_OK) return rc;
+  a.counters = reinterpret_cast<uint32_t*>(base);
+  a.ws_o = reinterpret_cast<float*>(base + kScratchCounterBytes);
+  a.ws_ml = a.ws_o + parts * cache->head_dim;
+  if (a.n_split == 0) a.n_split = 1;  // every row's zeros are still written
+  return kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a, s) ==
+                 hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
 
 int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,

@@ -40,7 +40,9 @@ extern "C" {
 #endif
 
 #define KVQ_BLOCK_TOKENS 64
-#define KVQ_VERSION 3
+#define KVQ_VERSION 4
+/* Size of the static device array decode_attn_qkv_noalloc works in (per GPU). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* Cache formats. */
 enum kvq_scheme {
@@ -204,6 +206,24 @@ size_t decode_attn_workspace_bytes(const kvq_cache* cache, int32_t max_len,
 int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, void* out,
                     void* workspace, size_t workspace_bytes, int32_t max_len,
                     int32_t blocks_per_split, void* stream);
+
+/* decode_attn_qkv without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, plan, kernels and result as
+ * decode_attn_qkv (bitwise). The arrival counters and partial softmax states live in a
+ * static device array of KVQ_NOALLOC_SCRATCH_BYTES that the library holds on every GPU
+ * it runs on until the process ends: 256 KiB of counters for up to 65,536 rows
+ * (batch * heads), then the partial states, rows * splits_per_row * (head_dim + 2) * 4
+ * bytes. Its device address is looked up once per GPU (first call with that GPU
+ * current), when the counters are also cleared; every call leaves them zero.
+ * Calls that overlap on one GPU (concurrent streams, or threads) share the array and
+ * race: the caller must order them.
+ * Returns decode_attn_qkv's status codes; KVQ_EWORKSPACE when batch * heads exceeds
+ * 65,536 or the partial states of the plan do not fit (use decode_attn_qkv then), and
+ * KVQ_EHIP when the array's address cannot be obtained. */
+int decode_attn_qkv_noalloc(const kvq_cache* cache, const void* q, float softmax_scale,
+                            void* out, int32_t max_len, int32_t blocks_per_split,
+                            void* stream);
 
 /* The same attention as two kernels, queued separately (same arguments, same plan):
  * decode_attn_split writes every split's partial state to the workspace (it does not

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = kvq.load_library()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert kvq.kvq_version() == 3
+    assert kvq.kvq_version() == 4
 
 
 def cache(scheme=0, B=2, H=4, D=128, MB=3, **kw):
@@ -233,3 +233,20 @@ def test_stream_read_probe_validation():
     assert probe(FAKE + 8, 4096, 256, FAKE, None) == EALIGN
     # one workgroup cannot stream 3 GiB in a slab below 2^31 bytes
     assert probe(FAKE, 3 << 30, 1, FAKE, None) == ENOTSUP
+
+
+def rc_noalloc(c, q=FAKE, out=FAKE, max_len=100, bps=0):
+    return kvq.load_library().decode_attn_qkv_noalloc(ctypes.byref(c), q, 0.1, out, max_len,
+                                                      bps, None)
+
+
+@no_gpu_only
+def test_noalloc_validation_before_any_hip_call():
+    assert rc_noalloc(cache(), q=0) == EINVAL
+    assert rc_noalloc(cache(), out=FAKE + 4) == EALIGN
+    assert rc_noalloc(cache(MB=3), max_len=3 * 64 + 1) == ECAP
+    assert rc_noalloc(cache(), bps=-1) == EINVAL
+    # more rows than the static array has counters for
+    assert rc_noalloc(cache(B=300, H=256)) == EWS
+    # partial states beyond the array: 1024 rows x 2048 splits x 130 floats
+    assert rc_noalloc(cache(B=32, H=32, MB=2048), max_len=2048 * 64, bps=1) == EWS
