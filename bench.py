@@ -58,6 +58,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_int4_b8h32d128_ctx8k_traffic.json")
 CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
 SAMPLED_STEPS = 32             # steps timed one by one for the percentiles
+COMPARE_ROUNDS = 3             # alternating eager / graph rounds for their comparison
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 KV_FORMATS = {0: "int4 block-64 symmetric", 1: "uint8 block-64 asymmetric",
               2: "fp8 e4m3 block-64 scaled"}
@@ -454,7 +455,14 @@ def timing_fields(stepper, steps, warmup, eager, launches_per_step, step_bytes_f
     wall0 = time.perf_counter()
     total_ms = stepper.run(steps, timed=True, graph=not eager)
     wall_s = time.perf_counter() - wall0
-    eager_ms = total_ms if eager else stepper.run(steps, timed=True, graph=False)
+    # graph replay against eager calls of the same steps, in alternating rounds (the
+    # first pass after a pause runs slower while the GPU ramps up, so neither may always
+    # go first); medians of the rounds
+    g_ms, e_ms = [], []
+    for _ in range(COMPARE_ROUNDS):
+        e_ms.append(stepper.run(steps, timed=True, graph=False))
+        g_ms.append(stepper.run(steps, timed=True, graph=True))
+    eager_ms = float(np.median(e_ms))
     samples = stepper.sample(SAMPLED_STEPS)
     bytes_ = step_bytes_fn(steps)
     launch_us = total_ms / (steps * launches_per_step) * 1e3
@@ -466,6 +474,10 @@ def timing_fields(stepper, steps, warmup, eager, launches_per_step, step_bytes_f
         "gbs": bytes_ / (total_ms / 1e3) / 1e9,
         "eager_ms_per_step": eager_ms / steps,
         "eager_gbs": bytes_ / (eager_ms / 1e3) / 1e9,
+        "graph_vs_eager": {"graph_ms_per_step": float(np.median(g_ms)) / steps,
+                           "eager_ms_per_step": eager_ms / steps,
+                           "rounds": COMPARE_ROUNDS,
+                           "note": "alternating rounds after the timed steps, medians"},
         "step_us": {k: v * 1e3 for k, v in pct(samples).items()},
         "step_us_sampling": (f"HIP event pairs around each of {len(samples)} steps queued "
                              "behind device copies (includes the events' own time)"),
@@ -520,7 +532,8 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, device_inputs, separ
     setup_s = time.perf_counter() - t_setup
 
     bps_eff, n_split = kvq.decode_attn_plan(caches[0], w.context + growth, bps)
-    one_launch = not separate and n_split == 1
+    one_launch = not separate and kvq.decode_step_launches(caches[0], w.context + growth,
+                                                           bps) == 1
 
     def queue(j):
         """Step j of a segment: copy j % copies gains its (j // copies)-th token."""
@@ -690,7 +703,8 @@ def run_layers(kvq, torch, w, steps, warmup, bps, eager=False, with_cpu=False, c
         "tokens_per_s": B * steps / (res["ms_per_step"] * steps / 1e3),
         "context": [int(lens.min()), L], "mean_context": float(lens.mean()),
         "blocks_per_split": bps_eff, "splits_per_row": n_split,
-        "plan": "automatic" if bps == 0 else f"{bps} blocks per split (caller's choice)",
+        "plan": ("automatic (each row's split chosen on the device from the lengths)"
+                 if bps == 0 else f"{bps} blocks per split (caller's choice)"),
         "prefill_quantize_ms_per_layer": float(np.median(prefill_ms)),
         "prefill_quantize_gbs": prefill_bytes(w, lens) / (float(np.median(prefill_ms)) / 1e3)
         / 1e9,
@@ -791,6 +805,7 @@ def main():
         "step_us_sampling": res["step_us_sampling"],
         "eager": {"ms_per_step": res["eager_ms_per_step"], "gbs": res["eager_gbs"],
                   "note": "the same steps queued one by one from the host"},
+        "graph_vs_eager": res["graph_vs_eager"],
         "prefill_quantize": {"ms": res.get("prefill_quantize_ms"),
                              "gbs": res.get("prefill_quantize_gbs")},
         "host_wall_s": res["host_wall_s"],

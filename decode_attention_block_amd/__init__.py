@@ -21,7 +21,7 @@ BLOCK_TOKENS = 64
 STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_ENOTSUP", -3: "KVQ_ECAPACITY",
           -4: "KVQ_EALIGN", -5: "KVQ_EWORKSPACE", -6: "KVQ_EHIP"}
 
-EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan",
+EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan", "decode_step_launches",
            "decode_attn_workspace_bytes", "decode_attn_qkv", "decode_attn_qkv_noalloc",
            "decode_attn_split",
            "decode_attn_combine", "decode_step_qkv", "decode_attn_gqa",
@@ -71,6 +71,7 @@ def load_library():
         "kv_append": ([C, P, P, i32, P], ctypes.c_int),
         "decode_attn_plan": ([C, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
                              ctypes.c_int),
+        "decode_step_launches": ([C, i32, i32], ctypes.c_int),
         "decode_attn_workspace_bytes": ([C, i32, i32], sz),
         "decode_attn_qkv": ([C, P, ctypes.c_float, P, P, sz, i32, i32, P], ctypes.c_int),
         "decode_attn_qkv_noalloc": ([C, P, ctypes.c_float, P, i32, i32, P], ctypes.c_int),
@@ -148,6 +149,15 @@ def decode_attn_plan(cache, max_len, blocks_per_split=0):
                                          ctypes.byref(bps), ctypes.byref(ns))
     _check(rc, "decode_attn_plan")
     return bps.value, ns.value
+
+
+def decode_step_launches(cache, max_len_after, blocks_per_split=0):
+    """1 when decode_step_qkv runs as one kernel launch for these arguments, else 2."""
+    rc = load_library().decode_step_launches(_desc(cache), int(max_len_after),
+                                             int(blocks_per_split))
+    if rc < 0:
+        raise KvqError(rc, "decode_step_launches")
+    return rc
 
 
 def decode_attn_gqa_plan(cache, group, max_len, blocks_per_split=0):

@@ -46,19 +46,31 @@ int check_len(const kvq_cache* c, int32_t max_len) {
 
 int n_blocks_for(int32_t len) { return (len + kBlockTokens - 1) / kBlockTokens; }
 
-// Blocks per split when the caller leaves it to the library: as few splits per row as
-// fill the GPU with about one workgroup per CU. Long unbroken runs of one row's codes
-// stream from HBM faster than many short ones, and every extra split costs a merge.
-// Grouped-query rows (group > 1) aim at two workgroups per CU: that kernel is bound by
-// its per-block work on one wave per SIMD, and a second workgroup on the CU overlaps
-// its latencies (measured on the 8K grouped-query workload, 8 queries per cached head:
-// 24.7 us with one workgroup per CU, 23.2 us with two, 33.8 us with four).
-int auto_blocks_per_split(const kvq_cache* c, int nb, int group) {
+// The split plan. A caller's blocks_per_split cuts every row into pieces of that many
+// blocks. With blocks_per_split = 0 the pieces are chosen on the device from the rows'
+// actual lengths (split_range in kvq_attn.hip): the batch's blocks are shared out in
+// chunks of about 1/target of them, one chunk per workgroup, where target is one
+// workgroup per CU, and two for grouped-query rows (that kernel is bound by its
+// per-block work on one wave per SIMD, and a second workgroup on the CU overlaps its
+// latencies: measured on the 8K grouped-query workload, 8 queries per cached head,
+// 24.7 us with one workgroup per CU, 23.2 us with two, 33.8 us with four). Long unbroken
+// runs of one row's codes stream from HBM faster than many short ones, and every extra
+// split costs a merge, so rows of equal length stay whole once they fill the GPU; the
+// host only bounds the pieces a row may take (the grid's split dimension): two once the
+// rows alone reach the target (a ragged batch cuts its long rows in two), else one more
+// than the splits that equal rows take (the target over the rows). Every column of the
+// grid that no row uses still runs as workgroups that exit at once, which costs little
+// while they fit on the CUs beside the working ones and about 1 us where they wait for
+// them (8K grouped-query workload with twice the columns: 21.3 against 20.2 us).
+constexpr int64_t kMaxGridSplits = 65535;  // the grid's split dimension (z)
+
+int64_t plan_target(int group) { return group > 1 ? 2 * kTargetWorkgroups : kTargetWorkgroups; }
+
+int device_plan_splits(const kvq_cache* c, int nb, int group) {
   const int64_t rows = static_cast<int64_t>(c->batch) * c->heads;
-  const int64_t target = group > 1 ? 2 * kTargetWorkgroups : kTargetWorkgroups;
-  const int64_t splits = (target + rows - 1) / rows;
-  const int64_t bps = (nb + splits - 1) / splits;
-  return static_cast<int>(bps < 1 ? 1 : bps);
+  const int64_t target = plan_target(group);
+  const int64_t s = rows >= target ? 2 : (target + rows - 1) / rows + 1;
+  return static_cast<int>(s < nb ? s : nb);
 }
 
 int plan(const kvq_cache* c, int32_t max_len, int32_t bps_req, int* bps, int* n_split,
@@ -69,9 +81,19 @@ int plan(const kvq_cache* c, int32_t max_len, int32_t bps_req, int* bps, int* n_
   if (rc != KVQ_OK) return rc;
   if (bps_req < 0) return KVQ_EINVAL;
   const int nb = n_blocks_for(max_len);
-  *bps = bps_req > 0 ? bps_req : auto_blocks_per_split(c, nb, group);
-  *n_split = nb == 0 ? 0 : (nb + *bps - 1) / *bps;
+  *bps = bps_req;  // 0: chosen per row on the device
+  *n_split = nb == 0 ? 0 : bps_req > 0 ? (nb + bps_req - 1) / bps_req
+                                       : device_plan_splits(c, nb, group);
   return KVQ_OK;
+}
+
+// decode_step_qkv is one launch (each row's workgroup appends, then attends the whole
+// row) when every row is one piece: the automatic plan once the rows alone fill the GPU,
+// or a caller's blocks_per_split that covers max_len_after.
+bool step_is_one_launch(const kvq_cache* c, int32_t max_len_after, int32_t bps_req) {
+  const int nb = n_blocks_for(max_len_after);
+  if (bps_req > 0) return nb <= bps_req;
+  return static_cast<int64_t>(c->batch) * c->heads >= kTargetWorkgroups;
 }
 
 // Workspace layout: [rows] uint32 arrival counters (padded to 256 bytes), then the
@@ -98,6 +120,7 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
   const int64_t row_code_bytes = static_cast<int64_t>(c->max_blocks) * kBlockTokens *
                                  (c->scheme == KVQ_INT4_SYM ? c->head_dim / 2 : c->head_dim);
   if (!c->block_table && row_code_bytes > INT32_MAX) return KVQ_ENOTSUP;
+  if (n_split > kMaxGridSplits) return KVQ_ENOTSUP;
   if (n_split > 0) {
     if (!workspace || workspace_bytes_given < workspace_bytes(c, n_split, group))
       return KVQ_EWORKSPACE;
@@ -123,6 +146,8 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
   a->max_len = max_len;
   a->bps = bps;
   a->n_split = n_split;
+  a->batch = c->batch;
+  a->plan_target = static_cast<int>(plan_target(group));
   a->qk_scale = softmax_scale * 1.44269504088896340736f;  // log2(e)
   a->block_table = c->block_table;
   a->num_pages = c->num_pages;
@@ -266,6 +291,14 @@ int decode_attn_plan(const kvq_cache* cache, int32_t max_len, int32_t blocks_per
   return KVQ_OK;
 }
 
+int decode_step_launches(const kvq_cache* cache, int32_t max_len_after,
+                         int32_t blocks_per_split) {
+  int bps, n_split;
+  const int rc = plan(cache, max_len_after, blocks_per_split, &bps, &n_split);
+  if (rc != KVQ_OK) return rc;
+  return step_is_one_launch(cache, max_len_after, blocks_per_split) ? 1 : 2;
+}
+
 size_t decode_attn_workspace_bytes(const kvq_cache* cache, int32_t max_len,
                                    int32_t blocks_per_split) {
   int bps, n_split;
@@ -359,13 +392,19 @@ int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new
   kvq::AttnArgs a = {};
   int rc = append_args(cache, k_new, v_new, max_len_after, &a.ap);
   if (rc != KVQ_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (step_is_one_launch(cache, max_len_after, blocks_per_split)) {
+    // one workgroup per row: it appends, then attends the whole row
+    const int32_t whole = n_blocks_for(max_len_after) > 0 ? n_blocks_for(max_len_after) : 1;
+    rc = attn_args(cache, q, softmax_scale, out, workspace, workspace_bytes_given,
+                   max_len_after, whole, 1, &a);
+    if (rc != KVQ_OK) return rc;
+    return kvq::launch_decode_step(cache->scheme, cache->head_dim, cache->batch, a, s) ==
+                   hipSuccess ? KVQ_OK : KVQ_EHIP;
+  }
   rc = attn_args(cache, q, softmax_scale, out, workspace, workspace_bytes_given, max_len_after,
                  blocks_per_split, 1, &a);
   if (rc != KVQ_OK) return rc;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.n_split == 1)  // one workgroup per row: it appends, then attends
-    return kvq::launch_decode_step(cache->scheme, cache->head_dim, cache->batch, a, s) ==
-                   hipSuccess ? KVQ_OK : KVQ_EHIP;
   // several splits per row: the splits must all see the appended token
   if (kvq::launch_append(cache->scheme, cache->head_dim, a.ap, s) != hipSuccess) return KVQ_EHIP;
   return kvq::launch_attn_split(cache->scheme, cache->head_dim, cache->batch, a, s) == hipSuccess

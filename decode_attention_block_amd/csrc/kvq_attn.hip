@@ -164,6 +164,77 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t row, int n,
   a.out[row * D + d] = __builtin_bit_cast(uint16_t, r);
 }
 
+// ---- the split of a row ---------------------------------------------------------------
+// Blocks [begin, end) of a row of nb blocks that split `split` streams, and the number of
+// splits n of the row (the merge's count). A caller's plan (a.bps > 0) cuts every row
+// into a.bps-block pieces. With a.bps == 0 the split is chosen here, from the lengths of
+// all rows, so that a batch of unequal lengths is balanced without the host knowing
+// them: the whole batch's blocks T = heads * sum_b ceil(len_b / 64) are shared out in
+// chunks of about T / plan_target blocks, a row of nb blocks is cut into
+// n = ceil(nb / chunk) equal pieces (at most a.n_split), and rows no longer than a chunk
+// stay whole. Rows of equal length therefore get the split the host would choose for
+// them (one piece per row once the rows fill the GPU), and in a ragged batch the long
+// rows are cut so that no workgroup streams much more than a chunk (the chunked,
+// schedulable sub-blocks of page "第一章：DeepSeek R1推理模型性能跃迁全景概览" chapter 1).
+// Every workgroup of a row, and the combine kernel, compute the same n from the same
+// lengths, which no call changes while it runs.
+struct SplitRange {
+  int begin, end, n;
+};
+
+// Sum over all 64 lanes, in the same order in every wave (DPP within rows of 16 lanes,
+// then the four rows' sums read out and added in order).
+__device__ __forceinline__ float row16_sum_all(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  const int iv = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ int clamp_len(const AttnArgs& a, int len, int cap) {
+  return len < 0 ? 0 : min(len, min(a.max_len, cap));
+}
+
+__device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int nb, int split, int cap) {
+  SplitRange r;
+  int piece = a.bps;
+  if (a.bps > 0) {
+    r.n = (nb + a.bps - 1) / a.bps;
+  } else {
+    // Every lane adds up the blocks of sequences lane, lane + 64, ..., then the wave
+    // (binary32: exact up to 2^24 blocks, and beyond that rounded the same way in every
+    // workgroup, which is all the plan needs: every workgroup of a row must find the same
+    // n). The total is made wave-uniform explicitly (readfirstlane): left as a per-lane
+    // value it would make the split bounds, and with them the streaming loop's trip
+    // count, divergent for the compiler, which then rebuilds the loop around them (the
+    // 8K int4 attention measured 49.4 us instead of 41.8 us).
+    float t = 0.0f;
+    for (int i = threadIdx.x % kWave; i < a.batch; i += kWave)
+      t += static_cast<float>((clamp_len(a, a.seq_lens[i], cap) + kBlock - 1) / kBlock);
+    t = row16_sum_all(t);
+    t = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t)));
+    const float chunk = fmaxf(ceilf(t * static_cast<float>(a.heads) /
+                                    static_cast<float>(a.plan_target)), 1.0f);
+    const float pieces = ceilf(static_cast<float>(nb) / chunk);
+    const int n_max = static_cast<int>(fminf(pieces, static_cast<float>(a.n_split)));
+    // equal pieces of ceil(nb / n_max) blocks; the count is recomputed from that size,
+    // since n_max pieces of it may cover the row with fewer (11 blocks in at most 8
+    // pieces: pieces of 2 blocks, 6 of them), and the merge must wait for exactly the
+    // splits that hold blocks
+    piece = nb > 0 ? (nb + n_max - 1) / n_max : 1;
+    r.n = nb > 0 ? (nb + piece - 1) / piece : 0;
+  }
+  r.begin = split * piece;
+  r.end = min(r.begin + piece, nb);
+  return r;
+}
+
 // End of a split: thread d < D holds channel d of the split's merged (unnormalised)
 // output, M and L its max and weight sum. A single-split row in fused mode is written
 // out directly. Otherwise the partial goes to the workspace; in fused mode the
@@ -484,9 +555,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const uint8_t* poo
 // it was re-quantized).
 // The append wave takes the sequence's arrival ticket (1 << 24 added to seq_lens[b], as
 // in kv_append) once its own loads have completed, and the last of the sequence's `heads`
-// workgroups stores the new length when its work is done. Every workgroup of the
-// sequence reads the length before it takes its ticket, and the length changes only at
-// the last ticket, so none can see the new length.
+// workgroups stores the new length once its append wave has done its work. Every
+// workgroup of the sequence reads the length before it takes its ticket, and the length
+// changes only after the last ticket, so none can see the new length.
 constexpr int kStepWaves = kSplitWaves + 1;
 
 struct StepLens {
@@ -496,12 +567,16 @@ struct StepLens {
   int len_streamed;  // tokens in the blocks the other waves attend
 };
 
+// The length is read with a plain load, which most workgroups find in their XCD's L2
+// (a system-scope atomic load goes to memory every time): within the kernel the low 24
+// bits of seq_lens[b] change only at the sequence's last ticket, which comes after every
+// workgroup of the sequence has read them, and the top 8 bits (the arrival count that
+// other workgroups are adding to) are masked off. The barrier orders the read before
+// this workgroup's own ticket.
 __device__ __forceinline__ StepLens step_lengths(const AttnArgs& a, int b, int cap) {
   __shared__ int len_shared;
   if (threadIdx.x == 0)
-    len_shared = static_cast<int>(
-        __hip_atomic_load(reinterpret_cast<uint32_t*>(a.ap.seq_lens) + b, __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_SYSTEM) & 0xFFFFFFu);  // low 24 bits: the length
+    len_shared = static_cast<int>(static_cast<uint32_t>(a.ap.seq_lens[b]) & 0xFFFFFFu);
   __syncthreads();
   StepLens r;
   r.len0 = len_shared;
@@ -559,16 +634,22 @@ __device__ __forceinline__ void step_stage_reduce(const StepLens& sl, int lane, 
 __device__ __forceinline__ void step_release() { __builtin_amdgcn_s_barrier(); }
 
 // The sequence's arrival ticket, taken by the append wave after the length was read;
-// step_ticket_done (after the wave's work) stores the new length if this was the
-// sequence's last arrival. The atomic's latency (the sequence's `heads` tickets are
-// serialized at memory) must overlap the wave's work, so nothing may wait for it before
-// the end: it is issued after the wave's loads have been waited for (vector memory
-// requests complete in order, so a later wait would include it), and as one request of
-// the whole wave whose lanes past the first fall outside a 4-byte buffer resource
-// (seq_lens[b]) and so do not touch memory; a branch around a one-lane atomic would
-// merge its result with the other lanes' value and make the compiler wait for it at
-// once. System scope (cache policy sc1): the add is performed at memory, past the per-XCD
-// L2s. The result is meaningful in lane 0.
+// step_ticket_done, once the wave has coded and attended the open block, stores the new
+// length if this was the sequence's last arrival. The atomic's latency (the sequence's
+// `heads` tickets are serialized at memory) must overlap the wave's work, so nothing
+// waits for it before that: it is issued after the wave's loads have been waited for
+// (vector memory requests complete in order, so a later wait would include it), and as
+// one request of the whole wave whose lanes past the first fall outside a 4-byte buffer
+// resource (seq_lens[b]) and so do not touch memory; a branch around a one-lane atomic
+// would merge its result with the other lanes' value and make the compiler wait for it
+// at once. System scope (cache policy sc1): the add is performed at memory, past the
+// per-XCD L2s. The result is meaningful in lane 0.
+// The new length may be stored while the other workgroups still stream: each workgroup
+// of the sequence read the length before it took its ticket, so all of them have read it
+// once the last ticket is taken, and no other workgroup reads seq_lens[b]. Stored in the
+// middle of the kernel instead of at its end, the store's trip to memory is off the
+// kernel's last path (an end-of-kernel store and exchange measured 1.5 us per launch on
+// the 8K int4 step).
 constexpr int kCachePolicySystem = 16;  // sc1
 
 __device__ __forceinline__ uint32_t step_ticket(const AttnArgs& a, int b, int lane) {
@@ -601,7 +682,7 @@ __device__ __forceinline__ BlockScales step_append(const AttnArgs& a, const Step
   return append_finish<D, kWave>(a.ap, row, sl.len0, lane, fresh, plan);
 }
 
-// ---- split kernel: grid (n_split, heads, batch), kSplitWaves waves ------------------
+// ---- split kernel: grid (heads, batch, n_split), kSplitWaves waves ------------------
 template <int SCHEME, int D, bool kAppend, bool kPaged>
 __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void attn_split_kernel(
     AttnArgs a) {
@@ -613,9 +694,9 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   __shared__ float red_m[kStates];
   __shared__ __align__(16) _Float16 xs[kAppend ? 2 * kBlock * D : 8];  // append staging
 
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int split = blockIdx.z;
   const int cap = a.max_blocks * kBlock;
   StepLens sl = {0, 0, -1, 0};
   int len;
@@ -623,12 +704,12 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
     sl = step_lengths(a, b, cap);
     len = sl.len;
   } else {
-    len = a.seq_lens[b];
-    len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+    len = clamp_len(a, a.seq_lens[b], cap);
     sl.len_streamed = len;
   }
   const int nb = (len + kBlock - 1) / kBlock;
-  const int blk_begin = split * a.bps;
+  const SplitRange sr = split_range(a, nb, split, cap);
+  const int blk_begin = sr.begin;
   if (!kAppend && blk_begin >= nb) {  // uniform over the workgroup
     // an empty row has no split to merge: in fused mode split 0 writes its zeros
     if (a.fused && nb == 0 && split == 0 && threadIdx.x < D)
@@ -636,7 +717,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
     return;
   }
   // the blocks this split streams (in a decode step, all but the new token's block)
-  const int blk_end = min(blk_begin + a.bps, (sl.len_streamed + kBlock - 1) / kBlock);
+  const int blk_end = min(sr.end, (sl.len_streamed + kBlock - 1) / kBlock);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -807,6 +888,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
         block_weights(sl.tail_blk, sc.ks, sc.kz, kr, p);
         block_accumulate(sl.tail_blk, sc.vs, sc.vz, vr, p);
       }
+      step_ticket_done(a, sl, b, cap, ticket, lane);
     }
   }
   if (streaming)
@@ -864,7 +946,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
     for (int g = 0; g < GROUPS; ++g) sw += red_l[w][g * LPT];
     L = __builtin_fmaf(alpha[w], sw, L);
   }
-  finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
+  finish_split<D>(a, row, split, sr.n, od, M, L);
   if constexpr (kAppend) {
     if (wave == kSplitWaves) {
       // The new codes, written once the row's other blocks have been streamed (stores
@@ -883,7 +965,6 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
           }
         }
       }
-      step_ticket_done(a, sl, b, cap, ticket, lane);
     }
   }
 }
@@ -976,9 +1057,9 @@ attn_split_int4_kernel(AttnArgs a) {
   __shared__ float red_m[kStates];
   __shared__ __align__(16) _Float16 xs[kAppend ? 2 * kBlock * D : 8];  // append staging
 
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int split = blockIdx.z;
   const int cap = a.max_blocks * kBlock;
   StepLens sl = {0, 0, -1, 0};
   int len;
@@ -986,12 +1067,12 @@ attn_split_int4_kernel(AttnArgs a) {
     sl = step_lengths(a, b, cap);
     len = sl.len;
   } else {
-    len = a.seq_lens[b];
-    len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+    len = clamp_len(a, a.seq_lens[b], cap);
     sl.len_streamed = len;
   }
   const int nb = (len + kBlock - 1) / kBlock;
-  const int blk_begin = split * a.bps;
+  const SplitRange sr = split_range(a, nb, split, cap);
+  const int blk_begin = sr.begin;
   if (!kAppend && blk_begin >= nb) {  // uniform over the workgroup
     // an empty row has no split to merge: in fused mode split 0 writes its zeros
     if (a.fused && nb == 0 && split == 0 && threadIdx.x < D)
@@ -999,7 +1080,7 @@ attn_split_int4_kernel(AttnArgs a) {
     return;
   }
   // the blocks this split streams (in a decode step, all but the new token's block)
-  const int blk_end = min(blk_begin + a.bps, (sl.len_streamed + kBlock - 1) / kBlock);
+  const int blk_end = min(sr.end, (sl.len_streamed + kBlock - 1) / kBlock);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -1185,6 +1266,7 @@ attn_split_int4_kernel(AttnArgs a) {
         block_weights(sl.tail_blk, sc.ks, kr, p);
         block_accumulate(sc.vs, vr, p);
       }
+      step_ticket_done(a, sl, b, cap, ticket, lane);
     }
   }
   if (streaming)
@@ -1230,7 +1312,7 @@ attn_split_int4_kernel(AttnArgs a) {
   float L = 0.0f;
 #pragma unroll
   for (int w = 0; w < kStates; ++w) L = __builtin_fmaf(alpha[w], red_l[w], L);
-  finish_split<D>(a, row, split, (nb + a.bps - 1) / a.bps, od, M, L);
+  finish_split<D>(a, row, split, sr.n, od, M, L);
   if constexpr (kAppend) {
     if (wave == kSplitWaves) {
       // The open block's new codes, written once the row's other blocks have been
@@ -1256,7 +1338,6 @@ attn_split_int4_kernel(AttnArgs a) {
           if (plan[1].full || v_line) store_b128(vc + (i * kWave + lane) * 16, vr[i]);
         }
       }
-      step_ticket_done(a, sl, b, cap, ticket, lane);
     }
   }
 }
@@ -1302,22 +1383,22 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
   __shared__ float red_l[kSplitWaves][G];
   __shared__ float red_m[kSplitWaves][G];
 
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int split = blockIdx.z;
   const int cap = a.max_blocks * kBlock;
   const int64_t row = static_cast<int64_t>(b) * a.heads + h;  // the cache row
-  int len = a.seq_lens[b];
-  len = len < 0 ? 0 : min(len, min(a.max_len, cap));
+  const int len = clamp_len(a, a.seq_lens[b], cap);
   const int nb = (len + kBlock - 1) / kBlock;
-  const int blk_begin = split * a.bps;
+  const SplitRange sr = split_range(a, nb, split, cap);
+  const int blk_begin = sr.begin;
   if (blk_begin >= nb) {  // uniform over the workgroup
     // an empty row has no split to merge: in fused mode split 0 writes its zeros
     if (a.fused && nb == 0 && split == 0)
       for (int t = threadIdx.x; t < G * D; t += kSplitWaves * kWave) a.out[row * G * D + t] = 0;
     return;
   }
-  const int blk_end = min(blk_begin + a.bps, nb);
+  const int blk_end = sr.end;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -1525,7 +1606,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
 
   // Merge the waves per (row, channel), then finish as the one-query kernel does, for all
   // G output rows of the cache row (one arrival ticket per cache row).
-  const int n_row = (nb + a.bps - 1) / a.bps;
+  const int n_row = sr.n;
   const int64_t qrow0 = row * G;  // first output row
   constexpr int kThreadsWg = kSplitWaves * kWave;
   auto merged = [&](int g, int d, float& M, float& L) {
@@ -1595,17 +1676,15 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
   const int b = blockIdx.y;
   const int d = threadIdx.x;
   const int cap = a.max_blocks * kBlock;
-  int len = a.seq_lens[b];
-  len = len < 0 ? 0 : min(len, min(a.max_len, cap));
-  const int nb = (len + kBlock - 1) / kBlock;
-  const int n = (nb + a.bps - 1) / a.bps;
+  const int nb = (clamp_len(a, a.seq_lens[b], cap) + kBlock - 1) / kBlock;
+  const int n = split_range(a, nb, 0, cap).n;
   const int64_t row = static_cast<int64_t>(b) * a.heads + h;
   merge_row<D, false>(a, row, n, d);
 }
 
 template <int SCHEME, int D, bool kAppend, bool kPaged>
 hipError_t split_t(int batch, const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.n_split, a.heads, batch);
+  dim3 grid(a.heads, batch, a.n_split);  // splits last: every row's first split comes first
   dim3 block((kAppend ? kStepWaves : kSplitWaves) * kWave);
   if constexpr (SCHEME == KVQ_INT4_SYM)
     hipLaunchKernelGGL((attn_split_int4_kernel<D, kAppend, kPaged>), grid, block, 0, s, a);
@@ -1651,7 +1730,7 @@ hipError_t launch_decode_step(int scheme, int head_dim, int batch, const AttnArg
 namespace {
 template <int D, int G>
 hipError_t gqa_t(int batch, const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.n_split, a.heads, batch);
+  dim3 grid(a.heads, batch, a.n_split);
   dim3 block(kSplitWaves * kWave);
   if (a.block_table)
     hipLaunchKernelGGL((attn_split_int4_gqa_kernel<D, G, true>), grid, block, 0, s, a);

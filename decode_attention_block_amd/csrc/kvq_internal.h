@@ -57,6 +57,10 @@ struct AttnArgs {
   float* ws_o;         // [rows][n_split][D] unnormalised partial outputs
   float* ws_ml;        // [rows][n_split][2]  (running max in log2 units, sum of weights)
   int heads, max_blocks, max_len, bps, n_split;
+  // bps == 0: the split of every row is chosen on the device from all the rows' lengths
+  // (split_plan in kvq_attn.hip), aiming at plan_target workgroups; n_split is then the
+  // most splits a row may take (the grid's split dimension)
+  int batch, plan_target;
   int fused;           // 1: the last workgroup of each row merges the splits and writes out
   float qk_scale;      // softmax_scale * log2(e)
   const int32_t* block_table;  // paged layout, else nullptr

@@ -9,8 +9,10 @@ decode_attn_qkv for attention over a fixed cache); only the host side changes:
     replay (`k_new`, `v_new`, `q` per layer), and the outputs land in fixed buffers
     (`out` per layer);
   * lengths advance on the device (seq_lens), as in eager calls, so the graph stays
-    valid from step to step; the host length bound is fixed at capture to the caches'
-    capacity, which also fixes the split plan;
+    valid from step to step; the host length bound is fixed at capture (max_len, by
+    default the caches' capacity). With the automatic split plan (blocks_per_split = 0)
+    each row's split is chosen on the device from the actual lengths, so the bound only
+    sizes the grid;
   * nothing in the captured calls clears memory (the workspaces' arrival counters are
     zeroed once, before capture, and the kernels leave them zero).
 """
@@ -20,14 +22,15 @@ import decode_attention_block_amd as kvq
 class DecodeGraph:
     """caches: one KVCache per layer (same shape). append=True captures
     decode_step_qkv per layer (append the layer's new K and V token, then attend);
-    append=False captures decode_attn_qkv per layer."""
+    append=False captures decode_attn_qkv per layer. max_len: the host bound on the
+    lengths during the replays (after the append), at most the capacity."""
 
-    def __init__(self, caches, softmax_scale, append=True, blocks_per_split=0):
+    def __init__(self, caches, softmax_scale, append=True, blocks_per_split=0, max_len=None):
         import torch
         c0 = caches[0]
         self.caches = list(caches)
         self.append = append
-        self.max_len = c0.capacity
+        self.max_len = c0.capacity if max_len is None else int(max_len)
         shape = (c0.batch, c0.heads, c0.head_dim)
         dev = c0.seq_lens.device
         new = lambda: torch.zeros(shape, dtype=torch.float16, device=dev)

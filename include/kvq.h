@@ -169,11 +169,27 @@ int kv_append(const kvq_cache* cache, const void* k_new, const void* v_new,
               int32_t max_len_after, void* stream);
 
 /* Work split of decode_attn_qkv: the context of each row is cut into splits of
- * `blocks_per_split` 64-token blocks (0 = chosen by the library from the shape), each
- * handled by one workgroup, then merged. Writes the effective blocks per split and the
- * number of splits per row for this max_len. Host only. */
+ * `blocks_per_split` 64-token blocks, each handled by one workgroup, then merged by
+ * their log-sum-exp. blocks_per_split = 0 lets the kernels choose each row's split on
+ * the device from the rows' actual lengths (the host does not know them): the batch's
+ * blocks are shared out in chunks of about 1/256 of them (1/512 for grouped-query rows),
+ * and a row is cut into ceil(its blocks / chunk) equal pieces, so equal rows that fill
+ * the GPU stay whole and the long rows of a ragged batch are cut ([Pg1] chapter 1:
+ * chunked attention as schedulable sub-blocks). Writes blocks_per_split_out (0 for the
+ * device's choice) and splits_per_row_out, the most splits a row may take for this
+ * max_len (the workspace is sized for it): ceil(blocks / blocks_per_split), or for the
+ * device's choice 2 once batch * heads reaches 256 (512 grouped-query rows), else one
+ * more than 256 / (batch * heads) (512 / ... for grouped-query rows), never more than
+ * the blocks. Host only. */
 int decode_attn_plan(const kvq_cache* cache, int32_t max_len, int32_t blocks_per_split,
                      int32_t* blocks_per_split_out, int32_t* splits_per_row_out);
+
+/* Kernel launches decode_step_qkv queues for these arguments: 1 when every row is one
+ * piece (blocks_per_split = 0 with batch * heads >= 256, or a blocks_per_split covering
+ * max_len_after), else 2 (kv_append's kernel, then the attention). Negative kvq_status
+ * on invalid arguments. Host only. */
+int decode_step_launches(const kvq_cache* cache, int32_t max_len_after,
+                         int32_t blocks_per_split);
 
 /* Bytes of device workspace decode_attn_qkv needs for these arguments (0 on invalid
  * arguments). The workspace holds, first, one uint32 arrival counter per row (B*H,
@@ -198,10 +214,11 @@ size_t decode_attn_workspace_bytes(const kvq_cache* cache, int32_t max_len,
  *   workspace       : device buffer of >= decode_attn_workspace_bytes(...) bytes,
  *                     16-byte aligned; must not be shared by concurrent calls.
  *   max_len         : host-side bound on seq_lens, sizes the launch; <= MB*64.
- *   blocks_per_split: 0 = automatic, else the split size in blocks.
+ *   blocks_per_split: 0 = chosen per row on the device (decode_attn_plan), else the
+ *                     split size in blocks.
  * A row's codes must stay below 2^31 bytes (MB*64*D/2 for int4, MB*64*D for uint8):
- * they are addressed with 32-bit offsets (KVQ_ENOTSUP otherwise, also from
- * decode_attn_split / decode_attn_combine).
+ * they are addressed with 32-bit offsets, and a row may take at most 65,535 splits
+ * (KVQ_ENOTSUP otherwise, also from decode_attn_split / decode_attn_combine).
  * Returns KVQ_OK or a negative kvq_status. */
 int decode_attn_qkv(const kvq_cache* cache, const void* q, float softmax_scale, void* out,
                     void* workspace, size_t workspace_bytes, int32_t max_len,
@@ -240,9 +257,9 @@ int decode_attn_combine(const kvq_cache* cache, void* out, void* workspace,
 /* One decode step of every row: kv_append of (k_new, v_new) followed by
  * decode_attn_qkv of q over the lengths after the append. The cache and seq_lens end
  * bitwise as after those two calls made in that order on one stream, and so does out
- * when they are what runs: when the plan for max_len_after has several splits per
- * row, the two kernels are queued. With one split per row (the automatic plan gives
- * it whenever B*H >= 256) the step is one kernel launch: each row's workgroup has one
+ * when they are what runs: unless every row is one piece, the two kernels are queued
+ * (decode_step_launches). With one piece per row (blocks_per_split = 0 whenever
+ * B*H >= 256) the step is one kernel launch: each row's workgroup has one
  * wave more than the attention, which appends the row's token and then attends the
  * block holding it while the other waves attend the rest of the row, so the append
  * costs no launch and no time on the attention's path. out then equals the two calls'

@@ -186,34 +186,58 @@ def test_decode_step_validates_like_append_and_attention():
 def test_plan_is_whole_blocks_and_covers_context():
     c = cache(B=8, H=32, D=128, MB=129)
     for max_len in (1, 64, 65, 8192, 8256):
-        bps, ns = kvq.decode_attn_plan(c, max_len)
         nb = (max_len + 63) // 64
-        assert bps >= 1 and ns == (nb + bps - 1) // bps
-    assert kvq.decode_attn_plan(c, 0) == (kvq.decode_attn_plan(c, 0)[0], 0)
-    assert kvq.decode_attn_plan(c, 8192, 5) == (5, (128 + 4) // 5)
+        for bps in (1, 5, 64, 200):
+            assert kvq.decode_attn_plan(c, max_len, bps) == (bps, (nb + bps - 1) // bps)
+    assert kvq.decode_attn_plan(c, 0) == (0, 0)
+    assert kvq.decode_attn_plan(c, 0, 5) == (5, 0)
 
 
-def test_automatic_plan_fills_the_gpu_with_fewest_splits():
-    # one workgroup per row once the rows alone fill the 256 CUs
-    assert kvq.decode_attn_plan(cache(B=8, H=32, MB=129), 8192) == (128, 1)
-    assert kvq.decode_attn_plan(cache(B=8, H=32, MB=129), 8220) == (129, 1)
-    assert kvq.decode_attn_plan(cache(B=16, H=32, MB=514), 32832) == (513, 1)
-    # fewer rows: just enough splits per row to reach about 256 workgroups
-    assert kvq.decode_attn_plan(cache(B=1, H=32, MB=2048), 131072) == (256, 8)
-    assert kvq.decode_attn_plan(cache(B=1, H=2, MB=4), 256) == (1, 4)
+def test_automatic_plan_bounds_the_pieces_a_row_may_take():
+    # the split of each row is chosen on the device (blocks_per_split_out = 0); the host
+    # bounds it: 2 pieces once the rows alone fill the 256 CUs (a ragged batch cuts its
+    # long rows in two) ...
+    assert kvq.decode_attn_plan(cache(B=8, H=32, MB=129), 8192) == (0, 2)
+    assert kvq.decode_attn_plan(cache(B=16, H=32, MB=514), 32832) == (0, 2)
+    assert kvq.decode_attn_plan(cache(B=8, H=32, MB=129), 64) == (0, 1)   # one block
+    # ... else one more than the pieces that equal rows take to reach about 256
+    # workgroups, never more than the blocks
+    assert kvq.decode_attn_plan(cache(B=1, H=32, MB=2048), 131072) == (0, 9)
+    assert kvq.decode_attn_plan(cache(B=1, H=2, MB=4), 256) == (0, 4)
+    assert kvq.decode_attn_plan(cache(B=3, H=5, MB=64), 4096) == (0, 19)
+
+
+def test_decode_step_is_one_launch_when_every_row_is_one_piece():
+    assert kvq.decode_step_launches(cache(B=8, H=32, MB=129), 8193) == 1
+    assert kvq.decode_step_launches(cache(B=16, H=32, MB=514), 32832) == 1
+    assert kvq.decode_step_launches(cache(B=1, H=32, MB=2048), 8193) == 2
+    assert kvq.decode_step_launches(cache(B=1, H=2, MB=4), 200, 4) == 1
+    assert kvq.decode_step_launches(cache(B=8, H=32, MB=129), 8193, 64) == 2
+    with pytest.raises(kvq.KvqError):
+        kvq.decode_step_launches(cache(B=8, H=32, MB=129), 129 * 64 + 1)
 
 
 def test_grouped_query_plan_aims_at_two_workgroups_per_cu():
-    # 8 sequences x 8 cached heads, 8K: 64 rows -> 8 splits of 16 blocks (512 workgroups)
+    # 8 sequences x 8 cached heads, 8K: 64 rows; equal rows take 512 / 64 = 8 pieces of
+    # 16 blocks on the device, and the grid allows one more
     c = cache(B=8, H=8, MB=128)
-    assert kvq.decode_attn_gqa_plan(c, 8, 8192) == (16, 8)
-    assert kvq.decode_attn_gqa_plan(c, 1, 8192) == kvq.decode_attn_plan(c, 8192) == (32, 4)
+    assert kvq.decode_attn_gqa_plan(c, 8, 8192) == (0, 9)
+    assert kvq.decode_attn_gqa_plan(c, 1, 8192) == kvq.decode_attn_plan(c, 8192) == (0, 5)
     assert kvq.decode_attn_gqa_plan(c, 4, 8192, 5) == (5, (128 + 4) // 5)
     # the workspace follows the grouped plan
     assert kvq.decode_attn_gqa_workspace_bytes(c, 8, 8192, 0) == \
-        kvq.decode_attn_gqa_workspace_bytes(c, 8, 8192, 16)
+        kvq.decode_attn_gqa_workspace_bytes(c, 8, 8192, 15)   # ceil(128 / 15) = 9 splits
     with pytest.raises(kvq.KvqError):
         kvq.decode_attn_gqa_plan(c, 0, 8192)
+
+
+@no_gpu_only
+def test_split_count_limit_of_the_grid():
+    # a row may take at most 65,535 splits (the grid's split dimension)
+    L = kvq.load_library()
+    c = cache(B=1, H=1, MB=(1 << 24) // 64 - 1)
+    rc = L.decode_attn_qkv(ctypes.byref(c), FAKE, 0.1, FAKE, FAKE, 1 << 40, 70000 * 64, 1, None)
+    assert rc == ENOTSUP
 
 
 def test_strerror_names_every_status():

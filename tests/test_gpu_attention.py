@@ -267,3 +267,35 @@ def test_many_splits_per_row(scheme, bps):
     torch.cuda.synchronize()
     assert np.array_equal(again.cpu().numpy(), o)
     assert np.array_equal(out.cpu().numpy(), o)
+
+
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
+def test_device_plan_cuts_the_long_rows_of_a_full_batch(scheme):
+    """blocks_per_split = 0 on 8 x 32 rows (the rows fill the GPU): each row's split is
+    chosen on the device from all the lengths. With one long sequence (10 blocks) among
+    one-block ones the batch holds 32 * 17 blocks, chunks of ceil(544 / 256) = 3 blocks,
+    so the long rows are cut into min(2, ceil(10 / 3)) = 2 pieces of 5 blocks and the
+    others stay whole: bitwise the output of the caller's plan of 5 blocks per split.
+    With all rows equal (10 blocks each) every row stays whole: bitwise the plan of 10.
+    Both within tolerance of the oracle."""
+    import decode_attention_block_amd as kvq
+    import torch
+    B, H, D, S = 8, 32, 64, 640
+    for lens, same_as in (((64, 600, 64, 64, 64, 64, 64, 64), 5), ((600,) * 8, 10)):
+        say("device plan", scheme, lens[:2], same_as)
+        k, v, q, lens = _small_case(scheme, D, seed=31, B=B, H=H, S=S, lens=lens)
+        c = gpu_quantize(scheme, k, v, lens, 10)
+        L = int(lens.max())
+        assert kvq.decode_attn_plan(c, L) == (0, 2)
+        sm = float(np.float32(1) / np.sqrt(np.float32(D)))
+        qt = to_gpu(q)
+        outs = []
+        for bps in (0, same_as):
+            out = torch.full_like(qt, 7.0)
+            kvq.decode_attn_qkv(c, qt, sm, out, kvq.make_workspace(c, L, bps), L, bps)
+            torch.cuda.synchronize()
+            outs.append(out)
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+        ref = oracle.attention(c.host_arrays(), q, lens, sm)
+        norm_err, _ = attn_errors(outs[0].cpu().numpy(), ref)
+        assert norm_err <= ATTN_TOL, norm_err

@@ -57,8 +57,8 @@ def _assert_same_output(out, out_ref, bitwise):
     assert norm_err <= 2.0 ** -10, norm_err
 
 
-# (B, H): 8 x 32 = 256 rows -> one split per row (single launch); 3 x 5 -> several
-# splits per row (append and attention as two launches).
+# (B, H): 8 x 32 = 256 rows -> one piece per row (single launch); 3 x 5 -> several
+# splits per row (append and attention as two launches, bitwise equal to the two calls).
 @pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("BH", [(8, 32), (3, 5)])
@@ -90,7 +90,7 @@ def test_step_equals_append_then_attention(scheme, D, BH):
         a, b = _state(ref_c), _state(c)
         assert np.array_equal(b["seq_lens"], lens)
         _assert_same_state(a, b)
-        _assert_same_output(out, out_ref, kvq.decode_attn_plan(c, max_after)[1] > 1)
+        _assert_same_output(out, out_ref, kvq.decode_step_launches(c, max_after) == 2)
         # the workspace counters are left zero for the next call
         n_rows = B * H
         assert not ws[: 4 * n_rows].any().item()
@@ -118,7 +118,7 @@ def test_step_on_full_rows_attends_without_appending():
     kn, vn, qt = to_gpu(k[np.arange(B), idx]), to_gpu(v[np.arange(B), idx]), to_gpu(q)
     out_ref = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
     out = torch.empty_like(out_ref)
-    assert kvq.decode_attn_plan(c, 128)[1] == 1   # the single-launch path
+    assert kvq.decode_step_launches(c, 128) == 1   # the single-launch path
     kvq.kv_append(ref_c, kn, vn, 128)
     kvq.decode_attn_qkv(ref_c, qt, sm, out_ref, kvq.make_workspace(ref_c, 128), 128)
     kvq.decode_step_qkv(c, kn, vn, qt, sm, out, kvq.make_workspace(c, 128), 128)
@@ -151,7 +151,7 @@ def test_step_with_lengths_beyond_the_bound(scheme):
     qt = to_gpu(q)
     out_ref = torch.empty((B, H, D), dtype=torch.float16, device="cuda")
     out = torch.empty_like(out_ref)
-    assert kvq.decode_attn_plan(c, bound)[1] == 1
+    assert kvq.decode_step_launches(c, bound) == 1
     kvq.kv_append(ref_c, kn, vn, bound)
     kvq.decode_attn_qkv(ref_c, qt, sm, out_ref, kvq.make_workspace(ref_c, bound), bound)
     kvq.decode_step_qkv(c, kn, vn, qt, sm, out, kvq.make_workspace(c, bound), bound)
