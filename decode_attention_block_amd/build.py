@@ -64,6 +64,36 @@ def build(verbose=False, extra=()):
     return LIB
 
 
+# Host-side sanitizers: AddressSanitizer and UndefinedBehaviorSanitizer on the host code
+# only (argument validation, the split plan, launch set-up); each -fsanitize= is preceded
+# by -Xarch_host so that no GPU code is built with them. Device code at -O0 (it is never
+# run from this build; only the host paths are exercised, without a GPU).
+SANITIZE_FLAGS = ["-O0", "-g", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+                  "-fno-fast-math", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                  "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=all",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "include"),
+                  "-I", CSRC]
+
+
+def build_sanitized(out_path):
+    """Builds the library with host-side ASan + UBSan into out_path (for the CPU tests;
+    load it with the clang ASan runtime preloaded, see sanitizer_runtime())."""
+    cmd = ["hipcc", *SANITIZE_FLAGS, "-o", out_path, *sources()]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc (sanitized) failed:\n" + r.stdout + r.stderr)
+    return out_path
+
+
+def sanitizer_runtime():
+    """Path of the clang AddressSanitizer runtime that matches hipcc (its UBSan handlers
+    included)."""
+    r = subprocess.run(["hipcc", "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip().splitlines()[-1] if r.returncode == 0 and r.stdout.strip() else ""
+    return path if os.path.isabs(path) and os.path.exists(path) else None
+
+
 def stale():
     """True when there is no built library or its sources (or flags) have changed since
     it was built: the recorded hash is compared with the current contents, so copying

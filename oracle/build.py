@@ -22,5 +22,15 @@ def build(verbose=False):
     return LIB
 
 
+def build_sanitized(out_path, clang="/opt/rocm/llvm/bin/clang++"):
+    """The oracle with AddressSanitizer + UndefinedBehaviorSanitizer (clang, so that one
+    sanitizer runtime serves it and the library's sanitized build in one process)."""
+    cmd = [clang, "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-o", out_path, SRC]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out_path
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
