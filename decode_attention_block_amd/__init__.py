@@ -25,7 +25,8 @@ EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan", "decode_step_l
            "decode_attn_workspace_bytes", "decode_attn_qkv", "decode_attn_qkv_noalloc",
            "decode_attn_split",
            "decode_attn_combine", "decode_step_qkv", "decode_attn_gqa",
-           "decode_attn_gqa_workspace_bytes", "decode_attn_gqa_plan", "kvq_probe_stream_read",
+           "decode_attn_gqa_workspace_bytes", "decode_attn_gqa_plan", "kvq_int4_to_natural",
+           "kvq_int4_from_natural", "kvq_probe_stream_read",
            "kvq_strerror", "kvq_version"]
 
 
@@ -82,6 +83,8 @@ def load_library():
         "decode_attn_gqa_workspace_bytes": ([C, i32, i32, i32], sz),
         "decode_attn_gqa_plan": ([C, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
                                  ctypes.c_int),
+        "kvq_int4_to_natural": ([P, P, i32, i32, i64], ctypes.c_int),
+        "kvq_int4_from_natural": ([P, P, i32, i32, i64], ctypes.c_int),
         "kvq_probe_stream_read": ([P, sz, i32, P, P], ctypes.c_int),
         "kvq_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "kvq_version": ([], ctypes.c_int),

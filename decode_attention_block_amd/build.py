@@ -14,7 +14,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["kvq_quant.hip", "kvq_attn.hip", "kvq_api.hip", "kvq_probe.hip"]
+SOURCES = ["kvq_quant.hip", "kvq_attn.hip", "kvq_api.hip", "kvq_probe.hip", "kvq_layout.hip"]
 HEADERS = ["kvq_device.h", "kvq_internal.h", "kvq_append.h"]
 LIB = os.path.join(HERE, "libkvq.so")
 ARCH = "gfx950"

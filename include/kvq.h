@@ -86,6 +86,7 @@ enum kvq_status {
  *                      ((f/4)*64 + l)*16 + (f%4)*4, nibble q (bits 4q..4q+3) =
  *                      K: channel 32*ks + 8*(l/16) + q of token 16*nt + l%16, f = nt*D/32 + ks;
  *                      V: token 32*ks + 8*(l/16) + q of channel 16*nt + l%16, f = 2*nt + ks.
+ *                      kvq_int4_to_natural / kvq_int4_from_natural convert (host).
  *                      Codes of tokens at or past a row's length inside its last block
  *                      are written as zero nibbles / bytes by the quantizing calls.
  *   k_scale, v_scale : float [B][H][MB].
@@ -306,6 +307,17 @@ size_t decode_attn_gqa_workspace_bytes(const kvq_cache* cache, int32_t group, in
 int decode_attn_gqa_plan(const kvq_cache* cache, int32_t group, int32_t max_len,
                          int32_t blocks_per_split, int32_t* blocks_per_split_out,
                          int32_t* splits_per_row_out);
+
+/* Host-side layout converters (host memory, no GPU work): n_regions consecutive int4
+ * block regions of 32 * head_dim bytes (the K or V codes of one block of one row, as in
+ * k_codes / v_codes; is_v selects the V order) from the stored matrix-core order to
+ * natural order [64 tokens][head_dim / 2] (channel 2k in the low nibble of byte k), and
+ * back. src and dst must not overlap. Returns KVQ_OK, KVQ_EINVAL (null pointer,
+ * n_regions < 0) or KVQ_ENOTSUP (head_dim other than 64 or 128). */
+int kvq_int4_to_natural(const uint8_t* stored, uint8_t* natural, int32_t head_dim,
+                        int32_t is_v, int64_t n_regions);
+int kvq_int4_from_natural(const uint8_t* natural, uint8_t* stored, int32_t head_dim,
+                          int32_t is_v, int64_t n_regions);
 
 /* Measurement aid (not part of the method): reads `bytes` bytes of device memory at
  * `buf` once, the way the attention kernels read a row's codes (each of at most

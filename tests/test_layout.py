@@ -73,3 +73,26 @@ def test_converters_match_nibble_by_nibble_formula(D, which):
     nat = layout.int4_to_natural(st, which)
     for i in range(2):
         assert np.array_equal(nat[i], _brute_force_to_natural(st[i].ravel(), D, which))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_c_abi_converters_match_the_stored_order(D, which):
+    """kvq_int4_to_natural / kvq_int4_from_natural (host C ABI) give the converters above
+    on several regions of random bytes, and invert each other."""
+    import ctypes
+
+    import decode_attention_block_amd as kvq
+    L = kvq.load_library()
+    n = 5
+    rs = np.random.default_rng(D + (which == "v"))
+    stored = rs.integers(0, 256, size=(n, 64, D // 2), dtype=np.uint8)
+    nat = np.empty_like(stored)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert L.kvq_int4_to_natural(ptr(stored), ptr(nat), D, which == "v", n) == 0
+    assert np.array_equal(nat, layout.int4_to_natural(stored, which))
+    back = np.empty_like(stored)
+    assert L.kvq_int4_from_natural(ptr(nat), ptr(back), D, which == "v", n) == 0
+    assert np.array_equal(back, stored)
+    assert L.kvq_int4_to_natural(ptr(stored), ptr(nat), 96, 0, 1) == -2
+    assert L.kvq_int4_to_natural(None, ptr(nat), D, 0, 1) == -1
