@@ -144,65 +144,33 @@ __device__ __forceinline__ float fp8_scale(float absmax) {
   return absmax == 0.0f ? 0.0f : absmax / 448.0f;
 }
 
-// The E4M3 code of q. Every step is exact but the rint: scaling by powers of two to the
-// position t on the binade's grid of 8 steps (the subnormal grid below 2^-6), whose
-// rounding carries into the next binade at 8. `near` is set when t lies within 2^-16
-// of a half step, i.e. within 2^-20 |q| of a decision boundary (t < 16): a value that
-// close to q may round the other way. There is no boundary at 448 (432 .. 448 -> 0x7E).
-__device__ __forceinline__ uint32_t fp8_round(float q, bool& near) {
-  const uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 24) & 0x80u;
-  const float a = fabsf(q);
-  if (a >= 448.0f) {
-    near = false;
-    return sign | 0x7Eu;
-  }
-  float t;
-  uint32_t base;
-  if (a < 0.015625f) {  // below 2^-6: the subnormal grid, steps of 2^-9
-    t = a * 512.0f;
-    base = 0u;
-  } else {
-    const int e = static_cast<int>((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;
-    t = __builtin_ldexpf(a, 3 - e) - 8.0f;  // 0 <= t < 8
-    base = static_cast<uint32_t>((e + 7) * 8);
-  }
-  const float m = __builtin_rintf(t);  // 8 carries into the next binade
-  near = 0.5f - fabsf(t - m) <= 0x1p-16f;
-  return sign | (base + static_cast<uint32_t>(m));
+// The E4M3 codes of 8 values are taken by the hardware conversion v_cvt_pk_fp8_f32 (two
+// values per instruction), which on gfx950 rounds a binary32 value to the nearest OCP
+// E4M3 value with ties to even, keeps the sign (so -0 and negative values that round to
+// zero give 0x80) and produces the subnormals m/8 * 2^-6. It is fed the correctly rounded
+// quotient RN(x / s) (an IEEE division, no reciprocal), clamped to +-448 so that values
+// the scheme saturates (|x / s| can exceed 448 by a rounding error) convert to 0x7E / 0xFE
+// instead of overflowing to NaN. Bit-exact against the oracle's search over all codes on
+// every rounding decision (ties, subnormals, signed zeros, 448: GPU test).
+__device__ __forceinline__ float fp8_quotient(float x, float s) {
+  return __builtin_fminf(__builtin_fmaxf(x / s, -448.0f), 448.0f);
 }
-
-__device__ __forceinline__ uint32_t fp8_code(float x, const Divisor& d) {
-  if (d.s == 0.0f) return 0u;
-  bool near;
-  const uint32_t c = fp8_round(x * d.r, near);
-  if (!near) return c;
-  return fp8_round(x / d.s, near);
-}
-
-// The packers below code 8 values with the multiply and take one branch, for all 8, in
-// the rare case that one of them needs the division.
 
 // 8 values -> 8 bytes of FP8 codes (x[i] in byte i).
 __device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], const Divisor& d) {
   if (d.s == 0.0f) return make_uint2(0u, 0u);
-  uint32_t c[8];
-  bool near = false;
+  float q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bool n;
-    c[i] = fp8_round(x[i] * d.r, n);
-    near |= n;
-  }
-  if (near) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      bool n;
-      c[i] = fp8_round(x[i] / d.s, n);
-    }
-  }
-  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                    c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+  for (int i = 0; i < 8; ++i) q[i] = fp8_quotient(x[i], d.s);
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);  // bytes 0, 1
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);      // bytes 2, 3
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
+  return make_uint2(static_cast<uint32_t>(w0), static_cast<uint32_t>(w1));
 }
+
+// The int4 and uint8 packers below code 8 values with the multiply and take one branch,
+// for all 8, in the rare case that one of them needs the division.
 
 // 8 values -> 4 bytes of int4 nibbles c + 8 (x[i] in bits 4i .. 4i+3; for 8 consecutive
 // channels: channel 2k in the low nibble of byte k).
