@@ -443,13 +443,12 @@ int decode_attn_gqa(const kvq_cache* cache, const void* q, int32_t group, float 
   if (!aligned16(q) || !aligned16(out)) return KVQ_EALIGN;
   int rc = check_cache(cache);
   if (rc != KVQ_OK) return rc;
-  if (cache->scheme != KVQ_INT4_SYM) return KVQ_ENOTSUP;
   kvq::AttnArgs a = {};
   rc = attn_args(cache, q, softmax_scale, out, workspace, workspace_bytes_given, max_len,
                  blocks_per_split, 1, &a, group);
   if (rc != KVQ_OK) return rc;
   if (a.n_split == 0) a.n_split = 1;  // every row's zeros are still written
-  return kvq::launch_attn_gqa(cache->head_dim, group, cache->batch, a,
+  return kvq::launch_attn_gqa(cache->scheme, cache->head_dim, group, cache->batch, a,
                               static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK
                                                                               : KVQ_EHIP;
 }

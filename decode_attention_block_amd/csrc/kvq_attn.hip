@@ -464,7 +464,10 @@ __device__ __forceinline__ float lane_value(float v, int i) {
 // `start()` runs once, after the wave's first code load has been issued and before
 // anything waits for it: work that waits for the query's own load goes there, so the
 // stream's first requests are not held behind it.
-template <int LOADS, class LoadParams, class Load, class OnK, class OnV, class Start>
+// STREAMS waves share the split this way (`wave` < STREAMS); waves given the same `wave`
+// stream the same blocks in the same order.
+template <int LOADS, int STREAMS = kSplitWaves, class LoadParams, class Load, class OnK,
+          class OnV, class Start>
 __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, int wave, int lane,
                                                    int64_t row, LoadParams load_params, Load load,
                                                    OnK on_k, OnV on_v, Start start) {
@@ -474,9 +477,9 @@ __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, i
     return;
   }
   const int rot = static_cast<int>((static_cast<uint32_t>(row) * 2654435761u) >> 8) % n;
-  const int n_wave = wave < n ? (n - wave + kSplitWaves - 1) / kSplitWaves : 0;
+  const int n_wave = wave < n ? (n - wave + STREAMS - 1) / STREAMS : 0;
   auto blk_of = [&](int i) {
-    const int b = wave + kSplitWaves * i + rot;
+    const int b = wave + STREAMS * i + rot;
     return blk_begin + (b >= n ? b - n : b);
   };
   uint4 kbuf[LOADS], vbuf[LOADS];
@@ -1669,6 +1672,299 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
   }
 }
 
+// ---- grouped-query attention over the 8-bit caches (uint8, FP8) ---------------------
+// The one-query VALU kernel's loads and arithmetic, with several query heads per wave:
+// each 16-byte chunk of codes is decoded once (FP8: to binary32 values with
+// v_cvt_pk_f32_fp8; uint8: to fp16 code pairs less the zero point) and multiplied into
+// every query head the wave holds (up to 4; registers bound it), each with its own
+// online softmax. With 8 query heads per cached head two waves read each block, one per
+// half of the group (the second read is served by the L2: HBM still sees the cache once),
+// so 2 of the 4 waves stream distinct blocks; with 2 or 4, every wave holds all of them
+// and the 4 waves stream distinct blocks. Splits, partial states and the last-arriver
+// merge are those of the int4 grouped-query kernel (one arrival counter per cache row,
+// partial states per query row).
+template <int SCHEME>
+__device__ __forceinline__ void chunk_values(const uint4& raw, half2_t off, float (&cv)[16]) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (SCHEME == KVQ_FP8_E4M3) {  // exact, two codes per instruction
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[j]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[j]), true);
+      cv[4 * j + 0] = lo[0];
+      cv[4 * j + 1] = lo[1];
+      cv[4 * j + 2] = hi[0];
+      cv[4 * j + 3] = hi[1];
+    } else {  // units of 2^-24, the zero point taken out of each fp16 pair (exact)
+      const half2_t e = as_h2(w[j] & 0x00FF00FFu) + off;         // channels 0, 2
+      const half2_t f = as_h2((w[j] >> 8) & 0x00FF00FFu) + off;  // channels 1, 3
+      cv[4 * j + 0] = static_cast<float>(e.x);
+      cv[4 * j + 1] = static_cast<float>(f.x);
+      cv[4 * j + 2] = static_cast<float>(e.y);
+      cv[4 * j + 3] = static_cast<float>(f.y);
+    }
+  }
+}
+
+template <int SCHEME, int D, int G, bool kPaged>
+__global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_gqa_kernel(AttnArgs a) {
+  using Geo = AGeo<SCHEME, D>;
+  constexpr int TPL = Geo::kTPL, DPL = Geo::kDPL, LPT = Geo::kLPT, GROUPS = Geo::kGroups;
+  constexpr int QW = G < 4 ? G : 4;             // query heads per wave
+  constexpr int QSETS = G / QW;                 // waves that read the same blocks
+  constexpr int STREAMS = kSplitWaves / QSETS;  // waves streaming distinct blocks
+  constexpr float kUnit = SCHEME == KVQ_FP8_E4M3 ? 1.0f : 16777216.0f;  // o's unit
+  __shared__ float red_o[kSplitWaves][kWave][DPL + 1];
+  __shared__ float red_l[kSplitWaves][kWave];
+  __shared__ float red_m[kSplitWaves];
+
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int split = blockIdx.z;
+  const int cap = a.max_blocks * kBlock;
+  const int64_t row = static_cast<int64_t>(b) * a.heads + h;  // the cache row
+  const int len = clamp_len(a, a.seq_lens[b], cap);
+  const int nb = (len + kBlock - 1) / kBlock;
+  const SplitRange sr = split_range(a, nb, split, cap);
+  if (sr.begin >= nb) {  // uniform over the workgroup
+    // an empty row has no split to merge: in fused mode split 0 writes its zeros
+    if (a.fused && nb == 0 && split == 0)
+      for (int t = threadIdx.x; t < G * D; t += kSplitWaves * kWave) a.out[row * G * D + t] = 0;
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int chunk = lane % LPT;
+  const int group = lane / LPT;
+  const int qset = wave % QSETS;   // the wave's query heads: qset * QW .. + QW - 1
+  const int stream = wave / QSETS;
+
+  Query<SCHEME, D> q[QW];
+#pragma unroll
+  for (int i = 0; i < QW; ++i) q[i].request(a.q + (row * G + qset * QW + i) * D + chunk * DPL);
+  float qsum[QW];
+  auto make_query = [&]() {
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+      q[i].ready();
+      qsum[i] = group_sum<LPT>(q[i].sum);
+    }
+  };
+
+  constexpr int kRegionBytes = kBlock * Geo::kRowBytes;
+  const int row_bytes = kPaged ? kRegionBytes : a.max_blocks * kRegionBytes;
+  const int64_t row_base = kPaged ? 0 : row * row_bytes;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.k_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.v_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
+  const int lane_off = lane * 16;
+  const int64_t sbase = kPaged ? 0 : row * a.max_blocks;
+  const float* ks = a.k_scale + sbase;
+  const float* vs = a.v_scale + sbase;
+  constexpr bool kZero = SCHEME == KVQ_UINT8_ASYM;
+  const float* kz = kZero ? a.k_zero + sbase : nullptr;
+  const float* vz = kZero ? a.v_zero + sbase : nullptr;
+
+  float o[QW][DPL];
+  float m[QW], l[QW];
+#pragma unroll
+  for (int i = 0; i < QW; ++i) {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[i][k] = 0.0f;
+    m[i] = -__builtin_inff();  // running max of query i's base-2 scores (wave-uniform)
+    l[i] = 0.0f;
+  }
+
+  auto load_codes = [&](bool is_v, int blk, int slot, uint4 (&r)[TPL]) {
+    if constexpr (kPaged) {
+      const __amdgpu_buffer_rsrc_t rs =
+          region_rsrc(is_v ? a.v_codes : a.k_codes, slot, kRegionBytes);
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) r[i] = load_stream(rs, lane_off, i * kWave * 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPL; ++i)
+        r[i] = load_stream(is_v ? vrsrc : krsrc, lane_off, blk * kRegionBytes + i * kWave * 16);
+    }
+  };
+  auto slot_of = [&](int blk) {
+    return kPaged ? static_cast<int>(block_slot(a.block_table, a.num_pages, a.heads,
+                                                a.max_blocks, b, h, blk))
+                  : blk;
+  };
+
+  // Scores of the lane's TPL tokens for every query head, then each head's online
+  // softmax update; p[i][t] = the weights relative to the running max m[i].
+  auto block_weights = [&](int blk, float kscale, float kzero, const uint4 (&kr)[TPL],
+                           float (&p)[QW][TPL]) {
+    const float sk = kscale * a.qk_scale;
+    float s[QW][TPL];
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      if constexpr (SCHEME == KVQ_FP8_E4M3) {
+        float cv[16];
+        chunk_values<SCHEME>(kr[t], half2_t{0, 0}, cv);
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+          float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 16; c += 2) {
+            a0 = __builtin_fmaf(cv[c], static_cast<float>(q[i].at(c)), a0);
+            a1 = __builtin_fmaf(cv[c + 1], static_cast<float>(q[i].at(c + 1)), a1);
+          }
+          s[i][t] = group_sum<LPT>(a0 + a1) * sk;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < QW; ++i)
+          s[i][t] = (group_sum<LPT>(chunk_dot<SCHEME, D>(kr[t], q[i])) - kzero * qsum[i]) * sk;
+      }
+    }
+    if (blk == nb - 1) {  // tokens past the length in the last block weigh nothing
+      const int valid = len - blk * kBlock;
+#pragma unroll
+      for (int t = 0; t < TPL; ++t)
+        if (t * GROUPS + group >= valid) {
+#pragma unroll
+          for (int i = 0; i < QW; ++i) s[i][t] = -__builtin_inff();
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+      float mb = s[i][0];
+#pragma unroll
+      for (int t = 1; t < TPL; ++t) mb = fmaxf(mb, s[i][t]);
+      mb = wave_max(mb);
+      if (mb > m[i]) {  // wave-uniform
+        const float alpha = __builtin_amdgcn_exp2f(m[i] - mb);
+        l[i] *= alpha;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) o[i][k] *= alpha;
+        m[i] = mb;
+      }
+#pragma unroll
+      for (int t = 0; t < TPL; ++t) {
+        p[i][t] = __builtin_amdgcn_exp2f(s[i][t] - m[i]);
+        l[i] += p[i][t];
+      }
+    }
+  };
+
+  // o[i] += sum_t p[i][t] * sv * (V code - zero point) over the lane's TPL tokens; the
+  // codes of tokens past the length are replaced by 0 in the last block (FP8: a byte of
+  // padding may decode to NaN, and 0 * NaN is NaN).
+  auto block_accumulate = [&](int blk, float vscale, float vzero, const uint4 (&vr_in)[TPL],
+                              const float (&p)[QW][TPL]) {
+    const int valid = blk == nb - 1 ? len - blk * kBlock : kBlock;
+    const _Float16 zh = static_cast<_Float16>(vzero * -5.9604644775390625e-08f);  // -zp 2^-24
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      uint4 vr = vr_in[t];
+      if constexpr (SCHEME == KVQ_FP8_E4M3)
+        if (t * GROUPS + group >= valid) vr = uint4{0u, 0u, 0u, 0u};
+      float cv[16];
+      chunk_values<SCHEME>(vr, half2_t{zh, zh}, cv);
+#pragma unroll
+      for (int i = 0; i < QW; ++i) {
+        const float pw = p[i][t] * vscale;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) o[i][c] = __builtin_fmaf(cv[c], pw, o[i][c]);
+      }
+    }
+  };
+
+  float p[QW][TPL];
+  stream_wave_blocks<TPL, STREAMS>(
+      sr.begin, sr.end, stream, lane, row,
+      [&](int blk) {
+        const int j = slot_of(blk);
+        if constexpr (kZero) return ScaleZeroParams{ks[j], kz[j], vs[j], vz[j], j};
+        else return ScaleZeroParams{ks[j], 0.0f, vs[j], 0.0f, j};
+      },
+      [&](bool is_v, int blk, const ScaleZeroParams& ps, int j, uint4 (&r)[TPL]) {
+        load_codes(is_v, blk, kPaged ? lane_int(ps.slot, j) : 0, r);
+      },
+      [&](int blk, const ScaleZeroParams& pb, const uint4 (&kr)[TPL]) {
+        block_weights(blk, pb.ks, pb.kz, kr, p);
+      },
+      [&](int blk, const ScaleZeroParams& pb, const uint4 (&vr)[TPL]) {
+        block_accumulate(blk, pb.vs, pb.vz, vr, p);
+      },
+      make_query);
+
+  // One query head of each wave at a time through LDS: the waves of a query set are
+  // merged per channel (then the row is written out, or its partial state stored).
+  const int n_row = sr.n;
+  const int64_t qrow0 = row * G;  // first output row of the cache row
+#pragma unroll
+  for (int i = 0; i < QW; ++i) {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) red_o[wave][lane][k] = o[i][k] * kUnit;
+    red_l[wave][lane] = l[i];
+    if (lane == 0) red_m[wave] = m[i];
+    __syncthreads();
+    if (threadIdx.x < QSETS * D) {
+      const int qs = threadIdx.x / D, d = threadIdx.x % D;
+      const int c = d / DPL, k = d % DPL;
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int sw = 0; sw < STREAMS; ++sw) M = fmaxf(M, red_m[sw * QSETS + qs]);
+      float od = 0.0f, L = 0.0f;
+#pragma unroll
+      for (int sw = 0; sw < STREAMS; ++sw) {
+        const int w = sw * QSETS + qs;
+        const float alpha = __builtin_amdgcn_exp2f(red_m[w] - M);
+        float so = 0.0f, sl = 0.0f;
+#pragma unroll
+        for (int g = 0; g < GROUPS; ++g) {
+          so += red_o[w][g * LPT + c][k];
+          sl += red_l[w][g * LPT];
+        }
+        od = __builtin_fmaf(alpha, so, od);
+        L = __builtin_fmaf(alpha, sl, L);
+      }
+      const int64_t qrow = qrow0 + qs * QW + i;
+      if (a.fused && n_row == 1) {
+        a.out[qrow * D + d] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(od / L));
+      } else {
+        float* po = a.ws_o + (qrow * a.n_split + split) * D;
+        float* ml = a.ws_ml + (qrow * a.n_split + split) * 2;
+        if (a.fused) {
+          store_shared(po + d, od);
+          if (d == 0) {
+            store_shared(ml, M);
+            store_shared(ml + 1, L);
+          }
+        } else {
+          po[d] = od;
+          if (d == 0) {
+            ml[0] = M;
+            ml[1] = L;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (!a.fused || n_row == 1) return;
+  __shared__ uint32_t ticket;
+  wait_own_stores();  // every wave's partial stores have reached memory
+  __syncthreads();
+  // system scope: the read-modify-write is performed at memory, past the per-XCD L2s
+  if (threadIdx.x == 0)
+    ticket = __hip_atomic_fetch_add(a.counters + row, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  if (ticket == static_cast<uint32_t>(n_row - 1)) {
+    // a wave's 64 threads share t / D (D is a multiple of the wave size): a uniform row
+    for (int t = threadIdx.x; t < G * D; t += kSplitWaves * kWave)
+      merge_row<D, true>(a, qrow0 + __builtin_amdgcn_readfirstlane(t / D), n_row, t % D);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(a.counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 // ---- combine kernel: grid (heads, batch), D threads ---------------------------------
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
@@ -1728,29 +2024,46 @@ hipError_t launch_decode_step(int scheme, int head_dim, int batch, const AttnArg
 }
 
 namespace {
-template <int D, int G>
+template <int SCHEME, int D, int G>
 hipError_t gqa_t(int batch, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.heads, batch, a.n_split);
   dim3 block(kSplitWaves * kWave);
-  if (a.block_table)
-    hipLaunchKernelGGL((attn_split_int4_gqa_kernel<D, G, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_split_int4_gqa_kernel<D, G, false>), grid, block, 0, s, a);
+  const bool paged = a.block_table != nullptr;
+  if constexpr (SCHEME == KVQ_INT4_SYM) {
+    if (paged)
+      hipLaunchKernelGGL((attn_split_int4_gqa_kernel<D, G, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_split_int4_gqa_kernel<D, G, false>), grid, block, 0, s, a);
+  } else {
+    if (paged)
+      hipLaunchKernelGGL((attn_split_gqa_kernel<SCHEME, D, G, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_split_gqa_kernel<SCHEME, D, G, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
-template <int D>
+template <int SCHEME, int D>
 hipError_t gqa_d(int group, int batch, const AttnArgs& a, hipStream_t s) {
   switch (group) {
-    case 2: return gqa_t<D, 2>(batch, a, s);
-    case 4: return gqa_t<D, 4>(batch, a, s);
-    default: return gqa_t<D, 8>(batch, a, s);
+    case 2: return gqa_t<SCHEME, D, 2>(batch, a, s);
+    case 4: return gqa_t<SCHEME, D, 4>(batch, a, s);
+    default: return gqa_t<SCHEME, D, 8>(batch, a, s);
   }
+}
+template <int SCHEME>
+hipError_t gqa_s(int head_dim, int group, int batch, const AttnArgs& a, hipStream_t s) {
+  return head_dim == 128 ? gqa_d<SCHEME, 128>(group, batch, a, s)
+                         : gqa_d<SCHEME, 64>(group, batch, a, s);
 }
 }  // namespace
 
-hipError_t launch_attn_gqa(int head_dim, int group, int batch, const AttnArgs& a,
+hipError_t launch_attn_gqa(int scheme, int head_dim, int group, int batch, const AttnArgs& a,
                            hipStream_t s) {
-  return head_dim == 128 ? gqa_d<128>(group, batch, a, s) : gqa_d<64>(group, batch, a, s);
+  switch (scheme) {
+    case KVQ_INT4_SYM: return gqa_s<KVQ_INT4_SYM>(head_dim, group, batch, a, s);
+    case KVQ_FP8_E4M3: return gqa_s<KVQ_FP8_E4M3>(head_dim, group, batch, a, s);
+    default: return gqa_s<KVQ_UINT8_ASYM>(head_dim, group, batch, a, s);
+  }
 }
 
 hipError_t launch_attn_combine(int head_dim, int batch, const AttnArgs& a, hipStream_t s) {

@@ -134,8 +134,9 @@ def test_grouped_query_rules():
     assert rc_gqa(cache(), group=3) == EINVAL
     assert rc_gqa(cache(), group=16) == EINVAL
     assert rc_gqa(cache(), group=0) == EINVAL
-    assert rc_gqa(cache(scheme=1), group=2) == ENOTSUP      # int4 only
-    assert rc_gqa(cache(scheme=2), group=2) == ENOTSUP
+    assert rc_gqa(cache(scheme=1), group=2, q=FAKE + 2) == EALIGN   # every scheme is taken
+    assert rc_gqa(cache(scheme=2), group=8, q=FAKE + 2) == EALIGN
+    assert rc_gqa(cache(scheme=1), group=5) == EINVAL
     assert rc_gqa(cache(), q=FAKE + 2) == EALIGN
     assert rc_gqa(cache(), out=0) == EINVAL
     c = cache(B=2, H=4, D=128, MB=3)
