@@ -164,6 +164,55 @@ __device__ __forceinline__ void merge_row(const AttnArgs& a, int64_t row, int n,
   a.out[row * D + d] = __builtin_bit_cast(uint16_t, r);
 }
 
+// The fused merge of R rows (row0 + k * step, k < R) of channel d by one thread, as
+// merge_row<D, true> each; with at most kMergeChunk splits the loads of all R rows are
+// issued before any is used (one memory round trip for the R rows instead of R).
+template <int D, int R>
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int64_t row0, int step, int n,
+                                           int d) {
+  if (n <= 0 || n > kMergeChunk) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) merge_row<D, true>(a, row0 + k * step, n, d);
+    return;
+  }
+  auto ld = [](__amdgpu_buffer_rsrc_t rs, int voff) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, kCachePolicyAgent));
+  };
+  float m[R][kMergeChunk], l[R][kMergeChunk], o[R][kMergeChunk];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int64_t row = row0 + k * step;
+    const __amdgpu_buffer_rsrc_t mlr = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_ml + row * a.n_split * 2, 0, n * 2 * 4, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t por = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_o + row * a.n_split * D, 0, n * D * 4, kBufferRsrcWord3);
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      m[k][j] = ld(mlr, j * 8);
+      l[k][j] = ld(mlr, j * 8 + 4);
+      o[k][j] = ld(por, (j * D + d) * 4);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every request out before the first use
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    float M = -__builtin_inff(), L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j)
+      if (j < n) M = fmaxf(M, m[k][j]);
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      if (j < n) {
+        const float w = __builtin_amdgcn_exp2f(m[k][j] - M);
+        L = __builtin_fmaf(w, l[k][j], L);
+        acc = __builtin_fmaf(w, o[k][j], acc);
+      }
+    }
+    a.out[(row0 + k * step) * D + d] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc / L));
+  }
+}
+
 // ---- the split of a row ---------------------------------------------------------------
 // Blocks [begin, end) of a row of nb blocks that split `split` streams, and the number of
 // splits n of the row (the merge's count). A caller's plan (a.bps > 0) cuts every row
@@ -1664,9 +1713,14 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
                                     __HIP_MEMORY_SCOPE_SYSTEM);
   __syncthreads();
   if (ticket == static_cast<uint32_t>(n_row - 1)) {
-    // a wave's 64 threads share t / D (D is a multiple of the wave size): a uniform row
-    for (int t = threadIdx.x; t < G * D; t += kThreadsWg)
-      merge_row<D, true>(a, qrow0 + __builtin_amdgcn_readfirstlane(t / D), n_row, t % D);
+    // thread t merges rows t / D + k * (threads / D) of channel t % D; a wave's 64 threads
+    // share t / D (D is a multiple of the wave size): uniform rows
+    constexpr int kRowsPerPass = kThreadsWg / D;
+    constexpr int R = (G * D + kThreadsWg - 1) / kThreadsWg;
+    const int t = threadIdx.x;
+    if (t < G * D)
+      merge_rows<D, R>(a, qrow0 + __builtin_amdgcn_readfirstlane(t / D), kRowsPerPass, n_row,
+                       t % D);
     if (threadIdx.x == 0)
       __hip_atomic_store(a.counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
@@ -1957,9 +2011,13 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_gqa_kernel(Att
                                     __HIP_MEMORY_SCOPE_SYSTEM);
   __syncthreads();
   if (ticket == static_cast<uint32_t>(n_row - 1)) {
-    // a wave's 64 threads share t / D (D is a multiple of the wave size): a uniform row
-    for (int t = threadIdx.x; t < G * D; t += kSplitWaves * kWave)
-      merge_row<D, true>(a, qrow0 + __builtin_amdgcn_readfirstlane(t / D), n_row, t % D);
+    // as in the int4 grouped-query kernel: thread t merges rows t / D + k * (threads / D)
+    constexpr int kThreadsWg = kSplitWaves * kWave;
+    constexpr int R = (G * D + kThreadsWg - 1) / kThreadsWg;
+    const int t = threadIdx.x;
+    if (t < G * D)
+      merge_rows<D, R>(a, qrow0 + __builtin_amdgcn_readfirstlane(t / D), kThreadsWg / D, n_row,
+                       t % D);
     if (threadIdx.x == 0)
       __hip_atomic_store(a.counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
