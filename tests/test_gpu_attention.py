@@ -189,6 +189,46 @@ def test_ragged_rows(scheme, D, bps):
     assert np.array_equal(out.cpu().numpy(), o)
 
 
+@pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
+def test_automatic_plan_with_more_rows_than_cus(scheme):
+    """The automatic plan over a batch of more rows (320) than compute units, with random
+    lengths (empty rows included), so the device cuts the long rows and leaves the
+    others whole. Every row within tolerance of the oracle; split + combine bitwise equal
+    to the fused call; counters back at zero; repeated calls identical."""
+    import decode_attention_block_amd as kvq
+    import torch
+    B, H, S, D = 40, 8, 700, 64
+    lens = np.random.default_rng(77).integers(0, S + 1, B).astype(np.int32)
+    lens[[3, 17]] = 0
+    lens[5] = S
+    k, v, q, _ = _small_case(scheme, D, seed=31, B=B, H=H, S=S, lens=lens)
+    c = gpu_quantize(scheme, k, v, lens, 11)
+    L = int(lens.max())
+    say("automatic plan, 320 rows", scheme, lens.tolist())
+    sm = 0.125
+    qt = to_gpu(q)
+    ws = kvq.make_workspace(c, L)
+    fused = torch.full_like(qt, 7.0)
+    kvq.decode_attn_qkv(c, qt, sm, fused, ws, L)
+    torch.cuda.synchronize()
+    o = fused.cpu().numpy()
+    ref = oracle.attention(c.host_arrays(), q, lens, sm)
+    norm_err, _ = attn_errors(o, ref)
+    print(f"automatic plan, 320 rows, scheme {scheme}: normwise {norm_err:.3e}")
+    assert norm_err <= ATTN_TOL
+    assert not o[3].any() and not o[17].any()
+    assert not ws[:4 * B * H].any()
+    again = torch.empty_like(qt)
+    kvq.decode_attn_qkv(c, qt, sm, again, ws, L)
+    torch.cuda.synchronize()
+    assert np.array_equal(again.cpu().numpy(), o)
+    out = torch.full_like(qt, 7.0)
+    kvq.decode_attn_split(c, qt, sm, ws, L)
+    kvq.decode_attn_combine(c, out, ws, L)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), o)
+
+
 @pytest.mark.parametrize("lens", [(5, 70), (0, 0, 0), (0, 130, 0)])
 def test_lengths_below_the_launch_bound(lens):
     """max_len well above every length (the launch sizes for capacity, the rows are
