@@ -38,8 +38,9 @@ prefill quantization and one decode step (append + attention), on one thread and
 the sample's heads split over every host thread.
 
 Prints one JSON line. --profile-loop runs only the timed loop of --workload (for
-rocprofv3), --copy-probe times a plain device copy of known size (the calibration
-kernel for the FETCH_SIZE / WRITE_SIZE counters).
+rocprofv3), --prefill-loop only its prefill quantization, --copy-probe times a plain
+device copy of known size (the calibration kernel for the FETCH_SIZE / WRITE_SIZE
+counters).
 """
 import argparse
 import json
@@ -67,7 +68,8 @@ DTYPES = {0: "int4 codes x fp16 query -> fp32 accumulate (matrix cores)",
           2: "fp8 e4m3 codes x fp16 query -> fp32 accumulate"}
 OTHERS = ("tiny_b1_h2_d64_ctx256_int4", "llama7b_b8_h32_d128_ctx8k_uint8",
           "llama7b_b8_h32_d128_ctx8k_fp8", "long_b16_h32_d128_ctx32k_append64_int4",
-          "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4", "llama70b_gqa8_b8_h8_d128_ctx8k_int4")
+          "llama7b_32layer_b8_h32_d128_ragged1k-8k_t3_int4", "llama70b_gqa8_b8_h8_d128_ctx8k_int4",
+          "llama70b_gqa8_b8_h8_d128_ctx8k_fp8")
 
 
 def parse():
@@ -91,6 +93,8 @@ def parse():
     p.add_argument("--profile-loop", action="store_true",
                    help="only the timed loop of --workload (for rocprofv3); no oracle, "
                         "no other workloads")
+    p.add_argument("--prefill-loop", action="store_true",
+                   help="only the prefill quantization of --workload, repeated (for rocprofv3)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only a 1 GiB device-to-device copy (counter calibration)")
     return p.parse_args()
@@ -236,6 +240,14 @@ class Stepper:
             torch.cuda.synchronize()
             self.graphs[n] = g
         return self.graphs[n]
+
+    def prepare(self, *step_counts):
+        """Captures every segment graph that runs of these step counts will replay, so
+        that no capture (host work with the GPU idle) falls between the warm-up and the
+        timed steps."""
+        for n_steps in step_counts:
+            for n in self._segments(n_steps):
+                self._graph(n)
 
     def _segments(self, n_steps):
         done = 0
@@ -437,6 +449,33 @@ def quantized_copies(kvq, torch, w, k, v, lens, max_blocks, n_copies, paged=Fals
     return caches, ms
 
 
+def prefill_loop(kvq, torch, w, steps, warmup):
+    """Only the prefill quantization of --workload (kv_quantize_blocks of its whole
+    context into one cache), warmup + steps times, for rocprofv3; HIP events around the
+    timed calls."""
+    wl = wl_mod()
+    lens = wl.lengths(w)
+    n = int(lens.max())
+    k, v = prefill_inputs(torch, w, 0, n, w.decode_steps > 0 or w.layers > 1)
+    c = kvq.KVCache(w.scheme, w.batch, w.heads, w.head_dim, w.max_blocks)
+    c.seq_lens.copy_(torch.from_numpy(np.asarray(lens, np.int32)))
+    for _ in range(warmup):
+        kvq.kv_quantize_blocks(c, k, v, n)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        kvq.kv_quantize_blocks(c, k, v, n)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": w.name, "call": "kv_quantize_blocks (whole prefill)",
+            "kernel": f"quantize_blocks_kernel<{w.scheme}, {w.head_dim}>", "steps": steps,
+            "warmup": warmup, "ms_per_call": ms,
+            "gbs": prefill_bytes(w, lens) / (ms / 1e3) / 1e9,
+            "bytes_per_call": prefill_bytes(w, lens)}
+
+
 def kernel_name(w, fused, paged=False):
     """The timed kernel as rocprofv3 lists it (template arguments: head_dim, whether the
     workgroup also appends the row's token, whether the cache is paged)."""
@@ -450,7 +489,11 @@ def timing_fields(stepper, steps, warmup, eager, launches_per_step, step_bytes_f
                   per_launch_bytes):
     """Warm-up, the timed steps (graph replays, or eager), the eager comparison and the
     per-step percentiles; step_bytes_fn(total steps) = algorithmic bytes of the timed
-    steps."""
+    steps. The timed steps follow the warm-up directly (their graphs are captured before
+    it, so no capture leaves the GPU idle between them); the comparison rounds come after
+    them, and their graph figure is reported as the later rounds' rate."""
+    if not eager:
+        stepper.prepare(warmup, steps)
     stepper.run(warmup, timed=False, graph=not eager)
     wall0 = time.perf_counter()
     total_ms = stepper.run(steps, timed=True, graph=not eager)
@@ -478,6 +521,8 @@ def timing_fields(stepper, steps, warmup, eager, launches_per_step, step_bytes_f
                            "eager_ms_per_step": eager_ms / steps,
                            "rounds": COMPARE_ROUNDS,
                            "note": "alternating rounds after the timed steps, medians"},
+        "later_ms_per_step": float(np.median(g_ms)) / steps,
+        "later_gbs": bytes_ / (float(np.median(g_ms)) / 1e3) / 1e9,
         "step_us": {k: v * 1e3 for k, v in pct(samples).items()},
         "step_us_sampling": (f"HIP event pairs around each of {len(samples)} steps queued "
                              "behind device copies (includes the events' own time)"),
@@ -640,7 +685,9 @@ def run_gqa(kvq, torch, w, steps, warmup, bps, paged=False, eager=False, with_cp
     res.update({
         "workload": w.name,
         "step": f"decode_attn_gqa ({G} query heads per cached head)",
-        "kernel": f"attn_split_int4_gqa_kernel<{D}, {G}, {'true' if paged else 'false'}>",
+        "kernel": (f"attn_split_int4_gqa_kernel<{D}, {G}, {'true' if paged else 'false'}>"
+                   if w.scheme == 0 else
+                   f"attn_split_gqa_kernel<{w.scheme}, {D}, {G}, {'true' if paged else 'false'}>"),
         "layout": "paged (block table over a shuffled page pool)" if paged else "dense",
         "tokens_per_s": B * steps / (res["ms_per_step"] * steps / 1e3),
         "context": [L, L], "cache_copies_rotated": copies,
@@ -753,6 +800,9 @@ def main():
 
     wl = wl_mod()
     w = wl.BY_NAME[args.workload]
+    if args.prefill_loop:
+        print(json.dumps(prefill_loop(kvq, torch, w, args.steps, args.warmup)), flush=True)
+        return
     with_cpu = not (args.no_cpu or args.profile_loop)
     print(f"[bench] {w.name}: {args.steps} steps after {args.warmup} warm-up",
           file=sys.stderr, flush=True)
@@ -806,6 +856,15 @@ def main():
         "eager": {"ms_per_step": res["eager_ms_per_step"], "gbs": res["eager_gbs"],
                   "note": "the same steps queued one by one from the host"},
         "graph_vs_eager": res["graph_vs_eager"],
+        "later_rounds": {"ms_per_step": res["later_ms_per_step"], "gbs": res["later_gbs"],
+                         "pct_of_hbm_peak": 100.0 * res["later_gbs"] / HBM_PEAK_GBS,
+                         "note": ("the same steps replayed in the comparison rounds right "
+                                  "after the timed ones (median): the timed steps come first "
+                                  "after setup and the warm-up, in the GPU's first "
+                                  "milliseconds of continuous work; these rounds fall in the "
+                                  "next few, where it runs slower, before it settles (the "
+                                  "steady rate is the one bench.py --profile-loop times after "
+                                  "300 warm-up steps)")},
         "prefill_quantize": {"ms": res.get("prefill_quantize_ms"),
                              "gbs": res.get("prefill_quantize_gbs")},
         "host_wall_s": res["host_wall_s"],

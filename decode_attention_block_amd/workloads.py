@@ -88,6 +88,10 @@ WORKLOADS = [
     # the 8K shape with the FP8 E4M3 cache (page "DeepSeek R1性能优化有哪些技巧" §一)
     Workload(6, "llama7b_b8_h32_d128_ctx8k_fp8", 8, 32, 128, 8192, FP8_E4M3,
              "normal_outliers", "normal_outliers"),
+    # grouped-query decode over the FP8 cache (the pages pair the FP8 KV cache with
+    # shared-head decode: page "DeepSeek R1性能优化有哪些技巧" §一, §二)
+    Workload(7, "llama70b_gqa8_b8_h8_d128_ctx8k_fp8", 8, 8, 128, 8192, FP8_E4M3,
+             "normal_outliers", "normal_outliers", group=8),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
