@@ -687,7 +687,7 @@ def run_gqa(kvq, torch, w, steps, warmup, bps, paged=False, eager=False, with_cp
         "step": f"decode_attn_gqa ({G} query heads per cached head)",
         "kernel": (f"attn_split_int4_gqa_kernel<{D}, {G}, {'true' if paged else 'false'}>"
                    if w.scheme == 0 else
-                   f"attn_split_gqa_kernel<{w.scheme}, {D}, {G}, {'true' if paged else 'false'}>"),
+                   f"attn_split_gqa8_kernel<{w.scheme}, {D}, {G}, {'true' if paged else 'false'}>"),
         "layout": "paged (block table over a shuffled page pool)" if paged else "dense",
         "tokens_per_s": B * steps / (res["ms_per_step"] * steps / 1e3),
         "context": [L, L], "cache_copies_rotated": copies,

@@ -513,10 +513,7 @@ __device__ __forceinline__ float lane_value(float v, int i) {
 // `start()` runs once, after the wave's first code load has been issued and before
 // anything waits for it: work that waits for the query's own load goes there, so the
 // stream's first requests are not held behind it.
-// STREAMS waves share the split this way (`wave` < STREAMS); waves given the same `wave`
-// stream the same blocks in the same order.
-template <int LOADS, int STREAMS = kSplitWaves, class LoadParams, class Load, class OnK,
-          class OnV, class Start>
+template <int LOADS, class LoadParams, class Load, class OnK, class OnV, class Start>
 __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, int wave, int lane,
                                                    int64_t row, LoadParams load_params, Load load,
                                                    OnK on_k, OnV on_v, Start start) {
@@ -526,9 +523,9 @@ __device__ __forceinline__ void stream_wave_blocks(int blk_begin, int blk_end, i
     return;
   }
   const int rot = static_cast<int>((static_cast<uint32_t>(row) * 2654435761u) >> 8) % n;
-  const int n_wave = wave < n ? (n - wave + STREAMS - 1) / STREAMS : 0;
+  const int n_wave = wave < n ? (n - wave + kSplitWaves - 1) / kSplitWaves : 0;
   auto blk_of = [&](int i) {
-    const int b = wave + STREAMS * i + rot;
+    const int b = wave + kSplitWaves * i + rot;
     return blk_begin + (b >= n ? b - n : b);
   };
   uint4 kbuf[LOADS], vbuf[LOADS];
@@ -1726,51 +1723,65 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
   }
 }
 
-// ---- grouped-query attention over the 8-bit caches (uint8, FP8) ---------------------
-// The one-query VALU kernel's loads and arithmetic, with several query heads per wave:
-// each 16-byte chunk of codes is decoded once (FP8: to binary32 values with
-// v_cvt_pk_f32_fp8; uint8: to fp16 code pairs less the zero point) and multiplied into
-// every query head the wave holds (up to 4; registers bound it), each with its own
-// online softmax. With 8 query heads per cached head two waves read each block, one per
-// half of the group (the second read is served by the L2: HBM still sees the cache once),
-// so 2 of the 4 waves stream distinct blocks; with 2 or 4, every wave holds all of them
-// and the 4 waves stream distinct blocks. Splits, partial states and the last-arriver
-// merge are those of the int4 grouped-query kernel (one arrival counter per cache row,
-// partial states per query row).
+// ---- grouped-query attention over the 8-bit caches on the matrix cores ---------------
+// The schedule of the int4 grouped-query kernel (queries in rows 0..G-1 of the A tile and
+// again in rows G..2G-1; P.V with the weights' fp16 high parts in rows g < G and low
+// parts in rows G + g of one A operand), over caches in natural token order:
+// - QK^T: B operand lane l holds 8 channels of token l % 16 of a 16-token tile. Lane
+//   (n, g) = (l % 16, l / 16) loads the D/4 bytes g * D/4 .. of token n (16-byte loads,
+//   a tile's 16 tokens x D bytes shared by the 64 lanes); K step s uses its bytes 8s ..
+//   8s + 7. The contraction runs over the channels in that order, so the query operand
+//   takes the same order (lane (r, g), step s: channels g * D/4 + 8s .. + 7 of query r).
+// - P.V: the B operand needs 8 tokens of one channel per lane, across the natural rows.
+//   Each wave stages its block of V codes in LDS (rows of D + 16 bytes: the 16 rows a
+//   transposing read gathers then fall in distinct banks) and reads it back with
+//   ds_read_b64_tr_b8, which gives lane l of each 16-lane group byte l % 8 of the 8-byte
+//   pieces pointed to by lanes 2j + l / 8 of the group (j = 0..7, measured on gfx950):
+//   with lane r of group g pointing at token 32 ks + 8 g + r / 2, channels 16 n + 8 (r %
+//   2) .., lane (n', g) receives tokens 32 ks + 8 g .. + 7 of channel 16 n + n', which is
+//   the B operand of K step ks and N tile n.
+// - Operands: FP8 codes convert exactly to fp16 (v_cvt_scalef32_pk_f16_fp8 with scale 1,
+//   two codes per instruction, every E4M3 value a normal fp16); uint8 codes become
+//   1024 + c by a byte permute with the bits of 1024, and one packed fp16 add of
+//   -(1024 + z) leaves c - z exactly (|c - z| <= 255). The scales apply to the fp32
+//   results. Tokens past the length in the last block are masked in the scores, and for
+//   FP8 their V bytes are replaced by 0 (a padding byte may be NaN, and 0 * NaN is NaN).
 template <int SCHEME>
-__device__ __forceinline__ void chunk_values(const uint4& raw, half2_t off, float (&cv)[16]) {
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (SCHEME == KVQ_FP8_E4M3) {  // exact, two codes per instruction
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[j]), false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[j]), true);
-      cv[4 * j + 0] = lo[0];
-      cv[4 * j + 1] = lo[1];
-      cv[4 * j + 2] = hi[0];
-      cv[4 * j + 3] = hi[1];
-    } else {  // units of 2^-24, the zero point taken out of each fp16 pair (exact)
-      const half2_t e = as_h2(w[j] & 0x00FF00FFu) + off;         // channels 0, 2
-      const half2_t f = as_h2((w[j] >> 8) & 0x00FF00FFu) + off;  // channels 1, 3
-      cv[4 * j + 0] = static_cast<float>(e.x);
-      cv[4 * j + 1] = static_cast<float>(f.x);
-      cv[4 * j + 2] = static_cast<float>(e.y);
-      cv[4 * j + 3] = static_cast<float>(f.y);
-    }
+__device__ __forceinline__ half8_t byte_operand(uint32_t w0, uint32_t w1, half2_t neg_off) {
+  half2_t h[4];
+  if constexpr (SCHEME == KVQ_FP8_E4M3) {
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w0), 1.0f, false);
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w0), 1.0f, true);
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w1), 1.0f, false);
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w1), 1.0f, true);
+  } else {
+    constexpr uint32_t kBits1024 = 0x64646464u;  // high byte of fp16 1024 in every byte
+    h[0] = as_h2(__builtin_amdgcn_perm(kBits1024, w0, 0x04010400u)) + neg_off;  // bytes 0, 1
+    h[1] = as_h2(__builtin_amdgcn_perm(kBits1024, w0, 0x04030402u)) + neg_off;  // bytes 2, 3
+    h[2] = as_h2(__builtin_amdgcn_perm(kBits1024, w1, 0x04010400u)) + neg_off;
+    h[3] = as_h2(__builtin_amdgcn_perm(kBits1024, w1, 0x04030402u)) + neg_off;
   }
+  return half8_t{h[0].x, h[0].y, h[1].x, h[1].y, h[2].x, h[2].y, h[3].x, h[3].y};
 }
 
+typedef int int2_t __attribute__((ext_vector_type(2)));
+
 template <int SCHEME, int D, int G, bool kPaged>
-__global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_gqa_kernel(AttnArgs a) {
-  using Geo = AGeo<SCHEME, D>;
-  constexpr int TPL = Geo::kTPL, DPL = Geo::kDPL, LPT = Geo::kLPT, GROUPS = Geo::kGroups;
-  constexpr int QW = G < 4 ? G : 4;             // query heads per wave
-  constexpr int QSETS = G / QW;                 // waves that read the same blocks
-  constexpr int STREAMS = kSplitWaves / QSETS;  // waves streaming distinct blocks
-  constexpr float kUnit = SCHEME == KVQ_FP8_E4M3 ? 1.0f : 16777216.0f;  // o's unit
-  __shared__ float red_o[kSplitWaves][kWave][DPL + 1];
-  __shared__ float red_l[kSplitWaves][kWave];
-  __shared__ float red_m[kSplitWaves];
+__global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_gqa8_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;             // 32-channel K steps of QK^T
+  constexpr int NTV = D / 16;            // 16-channel N tiles of P.V
+  constexpr int LPT = D / 64;            // 16-byte loads per lane per 16-token tile
+  constexpr int LOADS = 4 * LPT;         // 16-byte loads per lane per region
+  constexpr int kRegionBytes = kBlock * D;
+  constexpr int kRow = D + 16;           // LDS row stride of a staged V block
+  constexpr int kTile = kBlock * kRow;   // one wave's staged V block
+  __shared__ __align__(16) _Float16 pimg[kSplitWaves][2][4][16][8];
+  // the waves' staged V blocks while streaming; afterwards the waves' partial outputs
+  __shared__ __align__(16) uint8_t vstage[kSplitWaves * kTile];
+  __shared__ float red_l[kSplitWaves][G];
+  __shared__ float red_m[kSplitWaves][G];
+  static_assert(sizeof(float) * kSplitWaves * 2 * G * D <= sizeof(vstage), "red_o in vstage");
+  float(*red_o)[2 * G][D] = reinterpret_cast<float(*)[2 * G][D]>(vstage);
 
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -1788,58 +1799,74 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_gqa_kernel(Att
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
-  const int chunk = lane % LPT;
-  const int group = lane / LPT;
-  const int qset = wave % QSETS;   // the wave's query heads: qset * QW .. + QW - 1
-  const int stream = wave / QSETS;
+  const int r16 = lane % 16;  // A row / output column / B column of this lane
+  const int grp = lane / 16;  // K group of this lane's fragments; its output rows / 4
 
-  Query<SCHEME, D> q[QW];
+  {  // this wave's P image: rows 2G..15 stay zero
+    uint4* img = reinterpret_cast<uint4*>(&pimg[wave][0][0][0][0]);
 #pragma unroll
-  for (int i = 0; i < QW; ++i) q[i].request(a.q + (row * G + qset * QW + i) * D + chunk * DPL);
-  float qsum[QW];
+    for (int k = 0; k < 2; ++k) img[lane + k * kWave] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // Query operand: rows g and G + g (g < G) hold query g, K step s the channels
+  // grp * D/4 + 8s .. + 7; built by make_query once the first code requests are out.
+  uint4 qraw[KS];
+  {
+    const uint16_t* qrow = a.q + (row * G + (r16 < 2 * G ? r16 % G : 0)) * D + grp * (D / 4);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const uint4*>(qrow + 8 * ks);
+  }
+  half8_t aq[KS];
   auto make_query = [&]() {
+    const bool keep = r16 < 2 * G;
 #pragma unroll
-    for (int i = 0; i < QW; ++i) {
-      q[i].ready();
-      qsum[i] = group_sum<LPT>(q[i].sum);
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 qr = query_ready(qraw[ks]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) aq[ks][j] = keep ? half_of(qr, j) : static_cast<_Float16>(0.0f);
     }
   };
 
-  constexpr int kRegionBytes = kBlock * Geo::kRowBytes;
   const int row_bytes = kPaged ? kRegionBytes : a.max_blocks * kRegionBytes;
   const int64_t row_base = kPaged ? 0 : row * row_bytes;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.k_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.v_codes + row_base), 0, row_bytes, kBufferRsrcWord3);
-  const int lane_off = lane * 16;
+  // lane (n, g): token n of each tile, bytes g * D/4 ..
+  const int lane_off = r16 * D + grp * (D / 4);
   const int64_t sbase = kPaged ? 0 : row * a.max_blocks;
-  const float* ks = a.k_scale + sbase;
-  const float* vs = a.v_scale + sbase;
+  const float* ks_ptr = a.k_scale + sbase;
+  const float* vs_ptr = a.v_scale + sbase;
   constexpr bool kZero = SCHEME == KVQ_UINT8_ASYM;
-  const float* kz = kZero ? a.k_zero + sbase : nullptr;
-  const float* vz = kZero ? a.v_zero + sbase : nullptr;
+  const float* kz_ptr = kZero ? a.k_zero + sbase : nullptr;
+  const float* vz_ptr = kZero ? a.v_zero + sbase : nullptr;
 
-  float o[QW][DPL];
-  float m[QW], l[QW];
+  float o[NTV][4];
 #pragma unroll
-  for (int i = 0; i < QW; ++i) {
+  for (int n = 0; n < NTV; ++n)
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o[i][k] = 0.0f;
-    m[i] = -__builtin_inff();  // running max of query i's base-2 scores (wave-uniform)
+    for (int i = 0; i < 4; ++i) o[n][i] = 0.0f;
+  float m[4], l[4];  // per output row 4 * grp + i: running max (base 2), lane's weight sum
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -__builtin_inff();
     l[i] = 0.0f;
   }
 
-  auto load_codes = [&](bool is_v, int blk, int slot, uint4 (&r)[TPL]) {
+  // load i = tile * LPT + half: token 16 tile + n, bytes g * D/4 + 16 half ..
+  auto load_codes = [&](bool is_v, int blk, int slot, uint4 (&r)[LOADS]) {
     if constexpr (kPaged) {
       const __amdgpu_buffer_rsrc_t rs =
           region_rsrc(is_v ? a.v_codes : a.k_codes, slot, kRegionBytes);
 #pragma unroll
-      for (int i = 0; i < TPL; ++i) r[i] = load_stream(rs, lane_off, i * kWave * 16);
+      for (int i = 0; i < LOADS; ++i)
+        r[i] = load_stream(rs, lane_off, (i / LPT) * 16 * D + (i % LPT) * 16);
     } else {
 #pragma unroll
-      for (int i = 0; i < TPL; ++i)
-        r[i] = load_stream(is_v ? vrsrc : krsrc, lane_off, blk * kRegionBytes + i * kWave * 16);
+      for (int i = 0; i < LOADS; ++i)
+        r[i] = load_stream(is_v ? vrsrc : krsrc, lane_off,
+                           blk * kRegionBytes + (i / LPT) * 16 * D + (i % LPT) * 16);
     }
   };
   auto slot_of = [&](int blk) {
@@ -1847,161 +1874,217 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_gqa_kernel(Att
                                                 a.max_blocks, b, h, blk))
                   : blk;
   };
+  auto neg_offset = [](float zero) {  // -(1024 + z) in both halves (uint8)
+    const _Float16 v = static_cast<_Float16>(-(1024.0f + zero));
+    return half2_t{v, v};
+  };
 
-  // Scores of the lane's TPL tokens for every query head, then each head's online
-  // softmax update; p[i][t] = the weights relative to the running max m[i].
-  auto block_weights = [&](int blk, float kscale, float kzero, const uint4 (&kr)[TPL],
-                           float (&p)[QW][TPL]) {
+  // Scores of the block's 64 tokens for the lane's rows, the per-row online-softmax
+  // update, and the weights p[nt][i] (token 16 nt + r16, row 4 grp + i).
+  auto block_weights = [&](int blk, float kscale, float kzero, const uint4 (&kr)[LOADS],
+                           float (&p)[4][4]) {
     const float sk = kscale * a.qk_scale;
-    float s[QW][TPL];
+    const half2_t off = neg_offset(kzero);
+    float4_t acc[4];
 #pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-      if constexpr (SCHEME == KVQ_FP8_E4M3) {
-        float cv[16];
-        chunk_values<SCHEME>(kr[t], half2_t{0, 0}, cv);
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < QW; ++i) {
-          float a0 = 0.0f, a1 = 0.0f;
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int c = 0; c < 16; c += 2) {
-            a0 = __builtin_fmaf(cv[c], static_cast<float>(q[i].at(c)), a0);
-            a1 = __builtin_fmaf(cv[c + 1], static_cast<float>(q[i].at(c + 1)), a1);
-          }
-          s[i][t] = group_sum<LPT>(a0 + a1) * sk;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < QW; ++i)
-          s[i][t] = (group_sum<LPT>(chunk_dot<SCHEME, D>(kr[t], q[i])) - kzero * qsum[i]) * sk;
+      for (int nt = 0; nt < 4; ++nt) {
+        // bytes 8 ks .. 8 ks + 7 of the lane's slice of token 16 nt + r16
+        const int f = nt * 4 * LPT + 2 * ks;  // dword index over the loads
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            aq[ks], byte_operand<SCHEME>(dword_of(kr, f), dword_of(kr, f + 1), off), acc[nt],
+            0, 0, 0);
       }
-    }
+    float s[4][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[nt][i] = acc[nt][i] * sk;
     if (blk == nb - 1) {  // tokens past the length in the last block weigh nothing
       const int valid = len - blk * kBlock;
 #pragma unroll
-      for (int t = 0; t < TPL; ++t)
-        if (t * GROUPS + group >= valid) {
+      for (int nt = 0; nt < 4; ++nt)
+        if (16 * nt + r16 >= valid) {
 #pragma unroll
-          for (int i = 0; i < QW; ++i) s[i][t] = -__builtin_inff();
+          for (int i = 0; i < 4; ++i) s[nt][i] = -__builtin_inff();
         }
     }
+    float mb[4];
+    bool raise = false;
 #pragma unroll
-    for (int i = 0; i < QW; ++i) {
-      float mb = s[i][0];
+    for (int i = 0; i < 4; ++i) {
+      mb[i] = row16_max(fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i])));
+      raise |= mb[i] > m[i];
+    }
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // some row's max rose
 #pragma unroll
-      for (int t = 1; t < TPL; ++t) mb = fmaxf(mb, s[i][t]);
-      mb = wave_max(mb);
-      if (mb > m[i]) {  // wave-uniform
-        const float alpha = __builtin_amdgcn_exp2f(m[i] - mb);
+      for (int i = 0; i < 4; ++i) {
+        const float mn = fmaxf(m[i], mb[i]);
+        const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);
         l[i] *= alpha;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) o[i][k] *= alpha;
-        m[i] = mb;
-      }
-#pragma unroll
-      for (int t = 0; t < TPL; ++t) {
-        p[i][t] = __builtin_amdgcn_exp2f(s[i][t] - m[i]);
-        l[i] += p[i][t];
+        for (int n = 0; n < NTV; ++n) o[n][i] *= alpha;
+        m[i] = mn;
       }
     }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[nt][i] = __builtin_amdgcn_exp2f(s[nt][i] - m[i]);
+        l[i] += p[nt][i];
+      }
   };
 
-  // o[i] += sum_t p[i][t] * sv * (V code - zero point) over the lane's TPL tokens; the
-  // codes of tokens past the length are replaced by 0 in the last block (FP8: a byte of
-  // padding may decode to NaN, and 0 * NaN is NaN).
-  auto block_accumulate = [&](int blk, float vscale, float vzero, const uint4 (&vr_in)[TPL],
-                              const float (&p)[QW][TPL]) {
+  // o[n][i] += sv * sum_t w_t * v(t, 16 n + r16) for row r = 4 grp + i, where w is the
+  // high part of the weights of query r (r < G) or the low part of those of query r - G.
+  uint8_t* vt = vstage + wave * kTile;
+  // the transposing read: lane r16 of group grp points at token 8 grp + r16 / 2 of the K
+  // step, channels 8 (r16 % 2) .. of the N tile
+  const int tr_off = (8 * grp + r16 / 2) * kRow + 8 * (r16 % 2);
+  auto block_accumulate = [&](int blk, float vscale, float vzero, const uint4 (&vr)[LOADS],
+                              const float (&p)[4][4]) {
+    const float sv = vscale * (1.0f / 16384.0f);
+    const half2_t off = neg_offset(vzero);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      *reinterpret_cast<uint4*>(vt + (16 * (i / LPT) + r16) * kRow + grp * (D / 4) +
+                                16 * (i % LPT)) = vr[i];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int kstep = nt >> 1, kgrp = (nt & 1) * 2 + (r16 >> 3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * grp + i;
+        if (r < 2 * G) {
+          const float x = p[nt][i] * 16384.0f;
+          const _Float16 hi = static_cast<_Float16>(x);
+          pimg[wave][kstep][kgrp][r][r16 & 7] =
+              r < G ? hi : static_cast<_Float16>(x - static_cast<float>(hi));
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const half8_t ap0 = *reinterpret_cast<const half8_t*>(&pimg[wave][0][grp][r16][0]);
+    const half8_t ap1 = *reinterpret_cast<const half8_t*>(&pimg[wave][1][grp][r16][0]);
+    // FP8: tokens past the length get code 0 (their bytes j of the K step's read are
+    // tokens 32 ks + 8 grp + j)
     const int valid = blk == nb - 1 ? len - blk * kBlock : kBlock;
-    const _Float16 zh = static_cast<_Float16>(vzero * -5.9604644775390625e-08f);  // -zp 2^-24
 #pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-      uint4 vr = vr_in[t];
-      if constexpr (SCHEME == KVQ_FP8_E4M3)
-        if (t * GROUPS + group >= valid) vr = uint4{0u, 0u, 0u, 0u};
-      float cv[16];
-      chunk_values<SCHEME>(vr, half2_t{zh, zh}, cv);
+    for (int n = 0; n < NTV; ++n) {
+      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < QW; ++i) {
-        const float pw = p[i][t] * vscale;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) o[i][c] = __builtin_fmaf(cv[c], pw, o[i][c]);
+      for (int ks = 0; ks < 2; ++ks) {
+        int2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) int2_t*)(vt + 32 * ks * kRow + 16 * n + tr_off));
+        if constexpr (SCHEME == KVQ_FP8_E4M3) {
+          if (valid < kBlock) {  // uniform: the row's last block only
+            const int t0 = 32 * ks + 8 * grp;
+            uint64_t v = (static_cast<uint64_t>(static_cast<uint32_t>(w.y)) << 32) |
+                         static_cast<uint32_t>(w.x);
+            const int keep = min(max(valid - t0, 0), 8);  // leading tokens kept
+            v = keep >= 8 ? v : (v & ((uint64_t{1} << (8 * keep)) - 1));
+            w.x = static_cast<int>(static_cast<uint32_t>(v));
+            w.y = static_cast<int>(static_cast<uint32_t>(v >> 32));
+          }
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            ks == 0 ? ap0 : ap1,
+            byte_operand<SCHEME>(static_cast<uint32_t>(w.x), static_cast<uint32_t>(w.y), off),
+            acc, 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[n][i] = __builtin_fmaf(sv, acc[i], o[n][i]);
     }
+    __builtin_amdgcn_wave_barrier();
   };
 
-  float p[QW][TPL];
-  stream_wave_blocks<TPL, STREAMS>(
-      sr.begin, sr.end, stream, lane, row,
+  float p[4][4];
+  stream_wave_blocks<LOADS>(
+      sr.begin, sr.end, wave, lane, row,
       [&](int blk) {
         const int j = slot_of(blk);
-        if constexpr (kZero) return ScaleZeroParams{ks[j], kz[j], vs[j], vz[j], j};
-        else return ScaleZeroParams{ks[j], 0.0f, vs[j], 0.0f, j};
+        if constexpr (kZero) return ScaleZeroParams{ks_ptr[j], kz_ptr[j], vs_ptr[j], vz_ptr[j], j};
+        else return ScaleZeroParams{ks_ptr[j], 0.0f, vs_ptr[j], 0.0f, j};
       },
-      [&](bool is_v, int blk, const ScaleZeroParams& ps, int j, uint4 (&r)[TPL]) {
+      [&](bool is_v, int blk, const ScaleZeroParams& ps, int j, uint4 (&r)[LOADS]) {
         load_codes(is_v, blk, kPaged ? lane_int(ps.slot, j) : 0, r);
       },
-      [&](int blk, const ScaleZeroParams& pb, const uint4 (&kr)[TPL]) {
+      [&](int blk, const ScaleZeroParams& pb, const uint4 (&kr)[LOADS]) {
         block_weights(blk, pb.ks, pb.kz, kr, p);
       },
-      [&](int blk, const ScaleZeroParams& pb, const uint4 (&vr)[TPL]) {
+      [&](int blk, const ScaleZeroParams& pb, const uint4 (&vr)[LOADS]) {
         block_accumulate(blk, pb.vs, pb.vz, vr, p);
       },
       make_query);
 
-  // One query head of each wave at a time through LDS: the waves of a query set are
-  // merged per channel (then the row is written out, or its partial state stored).
+  // The waves' states per row through LDS, after every wave is done with its staged V
+  // block (red_o reuses that memory).
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * grp + i;
+    const float lr = row16_sum(l[i]);
+    if (r < G && r16 == 0) {
+      red_l[wave][r] = lr;
+      red_m[wave][r] = m[i];
+    }
+    if (r < 2 * G) {
+#pragma unroll
+      for (int n = 0; n < NTV; ++n) red_o[wave][r][16 * n + r16] = o[n][i];
+    }
+  }
+  __syncthreads();
+
   const int n_row = sr.n;
-  const int64_t qrow0 = row * G;  // first output row of the cache row
+  const int64_t qrow0 = row * G;  // first output row
+  constexpr int kThreadsWg = kSplitWaves * kWave;
+  auto merged = [&](int g, int d, float& M, float& L) {
+    M = red_m[0][g];
 #pragma unroll
-  for (int i = 0; i < QW; ++i) {
+    for (int w = 1; w < kSplitWaves; ++w) M = fmaxf(M, red_m[w][g]);
+    float od = 0.0f;
+    L = 0.0f;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) red_o[wave][lane][k] = o[i][k] * kUnit;
-    red_l[wave][lane] = l[i];
-    if (lane == 0) red_m[wave] = m[i];
-    __syncthreads();
-    if (threadIdx.x < QSETS * D) {
-      const int qs = threadIdx.x / D, d = threadIdx.x % D;
-      const int c = d / DPL, k = d % DPL;
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int sw = 0; sw < STREAMS; ++sw) M = fmaxf(M, red_m[sw * QSETS + qs]);
-      float od = 0.0f, L = 0.0f;
-#pragma unroll
-      for (int sw = 0; sw < STREAMS; ++sw) {
-        const int w = sw * QSETS + qs;
-        const float alpha = __builtin_amdgcn_exp2f(red_m[w] - M);
-        float so = 0.0f, sl = 0.0f;
-#pragma unroll
-        for (int g = 0; g < GROUPS; ++g) {
-          so += red_o[w][g * LPT + c][k];
-          sl += red_l[w][g * LPT];
-        }
-        od = __builtin_fmaf(alpha, so, od);
-        L = __builtin_fmaf(alpha, sl, L);
+    for (int w = 0; w < kSplitWaves; ++w) {
+      const float alpha = __builtin_amdgcn_exp2f(red_m[w][g] - M);
+      od = __builtin_fmaf(alpha, red_o[w][g][d] + red_o[w][G + g][d], od);
+      L = __builtin_fmaf(alpha, red_l[w][g], L);
+    }
+    return od;
+  };
+  if (a.fused && n_row == 1) {
+    for (int t = threadIdx.x; t < G * D; t += kThreadsWg) {
+      float M, L;
+      const float od = merged(t / D, t % D, M, L);
+      a.out[qrow0 * D + t] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(od / L));
+    }
+    return;
+  }
+  for (int t = threadIdx.x; t < G * D; t += kThreadsWg) {
+    const int g = t / D, d = t % D;
+    float M, L;
+    const float od = merged(g, d, M, L);
+    float* po = a.ws_o + ((qrow0 + g) * a.n_split + split) * D;
+    float* ml = a.ws_ml + ((qrow0 + g) * a.n_split + split) * 2;
+    if (a.fused) {
+      store_shared(po + d, od);
+      if (d == 0) {
+        store_shared(ml, M);
+        store_shared(ml + 1, L);
       }
-      const int64_t qrow = qrow0 + qs * QW + i;
-      if (a.fused && n_row == 1) {
-        a.out[qrow * D + d] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(od / L));
-      } else {
-        float* po = a.ws_o + (qrow * a.n_split + split) * D;
-        float* ml = a.ws_ml + (qrow * a.n_split + split) * 2;
-        if (a.fused) {
-          store_shared(po + d, od);
-          if (d == 0) {
-            store_shared(ml, M);
-            store_shared(ml + 1, L);
-          }
-        } else {
-          po[d] = od;
-          if (d == 0) {
-            ml[0] = M;
-            ml[1] = L;
-          }
-        }
+    } else {
+      po[d] = od;
+      if (d == 0) {
+        ml[0] = M;
+        ml[1] = L;
       }
     }
-    __syncthreads();
   }
-  if (!a.fused || n_row == 1) return;
+  if (!a.fused) return;
   __shared__ uint32_t ticket;
   wait_own_stores();  // every wave's partial stores have reached memory
   __syncthreads();
@@ -2011,8 +2094,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_gqa_kernel(Att
                                     __HIP_MEMORY_SCOPE_SYSTEM);
   __syncthreads();
   if (ticket == static_cast<uint32_t>(n_row - 1)) {
-    // as in the int4 grouped-query kernel: thread t merges rows t / D + k * (threads / D)
-    constexpr int kThreadsWg = kSplitWaves * kWave;
+    // thread t merges rows t / D + k * (threads / D) of channel t % D; a wave's 64 threads
+    // share t / D (D is a multiple of the wave size): uniform rows
     constexpr int R = (G * D + kThreadsWg - 1) / kThreadsWg;
     const int t = threadIdx.x;
     if (t < G * D)
@@ -2094,9 +2177,9 @@ hipError_t gqa_t(int batch, const AttnArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((attn_split_int4_gqa_kernel<D, G, false>), grid, block, 0, s, a);
   } else {
     if (paged)
-      hipLaunchKernelGGL((attn_split_gqa_kernel<SCHEME, D, G, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_split_gqa8_kernel<SCHEME, D, G, true>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((attn_split_gqa_kernel<SCHEME, D, G, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((attn_split_gqa8_kernel<SCHEME, D, G, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

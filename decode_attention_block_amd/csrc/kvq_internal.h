@@ -79,9 +79,9 @@ hipError_t launch_attn_split(int scheme, int head_dim, int batch, const AttnArgs
 hipError_t launch_decode_step(int scheme, int head_dim, int batch, const AttnArgs& a,
                               hipStream_t s);
 hipError_t launch_attn_combine(int head_dim, int batch, const AttnArgs& a, hipStream_t s);
-// Grouped-query attention: `group` (2, 4 or 8) query rows per cache row, in one launch
-// (int4 on the matrix cores, uint8 and FP8 on the VALU); out and the partial states are
-// indexed by query row (cache row * group + g).
+// Grouped-query attention: `group` (2, 4 or 8) query rows per cache row, in one launch,
+// on the matrix cores for every scheme; out and the partial states are indexed by query
+// row (cache row * group + g).
 hipError_t launch_attn_gqa(int scheme, int head_dim, int group, int batch, const AttnArgs& a,
                            hipStream_t s);
 

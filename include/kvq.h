@@ -280,10 +280,10 @@ int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new
  * multi-query and grouped-query attention): query head hq = h * group + g of sequence b
  * attends over cache row (b, h), for g < group. The result is decode_attn_qkv's for
  * each query head against its cache row (same definition, splits and merge for the
- * same blocks_per_split); the codes of a block are decoded once for all `group` queries
- * (int4: into matrix-core operands; uint8 and FP8: into fp32 values on the vector ALUs,
- * shared by up to 4 query heads per wave). The automatic plan (blocks_per_split = 0)
- * aims at about two workgroups per compute unit for group > 1 (decode_attn_gqa_plan).
+ * same blocks_per_split); the codes of a block are turned into matrix-core operands
+ * once for all `group` queries (uint8 and FP8 V codes reach the operand layout through a
+ * transposing LDS read). The automatic plan (blocks_per_split = 0) aims at about two
+ * workgroups per compute unit for group > 1 (decode_attn_gqa_plan).
  * (Decode attention as in decode_attn_qkv with cached heads shared between query
  * heads: MLA with its projections absorbed decodes as multi-query attention, [Pg3] §二.)
  *   q, out    : fp16 [B][H * group][D] contiguous, 16-byte aligned.
