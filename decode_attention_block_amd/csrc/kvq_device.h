@@ -147,26 +147,47 @@ __device__ __forceinline__ float fp8_scale(float absmax) {
 // The E4M3 codes of 8 values are taken by the hardware conversion v_cvt_pk_fp8_f32 (two
 // values per instruction), which on gfx950 rounds a binary32 value to the nearest OCP
 // E4M3 value with ties to even, keeps the sign (so -0 and negative values that round to
-// zero give 0x80) and produces the subnormals m/8 * 2^-6. It is fed the correctly rounded
-// quotient RN(x / s) (an IEEE division, no reciprocal), clamped to +-448 so that values
-// the scheme saturates (|x / s| can exceed 448 by a rounding error) convert to 0x7E / 0xFE
-// instead of overflowing to NaN. Bit-exact against the oracle's search over all codes on
-// every rounding decision (ties, subnormals, signed zeros, 448: GPU test).
-__device__ __forceinline__ float fp8_quotient(float x, float s) {
-  return __builtin_fminf(__builtin_fmaxf(x / s, -448.0f), 448.0f);
+// zero give 0x80) and produces the subnormals m/8 * 2^-6. Its input is the quotient
+// RN(x / s) clamped to +-448, so that values the scheme saturates (|x / s| can exceed 448
+// by a rounding error) convert to 0x7E / 0xFE instead of overflowing to NaN.
+//
+// The quotient is not divided out for every value: q = RN(x * r), r = RN(1 / s), lies
+// within 2^-22 (relative) of RN(x / s), so RN(x / s) lies between q * (1 - 2^-21) and
+// q * (1 + 2^-21) (each product rounded, which moves it by at most 2^-24 relative), and
+// the conversion and the clamp are monotonic: where both ends of that interval give the
+// same code, it is the code of RN(x / s). Only when one of the 8 values' ends differ
+// (its quotient next to the midpoint between two E4M3 values, or to 448) are the 8
+// quotients divided out. Bit-exact against the oracle's search over all codes on every
+// rounding decision (ties, subnormals, signed zeros, 448: GPU test).
+__device__ __forceinline__ float fp8_clamp(float q) {
+  return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
 }
 
-// 8 values -> 8 bytes of FP8 codes (x[i] in byte i).
-__device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], const Divisor& d) {
-  if (d.s == 0.0f) return make_uint2(0u, 0u);
-  float q[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = fp8_quotient(x[i], d.s);
+__device__ __forceinline__ uint2 fp8_codes8(const float (&q)[8]) {
   int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);  // bytes 0, 1
   w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);      // bytes 2, 3
   int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
   w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
   return make_uint2(static_cast<uint32_t>(w0), static_cast<uint32_t>(w1));
+}
+
+// 8 values -> 8 bytes of FP8 codes (x[i] in byte i).
+__device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], const Divisor& d) {
+  if (d.s == 0.0f) return make_uint2(0u, 0u);
+  float lo[8], hi[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q = x[i] * d.r;
+    lo[i] = fp8_clamp(q * (1.0f - 0x1p-21f));
+    hi[i] = fp8_clamp(q * (1.0f + 0x1p-21f));
+  }
+  const uint2 a = fp8_codes8(lo);
+  const uint2 b = fp8_codes8(hi);
+  if (a.x == b.x && a.y == b.y) return a;
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = fp8_clamp(x[i] / d.s);
+  return fp8_codes8(q);
 }
 
 // The int4 and uint8 packers below code 8 values with the multiply and take one branch,
