@@ -603,11 +603,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const uint8_t* poo
 // the append wave's registers (coded from the staged values) and are written at the end
 // of the kernel: int4 the whole block, uint8 and FP8 the token's row (the whole block if
 // it was re-quantized).
-// The append wave takes the sequence's arrival ticket (1 << 24 added to seq_lens[b], as
-// in kv_append) once its own loads have completed, and the last of the sequence's `heads`
-// workgroups stores the new length once its append wave has done its work. Every
-// workgroup of the sequence reads the length before it takes its ticket, and the length
-// changes only after the last ticket, so none can see the new length.
+// The append wave takes the sequence's arrival ticket (in two levels, see step_ticket)
+// once its own loads have completed, and the last of the sequence's `heads` workgroups
+// stores the new length once its append wave has done its work. Every workgroup of the
+// sequence reads the length before it takes its ticket, and the length changes only
+// after the last ticket, so none can see the new length.
 constexpr int kStepWaves = kSplitWaves + 1;
 
 struct StepLens {
@@ -678,36 +678,56 @@ __device__ __forceinline__ void step_stage_reduce(const StepLens& sl, int lane, 
       fresh, xs, nullptr, plan);
 }
 
-// The sequence's arrival ticket, taken by the append wave after the length was read;
-// step_ticket_done, once the wave has coded and attended the open block, stores the new
-// length if this was the sequence's last arrival. The atomic's latency (the sequence's
-// `heads` tickets are serialized at memory) must overlap the wave's work, so nothing
-// waits for it before that: it is issued after the wave's loads have been waited for
+// The sequence's arrival ticket, taken by the append wave after the length was read, in
+// two levels. The `heads` workgroups of a sequence arrive in groups of kTicketGroup
+// heads, each group on its own counter (the workspace's arrival counter of the group's
+// first row, which the one-launch step, one split per row, does not otherwise use); the
+// last arrival of a group then arrives, alone for its group, on the sequence's ticket in
+// the top 8 bits of seq_lens[b], and the last group's last arrival stores the new
+// length. Atomics on one address are performed one after another at memory: with one
+// counter per sequence, the 32 heads of the 8K workload queued 32 deep and the wait for
+// the ticket cost 1.8 us of the step (a timing-only build without it); in two levels
+// they queue at most kTicketGroup + ceil(heads / kTicketGroup) deep.
+// The group ticket's latency must overlap the wave's work, so nothing waits for it
+// before step_ticket_done: it is issued after the wave's loads have been waited for
 // (vector memory requests complete in order, so a later wait would include it), and as
 // one request of the whole wave whose lanes past the first fall outside a 4-byte buffer
-// resource (seq_lens[b]) and so do not touch memory; a branch around a one-lane atomic
-// would merge its result with the other lanes' value and make the compiler wait for it
-// at once. System scope (cache policy sc1): the add is performed at memory, past the
-// per-XCD L2s. The result is meaningful in lane 0.
-// The new length may be stored while the other workgroups still stream: each workgroup
-// of the sequence read the length before it took its ticket, so all of them have read it
-// once the last ticket is taken, and no other workgroup reads seq_lens[b]. It is stored
-// as soon as the append wave has attended its block rather than at the kernel's end
-// (0.1 us faster on the 8K int4 step).
+// resource and so do not touch memory; a branch around a one-lane atomic would merge
+// its result with the other lanes' value and make the compiler wait for it at once.
+// System scope (cache policy sc1): every add is performed at memory, past the per-XCD
+// L2s. The result is meaningful in lane 0.
+// Every workgroup of the sequence read the length before its group ticket; a group's
+// last arrival has seen all of its group's tickets, and the sequence's last one all the
+// groups', so the length changes only after every workgroup of the sequence has read it,
+// and no other workgroup reads seq_lens[b]. The new length is stored as soon as the
+// append wave has attended its block rather than at the kernel's end (0.1 us faster on
+// the 8K int4 step); the group counter is left at zero for the next call.
 constexpr int kCachePolicySystem = 16;  // sc1
+constexpr int kTicketGroup = 8;
 
-__device__ __forceinline__ uint32_t step_ticket(const AttnArgs& a, int b, int lane) {
+__device__ __forceinline__ uint32_t* step_group_counter(const AttnArgs& a, int b, int h) {
+  return a.counters + static_cast<int64_t>(b) * a.heads + (h - h % kTicketGroup);
+}
+
+__device__ __forceinline__ uint32_t step_ticket(const AttnArgs& a, int b, int h, int lane) {
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(a.ap.seq_lens + b, 0, 4, kBufferRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(step_group_counter(a, b, h), 0, 4, kBufferRsrcWord3);
   return static_cast<uint32_t>(__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(
-      1 << 24, rs, lane == 0 ? 0 : 4, 0, kCachePolicySystem));
+      1, rs, lane == 0 ? 0 : 4, 0, kCachePolicySystem));
 }
 
 __device__ __forceinline__ void step_ticket_done(const AttnArgs& a, const StepLens& sl, int b,
-                                                 int cap, uint32_t ticket, int lane) {
-  if (lane == 0 && (ticket >> 24) == static_cast<uint32_t>(a.heads - 1))
-    __hip_atomic_exchange(reinterpret_cast<uint32_t*>(a.ap.seq_lens) + b,
-                          static_cast<uint32_t>(sl.len0 < cap ? sl.len0 + 1 : sl.len0),
+                                                 int h, int cap, uint32_t ticket, int lane) {
+  const int in_group = min(kTicketGroup, a.heads - (h - h % kTicketGroup));
+  if (lane != 0 || ticket != static_cast<uint32_t>(in_group - 1)) return;
+  __hip_atomic_store(step_group_counter(a, b, h), 0u, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_SYSTEM);
+  const uint32_t groups = static_cast<uint32_t>((a.heads + kTicketGroup - 1) / kTicketGroup);
+  uint32_t* len = reinterpret_cast<uint32_t*>(a.ap.seq_lens) + b;
+  const uint32_t old =
+      __hip_atomic_fetch_add(len, 1u << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if ((old >> 24) == groups - 1)
+    __hip_atomic_exchange(len, static_cast<uint32_t>(sl.len0 < cap ? sl.len0 + 1 : sl.len0),
                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
@@ -908,7 +928,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
       const uint4 fresh[2] = {make_uint4(fresh_k.x, fresh_k.y, fresh_k.z, fresh_k.w),
                               make_uint4(fresh_v.x, fresh_v.y, fresh_v.z, fresh_v.w)};
       if (sl.len0 < cap) step_stage_reduce<SCHEME, D>(sl, lane, xs, fresh, plan);
-      ticket = step_ticket(a, b, lane);
+      ticket = step_ticket(a, b, h, lane);
       // The block's new codes, in registers until the end of the kernel, coded from the
       // staged values with the block's scale after the append: every stored code of an
       // open block is the code of its staged value under the block's current scale, so
@@ -931,7 +951,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
         block_weights(sl.tail_blk, sc.ks, sc.kz, kr, p);
         block_accumulate(sl.tail_blk, sc.vs, sc.vz, vr, p);
       }
-      step_ticket_done(a, sl, b, cap, ticket, lane);
+      step_ticket_done(a, sl, b, h, cap, ticket, lane);
     }
   }
   if (streaming)
@@ -1294,7 +1314,7 @@ attn_split_int4_kernel(AttnArgs a) {
       const uint4 fresh[2] = {make_uint4(fresh_k.x, fresh_k.y, fresh_k.z, fresh_k.w),
                               make_uint4(fresh_v.x, fresh_v.y, fresh_v.z, fresh_v.w)};
       if (sl.len0 < cap) step_stage_reduce<KVQ_INT4_SYM, D>(sl, lane, xs, fresh, plan);
-      ticket = step_ticket(a, b, lane);
+      ticket = step_ticket(a, b, h, lane);
       // the block's new codes, in registers until the end of the kernel
       const BlockScales sc = step_append<D>(
           a, sl, row, cap, lane, fresh, plan, [&](const AppendPlan (&plan)[2]) {
@@ -1307,7 +1327,7 @@ attn_split_int4_kernel(AttnArgs a) {
         block_weights(sl.tail_blk, sc.ks, kr, p);
         block_accumulate(sc.vs, vr, p);
       }
-      step_ticket_done(a, sl, b, cap, ticket, lane);
+      step_ticket_done(a, sl, b, h, cap, ticket, lane);
     }
   }
   if (streaming)

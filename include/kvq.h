@@ -263,13 +263,14 @@ int decode_attn_combine(const kvq_cache* cache, void* out, void* workspace,
  * B*H >= 256) the step is one kernel launch: each row's workgroup has one
  * wave more than the attention, which appends the row's token and then attends the
  * block holding it while the other waves attend the rest of the row, so the append
- * costs no launch and no time on the attention's path. out then equals the two calls'
+ * costs no launch. out then equals the two calls'
  * up to the order of the binary32 sums (the new token's block is merged last), i.e. to
  * the last place of the fp16 result. Arguments and limits are
  * those of kv_append and decode_attn_qkv (max_len_after bounds the lengths after the
  * append and sizes the plan; the workspace is sized by
- * decode_attn_workspace_bytes(cache, max_len_after, blocks_per_split)); the same
- * status codes. (The step is one iteration of the decode phase, one token generated
+ * decode_attn_workspace_bytes(cache, max_len_after, blocks_per_split), and its arrival
+ * counters, which the one-launch step uses to count the rows' appends, start at zero and
+ * are left zero); the same status codes. (The step is one iteration of the decode phase, one token generated
  * per sequence, [Pg1] §3.1; each such token reads the whole cache, [Pg2] §2.1.)
  * Returns KVQ_OK or a negative kvq_status. */
 int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
