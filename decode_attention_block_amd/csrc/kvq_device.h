@@ -266,9 +266,12 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // 16-byte store of a value (component by component, so that a uint4 held in a register
 // array is never copied out of memory).
+// Non-temporal: the decode step's code stores come at the very end of the kernel, which
+// completes only once they have reached memory; marked streaming they do not wait in the
+// L2 for the end-of-kernel write-back (8K int4 step 43.4 -> 42.8 us).
 __device__ __forceinline__ void store_b128(uint8_t* p, const uint4& v) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  *reinterpret_cast<u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
 }
 
 // 16-byte load through a buffer resource at voffset (per lane) + soffset (uniform);
