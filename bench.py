@@ -60,6 +60,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_int4_b8h32d128_ctx8k_
 CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
 SAMPLED_STEPS = 32             # steps timed one by one for the percentiles
 COMPARE_ROUNDS = 3             # alternating eager / graph rounds for their comparison
+HOLD_US = 200                  # stream hold before a timed graph segment (kvq_probe_hold)
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 KV_FORMATS = {0: "int4 block-64 symmetric", 1: "uint8 block-64 asymmetric",
               2: "fp8 e4m3 block-64 scaled"}
@@ -258,7 +259,10 @@ class Stepper:
 
     def run(self, n_steps, timed, graph=True):
         """n_steps steps; returns their total GPU time in ms (HIP events around every
-        segment) when timed."""
+        segment) when timed. A timed graph segment is queued behind a short hold of the
+        stream (kvq_probe_hold), so that its start event is taken when the GPU reaches
+        the segment, not when the host begins to submit it: the events then bracket the
+        GPU's execution of the steps without the graph launch's submission latency."""
         torch = self.torch
         total = 0.0
         for n in self._segments(n_steps):
@@ -267,6 +271,9 @@ class Stepper:
             if self.reset:
                 self.reset()
             torch.cuda.synchronize()
+            if timed and graph:
+                import decode_attention_block_amd as kvq
+                kvq.kvq_probe_hold(HOLD_US)
             if timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -512,7 +519,8 @@ def timing_fields(stepper, steps, warmup, eager, launches_per_step, step_bytes_f
     return {
         "steps": steps, "warmup": warmup,
         "timing": ("eager calls, HIP events around each segment" if eager else
-                   "HIP graph replay of each segment's steps, HIP events around each segment"),
+                   "HIP graph replay of each segment's steps, HIP events around each segment "
+                   f"(queued behind a {HOLD_US} us hold of the stream)"),
         "ms_per_step": total_ms / steps,
         "gbs": bytes_ / (total_ms / 1e3) / 1e9,
         "eager_ms_per_step": eager_ms / steps,

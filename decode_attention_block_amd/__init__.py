@@ -26,7 +26,7 @@ EXPORTS = ["kv_quantize_blocks", "kv_append", "decode_attn_plan", "decode_step_l
            "decode_attn_split",
            "decode_attn_combine", "decode_step_qkv", "decode_attn_gqa",
            "decode_attn_gqa_workspace_bytes", "decode_attn_gqa_plan", "kvq_int4_to_natural",
-           "kvq_int4_from_natural", "kvq_probe_stream_read",
+           "kvq_int4_from_natural", "kvq_probe_stream_read", "kvq_probe_hold",
            "kvq_strerror", "kvq_version"]
 
 
@@ -86,6 +86,7 @@ def load_library():
         "kvq_int4_to_natural": ([P, P, i32, i32, i64], ctypes.c_int),
         "kvq_int4_from_natural": ([P, P, i32, i32, i64], ctypes.c_int),
         "kvq_probe_stream_read": ([P, sz, i32, P, P], ctypes.c_int),
+        "kvq_probe_hold": ([ctypes.c_uint32, P], ctypes.c_int),
         "kvq_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "kvq_version": ([], ctypes.c_int),
     }
@@ -275,6 +276,13 @@ def kvq_probe_stream_read(buf, workgroups, sink, stream=None):
     rc = load_library().kvq_probe_stream_read(_ptr(buf), nbytes, int(workgroups), _ptr(sink),
                                               _stream(stream))
     _check(rc, "kvq_probe_stream_read")
+
+
+def kvq_probe_hold(microseconds, stream=None):
+    """Measurement aid: holds the stream for `microseconds` (1 .. 100000) of the GPU's
+    real-time counter with one sleeping wave, so that a timing event recorded next marks
+    when the GPU reaches the work queued after it."""
+    _check(load_library().kvq_probe_hold(int(microseconds), _stream(stream)), "kvq_probe_hold")
 
 
 class KVCache:

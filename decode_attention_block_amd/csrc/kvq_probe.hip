@@ -1,6 +1,8 @@
-// kvq_probe.hip — a measurement aid, not part of the method: a plain streaming read of
+// kvq_probe.hip — measurement aids, not part of the method: a plain streaming read of
 // a device buffer at the access pattern of the attention kernels, whose rate is the
-// practical read ceiling those kernels are compared with (HBM peak being the spec).
+// practical read ceiling those kernels are compared with (HBM peak being the spec), and
+// a kernel that holds a stream for a set time (so that timing events recorded behind it
+// bracket only the GPU's execution of the work queued after them).
 //
 // Each 256-thread workgroup reads one contiguous slab of the buffer (as an attention
 // workgroup reads one row's codes) with 16-byte non-temporal buffer loads, every lane
@@ -40,8 +42,27 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const uint8_t
   sink[static_cast<int64_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = acc;
 }
 
+// Holds its stream for `ticks` of the 100 MHz real-time counter: one wave sleeping in a
+// loop, no memory traffic. Bounded twice: by the counter and by kMaxSpins sleeps.
+constexpr uint32_t kMaxSpins = 1u << 22;
+
+__global__ __launch_bounds__(64) void hold_kernel(uint64_t ticks) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (uint32_t spins = 0; spins < kMaxSpins; ++spins) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
 }  // namespace
 }  // namespace kvq
+
+extern "C" int kvq_probe_hold(uint32_t microseconds, void* stream) {
+  if (microseconds == 0 || microseconds > 100000) return KVQ_EINVAL;
+  hipLaunchKernelGGL(kvq::hold_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint64_t>(microseconds) * 100u);
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
 
 extern "C" int kvq_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups,
                                      uint32_t* sink, void* stream) {

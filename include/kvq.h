@@ -40,7 +40,7 @@ extern "C" {
 #endif
 
 #define KVQ_BLOCK_TOKENS 64
-#define KVQ_VERSION 4
+#define KVQ_VERSION 5
 /* Size of the static device array decode_attn_qkv_noalloc works in (per GPU). */
 #define KVQ_NOALLOC_SCRATCH_BYTES (4u << 20)
 
@@ -333,6 +333,16 @@ int kvq_int4_from_natural(const uint8_t* natural, uint8_t* stored, int32_t head_
  * Returns KVQ_OK, KVQ_EINVAL, KVQ_EALIGN, KVQ_ENOTSUP or KVQ_EHIP. */
 int kvq_probe_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
                           void* stream);
+
+/* Measurement aid (not part of the method): launches one wave on `stream` that sleeps
+ * until `microseconds` of the GPU's 100 MHz real-time counter have passed (bounded also
+ * by a fixed number of sleeps), touching no memory. Work and timing events queued behind
+ * it on the same stream start when it ends, so a timing event recorded right after it
+ * marks the moment the GPU reaches the following work rather than the moment the host
+ * queued it.
+ *   microseconds : 1 .. 100000 (KVQ_EINVAL otherwise).
+ * Returns KVQ_OK, KVQ_EINVAL or KVQ_EHIP. */
+int kvq_probe_hold(uint32_t microseconds, void* stream);
 
 /* Human-readable text of a kvq_status (static storage). */
 const char* kvq_strerror(int status);

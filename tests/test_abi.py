@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = kvq.load_library()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert kvq.kvq_version() == 4
+    assert kvq.kvq_version() == 5
 
 
 def cache(scheme=0, B=2, H=4, D=128, MB=3, **kw):
@@ -258,6 +258,13 @@ def test_stream_read_probe_validation():
     assert probe(FAKE + 8, 4096, 256, FAKE, None) == EALIGN
     # one workgroup cannot stream 3 GiB in a slab below 2^31 bytes
     assert probe(FAKE, 3 << 30, 1, FAKE, None) == ENOTSUP
+
+
+@no_gpu_only
+def test_hold_probe_validation():
+    hold = kvq.load_library().kvq_probe_hold
+    assert hold(0, None) == EINVAL
+    assert hold(100001, None) == EINVAL
 
 
 def rc_noalloc(c, q=FAKE, out=FAKE, max_len=100, bps=0):
