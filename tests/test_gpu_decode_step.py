@@ -57,11 +57,13 @@ def _assert_same_output(out, out_ref, bitwise):
     assert norm_err <= 2.0 ** -10, norm_err
 
 
-# (B, H): 8 x 32 = 256 rows -> one piece per row (single launch); 3 x 5 -> several
-# splits per row (append and attention as two launches, bitwise equal to the two calls).
+# (B, H): 8 x 32 = 256 rows -> one piece per row (single launch); 20 x 13 = 260 rows ->
+# single launch with heads not a multiple of the ticket's groups of 8 (8 + 5); 3 x 5 ->
+# several splits per row (append and attention as two launches, bitwise equal to the two
+# calls).
 @pytest.mark.parametrize("scheme", [INT4, UINT8, FP8])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("BH", [(8, 32), (3, 5)])
+@pytest.mark.parametrize("BH", [(8, 32), (20, 13), (3, 5)])
 def test_step_equals_append_then_attention(scheme, D, BH):
     import decode_attention_block_amd as kvq
     import torch
@@ -69,7 +71,7 @@ def test_step_equals_append_then_attention(scheme, D, BH):
     say("decode step", scheme, D, B, H)
     MB, S = 5, 320
     k, v, q = _history(scheme, B, H, D, S, seed=D + B)
-    start = np.array([0, 1, 63, 64, 100, 127, 5, 250][:B], np.int32)
+    start = np.resize(np.array([0, 1, 63, 64, 100, 127, 5, 250], np.int32), B)
     ref_c = gpu_quantize(scheme, k, v, start, MB)
     c = gpu_quantize(scheme, k, v, start, MB)
     sm = 1.0 / np.sqrt(D)
