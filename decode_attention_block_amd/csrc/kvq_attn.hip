@@ -1091,10 +1091,10 @@ __device__ __forceinline__ uint32_t dword_of(const uint4 (&r)[N], int f) {
 
 // Maximum over lanes 0..15 (row 0 of the MFMA output), returned uniformly.
 __device__ __forceinline__ float row0_max(float v) {
-  v = fmaxf(v, dpp<kDppQuadXor1>(v));
-  v = fmaxf(v, dpp<kDppQuadXor2>(v));
-  v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  v = dpp_max<kDppQuadXor1>(v);
+  v = dpp_max<kDppQuadXor2>(v);
+  v = dpp_max<kDppHalfMirror>(v);
+  v = dpp_max<kDppRowMirror>(v);
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
 }
 
@@ -1420,16 +1420,26 @@ attn_split_int4_kernel(AttnArgs a) {
 
 // Maximum / sum over the 16 lanes of each DPP row; every lane of the row gets it.
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<kDppQuadXor1>(v));
-  v = fmaxf(v, dpp<kDppQuadXor2>(v));
-  v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  return fmaxf(v, dpp<kDppRowMirror>(v));
+  v = dpp_max<kDppQuadXor1>(v);
+  v = dpp_max<kDppQuadXor2>(v);
+  v = dpp_max<kDppHalfMirror>(v);
+  return dpp_max<kDppRowMirror>(v);
 }
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<kDppQuadXor1>(v);
   v += dpp<kDppQuadXor2>(v);
   v += dpp<kDppHalfMirror>(v);
   return v + dpp<kDppRowMirror>(v);
+}
+
+// The fp16 part of the scaled weight x = p * unit that a row of the P.V image holds:
+// the high part (x rounded to fp16) on rows g < G, the low part x - high on rows
+// G <= g < 2G. Both are x - h rounded to fp16, with h = high on the low-part rows
+// (cut = unit) and h = 0 on the others (cut = 0): two mixed-precision FMAs and no
+// select. x - high is exact in binary32, so the parts are those of the plain split.
+__device__ __forceinline__ _Float16 weight_part(float p, float unit, float cut) {
+  const _Float16 h = static_cast<_Float16>(p * cut);
+  return static_cast<_Float16>(__builtin_fmaf(p, unit, -static_cast<float>(h)));
 }
 
 template <int D, int G, bool kPaged>
@@ -1605,12 +1615,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_int4_gqa_kerne
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * grp + i;
-        if (r < 2 * G) {
-          const float x = p[nt][i] * p_unit;
-          const _Float16 hi = static_cast<_Float16>(x);
+        if (r < 2 * G)
           pimg[wave][kstep][kgrp][r][p_slot] =
-              r < G ? hi : static_cast<_Float16>(x - static_cast<float>(hi));
-        }
+              weight_part(p[nt][i], p_unit, r < G ? 0.0f : p_unit);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -1971,12 +1978,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void attn_split_gqa8_kernel(At
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * grp + i;
-        if (r < 2 * G) {
-          const float x = p[nt][i] * 16384.0f;
-          const _Float16 hi = static_cast<_Float16>(x);
+        if (r < 2 * G)
           pimg[wave][kstep][kgrp][r][r16 & 7] =
-              r < G ? hi : static_cast<_Float16>(x - static_cast<float>(hi));
-        }
+              weight_part(p[nt][i], 16384.0f, r < G ? 0.0f : 16384.0f);
       }
     }
     __builtin_amdgcn_wave_barrier();

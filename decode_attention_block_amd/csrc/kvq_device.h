@@ -25,6 +25,31 @@ __device__ __forceinline__ float dpp(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// max(v, dpp<CTRL>(v)) as one v_max_f32 with a DPP source operand. Written through
+// fmaxf, the exchange takes a separate v_mov_b32_dpp (after a move of the old value,
+// since the compiler cannot see that every source lane is valid) and an IEEE-mode
+// canonicalisation of the moved value before the max: four instructions per step.
+// s_nop 1 gives the two wait states a DPP read needs after a VALU write of its source.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  float r;
+  if constexpr (CTRL == kDppQuadXor1)
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "=v"(r) : "v"(v));
+  else if constexpr (CTRL == kDppQuadXor2)
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "=v"(r) : "v"(v));
+  else if constexpr (CTRL == kDppHalfMirror)
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf"
+        : "=v"(r) : "v"(v));
+  else if constexpr (CTRL == kDppRowMirror)
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_mirror row_mask:0xf bank_mask:0xf"
+        : "=v"(r) : "v"(v));
+  else
+    static_assert(CTRL == kDppQuadXor1, "unsupported DPP control");
+  return r;
+}
+
 // Sum over each group of N consecutive lanes (N in {1, 2, 4, 8}); every lane of the
 // group receives the group's sum.
 template <int N>
@@ -38,10 +63,10 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // Maximum over the whole wave, returned uniformly.
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<kDppQuadXor1>(v));
-  v = fmaxf(v, dpp<kDppQuadXor2>(v));
-  v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  v = dpp_max<kDppQuadXor1>(v);
+  v = dpp_max<kDppQuadXor2>(v);
+  v = dpp_max<kDppHalfMirror>(v);
+  v = dpp_max<kDppRowMirror>(v);
   const int iv = __builtin_bit_cast(int, v);
   const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0));
   const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16));
