@@ -50,10 +50,13 @@ int n_blocks_for(int32_t len) { return (len + kBlockTokens - 1) / kBlockTokens; 
 // blocks. With blocks_per_split = 0 the pieces are chosen on the device from the rows'
 // actual lengths (split_range in kvq_attn.hip): the batch's blocks are shared out in
 // chunks of about 1/target of them, one chunk per workgroup, where target is one
-// workgroup per CU, and two for grouped-query rows (that kernel is bound by its
+// workgroup per CU, and two for int4 grouped-query rows (that kernel is bound by its
 // per-block work on one wave per SIMD, and a second workgroup on the CU overlaps its
 // latencies: measured on the 8K grouped-query workload, 8 queries per cached head,
-// 24.7 us with one workgroup per CU, 23.2 us with two, 33.8 us with four). Long unbroken
+// 24.7 us with one workgroup per CU, 23.2 us with two, 33.8 us with four). The 8-bit
+// grouped-query kernel streams twice the bytes per block for the same operand work and
+// keeps one workgroup per CU (the same workload over FP8 and uint8 caches: 29.7 us
+// with one, 30.7 us with two). Long unbroken
 // runs of one row's codes stream from HBM faster than many short ones, and every extra
 // split costs a merge, so rows of equal length stay whole once they fill the GPU; the
 // host only bounds the pieces a row may take (the grid's split dimension): two once the
@@ -64,11 +67,13 @@ int n_blocks_for(int32_t len) { return (len + kBlockTokens - 1) / kBlockTokens; 
 // them (8K grouped-query workload with twice the columns: 21.3 against 20.2 us).
 constexpr int64_t kMaxGridSplits = 65535;  // the grid's split dimension (z)
 
-int64_t plan_target(int group) { return group > 1 ? 2 * kTargetWorkgroups : kTargetWorkgroups; }
+int64_t plan_target(int group, int scheme) {
+  return group > 1 && scheme == KVQ_INT4_SYM ? 2 * kTargetWorkgroups : kTargetWorkgroups;
+}
 
 int device_plan_splits(const kvq_cache* c, int nb, int group) {
   const int64_t rows = static_cast<int64_t>(c->batch) * c->heads;
-  const int64_t target = plan_target(group);
+  const int64_t target = plan_target(group, c->scheme);
   const int64_t s = rows >= target ? 2 : (target + rows - 1) / rows + 1;
   return static_cast<int>(s < nb ? s : nb);
 }
@@ -147,7 +152,7 @@ int attn_args(const kvq_cache* c, const void* q, float softmax_scale, void* out,
   a->bps = bps;
   a->n_split = n_split;
   a->batch = c->batch;
-  a->plan_target = static_cast<int>(plan_target(group));
+  a->plan_target = static_cast<int>(plan_target(group, c->scheme));
   a->qk_scale = softmax_scale * 1.44269504088896340736f;  // log2(e)
   a->block_table = c->block_table;
   a->num_pages = c->num_pages;

@@ -173,14 +173,14 @@ int kv_append(const kvq_cache* cache, const void* k_new, const void* v_new,
  * `blocks_per_split` 64-token blocks, each handled by one workgroup, then merged by
  * their log-sum-exp. blocks_per_split = 0 lets the kernels choose each row's split on
  * the device from the rows' actual lengths (the host does not know them): the batch's
- * blocks are shared out in chunks of about 1/256 of them (1/512 for grouped-query rows),
+ * blocks are shared out in chunks of about 1/256 of them (1/512 for int4 grouped-query rows),
  * and a row is cut into ceil(its blocks / chunk) equal pieces, so equal rows that fill
  * the GPU stay whole and the long rows of a ragged batch are cut ([Pg1] chapter 1:
  * chunked attention as schedulable sub-blocks). Writes blocks_per_split_out (0 for the
  * device's choice) and splits_per_row_out, the most splits a row may take for this
  * max_len (the workspace is sized for it): ceil(blocks / blocks_per_split), or for the
- * device's choice 2 once batch * heads reaches 256 (512 grouped-query rows), else one
- * more than 256 / (batch * heads) (512 / ... for grouped-query rows), never more than
+ * device's choice 2 once batch * heads reaches 256 (512 int4 grouped-query rows), else
+ * one more than 256 / (batch * heads) (512 / ... for int4 grouped-query rows), never more than
  * the blocks. Host only. */
 int decode_attn_plan(const kvq_cache* cache, int32_t max_len, int32_t blocks_per_split,
                      int32_t* blocks_per_split_out, int32_t* splits_per_row_out);
@@ -284,7 +284,8 @@ int decode_step_qkv(const kvq_cache* cache, const void* k_new, const void* v_new
  * same blocks_per_split); the codes of a block are turned into matrix-core operands
  * once for all `group` queries (uint8 and FP8 V codes reach the operand layout through a
  * transposing LDS read). The automatic plan (blocks_per_split = 0) aims at about two
- * workgroups per compute unit for group > 1 (decode_attn_gqa_plan).
+ * workgroups per compute unit for group > 1 over an int4 cache and one over the 8-bit
+ * caches (decode_attn_gqa_plan).
  * (Decode attention as in decode_attn_qkv with cached heads shared between query
  * heads: MLA with its projections absorbed decodes as multi-query attention, [Pg3] §二.)
  *   q, out    : fp16 [B][H * group][D] contiguous, 16-byte aligned.

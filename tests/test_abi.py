@@ -218,11 +218,14 @@ def test_decode_step_is_one_launch_when_every_row_is_one_piece():
         kvq.decode_step_launches(cache(B=8, H=32, MB=129), 129 * 64 + 1)
 
 
-def test_grouped_query_plan_aims_at_two_workgroups_per_cu():
-    # 8 sequences x 8 cached heads, 8K: 64 rows; equal rows take 512 / 64 = 8 pieces of
-    # 16 blocks on the device, and the grid allows one more
+def test_grouped_query_plan_aims_at_two_workgroups_per_cu_int4_one_8bit():
+    # 8 sequences x 8 cached heads, 8K: 64 rows; over an int4 cache equal rows take
+    # 512 / 64 = 8 pieces of 16 blocks on the device, over the 8-bit caches 256 / 64 = 4
+    # of 32, and the grid allows one more
     c = cache(B=8, H=8, MB=128)
     assert kvq.decode_attn_gqa_plan(c, 8, 8192) == (0, 9)
+    for scheme in (1, 2):
+        assert kvq.decode_attn_gqa_plan(cache(scheme, B=8, H=8, MB=128), 8, 8192) == (0, 5)
     assert kvq.decode_attn_gqa_plan(c, 1, 8192) == kvq.decode_attn_plan(c, 8192) == (0, 5)
     assert kvq.decode_attn_gqa_plan(c, 4, 8192, 5) == (5, (128 + 4) // 5)
     # the workspace follows the grouped plan
