@@ -25,7 +25,12 @@ headline takes the host about as long as the GPU, so eager timing measures the h
 The eager time of the same steps is reported beside it. Per-step times (p10, p50, p90)
 come from a separate sampling pass: HIP event pairs around each eagerly queued step,
 all queued behind a few large device copies so that the host is ahead of the GPU.
-Warm-up steps (the given number) run first through the same graphs.
+Warm-up steps (the given number) run first through the same graphs. The other
+workloads below run at least OTHER_MIN_WARMUP warm-up steps (the 32-layer one at least
+OTHER_MIN_WARMUP_LAYERED), a few milliseconds of GPU work, whatever --warmup says: timed
+right after their setup, with the GPU idle meanwhile, their first steps run slower until
+the GPU has been busy for a while, and their lines are meant to show the kernels. Each
+line records the warm-up it ran; --warmup applies to the headline step as given.
 
 The same run measures the other workloads (unless --headline-only) and reports them
 under "workloads": the tiny workload (call latency), the 8K uint8 and FP8 E4M3
@@ -61,6 +66,8 @@ CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
 SAMPLED_STEPS = 32             # steps timed one by one for the percentiles
 COMPARE_ROUNDS = 3             # alternating eager / graph rounds for their comparison
 HOLD_US = 200                  # stream hold before a timed graph segment (kvq_probe_hold)
+OTHER_MIN_WARMUP = 200         # warm-up floor of the other single-layer workloads (steps)
+OTHER_MIN_WARMUP_LAYERED = 5   # ... of the 32-layer workload (steps of 32 launches)
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 KV_FORMATS = {0: "int4 block-64 symmetric", 1: "uint8 block-64 asymmetric",
               2: "fp8 e4m3 block-64 scaled"}
@@ -903,9 +910,10 @@ def main():
             if ow.decode_steps:
                 st, warm = 64 * 3, 64
             elif ow.layers > 1:
-                st, warm = max(5, min(args.steps, 20)), max(2, min(args.warmup, 10))
+                st, warm = max(5, min(args.steps, 20)), max(OTHER_MIN_WARMUP_LAYERED,
+                                                            min(args.warmup, 10))
             else:
-                st, warm = args.steps, args.warmup
+                st, warm = args.steps, max(args.warmup, OTHER_MIN_WARMUP)
             r = measure(kvq, torch, ow, st, warm, args.blocks_per_split,
                         separate=args.separate, eager=args.eager, with_cpu=with_cpu,
                         cpu_budget=4.0)
@@ -913,8 +921,9 @@ def main():
             torch.cuda.empty_cache()
         if not args.paged and w.layers == 1 and w.group == 1:
             print(f"[bench] {w.name} paged", file=sys.stderr, flush=True)
-            r = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
-                        separate=args.separate, paged=True, eager=args.eager)
+            r = measure(kvq, torch, w, args.steps, max(args.warmup, OTHER_MIN_WARMUP),
+                        args.blocks_per_split, separate=args.separate, paged=True,
+                        eager=args.eager)
             others.append(r)
             torch.cuda.empty_cache()
         result["workloads"] = others
