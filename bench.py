@@ -26,11 +26,17 @@ The eager time of the same steps is reported beside it. Per-step times (p10, p50
 come from a separate sampling pass: HIP event pairs around each eagerly queued step,
 all queued behind a few large device copies so that the host is ahead of the GPU.
 Warm-up steps (the given number) run first through the same graphs. The other
-workloads below run at least OTHER_MIN_WARMUP warm-up steps (the 32-layer one at least
-OTHER_MIN_WARMUP_LAYERED), a few milliseconds of GPU work, whatever --warmup says: timed
-right after their setup, with the GPU idle meanwhile, their first steps run slower until
-the GPU has been busy for a while, and their lines are meant to show the kernels. Each
-line records the warm-up it ran; --warmup applies to the headline step as given.
+workloads below, and the read probes, then keep warming up until WARMUP_MS_OTHERS of
+wall time has passed, whatever --warmup says: timed right after their setup (and after
+the host-side oracle legs of the workload before), with the GPU idle meanwhile, their
+first milliseconds run slower, and their lines are meant to show the kernels. Each line
+records the warm-up steps it ran; --warmup applies to the headline step as given.
+
+Beside the HBM peak, every one-launch line is set against two streaming-read rates of
+the same GPU (kvq_probe_stream_read, one contiguous slab per workgroup): over 2 GiB
+(read_ceiling, the practical rate of long streams) and at the line's own bytes per
+launch, replayed back to back over rotated copies as the steps are
+(read_ceiling_same_size, which pays the same start-up and drain per launch).
 
 The same run measures the other workloads (unless --headline-only) and reports them
 under "workloads": the tiny workload (call latency), the 8K uint8 and FP8 E4M3
@@ -66,8 +72,7 @@ CACHE_BYTES_TARGET = 1 << 30   # total bytes of rotated cache copies
 SAMPLED_STEPS = 32             # steps timed one by one for the percentiles
 COMPARE_ROUNDS = 3             # alternating eager / graph rounds for their comparison
 HOLD_US = 200                  # stream hold before a timed graph segment (kvq_probe_hold)
-OTHER_MIN_WARMUP = 200         # warm-up floor of the other single-layer workloads (steps)
-OTHER_MIN_WARMUP_LAYERED = 5   # ... of the 32-layer workload (steps of 32 launches)
+WARMUP_MS_OTHERS = 30.0        # untimed GPU work before the other workloads' and probes' timing
 HEADLINE = "llama7b_b8_h32_d128_ctx8k_int4"
 KV_FORMATS = {0: "int4 block-64 symmetric", 1: "uint8 block-64 asymmetric",
               2: "fp8 e4m3 block-64 scaled"}
@@ -198,6 +203,64 @@ def copy_probe():
     return {"copy_bytes": n, "copy_ms": ms, "copy_gbs_read_plus_write": 2 * n / ms / 1e6}
 
 
+def read_ceiling_at(kvq, torch, nbytes):
+    """The streaming-read rate at one launch's size: kvq_probe_stream_read of `nbytes`,
+    launches replayed back to back from a HIP graph over enough copies (>=
+    CACHE_BYTES_TARGET in all) that the Infinity Cache cannot hold them, as the steps
+    are timed, at 256, 512 and 1024 workgroups (one contiguous slab each); the best
+    counts. A launch of a given size pays the same start-up and drain as the kernels
+    compared with it, which the 2 GiB ceiling hides. Some slab sizes read far slower than
+    their neighbours (in one run, 134.5 MB in 256 slabs: 52% of peak, with half the
+    bytes 65% and twice the bytes 80%), hence the several counts."""
+    n = (int(nbytes) + 4095) // 4096 * 4096
+    copies = max(1, math.ceil(CACHE_BYTES_TARGET / n))
+    reps = max(32, copies)
+    buf = torch.empty(copies * n, dtype=torch.uint8, device="cuda")
+    buf.fill_(7)
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    views = [buf[i * n:(i + 1) * n] for i in range(copies)]
+    by = {}
+    for wg in (256, 512, 1024):
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(reps):
+                kvq.kvq_probe_stream_read(views[j % copies], wg, sink)
+        torch.cuda.synchronize()
+        t_warm = time.perf_counter()
+        while (time.perf_counter() - t_warm) * 1e3 < (WARMUP_MS_OTHERS if wg == 256 else 2.0):
+            g.replay()
+            torch.cuda.synchronize()
+        us = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) / reps * 1e3)
+        by[str(wg)] = float(np.median(us))
+        del g
+    del views, buf, sink
+    torch.cuda.empty_cache()
+    best = min(by, key=by.get)
+    t = by[best]
+    return {"bytes": n, "us_per_launch": t, "gbs": n / t / 1e3,
+            "frac_of_peak": n / t / 1e3 / HBM_PEAK_GBS, "workgroups": int(best),
+            "us_by_workgroups": by, "launches_per_replay": reps, "copies": copies}
+
+
+def with_same_size_ceiling(kvq, torch, res):
+    """Adds the read ceiling at the workload's bytes per launch (one-launch steps)."""
+    per_launch = res.get("kernel_bytes_per_launch")
+    if not per_launch:
+        return res
+    c = read_ceiling_at(kvq, torch, per_launch)
+    res["read_ceiling_same_size"] = c
+    res["kernel_frac_of_same_size_read_ceiling"] = res["kernel_gbs"] / c["gbs"]
+    return res
+
+
 def read_ceiling(kvq, torch):
     """The GPU's practical streaming-read rate: kvq_probe_stream_read over 2 GiB (8x the
     Infinity Cache), at several workgroup counts; the best is the ceiling."""
@@ -205,6 +268,10 @@ def read_ceiling(kvq, torch):
     buf = torch.empty(n, dtype=torch.uint8, device="cuda")
     buf.fill_(7)
     sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    t_warm = time.perf_counter()
+    while (time.perf_counter() - t_warm) * 1e3 < WARMUP_MS_OTHERS:
+        kvq.kvq_probe_stream_read(buf, 256, sink)
+        torch.cuda.synchronize()
     by = {}
     for wg in (256, 512, 1024, 2048, 4096):
         for _ in range(2):
@@ -500,15 +567,20 @@ def kernel_name(w, fused, paged=False):
 
 
 def timing_fields(stepper, steps, warmup, eager, launches_per_step, step_bytes_fn,
-                  per_launch_bytes):
+                  per_launch_bytes, warmup_ms=0.0):
     """Warm-up, the timed steps (graph replays, or eager), the eager comparison and the
     per-step percentiles; step_bytes_fn(total steps) = algorithmic bytes of the timed
     steps. The timed steps follow the warm-up directly (their graphs are captured before
     it, so no capture leaves the GPU idle between them); the comparison rounds come after
-    them, and their graph figure is reported as the later rounds' rate."""
+    them, and their graph figure is reported as the later rounds' rate. With warmup_ms,
+    the warm-up goes on (in runs of `steps` steps) until that much wall time has passed."""
     if not eager:
         stepper.prepare(warmup, steps)
     stepper.run(warmup, timed=False, graph=not eager)
+    t_warm = time.perf_counter()
+    while (time.perf_counter() - t_warm) * 1e3 < warmup_ms:
+        stepper.run(steps, timed=False, graph=not eager)
+        warmup += steps
     wall0 = time.perf_counter()
     total_ms = stepper.run(steps, timed=True, graph=not eager)
     wall_s = time.perf_counter() - wall0
@@ -549,7 +621,8 @@ def timing_fields(stepper, steps, warmup, eager, launches_per_step, step_bytes_f
 
 
 def run_append_attention(kvq, torch, w, steps, warmup, bps, device_inputs, separate=False,
-                         paged=False, eager=False, with_cpu=False, cpu_budget=4.0):
+                         paged=False, eager=False, with_cpu=False, cpu_budget=4.0,
+                         warmup_ms=0.0):
     """Single-layer fixed-length workloads; step = decode_step_qkv (or, with separate,
     kv_append + decode_attn_qkv). The 32K workload's segments are its 64-step decode
     loop on one cache; the 8K workloads rotate over cache copies, each gaining one
@@ -621,7 +694,7 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, device_inputs, separ
     launches = 1 if one_launch else 2
     per_launch = step_bytes(steps) / steps
     res = timing_fields(stepper, steps, warmup, eager, launches, step_bytes,
-                        per_launch if one_launch else 0.0)
+                        per_launch if one_launch else 0.0, warmup_ms)
     res.update({
         "workload": w.name,
         "step": ("kv_append + decode_attn_qkv" if separate else
@@ -664,7 +737,7 @@ def run_append_attention(kvq, torch, w, steps, warmup, bps, device_inputs, separ
 
 
 def run_gqa(kvq, torch, w, steps, warmup, bps, paged=False, eager=False, with_cpu=False,
-            cpu_budget=4.0):
+            cpu_budget=4.0, warmup_ms=0.0):
     """Grouped-query workload: one step is decode_attn_gqa (w.group query heads per
     cached head) over one of enough cache copies (>= CACHE_BYTES_TARGET in all) that the
     Infinity Cache cannot hold them; lengths fixed at the context (no append)."""
@@ -695,7 +768,8 @@ def run_gqa(kvq, torch, w, steps, warmup, bps, paged=False, eager=False, with_cp
         kvq.decode_attn_gqa(caches[j % copies], q, G, sm, out, ws, L, bps)
 
     stepper = Stepper(torch, queue, max(steps, warmup, SAMPLED_STEPS))
-    res = timing_fields(stepper, steps, warmup, eager, 1, lambda n: n * per_launch, per_launch)
+    res = timing_fields(stepper, steps, warmup, eager, 1, lambda n: n * per_launch, per_launch,
+                        warmup_ms)
     bps_eff, n_split = kvq.decode_attn_gqa_plan(caches[0], G, L, bps)
     res.update({
         "workload": w.name,
@@ -721,7 +795,8 @@ def run_gqa(kvq, torch, w, steps, warmup, bps, paged=False, eager=False, with_cp
     return res
 
 
-def run_layers(kvq, torch, w, steps, warmup, bps, eager=False, with_cpu=False, cpu_budget=4.0):
+def run_layers(kvq, torch, w, steps, warmup, bps, eager=False, with_cpu=False, cpu_budget=4.0,
+               warmup_ms=0.0):
     """The 32-layer ragged workload: one step is decode_attn_qkv over every layer's
     cache, each layer with its own K, V and query (no append in this workload)."""
     wl = wl_mod()
@@ -756,7 +831,7 @@ def run_layers(kvq, torch, w, steps, warmup, bps, eager=False, with_cpu=False, c
 
     stepper = Stepper(torch, queue, max(steps, warmup, SAMPLED_STEPS))
     res = timing_fields(stepper, steps, warmup, eager, w.layers,
-                        lambda n: n * w.layers * per_launch, per_launch)
+                        lambda n: n * w.layers * per_launch, per_launch, warmup_ms)
     bps_eff, n_split = kvq.decode_attn_plan(caches[0], L, bps)
     res.update({
         "workload": w.name,
@@ -781,15 +856,17 @@ def run_layers(kvq, torch, w, steps, warmup, bps, eager=False, with_cpu=False, c
 
 
 def measure(kvq, torch, w, steps, warmup, bps, separate=False, paged=False, eager=False,
-            with_cpu=False, cpu_budget=4.0):
+            with_cpu=False, cpu_budget=4.0, warmup_ms=0.0):
     big = w.decode_steps > 0 or w.layers > 1
     if w.layers > 1:
-        res = run_layers(kvq, torch, w, steps, warmup, bps, eager, with_cpu, cpu_budget)
+        res = run_layers(kvq, torch, w, steps, warmup, bps, eager, with_cpu, cpu_budget,
+                         warmup_ms)
     elif w.group > 1:
-        res = run_gqa(kvq, torch, w, steps, warmup, bps, paged, eager, with_cpu, cpu_budget)
+        res = run_gqa(kvq, torch, w, steps, warmup, bps, paged, eager, with_cpu, cpu_budget,
+                      warmup_ms)
     else:
         res = run_append_attention(kvq, torch, w, steps, warmup, bps, big, separate, paged,
-                                   eager, with_cpu, cpu_budget)
+                                   eager, with_cpu, cpu_budget, warmup_ms)
     res["inputs"] = ("K/V drawn on the device (torch generator, same distributions)"
                      if big else "K/V from the seeded host recipe")
     return res
@@ -829,6 +906,7 @@ def main():
         return
     print("[bench] stream-read ceiling", file=sys.stderr, flush=True)
     ceiling = read_ceiling(kvq, torch)
+    with_same_size_ceiling(kvq, torch, res)
 
     B, H, D = w.batch, w.heads, w.head_dim
     fused = ", true," in res["kernel"]
@@ -864,8 +942,11 @@ def main():
                      "avg_kernel_us": res["kernel_avg_us"],
                      "timing": res["timing"] + " / launches",
                      "algorithmic_bytes_per_launch": res.get("kernel_bytes_per_launch"),
-                     "frac_of_read_ceiling": achieved / ceiling["gbs"] if achieved else None},
+                     "frac_of_read_ceiling": achieved / ceiling["gbs"] if achieved else None,
+                     "frac_of_same_size_read_ceiling":
+                         res.get("kernel_frac_of_same_size_read_ceiling")},
         "read_ceiling": ceiling,
+        "read_ceiling_same_size": res.get("read_ceiling_same_size"),
         "step_us": res["step_us"],
         "step_us_sampling": res["step_us_sampling"],
         "eager": {"ms_per_step": res["eager_ms_per_step"], "gbs": res["eager_gbs"],
@@ -910,21 +991,20 @@ def main():
             if ow.decode_steps:
                 st, warm = 64 * 3, 64
             elif ow.layers > 1:
-                st, warm = max(5, min(args.steps, 20)), max(OTHER_MIN_WARMUP_LAYERED,
-                                                            min(args.warmup, 10))
+                st, warm = max(5, min(args.steps, 20)), max(2, min(args.warmup, 10))
             else:
-                st, warm = args.steps, max(args.warmup, OTHER_MIN_WARMUP)
+                st, warm = args.steps, args.warmup
             r = measure(kvq, torch, ow, st, warm, args.blocks_per_split,
                         separate=args.separate, eager=args.eager, with_cpu=with_cpu,
-                        cpu_budget=4.0)
-            others.append(r)
+                        cpu_budget=4.0, warmup_ms=WARMUP_MS_OTHERS)
+            others.append(with_same_size_ceiling(kvq, torch, r))
             torch.cuda.empty_cache()
         if not args.paged and w.layers == 1 and w.group == 1:
             print(f"[bench] {w.name} paged", file=sys.stderr, flush=True)
-            r = measure(kvq, torch, w, args.steps, max(args.warmup, OTHER_MIN_WARMUP),
-                        args.blocks_per_split, separate=args.separate, paged=True,
-                        eager=args.eager)
-            others.append(r)
+            r = measure(kvq, torch, w, args.steps, args.warmup, args.blocks_per_split,
+                        separate=args.separate, paged=True, eager=args.eager,
+                        warmup_ms=WARMUP_MS_OTHERS)
+            others.append(with_same_size_ceiling(kvq, torch, r))
             torch.cuda.empty_cache()
         result["workloads"] = others
     print(json.dumps(result), flush=True)
