@@ -19,7 +19,7 @@
 //   textbook scaled dot-product attention (Vaswani et al., 2017) over the dequantized
 //   cache, for one query token.
 //
-// Readings taken where the pages are silent or garbled (each listed in the design doc):
+// Readings taken where the pages are silent or garbled:
 //   * a block is 64 consecutive tokens of ONE (sequence, head) row, all head_dim
 //     channels together (the listing flattens heads, the prose says per block);
 //   * rounding is round-half-to-even (the listing's torch.round), never half-away;
