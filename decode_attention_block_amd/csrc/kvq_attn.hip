@@ -250,24 +250,30 @@ __device__ __forceinline__ int clamp_len(const AttnArgs& a, int len, int cap) {
   return len < 0 ? 0 : min(len, min(a.max_len, cap));
 }
 
-__device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int nb, int split, int cap) {
+// The batch's blocks T = sum_b ceil(len_b / 64) for the device plan, wave-uniform.
+// Every lane adds up the blocks of sequences lane, lane + 64, ..., then the wave
+// (binary32: exact up to 2^24 blocks, and beyond that rounded the same way in every
+// workgroup, which is all the plan needs: every workgroup of a row must find the same
+// n). The total is made wave-uniform explicitly (readfirstlane): left as a per-lane
+// value it would make the split bounds, and with them the streaming loop's trip count,
+// divergent for the compiler, which then rebuilds the loop around them (the 8K int4
+// attention measured 49.4 us instead of 41.8 us).
+__device__ __forceinline__ float batch_blocks(const AttnArgs& a, int cap) {
+  float t = 0.0f;
+  for (int i = threadIdx.x % kWave; i < a.batch; i += kWave)
+    t += static_cast<float>((clamp_len(a, a.seq_lens[i], cap) + kBlock - 1) / kBlock);
+  t = row16_sum_all(t);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t)));
+}
+
+// split_range with the batch's blocks t (batch_blocks; unused for a caller's plan).
+__device__ __forceinline__ SplitRange split_range_of(const AttnArgs& a, int nb, int split,
+                                                     float t) {
   SplitRange r;
   int piece = a.bps;
   if (a.bps > 0) {
     r.n = (nb + a.bps - 1) / a.bps;
   } else {
-    // Every lane adds up the blocks of sequences lane, lane + 64, ..., then the wave
-    // (binary32: exact up to 2^24 blocks, and beyond that rounded the same way in every
-    // workgroup, which is all the plan needs: every workgroup of a row must find the same
-    // n). The total is made wave-uniform explicitly (readfirstlane): left as a per-lane
-    // value it would make the split bounds, and with them the streaming loop's trip
-    // count, divergent for the compiler, which then rebuilds the loop around them (the
-    // 8K int4 attention measured 49.4 us instead of 41.8 us).
-    float t = 0.0f;
-    for (int i = threadIdx.x % kWave; i < a.batch; i += kWave)
-      t += static_cast<float>((clamp_len(a, a.seq_lens[i], cap) + kBlock - 1) / kBlock);
-    t = row16_sum_all(t);
-    t = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t)));
     const float chunk = fmaxf(ceilf(t * static_cast<float>(a.heads) /
                                     static_cast<float>(a.plan_target)), 1.0f);
     const float pieces = ceilf(static_cast<float>(nb) / chunk);
@@ -282,6 +288,44 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int nb, int
   r.begin = split * piece;
   r.end = min(r.begin + piece, nb);
   return r;
+}
+
+__device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int nb, int split, int cap) {
+  return split_range_of(a, nb, split, a.bps > 0 ? 0.0f : batch_blocks(a, cap));
+}
+
+// Which sequence's row a workgroup of split column 1 streams, in the automatic plan with
+// two split columns (rows that fill the GPU; a long row of a ragged batch is cut in
+// two). The dispatcher sends workgroup i to XCD i % 8 and fills each XCD's compute units
+// in turn, and a column of the grid is a whole number of such rounds, so workgroup
+// (h, b, 1) runs on the compute unit of (h, b, 0) (a placement probe on MI355X: all 256
+// of 256): both halves of a cut row would stream on one CU while the CUs of uncut rows
+// stream one piece. Column 1 therefore takes the second piece of sequence sigma(b) of
+// the same head (same XCD), where sigma pairs the sequences' first pieces in ascending
+// size with the second pieces in descending size (ties by index; rows not cut have an
+// empty second piece), computed from the lengths by every wave for batches of at most
+// 64 sequences (larger batches keep sigma(b) = b). sigma is a permutation, so every
+// second piece is streamed exactly once, whatever the placement.
+__device__ __forceinline__ int paired_sequence(const AttnArgs& a, int b, int cap, float t) {
+  if (a.batch > kWave) return b;
+  const int c = threadIdx.x % kWave;
+  int first = 0x7FFFFFFF, second = -1;
+  if (c < a.batch) {
+    const int nb = (clamp_len(a, a.seq_lens[c], cap) + kBlock - 1) / kBlock;
+    const SplitRange r = split_range_of(a, nb, 0, t);
+    first = r.end - r.begin;
+    second = r.n > 1 ? nb - first : 0;
+  }
+  int rank_first = 0, rank_second = 0;
+  for (int d = 0; d < a.batch; ++d) {
+    const int fd = __builtin_amdgcn_readlane(first, d);
+    const int sd = __builtin_amdgcn_readlane(second, d);
+    rank_first += fd < first || (fd == first && d < c);
+    rank_second += sd > second || (sd == second && d < c);
+  }
+  const int i = __builtin_amdgcn_readlane(rank_first, b);
+  const uint64_t m = __builtin_amdgcn_ballot_w64(c < a.batch && rank_second == i);
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(m)));
 }
 
 // End of a split: thread d < D holds channel d of the split's merged (unnormalised)
@@ -759,20 +803,24 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   __shared__ __align__(16) _Float16 xs[kAppend ? 2 * kBlock * D : 8];  // append staging
 
   const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  int b = blockIdx.y;
   const int split = blockIdx.z;
   const int cap = a.max_blocks * kBlock;
   StepLens sl = {0, 0, -1, 0};
   int len;
+  float plan_t = 0.0f;  // the batch's blocks (automatic plan)
   if constexpr (kAppend) {
     sl = step_lengths(a, b, cap);
     len = sl.len;
   } else {
+    if (a.bps == 0) plan_t = batch_blocks(a, cap);
+    if (a.bps == 0 && a.n_split == 2 && split == 1) b = paired_sequence(a, b, cap, plan_t);
     len = clamp_len(a, a.seq_lens[b], cap);
     sl.len_streamed = len;
   }
   const int nb = (len + kBlock - 1) / kBlock;
-  const SplitRange sr = split_range(a, nb, split, cap);
+  const SplitRange sr =
+      kAppend ? split_range(a, nb, split, cap) : split_range_of(a, nb, split, plan_t);
   const int blk_begin = sr.begin;
   if (!kAppend && blk_begin >= nb) {  // uniform over the workgroup
     // an empty row has no split to merge: in fused mode split 0 writes its zeros
@@ -1121,20 +1169,24 @@ attn_split_int4_kernel(AttnArgs a) {
   __shared__ __align__(16) _Float16 xs[kAppend ? 2 * kBlock * D : 8];  // append staging
 
   const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  int b = blockIdx.y;
   const int split = blockIdx.z;
   const int cap = a.max_blocks * kBlock;
   StepLens sl = {0, 0, -1, 0};
   int len;
+  float plan_t = 0.0f;  // the batch's blocks (automatic plan)
   if constexpr (kAppend) {
     sl = step_lengths(a, b, cap);
     len = sl.len;
   } else {
+    if (a.bps == 0) plan_t = batch_blocks(a, cap);
+    if (a.bps == 0 && a.n_split == 2 && split == 1) b = paired_sequence(a, b, cap, plan_t);
     len = clamp_len(a, a.seq_lens[b], cap);
     sl.len_streamed = len;
   }
   const int nb = (len + kBlock - 1) / kBlock;
-  const SplitRange sr = split_range(a, nb, split, cap);
+  const SplitRange sr =
+      kAppend ? split_range(a, nb, split, cap) : split_range_of(a, nb, split, plan_t);
   const int blk_begin = sr.begin;
   if (!kAppend && blk_begin >= nb) {  // uniform over the workgroup
     // an empty row has no split to merge: in fused mode split 0 writes its zeros

@@ -229,6 +229,40 @@ def test_automatic_plan_with_more_rows_than_cus(scheme):
     assert np.array_equal(out.cpu().numpy(), o)
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_automatic_plan_pairing_limit(B):
+    """Two split columns under the automatic plan with a ragged batch of 64 sequences
+    (the second pieces of cut rows are streamed by the workgroups of other sequences'
+    positions) and of 65 (each row's pieces by its own positions): within tolerance of
+    the oracle, and bitwise the split + combine of the same plan."""
+    import decode_attention_block_amd as kvq
+    import torch
+    H, S, D = 4, 600, 64
+    lens = np.random.default_rng(5 + B).integers(1, S + 1, B).astype(np.int32)
+    lens[[0, B - 1]] = (S, 1)
+    k, v, q, _ = _small_case(INT4, D, seed=37, B=B, H=H, S=S, lens=lens)
+    c = gpu_quantize(INT4, k, v, lens, 10)
+    L = int(lens.max())
+    assert kvq.decode_attn_plan(c, L) == (0, 2)
+    say("pairing limit", B)
+    sm = 0.125
+    qt = to_gpu(q)
+    ws = kvq.make_workspace(c, L)
+    out = torch.full_like(qt, 7.0)
+    kvq.decode_attn_qkv(c, qt, sm, out, ws, L)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    ref = oracle.attention(c.host_arrays(), q, lens, sm)
+    norm_err, _ = attn_errors(o, ref)
+    print(f"pairing limit B={B}: normwise {norm_err:.3e}")
+    assert norm_err <= ATTN_TOL
+    split = torch.full_like(qt, 7.0)
+    kvq.decode_attn_split(c, qt, sm, ws, L)
+    kvq.decode_attn_combine(c, split, ws, L)
+    torch.cuda.synchronize()
+    assert np.array_equal(split.cpu().numpy(), o)
+
+
 @pytest.mark.parametrize("lens", [(5, 70), (0, 0, 0), (0, 130, 0)])
 def test_lengths_below_the_launch_bound(lens):
     """max_len well above every length (the launch sizes for capacity, the rows are
