@@ -59,9 +59,11 @@ int n_blocks_for(int32_t len) { return (len + kBlockTokens - 1) / kBlockTokens; 
 // with one, 30.7 us with two). Long unbroken
 // runs of one row's codes stream from HBM faster than many short ones, and every extra
 // split costs a merge, so rows of equal length stay whole once they fill the GPU; the
-// host only bounds the pieces a row may take (the grid's split dimension): two once the
-// rows alone reach the target (a ragged batch cuts its long rows in two), else one more
-// than the splits that equal rows take (the target over the rows). Every column of the
+// host only bounds the pieces a row may take (the grid's split dimension): once the rows
+// alone reach the target, three (a ragged batch cuts its long rows in two or three, and
+// the device pairs the pieces of different rows on each compute unit) or two for
+// grouped-query rows, else one more than the splits that equal rows take (the target
+// over the rows). Every column of the
 // grid that no row uses still runs as workgroups that exit at once, which costs little
 // while they fit on the CUs beside the working ones and about 1 us where they wait for
 // them (8K grouped-query workload with twice the columns: 21.3 against 20.2 us).
@@ -74,7 +76,7 @@ int64_t plan_target(int group, int scheme) {
 int device_plan_splits(const kvq_cache* c, int nb, int group) {
   const int64_t rows = static_cast<int64_t>(c->batch) * c->heads;
   const int64_t target = plan_target(group, c->scheme);
-  const int64_t s = rows >= target ? 2 : (target + rows - 1) / rows + 1;
+  const int64_t s = rows >= target ? (group > 1 ? 2 : 3) : (target + rows - 1) / rows + 1;
   return static_cast<int>(s < nb ? s : nb);
 }
 

@@ -250,6 +250,11 @@ __device__ __forceinline__ int clamp_len(const AttnArgs& a, int len, int cap) {
   return len < 0 ? 0 : min(len, min(a.max_len, cap));
 }
 
+// Whether the rows alone reach the automatic plan's workgroup target.
+__device__ __forceinline__ bool fills_gpu(const AttnArgs& a) {
+  return static_cast<int64_t>(a.batch) * a.heads >= a.plan_target;
+}
+
 // The batch's blocks T = sum_b ceil(len_b / 64) for the device plan, wave-uniform.
 // Every lane adds up the blocks of sequences lane, lane + 64, ..., then the wave
 // (binary32: exact up to 2^24 blocks, and beyond that rounded the same way in every
@@ -274,9 +279,16 @@ __device__ __forceinline__ SplitRange split_range_of(const AttnArgs& a, int nb, 
   if (a.bps > 0) {
     r.n = (nb + a.bps - 1) / a.bps;
   } else {
-    const float chunk = fmaxf(ceilf(t * static_cast<float>(a.heads) /
-                                    static_cast<float>(a.plan_target)), 1.0f);
-    const float pieces = ceilf(static_cast<float>(nb) / chunk);
+    const float work = t * static_cast<float>(a.heads);
+    const float chunk = fmaxf(ceilf(work / static_cast<float>(a.plan_target)), 1.0f);
+    float pieces = ceilf(static_cast<float>(nb) / chunk);
+    // once the rows fill the GPU, a row that is cut at all is cut in pieces of about
+    // 1/(1.5 target) of the batch's blocks (up to the grid's three split columns), which
+    // the column pairing (paired_sequence) can spread over compute units more evenly
+    // than halves; rows of equal length stay whole as before
+    if (fills_gpu(a) && pieces > 1.0f)
+      pieces = ceilf(static_cast<float>(nb) /
+                     fmaxf(ceilf(work / (1.5f * static_cast<float>(a.plan_target))), 1.0f));
     const int n_max = static_cast<int>(fminf(pieces, static_cast<float>(a.n_split)));
     // equal pieces of ceil(nb / n_max) blocks; the count is recomputed from that size,
     // since n_max pieces of it may cover the row with fewer (11 blocks in at most 8
@@ -294,38 +306,59 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int nb, int
   return split_range_of(a, nb, split, a.bps > 0 ? 0.0f : batch_blocks(a, cap));
 }
 
-// Which sequence's row a workgroup of split column 1 streams, in the automatic plan with
-// two split columns (rows that fill the GPU; a long row of a ragged batch is cut in
-// two). The dispatcher sends workgroup i to XCD i % 8 and fills each XCD's compute units
-// in turn, and a column of the grid is a whole number of such rounds, so workgroup
-// (h, b, 1) runs on the compute unit of (h, b, 0) (a placement probe on MI355X: all 256
-// of 256): both halves of a cut row would stream on one CU while the CUs of uncut rows
-// stream one piece. Column 1 therefore takes the second piece of sequence sigma(b) of
-// the same head (same XCD), where sigma pairs the sequences' first pieces in ascending
-// size with the second pieces in descending size (ties by index; rows not cut have an
-// empty second piece), computed from the lengths by every wave for batches of at most
-// 64 sequences (larger batches keep sigma(b) = b). sigma is a permutation, so every
-// second piece is streamed exactly once, whatever the placement.
-__device__ __forceinline__ int paired_sequence(const AttnArgs& a, int b, int cap, float t) {
+// Which sequence's row a workgroup of split column z >= 1 streams, in the automatic plan
+// once the rows fill the GPU (the grid then has three split columns, and the long rows
+// of a ragged batch are cut in two or three pieces). The dispatcher sends workgroup i to
+// XCD i % 8 and fills each XCD's compute units in turn, and a column of the grid is a
+// whole number of such rounds, so workgroup (h, b, z) runs on the compute unit of
+// (h, b, 0) (a placement probe on MI355X: all 256 of 256 for z = 1): all pieces of a
+// cut row would stream on one CU while the CUs of uncut rows stream one. Column z
+// therefore takes piece z of sequence sigma_z(b) of the same head (same XCD): after
+// column 0 (each position its own first piece), sigma_z pairs the positions' loads so
+// far in ascending order with the sequences' z-th pieces in descending order (ties by
+// index; a row of fewer pieces has empty ones), computed from the lengths by every
+// wave for batches of at most 64 sequences (larger batches keep sigma_z(b) = b). Each
+// sigma_z is a permutation, so every piece is streamed exactly once whatever the
+// placement; only the balance depends on it.
+constexpr int kPairedColumns = 3;
+
+__device__ __forceinline__ int paired_sequence(const AttnArgs& a, int b, int z, int cap,
+                                               float t) {
   if (a.batch > kWave) return b;
   const int c = threadIdx.x % kWave;
-  int first = 0x7FFFFFFF, second = -1;
+  int piece[kPairedColumns] = {0, 0, 0};
   if (c < a.batch) {
     const int nb = (clamp_len(a, a.seq_lens[c], cap) + kBlock - 1) / kBlock;
     const SplitRange r = split_range_of(a, nb, 0, t);
-    first = r.end - r.begin;
-    second = r.n > 1 ? nb - first : 0;
+    const int size = r.end - r.begin;
+#pragma unroll
+    for (int k = 0; k < kPairedColumns; ++k)
+      piece[k] = k < r.n ? min(size, nb - k * size) : 0;
   }
-  int rank_first = 0, rank_second = 0;
-  for (int d = 0; d < a.batch; ++d) {
-    const int fd = __builtin_amdgcn_readlane(first, d);
-    const int sd = __builtin_amdgcn_readlane(second, d);
-    rank_first += fd < first || (fd == first && d < c);
-    rank_second += sd > second || (sd == second && d < c);
+  int load = c < a.batch ? piece[0] : 0x7FFFFFFF;
+#pragma unroll
+  for (int col = 1; col < kPairedColumns; ++col) {
+    const int pc = c < a.batch ? piece[col] : -1;
+    int rank_load = 0, rank_piece = 0;
+    for (int d = 0; d < a.batch; ++d) {
+      const int ld = __builtin_amdgcn_readlane(load, d);
+      const int pd = __builtin_amdgcn_readlane(pc, d);
+      rank_load += ld < load || (ld == load && d < c);
+      rank_piece += pd > pc || (pd == pc && d < c);
+    }
+    if (col == z) {
+      const int i = __builtin_amdgcn_readlane(rank_load, b);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(c < a.batch && rank_piece == i);
+      return __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(m)));
+    }
+    // position c takes the piece of the sequence whose piece rank equals its load rank
+    int add = 0;
+    for (int d = 0; d < a.batch; ++d)
+      if (__builtin_amdgcn_readlane(rank_piece, d) == rank_load)
+        add = __builtin_amdgcn_readlane(pc, d);
+    load += add;
   }
-  const int i = __builtin_amdgcn_readlane(rank_first, b);
-  const uint64_t m = __builtin_amdgcn_ballot_w64(c < a.batch && rank_second == i);
-  return __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(m)));
+  return b;
 }
 
 // End of a split: thread d < D holds channel d of the split's merged (unnormalised)
@@ -814,7 +847,8 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
     len = sl.len;
   } else {
     if (a.bps == 0) plan_t = batch_blocks(a, cap);
-    if (a.bps == 0 && a.n_split == 2 && split == 1) b = paired_sequence(a, b, cap, plan_t);
+    if (a.bps == 0 && a.n_split == kPairedColumns && fills_gpu(a) && split >= 1)
+      b = paired_sequence(a, b, split, cap, plan_t);
     len = clamp_len(a, a.seq_lens[b], cap);
     sl.len_streamed = len;
   }
@@ -1180,7 +1214,8 @@ attn_split_int4_kernel(AttnArgs a) {
     len = sl.len;
   } else {
     if (a.bps == 0) plan_t = batch_blocks(a, cap);
-    if (a.bps == 0 && a.n_split == 2 && split == 1) b = paired_sequence(a, b, cap, plan_t);
+    if (a.bps == 0 && a.n_split == kPairedColumns && fills_gpu(a) && split >= 1)
+      b = paired_sequence(a, b, split, cap, plan_t);
     len = clamp_len(a, a.seq_lens[b], cap);
     sl.len_streamed = len;
   }

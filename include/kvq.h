@@ -176,11 +176,13 @@ int kv_append(const kvq_cache* cache, const void* k_new, const void* v_new,
  * blocks are shared out in chunks of about 1/256 of them (1/512 for int4 grouped-query rows),
  * and a row is cut into ceil(its blocks / chunk) equal pieces, so equal rows that fill
  * the GPU stay whole and the long rows of a ragged batch are cut ([Pg1] chapter 1:
- * chunked attention as schedulable sub-blocks). Writes blocks_per_split_out (0 for the
+ * chunked attention as schedulable sub-blocks); once the rows fill the GPU, a row that
+ * is cut takes pieces of about 1/384 of the blocks instead, at most three. Writes blocks_per_split_out (0 for the
  * device's choice) and splits_per_row_out, the most splits a row may take for this
  * max_len (the workspace is sized for it): ceil(blocks / blocks_per_split), or for the
- * device's choice 2 once batch * heads reaches 256 (512 int4 grouped-query rows), else
- * one more than 256 / (batch * heads) (512 / ... for int4 grouped-query rows), never more than
+ * device's choice 3 once batch * heads reaches 256 (2 once grouped-query rows reach 512
+ * over int4, 256 over 8-bit caches), else one more than 256 / (batch * heads)
+ * (512 / ... for int4 grouped-query rows), never more than
  * the blocks. Host only. */
 int decode_attn_plan(const kvq_cache* cache, int32_t max_len, int32_t blocks_per_split,
                      int32_t* blocks_per_split_out, int32_t* splits_per_row_out);

@@ -231,8 +231,8 @@ def test_automatic_plan_with_more_rows_than_cus(scheme):
 
 @pytest.mark.parametrize("B", [64, 65])
 def test_automatic_plan_pairing_limit(B):
-    """Two split columns under the automatic plan with a ragged batch of 64 sequences
-    (the second pieces of cut rows are streamed by the workgroups of other sequences'
+    """Three split columns under the automatic plan with a ragged batch of 64 sequences
+    (the later pieces of cut rows are streamed by the workgroups of other sequences'
     positions) and of 65 (each row's pieces by its own positions): within tolerance of
     the oracle, and bitwise the split + combine of the same plan."""
     import decode_attention_block_amd as kvq
@@ -243,7 +243,7 @@ def test_automatic_plan_pairing_limit(B):
     k, v, q, _ = _small_case(INT4, D, seed=37, B=B, H=H, S=S, lens=lens)
     c = gpu_quantize(INT4, k, v, lens, 10)
     L = int(lens.max())
-    assert kvq.decode_attn_plan(c, L) == (0, 2)
+    assert kvq.decode_attn_plan(c, L) == (0, 3)
     say("pairing limit", B)
     sm = 0.125
     qt = to_gpu(q)
@@ -348,19 +348,21 @@ def test_device_plan_cuts_the_long_rows_of_a_full_batch(scheme):
     """blocks_per_split = 0 on 8 x 32 rows (the rows fill the GPU): each row's split is
     chosen on the device from all the lengths. With one long sequence (10 blocks) among
     one-block ones the batch holds 32 * 17 blocks, chunks of ceil(544 / 256) = 3 blocks,
-    so the long rows are cut into min(2, ceil(10 / 3)) = 2 pieces of 5 blocks and the
-    others stay whole: bitwise the output of the caller's plan of 5 blocks per split.
-    With all rows equal (10 blocks each) every row stays whole: bitwise the plan of 10.
-    Both within tolerance of the oracle."""
+    so the long rows are cut, in pieces of about ceil(544 / 384) = 2 blocks, at most 3:
+    3 pieces of ceil(10 / 3) = 4 blocks (4, 4, 2), and the others stay whole: bitwise
+    the output of the caller's plan of 4 blocks per split (the pieces of the cut rows
+    are streamed by the workgroups of other sequences' positions). With all rows equal
+    (10 blocks each) every row stays whole: bitwise the plan of 10. Both within
+    tolerance of the oracle."""
     import decode_attention_block_amd as kvq
     import torch
     B, H, D, S = 8, 32, 64, 640
-    for lens, same_as in (((64, 600, 64, 64, 64, 64, 64, 64), 5), ((600,) * 8, 10)):
+    for lens, same_as in (((64, 600, 64, 64, 64, 64, 64, 64), 4), ((600,) * 8, 10)):
         say("device plan", scheme, lens[:2], same_as)
         k, v, q, lens = _small_case(scheme, D, seed=31, B=B, H=H, S=S, lens=lens)
         c = gpu_quantize(scheme, k, v, lens, 10)
         L = int(lens.max())
-        assert kvq.decode_attn_plan(c, L) == (0, 2)
+        assert kvq.decode_attn_plan(c, L) == (0, 3)
         sm = float(np.float32(1) / np.sqrt(np.float32(D)))
         qt = to_gpu(q)
         outs = []
