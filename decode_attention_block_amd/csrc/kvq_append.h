@@ -410,20 +410,7 @@ __device__ __forceinline__ BlockScales append_row(const AppendArgs& a, int64_t r
 
 // ---- int4 tail block kept in registers (fused decode step) ---------------------------
 // One wave's view of an int4 block region: lane l holds chunk i (i < D/32) = bytes
-// ((i * 64) + l) * 16 .. +15, i.e. its matrix-core fragments. Dword f of the lane is
-// component f % 4 of chunk f / 4 (selected without indexing the array at run time).
-template <int N>
-__device__ __forceinline__ uint32_t get_dword(const uint4 (&r)[N], int f) {
-  uint32_t v = 0;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    v = f == 4 * i + 0 ? r[i].x : v;
-    v = f == 4 * i + 1 ? r[i].y : v;
-    v = f == 4 * i + 2 ? r[i].z : v;
-    v = f == 4 * i + 3 ? r[i].w : v;
-  }
-  return v;
-}
+// ((i * 64) + l) * 16 .. +15, i.e. its matrix-core fragments.
 
 // The new codes of one int4 tensor's open block, built in registers by one wave: r
 // receives chunk i (i < D/32) of the lane, i.e. bytes ((i * 64) + lane) * 16 .. +15 of

@@ -44,7 +44,6 @@ struct AGeo {
   static constexpr int kGroups = kWave / kLPT;      // tokens per wave-wide load
   static constexpr int kTPL = kLPT;                 // tokens per lane per block
   static constexpr int kDPL = SCHEME == KVQ_INT4_SYM ? 32 : 16;  // channels per lane
-  static constexpr int kWords = 4;                  // 32-bit words per 16-byte load
 };
 
 __device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }

@@ -75,7 +75,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-__device__ __forceinline__ float wave_min(float v) { return -wave_max(-v); }
 
 // ---- fp16 helpers -------------------------------------------------------------------
 __device__ __forceinline__ float h2f_lo(uint32_t w) {
@@ -123,7 +122,10 @@ __device__ __forceinline__ void uint8_scale_zero(float mn, float mx, float& s, f
 // |q - RN(x / s)| < 2^-22 |q|. When q lies farther than 2^-20 |q| from every decision
 // boundary, both round to the same code; otherwise the division is done. (q - rint(q) and
 // the distance to the boundary are exact by Sterbenz's lemma, and 2^-20 |q| is a
-// power-of-two scaling, so the test itself does not round.) The slow path is taken for
+// power-of-two scaling; the compiler may fuse q - rint(q) with the product into one
+// FMA, x * r - rint(q) rounded once, which moves the tested distance by at most
+// 2^-24 |q| + 2^-25: inside the 2^-20 |q| - 2^-22 |q| of slack wherever a boundary is
+// near, since there |q| >= 1/2.) The slow path is taken for
 // about one value in 10^5 and for a block's extreme element, whose quotient sits on a
 // boundary (7.5 for int4).
 struct Divisor {
@@ -139,28 +141,6 @@ __device__ __forceinline__ float rint_quotient_fast(float x, const Divisor& d, b
   return c;
 }
 
-// rint(RN(x / s)) (round half to even), s != 0.
-__device__ __forceinline__ float rint_quotient(float x, const Divisor& d) {
-  bool near = false;
-  const float c = rint_quotient_fast(x, d, near);
-  return near ? __builtin_rintf(x / d.s) : c;
-}
-
-// int4 code c = clamp(rint(x / s), -8, 7) (0 when s = 0), returned as the stored
-// offset-binary nibble c + 8.
-__device__ __forceinline__ uint32_t int4_code(float x, const Divisor& d) {
-  if (d.s == 0.0f) return 8u;
-  int c = static_cast<int>(rint_quotient(x, d));
-  c = c < -8 ? -8 : (c > 7 ? 7 : c);
-  return static_cast<uint32_t>(c + 8);
-}
-
-__device__ __forceinline__ uint32_t uint8_code(float x, const Divisor& d, int zpi) {
-  if (d.s == 0.0f) return 0u;
-  int c = static_cast<int>(rint_quotient(x, d)) + zpi;
-  c = c < 0 ? 0 : (c > 255 ? 255 : c);
-  return static_cast<uint32_t>(c);
-}
 
 // FP8 E4M3 (OCP "fn": bias 7, subnormals (m/8)*2^-6, largest finite 448 = code 0x7E):
 // s = absmax / 448 (0 for an all-zero block); the code of x is the E4M3 value nearest
