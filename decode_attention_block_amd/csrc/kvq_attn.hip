@@ -37,13 +37,16 @@ namespace {
 
 constexpr int kSplitWaves = 4;
 
+// Geometry of the vector-ALU kernel over the 8-bit caches (uint8, FP8): one code byte
+// per channel, natural order; the int4 cache has its own kernels (matrix cores).
 template <int SCHEME, int D>
 struct AGeo {
-  static constexpr int kRowBytes = SCHEME == KVQ_INT4_SYM ? D / 2 : D;  // bytes per token
+  static_assert(SCHEME != KVQ_INT4_SYM, "the int4 cache has its own kernels");
+  static constexpr int kRowBytes = D;               // bytes per token
   static constexpr int kLPT = kRowBytes / 16;       // lanes per token row
   static constexpr int kGroups = kWave / kLPT;      // tokens per wave-wide load
   static constexpr int kTPL = kLPT;                 // tokens per lane per block
-  static constexpr int kDPL = SCHEME == KVQ_INT4_SYM ? 32 : 16;  // channels per lane
+  static constexpr int kDPL = 16;                   // channels per lane
 };
 
 __device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
@@ -455,36 +458,14 @@ __device__ __forceinline__ float fma_h(_Float16 a, _Float16 b, float c) {
   return __builtin_fmaf(static_cast<float>(a), static_cast<float>(b), c);
 }
 
-// Partial dot product of one 16-byte code chunk (channels c0 .. c0+31 for int4,
-// c0 .. c0+15 for uint8 and FP8) with the lane's query, in units of the stored unsigned
-// code u (int4: u = c + 8; uint8: u = c; FP8: the code's value itself). Code and query
-// are both fp16 operands of v_fma_mix_f32 (FP8: binary32 values); the products are
-// exact in binary32.
+// Partial dot product of one 16-byte code chunk (channels c0 .. c0+15) with the lane's
+// query, in units of the stored code u (uint8: u = c, the zero point taken out per
+// score; FP8: the code's value itself). Code and query are both fp16 operands of
+// v_fma_mix_f32 (FP8: binary32 values); the products are exact in binary32.
 template <int SCHEME, int D>
 __device__ __forceinline__ float chunk_dot(const uint4& raw, const Query<SCHEME, D>& q) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  if constexpr (SCHEME == KVQ_INT4_SYM) {
-    float lo = 0.0f, hi = 0.0f;  // units 2^-24 (low nibbles) and 2^-20 (high nibbles)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t u = w[j];
-      const uint32_t u8 = u >> 8;
-      const half2_t p0 = as_h2(u & 0x000F000Fu);   // channels 0, 4
-      const half2_t p1 = as_h2(u & 0x00F000F0u);   // channels 1, 5
-      const half2_t p2 = as_h2(u8 & 0x000F000Fu);  // channels 2, 6
-      const half2_t p3 = as_h2(u8 & 0x00F000F0u);  // channels 3, 7
-      const int c = 8 * j;
-      lo = fma_h(p0.x, q.at(c + 0), lo);
-      hi = fma_h(p1.x, q.at(c + 1), hi);
-      lo = fma_h(p2.x, q.at(c + 2), lo);
-      hi = fma_h(p3.x, q.at(c + 3), hi);
-      lo = fma_h(p0.y, q.at(c + 4), lo);
-      hi = fma_h(p1.y, q.at(c + 5), hi);
-      lo = fma_h(p2.y, q.at(c + 6), lo);
-      hi = fma_h(p3.y, q.at(c + 7), hi);
-    }
-    return __builtin_fmaf(hi, 1048576.0f, lo * 16777216.0f);
-  } else if constexpr (SCHEME == KVQ_FP8_E4M3) {
+  if constexpr (SCHEME == KVQ_FP8_E4M3) {
     // the hardware decodes E4M3 codes to binary32 exactly, two per instruction
     float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
@@ -514,36 +495,16 @@ __device__ __forceinline__ float chunk_dot(const uint4& raw, const Query<SCHEME,
   }
 }
 
-// o[k] += p * c_k for the 16-byte code chunk, c = u - offset. The offset is taken out
-// of each fp16 pair with one packed fp16 add before the binary32 FMA, so a heavily
-// weighted token whose codes sit at the offset adds (almost) nothing instead of two
-// large terms that cancel later. off_lo / off_hi: the pair (-offset * unit) for the
-// 2^-24 and 2^-20 unit positions (int4: exact; uint8: exact while |u - zp| < 2048,
-// else rounded to fp16, a 2^-11 relative error on a term that then dominates).
+// o[k] += p * c_k for the 16-byte code chunk, c = u - offset. The offset (the uint8 zero
+// point) is taken out of each fp16 pair with one packed fp16 add before the binary32 FMA,
+// so a heavily weighted token whose codes sit at the offset adds (almost) nothing
+// instead of two large terms that cancel later. off: the pair (-zp * 2^-24) (exact while
+// |u - zp| < 2048, else rounded to fp16, a 2^-11 relative error on a term that then
+// dominates).
 template <int SCHEME>
-__device__ __forceinline__ void chunk_axpy(const uint4& raw, float p, half2_t off_lo,
-                                           half2_t off_hi, float* o) {
+__device__ __forceinline__ void chunk_axpy(const uint4& raw, float p, half2_t off, float* o) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  if constexpr (SCHEME == KVQ_INT4_SYM) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t u = w[j];
-      const uint32_t u8 = u >> 8;
-      const half2_t p0 = as_h2(u & 0x000F000Fu) + off_lo;   // channels 0, 4   (2^-24)
-      const half2_t p1 = as_h2(u & 0x00F000F0u) + off_hi;   // channels 1, 5   (2^-20)
-      const half2_t p2 = as_h2(u8 & 0x000F000Fu) + off_lo;  // channels 2, 6   (2^-24)
-      const half2_t p3 = as_h2(u8 & 0x00F000F0u) + off_hi;  // channels 3, 7   (2^-20)
-      float* oj = o + 8 * j;
-      oj[0] = __builtin_fmaf(static_cast<float>(p0.x), p, oj[0]);
-      oj[4] = __builtin_fmaf(static_cast<float>(p0.y), p, oj[4]);
-      oj[1] = __builtin_fmaf(static_cast<float>(p1.x), p, oj[1]);
-      oj[5] = __builtin_fmaf(static_cast<float>(p1.y), p, oj[5]);
-      oj[2] = __builtin_fmaf(static_cast<float>(p2.x), p, oj[2]);
-      oj[6] = __builtin_fmaf(static_cast<float>(p2.y), p, oj[6]);
-      oj[3] = __builtin_fmaf(static_cast<float>(p3.x), p, oj[3]);
-      oj[7] = __builtin_fmaf(static_cast<float>(p3.y), p, oj[7]);
-    }
-  } else if constexpr (SCHEME == KVQ_FP8_E4M3) {
+  if constexpr (SCHEME == KVQ_FP8_E4M3) {
     // FP8 codes carry no offset and decode exactly to binary32
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -558,8 +519,8 @@ __device__ __forceinline__ void chunk_axpy(const uint4& raw, float p, half2_t of
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const half2_t e = as_h2(w[j] & 0x00FF00FFu) + off_lo;         // channels 0, 2
-      const half2_t f = as_h2((w[j] >> 8) & 0x00FF00FFu) + off_lo;  // channels 1, 3
+      const half2_t e = as_h2(w[j] & 0x00FF00FFu) + off;         // channels 0, 2
+      const half2_t f = as_h2((w[j] >> 8) & 0x00FF00FFu) + off;  // channels 1, 3
       float* oj = o + 4 * j;
       oj[0] = __builtin_fmaf(static_cast<float>(e.x), p, oj[0]);
       oj[2] = __builtin_fmaf(static_cast<float>(e.y), p, oj[2]);
@@ -930,7 +891,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   auto block_weights = [&](int blk, float kscale, float kzero, const uint4 (&kr)[TPL],
                            float (&p)[TPL]) {
     const float sk = kscale * a.qk_scale;
-    const float offset = SCHEME == KVQ_INT4_SYM ? 8.0f : SCHEME == KVQ_UINT8_ASYM ? kzero : 0.0f;
+    const float offset = SCHEME == KVQ_UINT8_ASYM ? kzero : 0.0f;
     const float bias_k = offset * qsum_row;
     float s[TPL];
 #pragma unroll
@@ -979,17 +940,10 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
       }
     }
     const float sv = vscale;
-    half2_t off_lo, off_hi;
-    if constexpr (SCHEME == KVQ_INT4_SYM) {
-      off_lo = as_h2(0x80088008u);  // -8 * 2^-24 in both halves
-      off_hi = as_h2(0x80808080u);  // -8 * 2^-20 = -128 * 2^-24
-    } else {
-      const _Float16 zh = static_cast<_Float16>(vzero * -5.9604644775390625e-08f);
-      off_lo = half2_t{zh, zh};
-      off_hi = off_lo;
-    }
+    const _Float16 zh = static_cast<_Float16>(vzero * -5.9604644775390625e-08f);
+    const half2_t off = half2_t{zh, zh};
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) chunk_axpy<SCHEME>(vr[i], p[i] * sv, off_lo, off_hi, o);
+    for (int i = 0; i < TPL; ++i) chunk_axpy<SCHEME>(vr[i], p[i] * sv, off, o);
   };
 
   float p[TPL];
@@ -1057,8 +1011,7 @@ __global__ __launch_bounds__((kAppend ? kStepWaves : kSplitWaves) * kWave) void 
   // Per-lane result in true units: o_true[k] = o[k] * unit(k).
 #pragma unroll
   for (int k = 0; k < DPL; ++k) {
-    float unit = SCHEME == KVQ_FP8_E4M3 ? 1.0f : 16777216.0f;
-    if constexpr (SCHEME == KVQ_INT4_SYM) unit = (k & 1) ? 1048576.0f : 16777216.0f;
+    const float unit = SCHEME == KVQ_FP8_E4M3 ? 1.0f : 16777216.0f;
     red_o[wave][lane][k] = o[k] * unit;
   }
   red_l[wave][lane] = l;
