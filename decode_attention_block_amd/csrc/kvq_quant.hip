@@ -47,7 +47,15 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(QuantArgs a) 
 
   uint4 raw[G::kPasses];
   float x[G::kPasses][8];
-  float amax = 0.0f, mn = __builtin_inff(), mx = -__builtin_inff();
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  float amax = 0.0f;
+  // int4 takes its absmax on the fp16 bit patterns: with the sign bit cleared, the
+  // patterns of finite values order as unsigned integers the way the values do, two per
+  // packed max, and tokens past the block's end load as zeros, which cannot raise it;
+  // its codes are taken from the values staged in LDS, so no binary32 copy of the
+  // inputs is made here. (FP8 and uint8 need that copy for their codes and reduce it.)
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 amax_bits = {0, 0};
 #pragma unroll
   for (int p = 0; p < G::kPasses; ++p) {
     const int t = p * G::kTokensPerPass + tr;
@@ -60,10 +68,16 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(QuantArgs a) 
       r4 = __builtin_nontemporal_load(
           reinterpret_cast<const v4u*>(src + static_cast<int64_t>(t) * a.stride_t));
     raw[p] = make_uint4(r4.x, r4.y, r4.z, r4.w);
-    unpack8(raw[p], x[p]);
+    if constexpr (SCHEME != KVQ_INT4_SYM) unpack8(raw[p], x[p]);
     if constexpr (SCHEME == KVQ_INT4_SYM)
       *reinterpret_cast<uint4*>(xs + t * D + chunk * 8) = raw[p];
-    if (valid) {
+    if constexpr (SCHEME == KVQ_INT4_SYM) {
+      const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        amax_bits = __builtin_elementwise_max(
+            amax_bits, __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu));
+    } else if (valid) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         amax = fmaxf(amax, fabsf(x[p][i]));
@@ -71,6 +85,10 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(QuantArgs a) 
         mx = fmaxf(mx, x[p][i]);
       }
     }
+  }
+  if constexpr (SCHEME == KVQ_INT4_SYM) {
+    const unsigned short bits = amax_bits.x > amax_bits.y ? amax_bits.x : amax_bits.y;
+    amax = static_cast<float>(__builtin_bit_cast(_Float16, bits));
   }
 
   float s, zp = 0.0f;
