@@ -200,23 +200,38 @@ __device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], const Divisor& 
 
 // 8 values -> 4 bytes of int4 nibbles c + 8 (x[i] in bits 4i .. 4i+3; for 8 consecutive
 // channels: channel 2k in the low nibble of byte k).
+// The quotient q = RN(x * r) is clamped to [-8, 7] first (rounding and a clamp to
+// integer bounds commute, and above 7 or below -8 every quotient near q gives the same
+// clamped code), then added to 1.5 * 2^23 + 8: in that binade the ulp is 1, so the add
+// rounds to the nearest integer with ties to even (1.5 * 2^23 + 8 is even), t =
+// 1.5 * 2^23 + 8 + rint(qc) exactly, and the low byte of t's bit pattern is the nibble
+// rint(qc) + 8 (the constant's low 22 bits are zero). t - (1.5 * 2^23 + 8) = rint(qc)
+// and qc - rint(qc) are exact (Sterbenz), and a block's quotients satisfy
+// |q| <= 7.5 (1 + 2^-22), so the test |qc - rint(qc)| < 1/2 - 2^-17 keeps q farther
+// than 2^-20 |q| from every boundary, as the division-free rule above requires.
 __device__ __forceinline__ uint32_t pack_int4x8(const float (&x)[8], const Divisor& d) {
   if (d.s == 0.0f) return 0x88888888u;
-  float c[8];
+  constexpr float kMagic = 12582920.0f;  // 1.5 * 2^23 + 8
+  float t[8];
   bool near = false;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = rint_quotient_fast(x[i], d, near);
+  for (int i = 0; i < 8; ++i) {
+    const float qc = __builtin_amdgcn_fmed3f(x[i] * d.r, -8.0f, 7.0f);
+    t[i] = qc + kMagic;
+    near |= !(fabsf(qc - (t[i] - kMagic)) < 0.5f - 0x1p-17f);
+  }
   if (near) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = __builtin_rintf(x[i] / d.s);
+    for (int i = 0; i < 8; ++i)
+      t[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(x[i] / d.s), -8.0f, 7.0f) + kMagic;
   }
-  uint32_t w = 0;
+  uint32_t b[4];  // byte k in the low 8 bits of b[k]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float v = __builtin_fminf(__builtin_fmaxf(c[i], -8.0f), 7.0f) + 8.0f;  // exact
-    w |= static_cast<uint32_t>(v) << (4 * i);
-  }
-  return w;
+  for (int k = 0; k < 4; ++k)
+    b[k] = (__builtin_bit_cast(uint32_t, t[2 * k + 1]) << 4) |
+           __builtin_bit_cast(uint32_t, t[2 * k]);
+  return __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) |
+         __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
 }
 
 // 8 values -> 8 bytes of uint8 codes (x[i] in byte i).
