@@ -83,12 +83,15 @@ __device__ __forceinline__ uint32_t int4_fragment_word(const _Float16* xs, int n
                                                        const Divisor& s, bool is_v, int lane,
                                                        int f) {
   constexpr int KS = D / 32;  // 32-channel K steps
-  float x[8];
+  _Float16 x[8];
   uint32_t mask = 0xFFFFFFFFu;
   if (!is_v) {
     const int t = 16 * (f / KS) + lane % 16;
     if (t >= ntok) return 0u;
-    unpack8(*reinterpret_cast<const uint4*>(xs + t * D + 32 * (f % KS) + 8 * (lane / 16)), x);
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const h8 v = *reinterpret_cast<const h8*>(xs + t * D + 32 * (f % KS) + 8 * (lane / 16));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = v[q];
   } else {
     const int d = 16 * (f / 2) + lane % 16;
     const int t0 = 32 * (f % 2) + 8 * (lane / 16);
@@ -96,7 +99,7 @@ __device__ __forceinline__ uint32_t int4_fragment_word(const _Float16* xs, int n
     if (n <= 0) return 0u;
     if (n < 8) mask = (1u << (4 * n)) - 1u;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) x[q] = static_cast<float>(xs[(t0 + q) * D + d]);
+    for (int q = 0; q < 8; ++q) x[q] = xs[(t0 + q) * D + d];
   }
   return pack_int4x8(x, s) & mask;
 }

@@ -209,21 +209,28 @@ __device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], const Divisor& 
 // and qc - rint(qc) are exact (Sterbenz), and a block's quotients satisfy
 // |q| <= 7.5 (1 + 2^-22), so the test |qc - rint(qc)| < 1/2 - 2^-17 keeps q farther
 // than 2^-20 |q| from every boundary, as the division-free rule above requires.
-__device__ __forceinline__ uint32_t pack_int4x8(const float (&x)[8], const Divisor& d) {
+// T: float, or _Float16 (the product then takes the fp16 operand as it is, one
+// mixed-precision FMA with a +0 addend: the same rounding decision on q, and a zero
+// product of either sign gives code 8).
+template <class T>
+__device__ __forceinline__ uint32_t pack_int4x8(const T (&x)[8], const Divisor& d) {
   if (d.s == 0.0f) return 0x88888888u;
   constexpr float kMagic = 12582920.0f;  // 1.5 * 2^23 + 8
   float t[8];
   bool near = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float qc = __builtin_amdgcn_fmed3f(x[i] * d.r, -8.0f, 7.0f);
+    const float q = __builtin_fmaf(static_cast<float>(x[i]), d.r, 0.0f);
+    const float qc = __builtin_amdgcn_fmed3f(q, -8.0f, 7.0f);
     t[i] = qc + kMagic;
     near |= !(fabsf(qc - (t[i] - kMagic)) < 0.5f - 0x1p-17f);
   }
   if (near) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      t[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(x[i] / d.s), -8.0f, 7.0f) + kMagic;
+      t[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(static_cast<float>(x[i]) / d.s), -8.0f,
+                                     7.0f) +
+             kMagic;
   }
   uint32_t b[4];  // byte k in the low 8 bits of b[k]
 #pragma unroll
