@@ -58,8 +58,8 @@ struct QGeo {
   static constexpr int kRowBytes = SCHEME == KVQ_INT4_SYM ? D / 2 : D;
 };
 
-template <int SCHEME, int D>
-__device__ __forceinline__ void store_codes(uint8_t* token_row, int chunk, const float (&x)[8],
+template <int SCHEME, int D, class T>
+__device__ __forceinline__ void store_codes(uint8_t* token_row, int chunk, const T (&x)[8],
                                             const Divisor& s, int zpi, bool valid) {
   if constexpr (SCHEME == KVQ_INT4_SYM) {
     const uint32_t w = valid ? pack_int4x8(x, s) : 0u;

@@ -176,13 +176,20 @@ __device__ __forceinline__ uint2 fp8_codes8(const float (&q)[8]) {
   return make_uint2(static_cast<uint32_t>(w0), static_cast<uint32_t>(w1));
 }
 
-// 8 values -> 8 bytes of FP8 codes (x[i] in byte i).
-__device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], const Divisor& d) {
+// 8 values -> 8 bytes of FP8 codes (x[i] in byte i). T: float, or _Float16 (the
+// quotient then takes the fp16 operand as it is, as in pack_int4x8, but with a -0
+// addend: fma(x, r, -0) = RN(x * r) with the product's sign, which the code keeps; the
+// addend is hidden from the compiler, which would otherwise turn the FMA back into a
+// multiply of the converted value).
+template <class T>
+__device__ __forceinline__ uint2 pack_fp8x8(const T (&x)[8], const Divisor& d) {
   if (d.s == 0.0f) return make_uint2(0u, 0u);
+  float neg_zero = -0.0f;
+  asm("" : "+v"(neg_zero));
   float lo[8], hi[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float q = x[i] * d.r;
+    const float q = __builtin_fmaf(static_cast<float>(x[i]), d.r, neg_zero);
     lo[i] = fp8_clamp(q * (1.0f - 0x1p-21f));
     hi[i] = fp8_clamp(q * (1.0f + 0x1p-21f));
   }
@@ -191,7 +198,7 @@ __device__ __forceinline__ uint2 pack_fp8x8(const float (&x)[8], const Divisor& 
   if (a.x == b.x && a.y == b.y) return a;
   float q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = fp8_clamp(x[i] / d.s);
+  for (int i = 0; i < 8; ++i) q[i] = fp8_clamp(static_cast<float>(x[i]) / d.s);
   return fp8_codes8(q);
 }
 
@@ -241,25 +248,59 @@ __device__ __forceinline__ uint32_t pack_int4x8(const T (&x)[8], const Divisor& 
          __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
 }
 
-// 8 values -> 8 bytes of uint8 codes (x[i] in byte i).
-__device__ __forceinline__ uint2 pack_uint8x8(const float (&x)[8], const Divisor& d, int zpi) {
+// 8 values -> 8 bytes of uint8 codes (x[i] in byte i). T as for pack_int4x8.
+// The code clamp(rint(q) + zp, 0, 255) is taken as in pack_int4x8: q is clamped to
+// [-zp, 255 - zp] (integer bounds), then added to 1.5 * 2^23 + zp, exact for |zp| <
+// 2^21 (fp16 inputs give |zp| <= 255 * 2^11), whose sum is 1.5 * 2^23 + zp + rint(qc)
+// with rint(qc) + zp in the low byte. Where 1.5 * 2^23 + zp is odd a tie would round
+// the other way, but a tie is always near and recomputed. The distance test is the
+// relative one above, 2^-20 |qc| (|qc| <= |q| where q is not clamped, and a clamped q
+// gives a code no nearby quotient changes).
+template <class T>
+__device__ __forceinline__ uint2 pack_uint8x8(const T (&x)[8], const Divisor& d, int zpi) {
   if (d.s == 0.0f) return make_uint2(0u, 0u);
-  float c[8];
-  bool near = false;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = rint_quotient_fast(x[i], d, near);
-  if (near) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = __builtin_rintf(x[i] / d.s);
-  }
   uint32_t b[8];
+  if (zpi > -(1 << 21) && zpi < (1 << 21)) {  // uniform over the block
+    const float zp = static_cast<float>(zpi);
+    const float magic = 12582912.0f + zp;  // 1.5 * 2^23 + zp
+    float t[8];
+    bool near = false;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int v = static_cast<int>(c[i]) + zpi;
-    b[i] = static_cast<uint32_t>(v < 0 ? 0 : (v > 255 ? 255 : v));
+    for (int i = 0; i < 8; ++i) {
+      const float q = __builtin_fmaf(static_cast<float>(x[i]), d.r, 0.0f);
+      const float qc = __builtin_amdgcn_fmed3f(q, -zp, 255.0f - zp);
+      t[i] = qc + magic;
+      near |= !(__builtin_fmaf(fabsf(qc), 0x1p-20f, fabsf(qc - (t[i] - magic))) < 0.5f);
+    }
+    if (near) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        t[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(static_cast<float>(x[i]) / d.s), -zp,
+                                       255.0f - zp) +
+               magic;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = __builtin_bit_cast(uint32_t, t[i]);
+  } else {
+    float c[8];
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = rint_quotient_fast(static_cast<float>(x[i]), d, near);
+    if (near) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = __builtin_rintf(static_cast<float>(x[i]) / d.s);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int v = static_cast<int>(c[i]) + zpi;
+      b[i] = static_cast<uint32_t>(v < 0 ? 0 : (v > 255 ? 255 : v));
+    }
   }
-  return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                    b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+  // byte i of the result = the low byte of b[i]
+  return make_uint2(__builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) |
+                        __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu),
+                    __builtin_amdgcn_perm(b[5], b[4], 0x0C0C0400u) |
+                        __builtin_amdgcn_perm(b[7], b[6], 0x04000C0Cu));
 }
 
 // ---- int4 cache block layout ---------------------------------------------------------

@@ -46,49 +46,57 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(QuantArgs a) 
                         static_cast<int64_t>(j) * kBlock * a.stride_t + chunk * 8;
 
   uint4 raw[G::kPasses];
-  float x[G::kPasses][8];
-  float mn = __builtin_inff(), mx = -__builtin_inff();
-  float amax = 0.0f;
-  // int4 takes its absmax on the fp16 bit patterns: with the sign bit cleared, the
-  // patterns of finite values order as unsigned integers the way the values do, two per
-  // packed max, and tokens past the block's end load as zeros, which cannot raise it;
-  // its codes are taken from the values staged in LDS, so no binary32 copy of the
-  // inputs is made here. (FP8 and uint8 need that copy for their codes and reduce it.)
+  // The block statistics are taken on the fp16 values as loaded, with no binary32 copy
+  // of them: the absmax schemes (int4, FP8) on the bit patterns (with the sign bit
+  // cleared, the patterns of finite values order as unsigned integers the way the
+  // values do, two per packed max; tokens past the block's end load as zeros, which
+  // cannot raise it), uint8 with packed fp16 min and max over the tokens that exist.
+  // The codes take the fp16 values as operands (int4: staged in LDS first).
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   u16x2 amax_bits = {0, 0};
+  h2 mn2 = {__builtin_inff16(), __builtin_inff16()};
+  h2 mx2 = {-__builtin_inff16(), -__builtin_inff16()};
+  // All of the thread's loads are requested before any is used (a use between them made
+  // the compiler wait for each load before requesting the next).
 #pragma unroll
   for (int p = 0; p < G::kPasses; ++p) {
     const int t = p * G::kTokensPerPass + tr;
-    const bool valid = t < ntok;
     // the fp16 inputs are read once: non-temporal loads (8K workload, all blocks: uint8
     // 384 -> 326 us, FP8 464 -> 456 us, int4 unchanged at about 340 us)
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
     v4u r4 = {0u, 0u, 0u, 0u};
-    if (valid)
+    if (t < ntok)
       r4 = __builtin_nontemporal_load(
           reinterpret_cast<const v4u*>(src + static_cast<int64_t>(t) * a.stride_t));
     raw[p] = make_uint4(r4.x, r4.y, r4.z, r4.w);
-    if constexpr (SCHEME != KVQ_INT4_SYM) unpack8(raw[p], x[p]);
+  }
+#pragma unroll
+  for (int p = 0; p < G::kPasses; ++p) {
+    const int t = p * G::kTokensPerPass + tr;
     if constexpr (SCHEME == KVQ_INT4_SYM)
       *reinterpret_cast<uint4*>(xs + t * D + chunk * 8) = raw[p];
-    if constexpr (SCHEME == KVQ_INT4_SYM) {
-      const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+    const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+    if constexpr (SCHEME != KVQ_UINT8_ASYM) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         amax_bits = __builtin_elementwise_max(
             amax_bits, __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu));
-    } else if (valid) {
+    } else if (t < ntok) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        amax = fmaxf(amax, fabsf(x[p][i]));
-        mn = fminf(mn, x[p][i]);
-        mx = fmaxf(mx, x[p][i]);
+      for (int k = 0; k < 4; ++k) {
+        mn2 = __builtin_elementwise_min(mn2, __builtin_bit_cast(h2, w[k]));
+        mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(h2, w[k]));
       }
     }
   }
-  if constexpr (SCHEME == KVQ_INT4_SYM) {
+  float amax = 0.0f, mn = 0.0f, mx = 0.0f;
+  if constexpr (SCHEME != KVQ_UINT8_ASYM) {
     const unsigned short bits = amax_bits.x > amax_bits.y ? amax_bits.x : amax_bits.y;
     amax = static_cast<float>(__builtin_bit_cast(_Float16, bits));
+  } else {
+    mn = fminf(static_cast<float>(mn2.x), static_cast<float>(mn2.y));
+    mx = fmaxf(static_cast<float>(mx2.x), static_cast<float>(mx2.y));
   }
 
   float s, zp = 0.0f;
@@ -113,7 +121,12 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(QuantArgs a) 
 #pragma unroll
     for (int p = 0; p < G::kPasses; ++p) {
       const int t = p * G::kTokensPerPass + tr;
-      store_codes<SCHEME, D>(codes + t * G::kRowBytes, chunk, x[p], dv, zpi, t < ntok);
+      typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+      const h8 v = __builtin_bit_cast(h8, raw[p]);
+      _Float16 xh[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xh[i] = v[i];
+      store_codes<SCHEME, D>(codes + t * G::kRowBytes, chunk, xh, dv, zpi, t < ntok);
     }
   }
   if (tid == 0) {
