@@ -263,22 +263,26 @@ __device__ __forceinline__ uint2 pack_uint8x8(const T (&x)[8], const Divisor& d,
   if (zpi > -(1 << 21) && zpi < (1 << 21)) {  // uniform over the block
     const float zp = static_cast<float>(zpi);
     const float magic = 12582912.0f + zp;  // 1.5 * 2^23 + zp
+    // Each value is divided out on its own where it is near: fp16 inputs put quotients
+    // on a rounding boundary far more often than random values would (a quotient
+    // 255 x / (max - min) of two fp16 values is often exactly a half-integer), and a
+    // branch over all 8 values made the whole wave divide all 8 whenever one lane had
+    // one near value.
     float t[8];
-    bool near = false;
+    bool near[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float q = __builtin_fmaf(static_cast<float>(x[i]), d.r, 0.0f);
       const float qc = __builtin_amdgcn_fmed3f(q, -zp, 255.0f - zp);
       t[i] = qc + magic;
-      near |= !(__builtin_fmaf(fabsf(qc), 0x1p-20f, fabsf(qc - (t[i] - magic))) < 0.5f);
+      near[i] = !(__builtin_fmaf(fabsf(qc), 0x1p-20f, fabsf(qc - (t[i] - magic))) < 0.5f);
     }
-    if (near) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
+      if (near[i])
         t[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(static_cast<float>(x[i]) / d.s), -zp,
                                        255.0f - zp) +
                magic;
-    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) b[i] = __builtin_bit_cast(uint32_t, t[i]);
   } else {
