@@ -183,3 +183,37 @@ def test_fp8_rounding_ties_subnormals_saturation_bitexact(D):
         lens = lens + 1
         torch.cuda.synchronize()
         assert_cache_equal(c.host_arrays(), oracle_cache(FP8, k, v, lens, MB), lens)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_uint8_zero_points_outside_the_code_range_bitexact(D):
+    """uint8 blocks whose values all lie on one side of zero, so that the zero point
+    falls outside 0..255 and the codes are clamp(rint(x / s) + zp) with |zp| large:
+    values in {1000, 1000.5} (s = 0.5 / 255, zp = -510000), in [100, 110] (zp about
+    -2550), in [-20, -10] (zp about 510), and a block mixing one such value with normal
+    ones. Prefill, then kv_append token by token across a block boundary, bit-exact
+    against the oracle after every step."""
+    import decode_attention_block_amd as kvq
+    import torch
+    say("uint8 zero points", D)
+    rs = np.random.default_rng(400 + D)
+    B, S = 4, 80
+    k = np.empty((B, S, 1, D), np.float16)
+    k[0] = (1000 + 0.5 * rs.integers(0, 2, (S, 1, D))).astype(np.float16)
+    k[1] = rs.uniform(100, 110, (S, 1, D)).astype(np.float16)
+    k[2] = rs.uniform(-20, -10, (S, 1, D)).astype(np.float16)
+    k[3] = rs.standard_normal((S, 1, D)).astype(np.float16)
+    k[3, 5, 0, 7] = np.float16(60000)
+    v = np.ascontiguousarray(k[::-1])
+    lens = np.array([60, 64, 63, 1], np.int32)
+    MB = 2
+    c = gpu_quantize(UINT8, k, v, lens, MB)
+    assert_cache_equal(c.host_arrays(), oracle_cache(UINT8, k, v, lens, MB), lens)
+    zero = c.host_arrays()["k_zero"]
+    assert zero.min() < -500000 and zero.max() > 255
+    for step in range(6):
+        kvq.kv_append(c, to_gpu(k[np.arange(B), lens]), to_gpu(v[np.arange(B), lens]),
+                      int(lens.max()) + 1)
+        lens = lens + 1
+        torch.cuda.synchronize()
+        assert_cache_equal(c.host_arrays(), oracle_cache(UINT8, k, v, lens, MB), lens)
