@@ -132,6 +132,32 @@ def test_append_at_capacity_leaves_row_unchanged():
     assert np.array_equal(after["k_scale"][0], before["k_scale"][0])
 
 
+@pytest.mark.parametrize("scheme", [INT4, UINT8])
+def test_append_with_255_heads_counts_every_arrival(scheme):
+    """kv_append on 255 heads (the most the arrival count in the top 8 bits of a length
+    can count: every head's workgroup adds 1 << 24, the 255th stores the new length):
+    lengths of 3 sequences, one at capacity, across a block boundary, 5 calls in a row;
+    after each the lengths and the whole cache equal the oracle's."""
+    import decode_attention_block_amd as kvq
+    import torch
+    say("append 255 heads", scheme)
+    B, H, D, MB = 3, 255, 64, 2
+    rs = np.random.default_rng(17 + scheme)
+    S = 128
+    k = rs.standard_normal((B, S, H, D)).astype(np.float16)
+    v = rs.standard_normal((B, S, H, D)).astype(np.float16)
+    lens = np.array([62, 128, 5], np.int32)            # sequence 1 at capacity
+    c = gpu_quantize(scheme, k, v, lens, MB)
+    for step in range(5):
+        kn = np.ascontiguousarray(k[np.arange(B), np.minimum(lens, S - 1)])
+        vn = np.ascontiguousarray(v[np.arange(B), np.minimum(lens, S - 1)])
+        kvq.kv_append(c, to_gpu(kn), to_gpu(vn), int(lens.max()))
+        torch.cuda.synchronize()
+        lens = np.minimum(lens + 1, S).astype(np.int32)
+        assert list(c.seq_lens.cpu().numpy()) == lens.tolist()
+        assert_cache_equal(c.host_arrays(), oracle_cache(scheme, k, v, lens, MB), lens)
+
+
 def _fp8_rounding_history(D, rs):
     """[2][S=160][H=4][D] fp16 values whose blocks have power-of-two FP8 scales
     (absmax 448 * 2^k, so x / s is exact): every halfway point between neighbouring
