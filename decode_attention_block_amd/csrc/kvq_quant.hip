@@ -10,8 +10,10 @@
 // One 256-thread workgroup owns one 64-token block of one (sequence, head, K|V) row.
 // Each thread holds 8 channels of one token per 16-byte load, so every wave-wide load
 // instruction reads whole token rows (coalesced). The block statistic is reduced with
-// DPP inside each wave and through LDS across the 4 waves; every element is divided by
-// the scale with the correctly rounded binary32 division and rounded half-to-even.
+// DPP inside each wave and through LDS across the 4 waves. Each code is the rounding
+// (half to even) of the correctly rounded binary32 quotient x / s, taken from the
+// scale's reciprocal where that provably decides the same code and from the division
+// otherwise (the encoders in kvq_device.h).
 // uint8 codes are written in natural order ([token][channel]); int4 blocks are staged
 // in LDS and written in the matrix-core fragment order described in kvq_device.h, one
 // 16-byte store per thread.

@@ -27,7 +27,8 @@
  *   * Block: 64 tokens of one (sequence, head) row, all head_dim channels — one scale
  *     (and, for uint8, one zero point) per block.
  *   * Rounding: codes use round-half-to-even of the IEEE binary32 quotient x / s, the
- *     division correctly rounded (never a reciprocal multiply).
+ *     division correctly rounded: the kernels take the code from a reciprocal multiply
+ *     only where it provably decides the same code, and divide otherwise.
  */
 #ifndef KVQ_H
 #define KVQ_H
