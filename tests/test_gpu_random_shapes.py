@@ -1,0 +1,77 @@
+"""Seeded random shapes through the whole path, each case against the oracle: batch
+sizes up to 80 (past the 64 sequences the automatic plan pairs), 1 to 40 heads, head_dim
+64 or 128, lengths drawn over empty, one-token, block-edge and long rows, the automatic
+split plan or a caller's, every cache format. Per case: prefill bit-exact, two appends
+bit-exact, attention within 2e-3 of the oracle, split + combine bitwise the fused call,
+the workspace's arrival counters back at zero."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import (ATTN_TOL, assert_cache_equal, attn_errors, gpu_quantize, oracle_cache,
+                     say, to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+SCHEMES = (oracle.INT4_SYM, oracle.UINT8_ASYM, oracle.FP8_E4M3)
+
+
+def _case(seed):
+    rs = np.random.default_rng(1000 + seed)
+    scheme = SCHEMES[seed % 3]
+    D = (64, 128)[(seed // 3) % 2]
+    B = int(rs.choice([1, 3, 8, 33, 64, 65, 80]))
+    H = int(rs.choice([1, 2, 5, 8, 13, 40]))
+    while B * H * D > 400000:  # keep the oracle's work to seconds
+        H = max(1, H // 2)
+    MB = int(rs.integers(2, 7))
+    cap = MB * 64
+    pool = [0, 1, 63, 64, 65, 127, 128, cap - 2]
+    lens = np.where(rs.random(B) < 0.5, rs.choice(pool, B), rs.integers(0, cap - 1, B))
+    lens = np.minimum(lens, cap - 2).astype(np.int32)
+    bps = 0 if rs.random() < 0.6 else int(rs.integers(1, MB + 1))
+    if seed % 4 in (1, 2):  # the automatic plan on the larger batches
+        bps = 0
+    return rs, scheme, D, B, H, MB, lens, bps
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shape_end_to_end(seed):
+    import decode_attention_block_amd as kvq
+    import torch
+    rs, scheme, D, B, H, MB, lens, bps = _case(seed)
+    say("random shape", seed, "scheme", scheme, "D", D, "B", B, "H", H, "MB", MB, "bps", bps)
+    S = MB * 64
+    dist_v = 1.0 if scheme != oracle.UINT8_ASYM else 0.5
+    k = rs.standard_normal((B, S, H, D)).astype(np.float16)
+    v = (rs.standard_normal((B, S, H, D)) * dist_v).astype(np.float16)
+    c = gpu_quantize(scheme, k, v, lens, MB)
+    assert_cache_equal(c.host_arrays(), oracle_cache(scheme, k, v, lens, MB), lens)
+    for _ in range(2):
+        kn = np.ascontiguousarray(k[np.arange(B), lens])
+        vn = np.ascontiguousarray(v[np.arange(B), lens])
+        kvq.kv_append(c, to_gpu(kn), to_gpu(vn), int(lens.max()) + 1)
+        torch.cuda.synchronize()
+        lens = (lens + 1).astype(np.int32)
+        assert list(c.seq_lens.cpu().numpy()) == lens.tolist()
+        assert_cache_equal(c.host_arrays(), oracle_cache(scheme, k, v, lens, MB), lens)
+    q = rs.standard_normal((B, H, D)).astype(np.float16)
+    sm = float(np.float32(1) / np.sqrt(np.float32(D)))
+    L = int(lens.max())
+    qt = to_gpu(q)
+    ws = kvq.make_workspace(c, L, bps)
+    fused = torch.full_like(qt, 7.0)
+    kvq.decode_attn_qkv(c, qt, sm, fused, ws, L, bps)
+    torch.cuda.synchronize()
+    o = fused.cpu().numpy()
+    assert not ws[:4 * B * H].any()
+    ref = oracle.attention(c.host_arrays(), q, lens, sm)
+    norm_err, _ = attn_errors(o, ref)
+    print(f"random shape {seed}: normwise {norm_err:.3e}")
+    assert norm_err <= ATTN_TOL
+    assert not o[lens == 0].any()
+    split = torch.full_like(qt, 7.0)
+    kvq.decode_attn_split(c, qt, sm, ws, L, bps)
+    kvq.decode_attn_combine(c, split, ws, L, bps)
+    torch.cuda.synchronize()
+    assert np.array_equal(split.cpu().numpy(), o)
