@@ -75,3 +75,54 @@ def test_random_shape_end_to_end(seed):
     kvq.decode_attn_combine(c, split, ws, L, bps)
     torch.cuda.synchronize()
     assert np.array_equal(split.cpu().numpy(), o)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shape_grouped_query(seed):
+    """decode_attn_gqa on seeded random shapes (group 2, 4 or 8; batches up to 80; the
+    automatic plan or a caller's; every format) against the oracle's attention over the
+    cache with every cached head repeated G times (query head h * G + g reads cached head
+    h); the workspace's arrival counters back at zero."""
+    import decode_attention_block_amd as kvq
+    import torch
+    rs = np.random.default_rng(2000 + seed)
+    scheme = SCHEMES[seed % 3]
+    D = (64, 128)[(seed // 3) % 2]
+    G = int(rs.choice([2, 4, 8]))
+    B = int(rs.choice([1, 5, 8, 40, 80]))
+    H = int(rs.choice([1, 2, 3, 8]))
+    while B * H * D * G > 600000:
+        H = max(1, H // 2)
+        if B * H * D * G > 600000 and H == 1:
+            B = max(1, B // 2)
+    MB = int(rs.integers(2, 6))
+    cap = MB * 64
+    lens = np.where(rs.random(B) < 0.4, rs.choice([0, 1, 63, 64, 65, cap], B),
+                    rs.integers(0, cap + 1, B)).astype(np.int32)
+    bps = 0 if seed % 2 == 0 else int(rs.integers(1, MB + 1))
+    say("random gqa", seed, "scheme", scheme, "D", D, "G", G, "B", B, "H", H, "MB", MB, "bps", bps)
+    S = cap
+    dist_v = 1.0 if scheme != oracle.UINT8_ASYM else 0.5
+    k = rs.standard_normal((B, S, H, D)).astype(np.float16)
+    v = (rs.standard_normal((B, S, H, D)) * dist_v).astype(np.float16)
+    q = rs.standard_normal((B, H * G, D)).astype(np.float16)
+    c = gpu_quantize(scheme, k, v, lens, MB)
+    L = max(int(lens.max()), 1)
+    sm = float(np.float32(1) / np.sqrt(np.float32(D)))
+    out = torch.full((B, H * G, D), 7.0, dtype=torch.float16, device="cuda")
+    ws = kvq.make_workspace(c, L, bps, group=G)
+    kvq.decode_attn_gqa(c, to_gpu(q), G, sm, out, ws, L, bps)
+    torch.cuda.synchronize()
+    assert not ws[:4 * B * H].any()
+    o = out.cpu().numpy()
+    host = c.host_arrays()
+    rep = dict(host)
+    for key in ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero"):
+        if host.get(key) is not None:
+            rep[key] = np.ascontiguousarray(np.repeat(host[key], G, axis=1))
+    rep["H"] = H * G
+    ref = oracle.attention(rep, q, lens, sm)
+    norm_err, _ = attn_errors(o, ref)
+    print(f"random gqa {seed}: normwise {norm_err:.3e}")
+    assert norm_err <= ATTN_TOL
+    assert not o[lens == 0].any()
