@@ -126,3 +126,55 @@ def test_random_shape_grouped_query(seed):
     print(f"random gqa {seed}: normwise {norm_err:.3e}")
     assert norm_err <= ATTN_TOL
     assert not o[lens == 0].any()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shape_decode_steps(seed):
+    """decode_step_qkv on seeded random shapes, dense or paged (a shuffled page pool 1.5
+    times the blocks), one launch (the rows fill the GPU) or two: three steps, after each
+    the lengths and the whole cache bit-exact against the oracle's quantization of the
+    history and the output within 2e-3 of the oracle's attention over the new length."""
+    import decode_attention_block_amd as kvq
+    import torch
+    rs = np.random.default_rng(3000 + seed)
+    scheme = SCHEMES[seed % 3]
+    D = (64, 128)[(seed // 3) % 2]
+    B, H = [(8, 32), (3, 5), (20, 13), (1, 40), (70, 4), (6, 7)][seed]
+    paged = seed % 2 == 1
+    MB = int(rs.integers(2, 5))
+    cap = MB * 64
+    lens = np.where(rs.random(B) < 0.4, rs.choice([0, 1, 63, 64, 65], B),
+                    rs.integers(0, cap - 3, B))
+    lens = np.minimum(lens, cap - 3).astype(np.int32)
+    say("random steps", seed, "scheme", scheme, "D", D, "B", B, "H", H, "MB", MB,
+        "paged", paged, "launches", "1" if B * H >= 256 else "2")
+    S = cap
+    dist_v = 1.0 if scheme != oracle.UINT8_ASYM else 0.5
+    k = rs.standard_normal((B, S, H, D)).astype(np.float16)
+    v = (rs.standard_normal((B, S, H, D)) * dist_v).astype(np.float16)
+    if paged:
+        n_pages = (3 * B * MB) // 2
+        c = kvq.KVCache(scheme, B, H, D, MB, num_pages=n_pages)
+        perm = rs.permutation(n_pages)[: B * MB].astype(np.int32)
+        c.block_table.copy_(torch.from_numpy(perm.reshape(B, MB)))
+    else:
+        c = kvq.KVCache(scheme, B, H, D, MB)
+    c.seq_lens.copy_(torch.from_numpy(lens))
+    kvq.kv_quantize_blocks(c, to_gpu(k), to_gpu(v), max(int(lens.max()), 1))
+    torch.cuda.synchronize()
+    sm = float(np.float32(1) / np.sqrt(np.float32(D)))
+    for step in range(3):
+        after = int(lens.max()) + 1
+        kn = to_gpu(np.ascontiguousarray(k[np.arange(B), lens]))
+        vn = to_gpu(np.ascontiguousarray(v[np.arange(B), lens]))
+        q = rs.standard_normal((B, H, D)).astype(np.float16)
+        out = torch.full((B, H, D), 7.0, dtype=torch.float16, device="cuda")
+        kvq.decode_step_qkv(c, kn, vn, to_gpu(q), sm, out, kvq.make_workspace(c, after), after)
+        torch.cuda.synchronize()
+        lens = (lens + 1).astype(np.int32)
+        assert list(c.seq_lens.cpu().numpy()) == lens.tolist()
+        host = c.host_arrays()
+        assert_cache_equal(host, oracle_cache(scheme, k, v, lens, MB), lens)
+        norm_err, _ = attn_errors(out.cpu().numpy(), oracle.attention(host, q, lens, sm))
+        print(f"random steps {seed} step {step}: normwise {norm_err:.3e}")
+        assert norm_err <= ATTN_TOL
