@@ -210,8 +210,10 @@ __device__ __forceinline__ uint2 pack_fp8x8(const T (&x)[8], const Divisor& d) {
   return fp8_codes8(q);
 }
 
-// The int4 and uint8 packers below code 8 values with the multiply and take one branch,
-// for all 8, in the rare case that one of them needs the division.
+// The packers below code 8 values with the multiply. The int4 packer takes one branch,
+// for all 8, in the rare case that one of them needs the division; the uint8 and FP8
+// packers, whose quotients sit near a boundary far more often, divide each such value
+// on its own.
 
 // 8 values -> 4 bytes of int4 nibbles c + 8 (x[i] in bits 4i .. 4i+3; for 8 consecutive
 // channels: channel 2k in the low nibble of byte k).
